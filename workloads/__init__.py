@@ -1,0 +1,32 @@
+"""Seeded synthetic workloads for the greedy speculative-decoding verify step.
+
+This package holds only input generation: the model shapes of the five
+workloads, seeded weight / KV-cache / context-length / draft-randomness
+generators, and the byte accounting used to price a step.  It contains none
+of the verify step's arithmetic; both the HIP library's callers and the CPU
+oracle's callers draw their inputs from here.
+"""
+from .configs import CONFIGS, VerifyConfig, get_config, scaled
+from .synth import (
+    capacity_for,
+    context_lengths,
+    draft_randomness,
+    kv_cache,
+    make_weights,
+    committed_tokens,
+    tensor_seed,
+)
+
+__all__ = [
+    "CONFIGS",
+    "VerifyConfig",
+    "get_config",
+    "scaled",
+    "capacity_for",
+    "context_lengths",
+    "draft_randomness",
+    "kv_cache",
+    "make_weights",
+    "committed_tokens",
+    "tensor_seed",
+]

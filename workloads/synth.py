@@ -1,0 +1,191 @@
+"""Seeded synthetic inputs: weights, KV cache, context lengths, draft randomness.
+
+Every tensor has its own seed, derived from the workload seed and the tensor's
+name, so any one of them can be regenerated alone.  Generation uses torch on
+the requested device; values drawn on different devices differ, so a test that
+feeds both the GPU library and the CPU oracle draws once and copies.
+
+Distributions (the pages train real weights; these stand in for them):
+  * every linear weight and the embedding: N(0, 0.02^2); norm gains 1
+    (or 1 + N(0, norm_gain_std^2) for tests that need distinct gains);
+  * bf16 storage: fp32 samples rounded to nearest-even bf16;
+  * fp8 storage: one scale per output row, s = max|w| / 448, codes
+    e4m3fn(round-to-nearest-even(w / s)), clamped to +-448;
+  * cached keys/values before the step: N(0, (0.02 sqrt(H))^2), the spread a
+    unit-RMS input gives through an N(0, 0.02^2) projection, in cache storage;
+  * context lengths: fixed, uniform integer, or log-uniform (rounded);
+  * drafts: per position a Bernoulli coin with the workload's match
+    probability and a uniform token used when the coin says "no match".
+"""
+from __future__ import annotations
+
+import math
+import zlib
+
+import torch
+
+from .configs import VerifyConfig
+
+_TORCH_DT = {"f32": torch.float32, "bf16": torch.bfloat16}
+
+
+def tensor_seed(base: int, name: str) -> int:
+    return (zlib.crc32(name.encode()) ^ (base * 0x9E3779B1)) & 0x7FFFFFFF
+
+
+def _gen(device, base: int, name: str) -> torch.Generator:
+    g = torch.Generator(device=device)
+    g.manual_seed(tensor_seed(base, name))
+    return g
+
+
+def _normal(shape, std, device, base, name) -> torch.Tensor:
+    g = _gen(device, base, name)
+    return torch.randn(*shape, generator=g, device=device, dtype=torch.float32) * std
+
+
+def _quant_e4m3_rows(w: torch.Tensor):
+    """Per-output-row e4m3fn codes (uint8) and fp32 scales."""
+    s = w.abs().amax(dim=-1, keepdim=True) / 448.0
+    s = torch.where(s > 0, s, torch.ones_like(s))
+    q = (w / s).clamp(-448.0, 448.0).to(torch.float8_e4m3fn)
+    return q.view(torch.uint8), s.squeeze(-1).to(torch.float32)
+
+
+def _linear(cfg: VerifyConfig, shape, device, name):
+    """A linear weight of the given shape in the workload's storage format.
+    Returns (tensor, per-row scale or None)."""
+    w = _normal(shape, cfg.weight_std, device, cfg.seed, name)
+    if cfg.wdtype == "fp8":
+        return _quant_e4m3_rows(w)
+    return w.to(_TORCH_DT[cfg.wdtype]), None
+
+
+def _gain(cfg: VerifyConfig, n, device, name):
+    if cfg.norm_gain_std == 0.0:
+        return torch.ones(n, dtype=torch.float32, device=device)
+    return 1.0 + _normal((n,), cfg.norm_gain_std, device, cfg.seed, name)
+
+
+def make_weights(cfg: VerifyConfig, device="cpu") -> dict:
+    """All weights of the target decoder, row-major [out][in] per matrix.
+
+    Keys: embed [V][H]; final_norm [H]; lm_head [V][H] (+ lm_scale [V] for
+    fp8); layers: list of dicts with attn_norm [H], w_qkv [(n_q+2n_kv)D][H],
+    w_o [H][n_q D], ffn_norm [H] and either (MoE) w_router [E][H],
+    w_gate_up [E][2I][H], w_down [E][H][I], w_sh_gate_up [S][2I][H],
+    w_sh_down [S][H][I], or (dense) w_gate_up [2I][H], w_down [H][I].  Each
+    matrix `w_x` stored in fp8 has a companion `s_x` of per-row scales.
+    """
+    H, D = cfg.hidden, cfg.head_dim
+    out = {}
+    emb = _normal((cfg.vocab, H), cfg.weight_std, device, cfg.seed, "embed")
+    out["embed"] = emb.to(_TORCH_DT[cfg.embdtype])
+    del emb
+    layers = []
+    for l in range(cfg.n_layers):
+        p = f"layer{l}."
+        L = {"attn_norm": _gain(cfg, H, device, p + "attn_norm"),
+             "ffn_norm": _gain(cfg, H, device, p + "ffn_norm")}
+        L["w_qkv"], L["s_qkv"] = _linear(cfg, (cfg.qkv_dim, H), device, p + "w_qkv")
+        L["w_o"], L["s_o"] = _linear(cfg, (H, cfg.n_q * D), device, p + "w_o")
+        if cfg.ffn == "moe":
+            E, I, S = cfg.n_experts, cfg.expert_inter, cfg.n_shared
+            L["w_router"], L["s_router"] = _linear(cfg, (E, H), device, p + "w_router")
+            L["w_gate_up"], L["s_gate_up"] = _linear(cfg, (E, 2 * I, H), device, p + "w_gate_up")
+            L["w_down"], L["s_down"] = _linear(cfg, (E, H, I), device, p + "w_down")
+            L["w_sh_gate_up"], L["s_sh_gate_up"] = _linear(cfg, (S, 2 * I, H), device,
+                                                          p + "w_sh_gate_up")
+            L["w_sh_down"], L["s_sh_down"] = _linear(cfg, (S, H, I), device, p + "w_sh_down")
+        else:
+            I = cfg.dense_inter
+            L["w_gate_up"], L["s_gate_up"] = _linear(cfg, (2 * I, H), device, p + "w_gate_up")
+            L["w_down"], L["s_down"] = _linear(cfg, (H, I), device, p + "w_down")
+        layers.append(L)
+    out["layers"] = layers
+    out["final_norm"] = _gain(cfg, H, device, "final_norm")
+    out["lm_head"], out["lm_scale"] = _linear(cfg, (cfg.vocab, H), device, "lm_head")
+    return out
+
+
+def capacity_for(cfg: VerifyConfig) -> int:
+    """Cache slots per (sequence, layer, KV head): the largest starting
+    context plus every position the workload's steps can add, rounded up to a
+    multiple of 64."""
+    kind = cfg.ctx[0]
+    hi = cfg.ctx[1] if kind == "fixed" else cfg.ctx[2]
+    need = hi + cfg.steps * (cfg.k_draft + 1)
+    return (need + 63) // 64 * 64
+
+
+def context_lengths(cfg: VerifyConfig) -> torch.Tensor:
+    """Starting context length of every sequence (int32, CPU)."""
+    g = _gen("cpu", cfg.seed, "ctx_lens")
+    B = cfg.batch
+    kind = cfg.ctx[0]
+    if kind == "fixed":
+        return torch.full((B,), cfg.ctx[1], dtype=torch.int32)
+    if kind == "uniform":
+        lo, hi = cfg.ctx[1], cfg.ctx[2]
+        return torch.randint(lo, hi + 1, (B,), generator=g, dtype=torch.int64).to(torch.int32)
+    if kind == "loguniform":
+        lo, hi = cfg.ctx[1], cfg.ctx[2]
+        u = torch.rand(B, generator=g, dtype=torch.float64)
+        v = torch.exp(math.log(lo) + u * (math.log(hi) - math.log(lo)))
+        return torch.round(v).clamp(lo, hi).to(torch.int32)
+    raise ValueError(kind)
+
+
+def committed_tokens(cfg: VerifyConfig) -> torch.Tensor:
+    """The last committed token of every sequence (int32, CPU)."""
+    g = _gen("cpu", cfg.seed, "committed")
+    return torch.randint(0, cfg.vocab, (cfg.batch,), generator=g, dtype=torch.int64).to(torch.int32)
+
+
+def match_probabilities(cfg: VerifyConfig) -> torch.Tensor:
+    """Per-(sequence, draft position) probability that the draft equals the
+    target's greedy token, float64 [B][K]."""
+    B, K = cfg.batch, cfg.k_draft
+    kind = cfg.draft_p[0]
+    if kind == "const":
+        return torch.full((B, K), float(cfg.draft_p[1]), dtype=torch.float64)
+    if kind == "per_seq_uniform":
+        g = _gen("cpu", cfg.seed, "draft_p_seq")
+        lo, hi = cfg.draft_p[1], cfg.draft_p[2]
+        p = lo + (hi - lo) * torch.rand(B, 1, generator=g, dtype=torch.float64)
+        return p.expand(B, K).clone()
+    if kind == "decay":
+        p0, r = cfg.draft_p[1], cfg.draft_p[2]
+        p = torch.tensor([p0 * r ** i for i in range(K)], dtype=torch.float64)
+        return p.expand(B, K).clone()
+    raise ValueError(kind)
+
+
+def draft_randomness(cfg: VerifyConfig, steps: int | None = None):
+    """Coins (uint8 [S][B][K]: 1 = the draft copies the target's greedy token)
+    and fallback tokens (int32 [S][B][K], uniform over the vocabulary)."""
+    S = cfg.steps if steps is None else steps
+    B, K = cfg.batch, cfg.k_draft
+    p = match_probabilities(cfg)
+    g = _gen("cpu", cfg.seed, "draft_coins")
+    u = torch.rand(S, B, K, generator=g, dtype=torch.float64)
+    coins = (u < p.unsqueeze(0)).to(torch.uint8)
+    g2 = _gen("cpu", cfg.seed, "draft_tokens")
+    toks = torch.randint(0, cfg.vocab, (S, B, K), generator=g2, dtype=torch.int64).to(torch.int32)
+    return coins, toks
+
+
+def kv_cache(cfg: VerifyConfig, device="cpu", capacity: int | None = None):
+    """Key and value caches before the step, natural layout
+    [B][L][n_kv][capacity][D] in the cache storage type."""
+    cap = capacity_for(cfg) if capacity is None else capacity
+    shape = (cfg.batch, cfg.n_layers, cfg.n_kv, cap, cfg.head_dim)
+    std = cfg.weight_std * math.sqrt(cfg.hidden)
+    dt = _TORCH_DT[cfg.kvdtype]
+    out = []
+    for name in ("k_cache", "v_cache"):
+        t = torch.empty(shape, dtype=dt, device=device)
+        for b in range(cfg.batch):   # per sequence keeps the fp32 temporary small
+            t[b] = _normal(shape[1:], std, device, cfg.seed, f"{name}.{b}").to(dt)
+        out.append(t)
+    return out[0], out[1]
