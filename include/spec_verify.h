@@ -1,0 +1,249 @@
+/*
+ * spec_verify.h -- C ABI of the MI355X (gfx950) greedy speculative-decoding
+ * verify step.
+ *
+ * One call runs the target decoder over the K+1 positions of every sequence
+ * of a batch (the last committed token plus K draft tokens) against the
+ * sequence's KV cache, takes the target's greedy token at every position,
+ * keeps the longest prefix of drafts that agrees with them plus one token of
+ * the target's own, and commits the new context length.
+ *
+ * Where the operation is defined:
+ *   - Jina-OCR-v1 paper, abstract and section 3: a DeepSeekMoE decoder
+ *     verifies K=3 drafts; greedy verification is lossless.
+ *   - jina-ocr-v1 tweet digest, FastMTP paragraph: greedy verification keeps
+ *     the longest matching prefix and the output equals ordinary greedy
+ *     autoregressive decoding; 64 routed + 2 shared experts, top-6 routing.
+ *   - Jina-OCR-v1 release article, L4 paragraph: tokens per verify counts the
+ *     bonus token that verification brings out.
+ *   - "Architecture and acceleration of an end-to-end OCR expert model",
+ *     section 6.1 (verification is one teacher-forced parallel forward; accept
+ *     left to right up to the first disagreement, where the target supplies
+ *     the token) and section 7 (the draft / verify / accept loop).
+ * The pages give no layer-level formulas; the decoder layer is the plain
+ * pre-norm block: RMSNorm (eps from the config), rotary embedding with
+ * rotate-half pairing (i, i + D/2) and angle pos * theta^(-2i/D), causal
+ * softmax attention with scale 1/sqrt(D) where query head h reads KV head
+ * floor(h * n_kv / n_q), residual add, RMSNorm, then a top-k softmax-routed
+ * SwiGLU mixture of experts (gate = the selected softmax probability) plus
+ * always-on shared experts, or a dense SwiGLU, residual add.  A final RMSNorm,
+ * the LM head and an argmax (lowest index on ties, compared in fp32) give the
+ * greedy token.
+ *
+ * Conventions for every entry point:
+ *   - All tensor pointers are DEVICE pointers owned by the caller and only
+ *     borrowed for the duration of the call, except where "host" is written.
+ *   - Work is enqueued on the given HIP stream (NULL = the default stream) and
+ *     the call returns before the GPU finishes; outputs are valid once the
+ *     caller has synchronised that stream.  No entry point synchronises the
+ *     device except spec_verify_error_word and spec_verify_kernel_time.
+ *   - Return value: SV_OK (0) or a negative status (see below); no exception
+ *     or abort crosses the ABI.  Problems only the device can see (a token id
+ *     outside the vocabulary, a context that does not leave room for K+1 new
+ *     positions, a NaN logit) are reported per sequence -- accepted_len and
+ *     next_tok are set to -1 and ctx_lens_out = ctx_lens_in -- and in a sticky
+ *     error word read with spec_verify_error_word.
+ *   - Calls that share one context must not overlap in time (they share its
+ *     workspace); distinct contexts are independent.
+ *
+ * Storage formats:
+ *   SV_F32   IEEE binary32.
+ *   SV_BF16  bfloat16 (the upper 16 bits of a binary32).
+ *   SV_FP8   OCP 8-bit float E4M3FN (bias 7, max 448, no infinities), with one
+ *            fp32 scale per output row of every matrix: W[n][k] = code * s[n].
+ * Supported combinations: weights, embedding, activations and KV cache all
+ * SV_F32; or weights SV_BF16 or SV_FP8 with embedding and KV cache SV_BF16
+ * (activations bf16, accumulation fp32).
+ *
+ * Weight layouts (row-major, [out][in] per matrix, contiguous):
+ *   embed        [V][H]                       embedding storage type
+ *   attn_norm, ffn_norm, final_norm  [H]     fp32 gains
+ *   w_qkv        [(n_q + 2 n_kv) D][H]        q rows, then k rows, then v rows
+ *   w_o          [H][n_q D]
+ *   MoE:  w_router [E][H], w_gate_up [E][2I][H] (rows 0..I-1 gate, I..2I-1 up),
+ *         w_down [E][H][I], w_sh_gate_up [S][2I][H], w_sh_down [S][H][I]
+ *   dense: w_gate_up [2 I_d][H], w_down [H][I_d]
+ *   lm_head      [V][H]
+ *   fp8 scales: s_x has one fp32 per row of w_x, laid out like w_x without
+ *   its last dimension (e.g. s_gate_up [E][2I]).
+ *
+ * KV-cache layout (storage = kv dtype), capacity slots per (sequence, layer,
+ * KV head), sequence b occupying one contiguous region:
+ *   K cache: [B_max][L][n_kv][capacity][D]   (position-major)
+ *   V cache: [B_max][L][n_kv][D][capacity]   (channel-major: transposed)
+ * Positions 0 .. ctx_lens_in[b]-1 hold the cached context.  The step writes
+ * positions ctx .. ctx+K; after the commit, slots at or past ctx_lens_out[b]
+ * are dead and will be overwritten by the next step (rollback is by length).
+ */
+#ifndef SPEC_VERIFY_H
+#define SPEC_VERIFY_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define SPEC_VERIFY_ABI_VERSION 1
+
+/* status codes */
+#define SV_OK 0
+#define SV_ERR_INVALID_ARG (-1)   /* null pointer, bad size, batch out of range */
+#define SV_ERR_UNSUPPORTED (-2)   /* shape or dtype combination not supported */
+#define SV_ERR_HIP (-3)           /* a HIP runtime call failed (message kept) */
+#define SV_ERR_NO_DEVICE (-4)     /* no usable gfx950 device */
+#define SV_ERR_NOT_SET (-5)       /* requested data was never produced */
+
+/* storage types */
+#define SV_F32 0
+#define SV_BF16 1
+#define SV_FP8 2
+
+/* feed-forward kinds */
+#define SV_FFN_MOE 0
+#define SV_FFN_DENSE 1
+
+/* bits of the sticky device error word and of per-sequence errors */
+#define SV_DEV_BAD_TOKEN 1u       /* a committed or draft token outside [0, V) */
+#define SV_DEV_CAPACITY 2u        /* ctx < 0 or ctx + K + 1 > capacity */
+#define SV_DEV_NAN_LOGIT 4u       /* a NaN among a position's logits */
+
+/* kernel classes for spec_verify_kernel_time */
+#define SV_KC_LM_HEAD 0           /* final norm output x LM head + argmax partials */
+#define SV_KC_ATTENTION 1         /* split-KV verify attention (not the merge) */
+#define SV_KC_EXPERT_GATE_UP 2    /* grouped expert gate/up + SwiGLU (MoE) or dense gate/up */
+#define SV_KC_EXPERT_DOWN 3       /* grouped expert down projection (MoE) or dense down */
+#define SV_KC_QKV 4               /* QKV projection */
+#define SV_KC_COUNT 5
+
+typedef struct spec_verify_ctx spec_verify_ctx;   /* opaque; owns only its workspace */
+
+typedef struct {
+    int n_layers;       /* L >= 1 */
+    int hidden;         /* H, multiple of 64 */
+    int n_q_heads;      /* n_q */
+    int n_kv_heads;     /* n_kv, divides n_q */
+    int head_dim;       /* D: 64 or 128 */
+    int ffn_kind;       /* SV_FFN_MOE or SV_FFN_DENSE */
+    int n_experts;      /* E (MoE), multiple of 4, <= 256 */
+    int expert_inter;   /* I (MoE), multiple of 64 */
+    int top_k;          /* k (MoE), 1 <= k <= min(E, 8) */
+    int n_shared;       /* shared experts (MoE), >= 0 */
+    int renorm_topk;    /* 1: gates renormalised to sum 1 over the selected experts */
+    int dense_inter;    /* I_d (dense), multiple of 64 */
+    int vocab;          /* V, multiple of 16 */
+    int max_batch;      /* B_max: largest batch a step may be called with */
+    int k_draft;        /* K >= 1 drafts per sequence */
+    int kv_capacity;    /* slots per (sequence, layer, KV head), multiple of 64 */
+    float rope_theta;   /* rotary base */
+    float rms_eps;      /* RMSNorm epsilon */
+    int weight_dtype;   /* SV_F32 / SV_BF16 / SV_FP8 */
+    int embed_dtype;    /* SV_F32 / SV_BF16 */
+    int kv_dtype;       /* SV_F32 / SV_BF16 */
+} spec_verify_config;
+
+typedef struct {
+    const float* attn_norm;
+    const void* w_qkv;        const float* s_qkv;
+    const void* w_o;          const float* s_o;
+    const float* ffn_norm;
+    const void* w_router;     const float* s_router;
+    const void* w_gate_up;    const float* s_gate_up;
+    const void* w_down;       const float* s_down;
+    const void* w_sh_gate_up; const float* s_sh_gate_up;
+    const void* w_sh_down;    const float* s_sh_down;
+} spec_verify_layer;          /* s_* are used only for SV_FP8 weights (NULL otherwise) */
+
+typedef struct {
+    const void* embed;
+    const spec_verify_layer* layers;   /* HOST array of n_layers entries */
+    const float* final_norm;
+    const void* lm_head;
+    const float* lm_scale;             /* SV_FP8 only */
+} spec_verify_weights;
+
+/* Validate `cfg` (host), pick the kernel plan, allocate the workspace for
+ * max_batch sequences and upload the rotary table (cos/sin of pos *
+ * theta^(-2i/D), computed in double on the host, stored fp32) for positions
+ * 0 .. kv_capacity-1.  *out receives the context.  Uses the current HIP
+ * device. */
+int spec_verify_init(const spec_verify_config* cfg, spec_verify_ctx** out);
+
+/* Free the workspace.  NULL is allowed. */
+void spec_verify_destroy(spec_verify_ctx* ctx);
+
+/*
+ * One verify step for sequences 0 .. batch-1 (1 <= batch <= max_batch).
+ *   committed_tok [batch]       int32, the last committed token of each sequence
+ *   draft_toks    [batch][K]    int32 drafts
+ *   ctx_lens_in   [batch]       int32 tokens already cached
+ *   ctx_lens_out  [batch]       int32 <- ctx_lens_in + accepted_len + 1 (may alias
+ *                               ctx_lens_in)
+ *   accepted_len  [batch]       int32 <- drafts kept, 0..K
+ *   next_tok      [batch]       int32 <- the target's token after the kept drafts
+ *                               (the bonus); the caller feeds it back as the next
+ *                               committed token
+ *   k_cache, v_cache            the caches (layout above); positions ctx..ctx+K of
+ *                               every layer are written
+ * The step reads and updates context lengths on the device only, so it needs no
+ * host synchronisation and may be captured into a HIP graph.
+ */
+int spec_verify_step(spec_verify_ctx* ctx, const spec_verify_weights* w, void* k_cache,
+                     void* v_cache, const int32_t* committed_tok, const int32_t* draft_toks,
+                     const int32_t* ctx_lens_in, int32_t* ctx_lens_out, int batch,
+                     int32_t* accepted_len, int32_t* next_tok, void* stream);
+
+/*
+ * Debug outputs for the following steps (any pointer may be NULL; all NULL
+ * turns them off).  logits [batch][K+1][V] fp32 (scaled logits of every
+ * verified position), hidden [L][batch (K+1)][H] fp32 (residual stream after
+ * each layer), target_tok [batch][K+1] int32 (greedy token of every position),
+ * routing [L][batch (K+1)][top_k] int32 (MoE only: the experts each position
+ * was routed to, in rank order).  Writing logits costs an extra pass of
+ * V*T*4 bytes.
+ */
+int spec_verify_set_debug(spec_verify_ctx* ctx, float* logits, float* hidden,
+                          int32_t* target_tok, int32_t* routing);
+
+/*
+ * Acceptance and commit alone, from given fp32 logits [batch][K+1][V]
+ * (device): argmax per position (lowest index on ties, NaN -> error) and the
+ * same acceptance / commit as spec_verify_step.  target_tok may be NULL.
+ */
+int spec_verify_accept_from_logits(spec_verify_ctx* ctx, const float* logits,
+                                   const int32_t* draft_toks, const int32_t* ctx_lens_in,
+                                   int32_t* ctx_lens_out, int batch, int32_t* accepted_len,
+                                   int32_t* next_tok, int32_t* target_tok, void* stream);
+
+/* Read (host) the sticky device error word (SV_DEV_* bits) accumulated since
+ * the last clear; synchronises `stream` first.  clear != 0 resets it. */
+int spec_verify_error_word(spec_verify_ctx* ctx, uint32_t* out, int clear, void* stream);
+
+/*
+ * Kernel timing with HIP events on the launch stream.  enable = 1 starts
+ * recording events around every launch of class `kclass` (SV_KC_*) and resets
+ * the totals, enable = 0 stops recording, any other value leaves the state
+ * as it is.  With out pointers given (before the state changes), synchronises
+ * the recorded events and returns (host) the summed duration in milliseconds
+ * and the number of launches timed since the last reset.  At most 8192
+ * launches are recorded per reset.
+ */
+int spec_verify_kernel_time(spec_verify_ctx* ctx, int kclass, int enable, double* total_ms,
+                            int* launches);
+
+/* Copy (host) the message of the most recent failed call in this process
+ * (validation or HIP error) into buf, NUL-terminated and truncated to len
+ * bytes; returns its full length. */
+int spec_verify_last_error(char* buf, int len);
+
+/* Static description of a status code. */
+const char* spec_verify_status_string(int status);
+
+/* SPEC_VERIFY_ABI_VERSION of the built library. */
+int spec_verify_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SPEC_VERIFY_H */

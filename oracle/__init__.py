@@ -60,6 +60,10 @@ class _Layer(ctypes.Structure):
                 ("w_dense_down", _Mat)]
 
 
+class _RouteIO(ctypes.Structure):
+    _fields_ = [("force", c_void_p), ("sel_out", c_void_p), ("rlogits_out", c_void_p)]
+
+
 class _Weights(ctypes.Structure):
     _fields_ = [("embed", c_void_p), ("layers", POINTER(_Layer)), ("final_norm", c_void_p),
                 ("lm_head", _Mat)]
@@ -75,7 +79,7 @@ def _load():
             build(force=False)
         lib = ctypes.CDLL(_LIB)
         P = c_void_p
-        lib.or_verify_step.argtypes = [P, P, P, P, c_int, P, P, P, P, P, P, P, P, P, P, P]
+        lib.or_verify_step.argtypes = [P, P, P, P, c_int, P, P, P, P, P, P, P, P, P, P, P, P]
         lib.or_verify_step.restype = None
         lib.or_decode_one.argtypes = [P, P, P, P, c_long, c_long, c_int, P, P]
         lib.or_decode_one.restype = c_int
@@ -95,7 +99,7 @@ def _load():
         lib.or_topk.argtypes = [P, c_int, c_int, P]
         lib.or_silu.argtypes = [c_double]
         lib.or_silu.restype = c_double
-        lib.or_ffn.argtypes = [P, P, P, P, P]
+        lib.or_ffn.argtypes = [P, P, P, P, P, P, P]
         lib.or_argmax.argtypes = [P, c_long]
         lib.or_argmax.restype = c_int
         lib.or_accept.argtypes = [c_int, P, P, P, P]
@@ -196,8 +200,12 @@ class Oracle:
         return np.array(as_np(k_cache), copy=True), np.array(as_np(v_cache), copy=True)
 
     def verify_step(self, k_cache: np.ndarray, v_cache: np.ndarray, committed, drafts, ctx_in,
-                    want_logits=False, want_hidden=False, want_layer_hidden=False) -> dict:
-        """One verify step; caches (numpy, natural layout) are updated in place."""
+                    want_logits=False, want_hidden=False, want_layer_hidden=False,
+                    force_sel=None, want_routing=False) -> dict:
+        """One verify step; caches (numpy, natural layout) are updated in place.
+        force_sel [B][L][K+1][top_k] replaces the experts' top-k choice (test
+        hook); want_routing returns the selections used ("sel") and the
+        router logits ("router_logits")."""
         cfg = self.cfg
         K = cfg.k_draft
         com = np.ascontiguousarray(as_np(committed), dtype=np.int32).reshape(-1)
@@ -210,11 +218,26 @@ class Oracle:
         hidden = np.zeros((B, K + 1, cfg.hidden)) if want_hidden else None
         lh = np.zeros((B, cfg.n_layers, K + 1, cfg.hidden)) if want_layer_hidden else None
         self._check_kv(k_cache, v_cache, B)
+        rio = _RouteIO()
+        moe = cfg.ffn == "moe"
+        fs = sel = rl = None
+        if moe and force_sel is not None:
+            fs = np.ascontiguousarray(force_sel, dtype=np.int32).reshape(
+                B, cfg.n_layers, K + 1, cfg.top_k)
+            if fs.min() < 0 or fs.max() >= cfg.n_experts:
+                raise ValueError("forced expert out of range")
+            rio.force = _ptr(fs)
+        if moe and want_routing:
+            sel = np.zeros((B, cfg.n_layers, K + 1, cfg.top_k), np.int32)
+            rl = np.zeros((B, cfg.n_layers, K + 1, cfg.n_experts))
+            rio.sel_out, rio.rlogits_out = _ptr(sel), _ptr(rl)
         _load().or_verify_step(ctypes.byref(self._c), ctypes.byref(self._w), _ptr(k_cache),
                                _ptr(v_cache), B, _ptr(com), _ptr(dr), _ptr(ci),
                                _ptr(out["ctx_out"]), _ptr(out["accepted"]),
                                _ptr(out["next_tok"]), _ptr(out["status"]), _ptr(out["target"]),
-                               _ptr(logits), _ptr(hidden), _ptr(lh))
+                               _ptr(logits), _ptr(hidden), _ptr(lh), ctypes.byref(rio))
+        if sel is not None:
+            out["sel"], out["router_logits"] = sel, rl
         if want_logits:
             out["logits"] = logits
         if want_hidden:
@@ -345,5 +368,5 @@ def ffn(orc: Oracle, layer: int, h):
     k = max(orc.cfg.top_k, 1)
     sel = np.zeros(k, np.int32)
     lay = ctypes.byref(orc._layers[layer])
-    _load().or_ffn(ctypes.byref(orc._c), lay, _ptr(h), _ptr(y), _ptr(sel))
+    _load().or_ffn(ctypes.byref(orc._c), lay, _ptr(h), _ptr(y), None, _ptr(sel), None)
     return y, (sel if orc.cfg.ffn == "moe" else None)

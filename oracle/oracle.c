@@ -181,7 +181,10 @@ void or_matvec(const void* W, const float* scale, int dtype, long row0, int N, i
         } break;
         default: {
             const uint8_t* w = (const uint8_t*)W + base;
-            for (k = 0; k < K; k++) acc += or_e4m3_to_double(w[k]) * x[k];
+            double tab[256];
+            int c;
+            for (c = 0; c < 256; c++) tab[c] = or_e4m3_to_double((uint8_t)c);
+            for (k = 0; k < K; k++) acc += tab[w[k]] * x[k];
             acc *= (double)scale[row0 + n];
         } break;
         }
@@ -287,8 +290,11 @@ void or_swiglu(const or_mat* gu, long gu_row0, const or_mat* dn, long dn_row0, i
  * (softmax over all E router logits, top-k on the probabilities, gates are
  * the selected probabilities, optionally renormalised to sum 1) in rank
  * order, then the shared experts in index order; or a dense SwiGLU.
- * `sel` (optional, [top_k]) receives the selected experts. */
-void or_ffn(const or_config* c, const or_layer* L, const double* h, double* y, int* sel)
+ * Test hooks (each optional): `force` [top_k] replaces the top-k choice by
+ * the given experts (gates stay this function's own probabilities), `sel`
+ * [top_k] receives the experts used, `rlogits` [E] the router logits. */
+void or_ffn(const or_config* c, const or_layer* L, const double* h, double* y, const int* force,
+            int* sel, double* rlogits)
 {
     int H = c->hidden, i, r;
     if (c->ffn_kind == OR_FFN_DENSE) {
@@ -308,7 +314,9 @@ void or_ffn(const or_config* c, const or_layer* L, const double* h, double* y, i
         double gsum = 0.0;
         or_matvec(L->w_router.data, L->w_router.scale, c->wdtype, 0, E, H, h, logit);
         or_softmax(logit, E, prob);
-        or_topk(prob, E, k, idx);
+        if (force) for (r = 0; r < k; r++) idx[r] = force[r];
+        else or_topk(prob, E, k, idx);
+        if (rlogits) for (i = 0; i < E; i++) rlogits[i] = logit[i];
         for (r = 0; r < k; r++) gsum += prob[idx[r]];
         for (i = 0; i < H; i++) y[i] = 0.0;
         for (r = 0; r < k; r++) {
@@ -363,6 +371,16 @@ static size_t kv_off(const or_config* c, long b, int l, int h, long pos)
            (size_t)c->head_dim;
 }
 
+/* Test hooks on the expert routing of one verify step (all optional):
+ * force [B][L][K+1][top_k] selections to use instead of the top-k choice,
+ * sel_out [B][L][K+1][top_k] the selections used, rlogits_out
+ * [B][L][K+1][E] the router logits. */
+typedef struct {
+    const int* force;
+    int* sel_out;
+    double* rlogits_out;
+} or_route_io;
+
 /* Embedding row of token t, widened. */
 static void embed_row(const or_config* c, const or_weights* w, int t, double* x)
 {
@@ -388,7 +406,8 @@ static void lm_logits(const or_config* c, const or_weights* w, const double* x, 
  * (optional, [L][n][H]) receives it after each layer.
  */
 static void forward_block(const or_config* c, const or_weights* w, void* kc, void* vc, long b,
-                          long ctx, int n, const int* tok, double* x, double* layer_hidden)
+                          long ctx, int n, const int* tok, double* x, double* layer_hidden,
+                          const or_route_io* rio)
 {
     int H = c->hidden, D = c->head_dim, nq = c->n_q, nkv = c->n_kv;
     int QKV = (nq + 2 * nkv) * D;
@@ -436,7 +455,14 @@ static void forward_block(const or_config* c, const or_weights* w, void* kc, voi
             or_matvec(L->w_o.data, L->w_o.scale, c->wdtype, 0, H, nq * D, att, o);
             for (i = 0; i < H; i++) xj[i] += o[i];
             or_rmsnorm(xj, L->ffn_norm, H, c->rms_eps, h);
-            or_ffn(c, L, h, o, NULL);
+            {
+                size_t rs = ((size_t)l * n + j) * (size_t)c->top_k;   /* this (layer, position) */
+                or_ffn(c, L, h, o, rio && rio->force ? rio->force + rs : NULL,
+                       rio && rio->sel_out ? rio->sel_out + rs : NULL,
+                       rio && rio->rlogits_out
+                           ? rio->rlogits_out + ((size_t)l * n + j) * (size_t)c->n_experts
+                           : NULL);
+            }
             for (i = 0; i < H; i++) xj[i] += o[i];
         }
         if (layer_hidden)
@@ -452,13 +478,13 @@ static void forward_block(const or_config* c, const or_weights* w, void* kc, voi
  * accepted + 1, status[b] (0 or OR_* bits; on error accepted = next = -1 and
  * ctx_out = ctx_in).  Optional outputs (NULL to skip): target[b][K+1] greedy
  * tokens, logits[b][K+1][V], hidden[b][K+1][H] (residual after the last
- * layer), layer_hidden[b][L][K+1][H].  The caches are updated in place at the
- * K+1 new positions.
+ * layer), layer_hidden[b][L][K+1][H], route (routing test hooks).  The caches
+ * are updated in place at the K+1 new positions.
  */
 void or_verify_step(const or_config* c, const or_weights* w, void* kc, void* vc, int B,
                     const int* committed, const int* drafts, const int* ctx_in, int* ctx_out,
                     int* accepted, int* next_tok, int* status, int* target, double* logits,
-                    double* hidden, double* layer_hidden)
+                    double* hidden, double* layer_hidden, const or_route_io* route)
 {
     int K = c->k_draft, n = K + 1, H = c->hidden;
     long V = c->vocab;
@@ -474,8 +500,17 @@ void or_verify_step(const or_config* c, const or_weights* w, void* kc, void* vc,
         for (j = 0; j < n; j++) if (tok[j] < 0 || tok[j] >= V) st |= OR_BAD_TOKEN;
         if (ctx_in[b] < 0 || (long)ctx_in[b] + n > c->capacity) st |= OR_CAPACITY;
         if (st == 0) {
+            or_route_io rio = {NULL, NULL, NULL};
+            size_t per_b = (size_t)c->n_layers * n;
+            if (route && c->ffn_kind == OR_FFN_MOE) {
+                if (route->force) rio.force = route->force + (size_t)b * per_b * c->top_k;
+                if (route->sel_out) rio.sel_out = route->sel_out + (size_t)b * per_b * c->top_k;
+                if (route->rlogits_out)
+                    rio.rlogits_out = route->rlogits_out + (size_t)b * per_b * c->n_experts;
+            }
             forward_block(c, w, kc, vc, b, ctx_in[b], n, tok, x,
-                          layer_hidden ? layer_hidden + (size_t)b * c->n_layers * n * H : NULL);
+                          layer_hidden ? layer_hidden + (size_t)b * c->n_layers * n * H : NULL,
+                          &rio);
             for (j = 0; j < n; j++) {
                 lm_logits(c, w, x + (size_t)j * H, lg);
                 g[j] = or_argmax(lg, V);
@@ -509,7 +544,7 @@ int or_decode_one(const or_config* c, const or_weights* w, void* kc, void* vc, l
     double* x = (double*)malloc(sizeof(double) * c->hidden);
     double* lg = (double*)malloc(sizeof(double) * c->vocab);
     int g;
-    forward_block(c, w, kc, vc, b, pos, 1, &tok, x, NULL);
+    forward_block(c, w, kc, vc, b, pos, 1, &tok, x, NULL, NULL);
     lm_logits(c, w, x, lg);
     g = or_argmax(lg, c->vocab);
     if (logits) memcpy(logits, lg, sizeof(double) * c->vocab);

@@ -1,0 +1,270 @@
+"""Python binding of the MI355X greedy speculative-decoding verify step.
+
+A thin ctypes layer over libspecverify.so (include/spec_verify.h): the
+functions carry the C ABI's names and only marshal arguments -- every step of
+the verify path runs in the library's HIP kernels.  PyTorch is used for device
+memory and streams only.  If the library has not been built the import fails
+loudly; there is no fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from ctypes import POINTER, c_char_p, c_double, c_float, c_int, c_uint32, c_void_p
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libspecverify.so")
+
+SV_OK, SV_ERR_INVALID_ARG, SV_ERR_UNSUPPORTED, SV_ERR_HIP, SV_ERR_NO_DEVICE, SV_ERR_NOT_SET = (
+    0, -1, -2, -3, -4, -5)
+SV_F32, SV_BF16, SV_FP8 = 0, 1, 2
+SV_FFN_MOE, SV_FFN_DENSE = 0, 1
+SV_DEV_BAD_TOKEN, SV_DEV_CAPACITY, SV_DEV_NAN_LOGIT = 1, 2, 4
+SV_KC_LM_HEAD, SV_KC_ATTENTION, SV_KC_EXPERT_GATE_UP, SV_KC_EXPERT_DOWN, SV_KC_QKV = range(5)
+KERNEL_CLASSES = {"lm_head": 0, "attention": 1, "expert_gate_up": 2, "expert_down": 3, "qkv": 4}
+_DT = {"f32": SV_F32, "bf16": SV_BF16, "fp8": SV_FP8}
+
+# every function include/spec_verify.h declares
+EXPORTS = ("spec_verify_init", "spec_verify_destroy", "spec_verify_step", "spec_verify_set_debug",
+           "spec_verify_accept_from_logits", "spec_verify_error_word", "spec_verify_kernel_time",
+           "spec_verify_last_error", "spec_verify_status_string", "spec_verify_abi_version")
+
+
+class SpecVerifyConfig(ctypes.Structure):
+    _fields_ = [("n_layers", c_int), ("hidden", c_int), ("n_q_heads", c_int),
+                ("n_kv_heads", c_int), ("head_dim", c_int), ("ffn_kind", c_int),
+                ("n_experts", c_int), ("expert_inter", c_int), ("top_k", c_int),
+                ("n_shared", c_int), ("renorm_topk", c_int), ("dense_inter", c_int),
+                ("vocab", c_int), ("max_batch", c_int), ("k_draft", c_int),
+                ("kv_capacity", c_int), ("rope_theta", c_float), ("rms_eps", c_float),
+                ("weight_dtype", c_int), ("embed_dtype", c_int), ("kv_dtype", c_int)]
+
+
+class SpecVerifyLayer(ctypes.Structure):
+    _fields_ = [(n, c_void_p) for n in (
+        "attn_norm", "w_qkv", "s_qkv", "w_o", "s_o", "ffn_norm", "w_router", "s_router",
+        "w_gate_up", "s_gate_up", "w_down", "s_down", "w_sh_gate_up", "s_sh_gate_up",
+        "w_sh_down", "s_sh_down")]
+
+
+class SpecVerifyWeights(ctypes.Structure):
+    _fields_ = [("embed", c_void_p), ("layers", POINTER(SpecVerifyLayer)),
+                ("final_norm", c_void_p), ("lm_head", c_void_p), ("lm_scale", c_void_p)]
+
+
+class SpecVerifyError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {spec_verify_status_string(status)} ({status}): "
+                         f"{spec_verify_last_error()}")
+
+
+_lib = None
+
+
+def load_library() -> ctypes.CDLL:
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(f"{LIB_PATH} is missing: build it with "
+                              f"`python -m speculative_decoding_verify_step_amd._build`")
+        lib = ctypes.CDLL(LIB_PATH)
+        P = c_void_p
+        lib.spec_verify_init.argtypes = [P, P]
+        lib.spec_verify_destroy.argtypes = [P]
+        lib.spec_verify_destroy.restype = None
+        lib.spec_verify_step.argtypes = [P, P, P, P, P, P, P, P, c_int, P, P, P]
+        lib.spec_verify_set_debug.argtypes = [P, P, P, P, P]
+        lib.spec_verify_accept_from_logits.argtypes = [P, P, P, P, P, c_int, P, P, P, P]
+        lib.spec_verify_error_word.argtypes = [P, P, c_int, P]
+        lib.spec_verify_kernel_time.argtypes = [P, c_int, c_int, P, P]
+        lib.spec_verify_last_error.argtypes = [c_char_p, c_int]
+        lib.spec_verify_status_string.argtypes = [c_int]
+        lib.spec_verify_status_string.restype = c_char_p
+        lib.spec_verify_abi_version.argtypes = []
+        for f in EXPORTS:
+            if f not in ("spec_verify_destroy", "spec_verify_status_string"):
+                getattr(lib, f).restype = c_int
+        _lib = lib
+    return _lib
+
+
+def _check(rc: int, where: str):
+    if rc != SV_OK:
+        raise SpecVerifyError(rc, where)
+
+
+def _p(t):
+    """Device (or host) address of a tensor, or None."""
+    if t is None:
+        return None
+    if isinstance(t, int):
+        return t
+    return t.data_ptr()
+
+
+def _stream(stream):
+    if stream is None:
+        import torch
+        return torch.cuda.current_stream().cuda_stream
+    return stream if isinstance(stream, int) else stream.cuda_stream
+
+
+# ----------------------------------------------------------- ABI functions
+def spec_verify_abi_version() -> int:
+    return load_library().spec_verify_abi_version()
+
+
+def spec_verify_status_string(status: int) -> str:
+    return load_library().spec_verify_status_string(status).decode()
+
+
+def spec_verify_last_error() -> str:
+    buf = ctypes.create_string_buffer(1024)
+    load_library().spec_verify_last_error(buf, 1024)
+    return buf.value.decode(errors="replace")
+
+
+def make_config(cfg, max_batch: int, kv_capacity: int) -> SpecVerifyConfig:
+    """Config struct from any object with the workload fields."""
+    c = SpecVerifyConfig()
+    c.n_layers, c.hidden, c.n_q_heads, c.n_kv_heads = cfg.n_layers, cfg.hidden, cfg.n_q, cfg.n_kv
+    c.head_dim = cfg.head_dim
+    c.ffn_kind = SV_FFN_MOE if cfg.ffn == "moe" else SV_FFN_DENSE
+    c.n_experts, c.expert_inter, c.top_k = cfg.n_experts, cfg.expert_inter, cfg.top_k
+    c.n_shared, c.renorm_topk, c.dense_inter = cfg.n_shared, cfg.renorm_topk, cfg.dense_inter
+    c.vocab, c.max_batch, c.k_draft, c.kv_capacity = cfg.vocab, max_batch, cfg.k_draft, kv_capacity
+    c.rope_theta, c.rms_eps = cfg.rope_theta, cfg.rms_eps
+    c.weight_dtype, c.embed_dtype, c.kv_dtype = _DT[cfg.wdtype], _DT[cfg.embdtype], _DT[cfg.kvdtype]
+    return c
+
+
+def spec_verify_init(config: SpecVerifyConfig) -> int:
+    """Returns the opaque context handle (an address)."""
+    h = c_void_p()
+    _check(load_library().spec_verify_init(ctypes.byref(config), ctypes.byref(h)),
+           "spec_verify_init")
+    return h.value
+
+
+def spec_verify_destroy(ctx: int) -> None:
+    load_library().spec_verify_destroy(ctx)
+
+
+def make_weights(weights: dict, n_layers: int):
+    """Weights struct from a dict of device tensors laid out as the header
+    documents; returns (struct, keep-alive list)."""
+    keep = []
+    layers = (SpecVerifyLayer * n_layers)()
+    for l, L in enumerate(weights["layers"]):
+        lay = layers[l]
+        for name, _ in SpecVerifyLayer._fields_:
+            t = L.get(name)
+            if t is not None:
+                keep.append(t)
+                setattr(lay, name, t.data_ptr())
+    w = SpecVerifyWeights()
+    w.embed = weights["embed"].data_ptr()
+    w.layers = ctypes.cast(layers, POINTER(SpecVerifyLayer))
+    w.final_norm = weights["final_norm"].data_ptr()
+    w.lm_head = weights["lm_head"].data_ptr()
+    sc = weights.get("lm_scale")
+    w.lm_scale = sc.data_ptr() if sc is not None else None
+    keep += [layers, weights]
+    return w, keep
+
+
+def spec_verify_step(ctx: int, weights: SpecVerifyWeights, k_cache, v_cache, committed_tok,
+                     draft_toks, ctx_lens_in, ctx_lens_out, batch: int, accepted_len, next_tok,
+                     stream=None) -> None:
+    _check(load_library().spec_verify_step(
+        ctx, ctypes.byref(weights), _p(k_cache), _p(v_cache), _p(committed_tok), _p(draft_toks),
+        _p(ctx_lens_in), _p(ctx_lens_out), int(batch), _p(accepted_len), _p(next_tok),
+        _stream(stream)), "spec_verify_step")
+
+
+def spec_verify_set_debug(ctx: int, logits=None, hidden=None, target_tok=None,
+                          routing=None) -> None:
+    _check(load_library().spec_verify_set_debug(ctx, _p(logits), _p(hidden), _p(target_tok),
+                                                _p(routing)), "spec_verify_set_debug")
+
+
+def spec_verify_accept_from_logits(ctx: int, logits, draft_toks, ctx_lens_in, ctx_lens_out,
+                                   batch: int, accepted_len, next_tok, target_tok=None,
+                                   stream=None) -> None:
+    _check(load_library().spec_verify_accept_from_logits(
+        ctx, _p(logits), _p(draft_toks), _p(ctx_lens_in), _p(ctx_lens_out), int(batch),
+        _p(accepted_len), _p(next_tok), _p(target_tok), _stream(stream)),
+        "spec_verify_accept_from_logits")
+
+
+def spec_verify_error_word(ctx: int, clear: bool = False, stream=None) -> int:
+    v = c_uint32()
+    _check(load_library().spec_verify_error_word(ctx, ctypes.byref(v), int(clear),
+                                                 _stream(stream)), "spec_verify_error_word")
+    return v.value
+
+
+def spec_verify_kernel_time(ctx: int, kclass: int, enable: int = -1, query: bool = True):
+    """enable 1: start/reset recording class `kclass`; 0: stop; -1: keep.
+    Returns (total_ms, launches) when query is true."""
+    ms, n = c_double(), c_int()
+    args = (ctypes.byref(ms), ctypes.byref(n)) if query else (None, None)
+    _check(load_library().spec_verify_kernel_time(ctx, kclass, enable, *args),
+           "spec_verify_kernel_time")
+    return (ms.value, n.value) if query else None
+
+
+# --------------------------------------------------------------- helpers
+def to_library_v_layout(v_cache):
+    """The V cache in the library's channel-major layout [B][L][n_kv][D][cap]
+    from the natural [B][L][n_kv][cap][D]."""
+    return v_cache.transpose(-1, -2).contiguous()
+
+
+def from_library_v_layout(v_cache):
+    return v_cache.transpose(-1, -2).contiguous()
+
+
+class VerifyContext:
+    """Owns one library context; wraps spec_verify_step for torch tensors."""
+
+    def __init__(self, cfg, max_batch: int, kv_capacity: int, weights: dict):
+        self.cfg = cfg
+        self.max_batch = max_batch
+        self.kv_capacity = kv_capacity
+        self._config = make_config(cfg, max_batch, kv_capacity)
+        self.handle = spec_verify_init(self._config)
+        self._w, self._keep = make_weights(weights, cfg.n_layers)
+
+    def step(self, k_cache, v_cache, committed, drafts, ctx_in, ctx_out, accepted, next_tok,
+             batch=None, stream=None):
+        B = committed.shape[0] if batch is None else batch
+        spec_verify_step(self.handle, self._w, k_cache, v_cache, committed, drafts, ctx_in,
+                         ctx_out, B, accepted, next_tok, stream)
+
+    def set_debug(self, logits=None, hidden=None, target_tok=None, routing=None):
+        self._dbg = (logits, hidden, target_tok, routing)
+        spec_verify_set_debug(self.handle, logits, hidden, target_tok, routing)
+
+    def accept_from_logits(self, logits, drafts, ctx_in, ctx_out, accepted, next_tok,
+                           target_tok=None, stream=None):
+        spec_verify_accept_from_logits(self.handle, logits, drafts, ctx_in, ctx_out,
+                                       drafts.shape[0], accepted, next_tok, target_tok, stream)
+
+    def error_word(self, clear=False, stream=None) -> int:
+        return spec_verify_error_word(self.handle, clear, stream)
+
+    def kernel_time(self, kclass, enable=-1, query=True):
+        return spec_verify_kernel_time(self.handle, kclass, enable, query)
+
+    def close(self):
+        if self.handle:
+            spec_verify_destroy(self.handle)
+            self.handle = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass

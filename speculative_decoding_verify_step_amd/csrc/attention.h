@@ -1,0 +1,216 @@
+// attention.h -- split-KV verify attention with MFMA tiles (gfx950).
+//
+// For every sequence b and KV head h the verify step has R = (K+1) * G query
+// rows (K+1 positions times the G = n_q / n_kv query heads that read this KV
+// head; row r is position r / G, query head h*G + r % G).  Row r attends to
+// cache positions 0 .. ctx_b + r/G: the cached context, then the block's own
+// new positions up to itself (causal).
+//
+// The key range of a sequence is cut into chunks of CH keys; one wave takes
+// one chunk for QPW 16-row query fragments and keeps a flash-style running
+// (max, sum, output) per row, then writes the unnormalised partial.  A second
+// kernel merges the partials of all chunks in chunk order.
+//
+// Tile shapes (KL = elements per 16-byte slice: 8 for bf16, 4 for fp32):
+//   scores   S^T[key][row] = K[key][:] . Q[row][:]  -- key tile = A operand,
+//            query fragment = B operand (held in registers for the chunk);
+//   output   O^T[d][row] += V^T[d][keys] . P^T[keys][row] -- the V cache is
+//            stored channel-major (V^T[d][pos]) so a lane's A slice is 16
+//            contiguous bytes, and the probabilities a lane produced by the
+//            score product are exactly its B slice (no shuffles):
+// a 4*KL-key tile is computed as KL/4 score blocks of 16 keys whose slot s
+// maps to key KL*(s/4) + 4*blk + s%4, so that lane group g ends up holding
+// keys KL*g .. KL*g + KL-1 for its row.
+#pragma once
+#include "common.h"
+
+struct AttnArgs {
+    const void* q;            // [T][n_q][D] activations (rotary applied)
+    const void* kc;           // K cache [B_max][L][n_kv][cap][D]
+    const void* vc;           // V cache [B_max][L][n_kv][D][cap]
+    const int* ctx_in;        // [B]
+    const int* seq_err;       // [B]
+    int layer, L, n_q, n_kv, D, K1, cap, CH, maxch, QG;
+    float scale_log2;         // log2(e) / sqrt(D)
+    float* opart;             // [B][n_q][K1][maxch][D]
+    float* mlpart;            // [B][n_q][K1][maxch][2]  (max in log2 units, sum)
+};
+
+template <bool BF, int QPW, int DH>
+__global__ __launch_bounds__(64) void attn_split_kernel(AttnArgs a)
+{
+    constexpr int ESZ = BF ? 2 : 4;
+    constexpr int KL = BF ? 8 : 4;          // elements per 16-byte slice
+    constexpr int KT = 4 * KL;              // keys per tile
+    constexpr int DS = DH / (4 * KL);       // reduction steps over the head dimension
+    constexpr int DF = DH / 16;             // output fragments over the head dimension
+    constexpr int NB = KL / 4;              // 16-key score blocks per tile
+
+    const int lane = threadIdx.x, l16 = lane & 15, lg = lane >> 4;
+    const int chunk = blockIdx.x;
+    const int hkv = blockIdx.y / a.QG, qgi = blockIdx.y % a.QG;
+    const int b = blockIdx.z;
+    const int K1 = a.K1, G = a.n_q / a.n_kv, R = K1 * G;
+    const int ctx = min(max(a.ctx_in[b], 0), a.cap - K1);
+    const int total = ctx + K1;
+    const int c0 = chunk * a.CH;
+    if (c0 >= total) return;
+    const int c1 = min(c0 + a.CH, total);
+
+    const size_t head = ((size_t)b * a.L + a.layer) * a.n_kv + hkv;
+    const char* kbase = (const char*)a.kc + head * (size_t)a.cap * DH * ESZ;
+    const char* vbase = (const char*)a.vc + head * (size_t)DH * a.cap * ESZ;
+
+    // query fragments (B operand): lane supplies row l16, slice lg of each step
+    uint4 qf[QPW][DS];
+    int limit[QPW];
+#pragma unroll
+    for (int f = 0; f < QPW; f++) {
+        int r = (qgi * QPW + f) * 16 + l16;
+        bool ok = r < R;
+        int j = ok ? r / G : 0;
+        int hq = hkv * G + (ok ? r % G : 0);
+        limit[f] = ok ? ctx + j : -1;
+        const char* qp = (const char*)a.q + (((size_t)b * K1 + j) * a.n_q + hq) * DH * ESZ;
+#pragma unroll
+        for (int s = 0; s < DS; s++) {
+            qf[f][s] = ok ? ldg16(qp + (size_t)(s * 4 * KL + lg * KL) * ESZ) : make_uint4(0, 0, 0, 0);
+        }
+    }
+
+    float m_run[QPW], l_run[QPW];
+    f32x4_t o[QPW][DF];
+#pragma unroll
+    for (int f = 0; f < QPW; f++) {
+        m_run[f] = -INFINITY;
+        l_run[f] = 0.f;
+#pragma unroll
+        for (int d = 0; d < DF; d++) o[f][d] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    }
+
+    const int cap = a.cap;
+    for (int kt = c0; kt < c1; kt += KT) {
+        // key tile (A operand of the score product)
+        uint4 kf[NB][DS];
+#pragma unroll
+        for (int blk = 0; blk < NB; blk++) {
+            int key = kt + KL * (l16 >> 2) + 4 * blk + (l16 & 3);
+            key = min(key, cap - 1);
+            const char* kp = kbase + ((size_t)key * DH + lg * KL) * ESZ;
+#pragma unroll
+            for (int s = 0; s < DS; s++) kf[blk][s] = ldg16(kp + (size_t)s * 4 * KL * ESZ);
+        }
+        // V^T tile (A operand of the output product): d = 16 df + l16, keys KL*lg ..
+        uint4 vf[DF];
+        {
+            int key = min(kt + KL * lg, cap - KL);
+#pragma unroll
+            for (int d = 0; d < DF; d++)
+                vf[d] = ldg16(vbase + ((size_t)(16 * d + l16) * cap + key) * ESZ);
+        }
+#pragma unroll
+        for (int f = 0; f < QPW; f++) {
+            float s[KL];
+#pragma unroll
+            for (int blk = 0; blk < NB; blk++) {
+                f32x4_t acc = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int st = 0; st < DS; st++) {
+                    if constexpr (BF) acc = mma_bf16(kf[blk][st], qf[f][st], acc);
+                    else acc = mma_f32x4(kf[blk][st], qf[f][st], acc);
+                }
+#pragma unroll
+                for (int r = 0; r < 4; r++) s[4 * blk + r] = acc[r];
+            }
+            // lane (lg, l16) holds keys kt + KL*lg + e for row l16 of fragment f
+            float mt = -INFINITY;
+#pragma unroll
+            for (int e = 0; e < KL; e++) {
+                int key = kt + KL * lg + e;
+                s[e] = (key <= limit[f]) ? s[e] * a.scale_log2 : -INFINITY;
+                mt = fmaxf(mt, s[e]);
+            }
+            mt = fmaxf(mt, __shfl_xor(mt, 16, 64));
+            mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
+            float mnew = fmaxf(m_run[f], mt);
+            float muse = (mnew == -INFINITY) ? 0.f : mnew;
+            float alpha = exp2f(m_run[f] - muse);
+            m_run[f] = mnew;
+            float p[KL], ps = 0.f;
+#pragma unroll
+            for (int e = 0; e < KL; e++) { p[e] = exp2f(s[e] - muse); ps += p[e]; }
+            l_run[f] = l_run[f] * alpha + ps;
+            uint4 pb;
+            if constexpr (BF) {
+                pb = make_uint4(pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]),
+                                pack_bf16x2(p[4], p[5]), pack_bf16x2(p[6], p[7]));
+            } else {
+                pb = make_uint4(__float_as_uint(p[0]), __float_as_uint(p[1]), __float_as_uint(p[2]),
+                                __float_as_uint(p[3]));
+            }
+#pragma unroll
+            for (int d = 0; d < DF; d++) {
+                o[f][d] = o[f][d] * alpha;
+                if constexpr (BF) o[f][d] = mma_bf16(vf[d], pb, o[f][d]);
+                else o[f][d] = mma_f32x4(vf[d], pb, o[f][d]);
+            }
+        }
+    }
+
+    // partial of this chunk: O^T[d = 16 df + 4 lg + r][row l16]
+#pragma unroll
+    for (int f = 0; f < QPW; f++) {
+        float l = l_run[f];
+        l += __shfl_xor(l, 16, 64);
+        l += __shfl_xor(l, 32, 64);
+        int r = (qgi * QPW + f) * 16 + l16;
+        if (r >= R) continue;
+        int j = r / G, hq = hkv * G + r % G;
+        size_t slot = (((size_t)b * a.n_q + hq) * K1 + j) * a.maxch + chunk;
+        float* op = a.opart + slot * DH;
+#pragma unroll
+        for (int d = 0; d < DF; d++)
+            *reinterpret_cast<float4*>(op + 16 * d + 4 * lg) =
+                make_float4(o[f][d][0], o[f][d][1], o[f][d][2], o[f][d][3]);
+        if (lg == 0) {
+            a.mlpart[slot * 2] = m_run[f];
+            a.mlpart[slot * 2 + 1] = l;
+        }
+    }
+}
+
+// Merge the chunk partials of one (sequence, query head, position) row in
+// chunk order and write the attention output row in the activation type.
+template <bool BF>
+__global__ __launch_bounds__(64) void attn_merge_kernel(AttnArgs a, void* out /* [T][n_q*D] */)
+{
+    const int row = blockIdx.x;                     // ((b * n_q + hq) * K1 + j)
+    const int K1 = a.K1;
+    const int j = row % K1;
+    const int hq = (row / K1) % a.n_q;
+    const int b = row / (K1 * a.n_q);
+    const int ctx = min(max(a.ctx_in[b], 0), a.cap - K1);
+    const int nch = (ctx + K1 + a.CH - 1) / a.CH;
+    const float* ml = a.mlpart + (size_t)row * a.maxch * 2;
+    const float* op = a.opart + (size_t)row * a.maxch * a.D;
+    float M = -INFINITY;
+    for (int c = 0; c < nch; c++) M = fmaxf(M, ml[2 * c]);
+    float Lsum = 0.f;
+    for (int c = 0; c < nch; c++) {
+        float mc = ml[2 * c];
+        if (mc != -INFINITY) Lsum += exp2f(mc - M) * ml[2 * c + 1];
+    }
+    float inv = 1.f / Lsum;
+    size_t t = (size_t)b * K1 + j;
+    for (int d = threadIdx.x; d < a.D; d += 64) {
+        float acc = 0.f;
+        for (int c = 0; c < nch; c++) {
+            float mc = ml[2 * c];
+            if (mc != -INFINITY) acc += exp2f(mc - M) * op[(size_t)c * a.D + d];
+        }
+        float v = acc * inv;
+        size_t o = t * (size_t)a.n_q * a.D + (size_t)hq * a.D + d;
+        if constexpr (BF) ((uint16_t*)out)[o] = (uint16_t)f32_to_bf16_bits(v);
+        else ((float*)out)[o] = v;
+    }
+}

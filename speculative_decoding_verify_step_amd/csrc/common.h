@@ -1,0 +1,123 @@
+// common.h -- device helpers shared by the verify-step kernels (gfx950).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "spec_verify.h"
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+#define SV_DEV __device__ __forceinline__
+
+// ----------------------------------------------------------------- formats
+SV_DEV float bf16_bits_to_f32(uint32_t b) { return __uint_as_float(b << 16); }
+
+// fp32 -> bf16 bits, round to nearest even; NaN stays a quiet NaN.
+SV_DEV uint32_t f32_to_bf16_bits(float f)
+{
+    uint32_t u = __float_as_uint(f);
+    if ((u & 0x7fffffffu) > 0x7f800000u) return 0x7fc0u;
+    u += 0x7fffu + ((u >> 16) & 1u);
+    return u >> 16;
+}
+
+SV_DEV uint32_t pack_bf16x2(float lo, float hi)
+{
+    return f32_to_bf16_bits(lo) | (f32_to_bf16_bits(hi) << 16);
+}
+
+// One OCP e4m3fn byte -> the fp32 with the same value.  The 7 magnitude bits
+// are placed at the bottom of the fp32 exponent field and the top of its
+// mantissa, which reads as 2^(e-127) * 1.mmm (or 2^-126 * 0.mmm when e = 0);
+// multiplying by 2^120 rebases the exponent from bias 127 to bias 7.  Exact.
+SV_DEV float e4m3_to_f32(uint32_t c)
+{
+    float f = __uint_as_float(((c & 0x7fu) << 20) | ((c & 0x80u) << 24));
+    return f * 0x1p120f;
+}
+
+// Two e4m3fn bytes (bits 0-7 and 8-15 of w) -> two packed bf16 (exact: every
+// e4m3fn value has at most 4 significant bits).
+SV_DEV uint32_t e4m3x2_to_bf16x2(uint32_t w)
+{
+    uint32_t lo = __float_as_uint(e4m3_to_f32(w & 0xffu));
+    uint32_t hi = __float_as_uint(e4m3_to_f32((w >> 8) & 0xffu));
+    return (lo >> 16) | (hi & 0xffff0000u);
+}
+
+// 16 e4m3fn bytes -> 16 bf16 as two 16-byte operands (elements 0-7, 8-15).
+SV_DEV void e4m3x16_to_bf16(uint4 w, uint4& lo, uint4& hi)
+{
+    lo.x = e4m3x2_to_bf16x2(w.x);
+    lo.y = e4m3x2_to_bf16x2(w.x >> 16);
+    lo.z = e4m3x2_to_bf16x2(w.y);
+    lo.w = e4m3x2_to_bf16x2(w.y >> 16);
+    hi.x = e4m3x2_to_bf16x2(w.z);
+    hi.y = e4m3x2_to_bf16x2(w.z >> 16);
+    hi.z = e4m3x2_to_bf16x2(w.w);
+    hi.w = e4m3x2_to_bf16x2(w.w >> 16);
+}
+
+// ------------------------------------------------------------------- MFMA
+// 16x16 output tiles, fp32 accumulate.  Lane l holds output rows
+// 4*(l/16) .. +3 of column l%16.  Operand lanes: lane l supplies row l%16
+// of A (column l%16 of B) and a slice of the reduction index chosen by l/16;
+// A and B always use the same slice mapping, so the reduction covers every
+// index exactly once.
+SV_DEV f32x4_t mma_bf16(uint4 a, uint4 b, f32x4_t c)
+{
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                   __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
+}
+
+// four 16x16x4 fp32 products, element e of each lane's 16-byte slice in step e
+SV_DEV f32x4_t mma_f32x4(uint4 a, uint4 b, f32x4_t c)
+{
+    c = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(a.x), __uint_as_float(b.x), c, 0, 0, 0);
+    c = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(a.y), __uint_as_float(b.y), c, 0, 0, 0);
+    c = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(a.z), __uint_as_float(b.z), c, 0, 0, 0);
+    c = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(a.w), __uint_as_float(b.w), c, 0, 0, 0);
+    return c;
+}
+
+SV_DEV uint4 ldg16(const void* p) { return *reinterpret_cast<const uint4*>(p); }
+
+// streamed once: keep weights from displacing reusable lines
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+SV_DEV uint4 ldg16_stream(const void* p)
+{
+    u32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
+    return make_uint4(v.x, v.y, v.z, v.w);
+}
+
+// ---------------------------------------------------------------- argmax
+// Order-preserving key of (value, index): larger value wins, then the lower
+// index; a NaN value maps to the all-ones key so it wins every comparison
+// and is detected after the reduction.
+SV_DEV unsigned long long argmax_key(float v, uint32_t idx)
+{
+    if (v != v) return ~0ull;
+    uint32_t u = __float_as_uint(v);
+    u = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+    return ((unsigned long long)u << 32) | (unsigned long long)(0xffffffffu - idx);
+}
+
+SV_DEV unsigned long long umax64(unsigned long long a, unsigned long long b) { return a > b ? a : b; }
+
+SV_DEV unsigned long long shfl_xor_u64(unsigned long long v, int m)
+{
+    uint32_t lo = (uint32_t)v, hi = (uint32_t)(v >> 32);
+    lo = __shfl_xor(lo, m, 64);
+    hi = __shfl_xor(hi, m, 64);
+    return ((unsigned long long)hi << 32) | lo;
+}
+
+SV_DEV float wave_sum(float v)
+{
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m, 64);
+    return v;
+}
+
+SV_DEV float silu_f32(float z) { return z / (1.0f + __expf(-z)); }

@@ -1,0 +1,285 @@
+// gemm.h -- weight-streaming MFMA GEMM for the verify step:
+//   Y[m][n] = sum_k X[m][k] * W[n][k]     (W row-major [N][K], one row per output)
+// with the epilogue chosen at compile time:
+//   GM_STORE   fp32 partial sums (one slab per K split) for a consumer kernel
+//   GM_SWIGLU  gate rows n and up rows n + dual_off in the same wave; writes
+//              silu(gate) * up in the activation type
+//   GM_ARGMAX  per-row (value, index) maximum over the workgroup's columns as
+//              an order-preserving 64-bit key, plus optional fp32 logits
+//
+// Shapes on the verify path are "few rows, many weights": M = B (K+1) rows of
+// activations (4 .. 256) against weight matrices of 0.2 - 390 MB, so the
+// kernel streams each weight element from HBM once and keeps the activations
+// in cache.  Operand roles: the weight fragment is the MFMA A operand (16
+// output columns), the activation fragment is the B operand (16 rows); a wave
+// owns 16*NF output columns and 16*MF rows, and four waves side by side make
+// a 64*NF-column workgroup tile.  Every lane loads 16 contiguous bytes of a
+// weight row per step (the 16 rows of a fragment are 16 separate 64-byte
+// runs, and consecutive steps walk along the rows).
+//
+// Grouped mode (mixture of experts): a device-built tile list names, per
+// grid row, (group, first row, row count) over the permuted assignment rows;
+// the group selects the expert's weights (groups >= G1 use the second weight
+// set: shared experts), and `gather` maps a permuted row to its token's
+// activation row.  The grid is sized for the largest possible list and
+// workgroups past the device-side count exit at once (graph-safe, no host
+// round trip).
+//
+// Launch mapping is XCD-aware: workgroup ids are dealt to the 8 XCDs round
+// robin, so the tiles that share one weight slab (same column tile, different
+// row tiles) are given ids 8 apart and land on the same XCD's L2.
+#pragma once
+#include "common.h"
+
+enum { GM_STORE = 0, GM_SWIGLU = 1, GM_ARGMAX = 2 };
+
+struct GemmArgs {
+    const void* X;          // activations [rows][ldx] (fp32 or bf16)
+    long ldx;
+    const int* gather;      // grouped: permuted row -> activation row (or null)
+    int M;                  // dense: rows
+    int N;                  // output columns, a multiple of 4 (SWIGLU: columns of gate = of up)
+    int K;                  // full reduction length
+    int ksplit;             // K splits (grid.y); K / ksplit is a multiple of the step
+    const void* W;          // weights of groups 0 .. G1-1
+    const float* ws;        // fp8 per-row scales of W
+    long w_gstride;         // elements between groups of W
+    long s_gstride;         // scales between groups
+    const void* W2;         // weights of groups G1 ..
+    const float* ws2;
+    long w2_gstride, s2_gstride;
+    int G1;
+    int dual_off;           // SWIGLU: row offset of the "up" rows
+    const int* tiles;       // grouped: [max_tiles][3] = (group, row0, nrows); null = dense
+    const int* n_tiles;     // grouped: device count of valid tiles
+    int MT;                 // row tiles in the grid (dense: ceil(M / BM); grouped: max tiles)
+    int NT;                 // column tiles (64*NF columns each)
+    void* out;              // STORE: fp32 [ksplit][rows][ldo]; SWIGLU: act [rows][ldo]
+    long ldo;
+    long split_stride;      // STORE: elements between K-split slabs
+    unsigned long long* keys;   // ARGMAX: [NT][key_ld]
+    long key_ld;
+    float* dbg;             // ARGMAX: optional fp32 logits [rows][dbg_ld]
+    long dbg_ld;
+};
+
+// per weight storage type: elements per 16-byte lane slice, reduction step
+template <int WT> struct WTraits;
+template <> struct WTraits<SV_F32> { static constexpr int KL = 4, SK = 16, XU = 1, ESZ = 4; };
+template <> struct WTraits<SV_BF16> { static constexpr int KL = 8, SK = 32, XU = 1, ESZ = 2; };
+template <> struct WTraits<SV_FP8> { static constexpr int KL = 16, SK = 64, XU = 2, ESZ = 1; };
+
+// activation element size: fp32 with fp32 weights, bf16 otherwise
+template <int WT> struct ATraits { static constexpr int ESZ = (WT == SV_F32) ? 4 : 2; };
+
+template <int WT>
+SV_DEV f32x4_t mma_step(uint4 w, const uint4* x, f32x4_t c)
+{
+    if constexpr (WT == SV_F32) {
+        return mma_f32x4(w, x[0], c);
+    } else if constexpr (WT == SV_BF16) {
+        return mma_bf16(w, x[0], c);
+    } else {
+        uint4 lo, hi;
+        e4m3x16_to_bf16(w, lo, hi);
+        c = mma_bf16(lo, x[0], c);
+        return mma_bf16(hi, x[1], c);
+    }
+}
+
+template <int WT, int MF, int NF, int MODE>
+__global__ __launch_bounds__(256) void gemm_kernel(GemmArgs a)
+{
+    using Tr = WTraits<WT>;
+    constexpr int KL = Tr::KL, SK = Tr::SK, XU = Tr::XU, WESZ = Tr::ESZ;
+    constexpr int AESZ = ATraits<WT>::ESZ;
+    constexpr int NFT = (MODE == GM_SWIGLU) ? 2 * NF : NF;   // weight fragments per wave
+    constexpr int BM = 16 * MF;
+    constexpr int U = (MF >= 4) ? 2 : 4;                      // reduction steps per stage
+
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const int l16 = lane & 15;
+    const int lg = lane >> 4;
+
+    // XCD-aware tile mapping
+    const int id = blockIdx.x;
+    const int xcd = id & 7;
+    const int q = id >> 3;
+    const int mt = q % a.MT;
+    const int nt = (q / a.MT) * 8 + xcd;
+    if (nt >= a.NT) return;
+
+    int group = 0, row0, nrows;
+    if (a.tiles) {
+        if (mt >= *a.n_tiles) return;
+        group = a.tiles[3 * mt];
+        row0 = a.tiles[3 * mt + 1];
+        nrows = a.tiles[3 * mt + 2];
+    } else {
+        row0 = mt * BM;
+        nrows = min(BM, a.M - row0);
+    }
+    if (nrows <= 0) return;
+
+    const char* Wb;
+    const float* sc;
+    if (group < a.G1) {
+        Wb = (const char*)a.W + (size_t)group * a.w_gstride * WESZ;
+        sc = a.ws ? a.ws + (size_t)group * a.s_gstride : nullptr;
+    } else {
+        Wb = (const char*)a.W2 + (size_t)(group - a.G1) * a.w2_gstride * WESZ;
+        sc = a.ws2 ? a.ws2 + (size_t)(group - a.G1) * a.s2_gstride : nullptr;
+    }
+
+    const int ncol0 = nt * 64 * NF + wave * 16 * NF;      // this wave's first column
+    const int K = a.K;
+    const int kspan = K / a.ksplit;
+    const int kb = blockIdx.y * kspan;
+    const int ke = kb + kspan;
+
+    // weight rows of this lane, one per fragment (invalid fragments read row 0)
+    const char* wrow[NFT];
+    bool fvalid[NF];
+#pragma unroll
+    for (int f = 0; f < NF; f++) {
+        int n0 = ncol0 + 16 * f;
+        fvalid[f] = n0 < a.N;
+        int r = fvalid[f] ? min(n0 + l16, a.N - 1) : 0;   // rows past N read row N-1
+        wrow[f] = Wb + ((size_t)r * K + (size_t)lg * KL) * WESZ;
+        if constexpr (MODE == GM_SWIGLU)
+            wrow[NF + f] = Wb + ((size_t)(r + a.dual_off) * K + (size_t)lg * KL) * WESZ;
+    }
+    // activation rows of this lane, one per row fragment
+    const char* xrow[MF];
+#pragma unroll
+    for (int m = 0; m < MF; m++) {
+        int r = 16 * m + l16;
+        r = (r < nrows) ? row0 + r : row0;
+        int xr = a.gather ? a.gather[r] : r;
+        xrow[m] = (const char*)a.X + ((size_t)xr * a.ldx + (size_t)lg * KL) * AESZ;
+    }
+
+    f32x4_t acc[MF][NFT];
+#pragma unroll
+    for (int m = 0; m < MF; m++)
+#pragma unroll
+        for (int f = 0; f < NFT; f++) acc[m][f] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+    uint4 wA[U][NFT], wB[U][NFT];
+    uint4 xA[U][MF][XU], xB[U][MF][XU];
+
+    auto load = [&](int k, uint4 (&w)[U][NFT], uint4 (&x)[U][MF][XU]) {
+#pragma unroll
+        for (int u = 0; u < U; u++) {
+            int kk = k + u * SK;
+            if (kk < ke) {
+#pragma unroll
+                for (int f = 0; f < NFT; f++) w[u][f] = ldg16_stream(wrow[f] + (size_t)kk * WESZ);
+#pragma unroll
+                for (int m = 0; m < MF; m++)
+#pragma unroll
+                    for (int v = 0; v < XU; v++)
+                        x[u][m][v] = ldg16(xrow[m] + ((size_t)kk + 8 * v) * AESZ);
+            }
+        }
+    };
+    auto compute = [&](int k, uint4 (&w)[U][NFT], uint4 (&x)[U][MF][XU]) {
+#pragma unroll
+        for (int u = 0; u < U; u++) {
+            if (k + u * SK < ke) {
+#pragma unroll
+                for (int m = 0; m < MF; m++)
+#pragma unroll
+                    for (int f = 0; f < NFT; f++) acc[m][f] = mma_step<WT>(w[u][f], x[u][m], acc[m][f]);
+            }
+        }
+    };
+
+    constexpr int STAGE = U * SK;
+    load(kb, wA, xA);
+    for (int k = kb; k < ke; k += 2 * STAGE) {
+        if (k + STAGE < ke) load(k + STAGE, wB, xB);
+        compute(k, wA, xA);
+        if (k + 2 * STAGE < ke) load(k + 2 * STAGE, wA, xA);
+        if (k + STAGE < ke) compute(k + STAGE, wB, xB);
+    }
+
+    // ------------------------------------------------------------ epilogue
+    // lane holds columns n0 + 4*lg + r (r = 0..3) of row 16*m + l16
+    if constexpr (MODE == GM_STORE) {
+        float* out = (float*)a.out + (size_t)blockIdx.y * a.split_stride;
+#pragma unroll
+        for (int f = 0; f < NF; f++) {
+            int n = ncol0 + 16 * f + 4 * lg;
+            if (!fvalid[f] || n >= a.N) continue;
+            float s0 = 1.f, s1 = 1.f, s2 = 1.f, s3 = 1.f;
+            if constexpr (WT == SV_FP8) { s0 = sc[n]; s1 = sc[n + 1]; s2 = sc[n + 2]; s3 = sc[n + 3]; }
+#pragma unroll
+            for (int m = 0; m < MF; m++) {
+                int r = 16 * m + l16;
+                if (r >= nrows) continue;
+                float4 v = make_float4(acc[m][f][0] * s0, acc[m][f][1] * s1, acc[m][f][2] * s2,
+                                       acc[m][f][3] * s3);
+                *reinterpret_cast<float4*>(out + (size_t)(row0 + r) * a.ldo + n) = v;
+            }
+        }
+    } else if constexpr (MODE == GM_SWIGLU) {
+#pragma unroll
+        for (int f = 0; f < NF; f++) {
+            int n = ncol0 + 16 * f + 4 * lg;
+            if (!fvalid[f] || n >= a.N) continue;
+            float gs[4] = {1.f, 1.f, 1.f, 1.f}, us[4] = {1.f, 1.f, 1.f, 1.f};
+            if constexpr (WT == SV_FP8) {
+#pragma unroll
+                for (int r = 0; r < 4; r++) { gs[r] = sc[n + r]; us[r] = sc[a.dual_off + n + r]; }
+            }
+#pragma unroll
+            for (int m = 0; m < MF; m++) {
+                int r = 16 * m + l16;
+                if (r >= nrows) continue;
+                float v[4];
+#pragma unroll
+                for (int e = 0; e < 4; e++)
+                    v[e] = silu_f32(acc[m][f][e] * gs[e]) * (acc[m][NF + f][e] * us[e]);
+                size_t o = (size_t)(row0 + r) * a.ldo + n;
+                if constexpr (AESZ == 2) {
+                    uint2 p = make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
+                    *reinterpret_cast<uint2*>((uint16_t*)a.out + o) = p;
+                } else {
+                    *reinterpret_cast<float4*>((float*)a.out + o) = make_float4(v[0], v[1], v[2], v[3]);
+                }
+            }
+        }
+    } else {   // GM_ARGMAX
+        __shared__ unsigned long long red[4][BM];
+#pragma unroll
+        for (int m = 0; m < MF; m++) {
+            unsigned long long best = 0ull;
+            int r = 16 * m + l16;
+#pragma unroll
+            for (int f = 0; f < NF; f++) {
+                int n = ncol0 + 16 * f + 4 * lg;
+                if (!fvalid[f] || n >= a.N) continue;
+                float v[4];
+#pragma unroll
+                for (int e = 0; e < 4; e++) {
+                    v[e] = acc[m][f][e];
+                    if constexpr (WT == SV_FP8) v[e] *= sc[n + e];
+                    best = umax64(best, argmax_key(v[e], (uint32_t)(n + e)));
+                }
+                if (a.dbg && r < nrows)
+                    *reinterpret_cast<float4*>(a.dbg + (size_t)(row0 + r) * a.dbg_ld + n) =
+                        make_float4(v[0], v[1], v[2], v[3]);
+            }
+            best = umax64(best, shfl_xor_u64(best, 16));
+            best = umax64(best, shfl_xor_u64(best, 32));
+            if (lg == 0) red[wave][r] = best;
+        }
+        __syncthreads();
+        for (int r = threadIdx.x; r < nrows; r += 256) {
+            unsigned long long b = umax64(umax64(red[0][r], red[1][r]), umax64(red[2][r], red[3][r]));
+            a.keys[(size_t)nt * a.key_ld + row0 + r] = b;
+        }
+    }
+}

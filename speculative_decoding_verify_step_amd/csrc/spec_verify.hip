@@ -1,0 +1,795 @@
+// spec_verify.hip -- host runtime and C ABI of the verify step (see
+// include/spec_verify.h for the contract).  The runtime validates arguments,
+// owns one workspace per context, plans split factors and tile shapes from the
+// batch size, and enqueues the kernels of one step on the caller's stream:
+//
+//   embed + norm
+//   per layer: QKV GEMM -> rotary + KV append -> split-KV attention -> merge
+//              -> O GEMM -> residual + norm
+//              -> MoE: router GEMM -> routing -> grouped gate/up (SwiGLU)
+//                      -> grouped down -> combine + residual + norm
+//              -> dense: gate/up (SwiGLU) -> down -> residual + norm
+//   LM-head GEMM with argmax epilogue -> acceptance + commit
+//
+// Nothing here reads device memory back: context lengths, routing and
+// acceptance stay on the device, so a step can be captured in a HIP graph.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdio>
+#include <cstring>
+#include <mutex>
+#include <string>
+#include <vector>
+
+#include "attention.h"
+#include "common.h"
+#include "gemm.h"
+#include "small_kernels.h"
+
+namespace {
+
+std::mutex g_err_mu;
+std::string g_err;
+
+int fail(int code, const std::string& msg)
+{
+    std::lock_guard<std::mutex> lk(g_err_mu);
+    g_err = msg;
+    return code;
+}
+
+#define HIP_TRY(expr)                                                                      \
+    do {                                                                                   \
+        hipError_t e_ = (expr);                                                            \
+        if (e_ != hipSuccess)                                                              \
+            return fail(SV_ERR_HIP, std::string(#expr) + ": " + hipGetErrorString(e_));   \
+    } while (0)
+
+constexpr int KS_MAX = 16;           // largest K split
+constexpr int ATT_MAXCH_CAP = 4096;  // sanity bound on chunks per sequence
+
+inline int cdiv(long a, long b) { return (int)((a + b - 1) / b); }
+
+int wsteps(int wt)
+{
+    return wt == SV_F32 ? 16 : (wt == SV_BF16 ? 32 : 64);
+}
+
+struct EventPair {
+    hipEvent_t a, b;
+};
+
+}  // namespace
+
+struct spec_verify_ctx {
+    spec_verify_config c;
+    int device = 0;
+    int T_max = 0, K1 = 0, QKV = 0, QD = 0;
+    bool bf = true;
+    int att_CH = 256, att_maxch = 1, att_QPW = 1, att_QG = 1;
+    // workspace
+    std::vector<void*> allocs;
+    float* x = nullptr;
+    void* h = nullptr;
+    float* parts = nullptr;
+    size_t parts_elems = 0;
+    void* q = nullptr;
+    void* o = nullptr;
+    float* opart = nullptr;
+    float* mlpart = nullptr;
+    float2* rope = nullptr;
+    float* probs = nullptr;
+    int* sel = nullptr;
+    float* gate = nullptr;
+    int* slot = nullptr;
+    int* perm_tok = nullptr;
+    int* tiles = nullptr;
+    int* n_tiles = nullptr;
+    void* act = nullptr;
+    float* y = nullptr;
+    unsigned long long* keys = nullptr;
+    size_t keys_elems = 0;
+    int* seq_err = nullptr;
+    unsigned* err_word = nullptr;
+    // debug outputs
+    float* dbg_logits = nullptr;
+    float* dbg_hidden = nullptr;
+    int* dbg_target = nullptr;
+    int* dbg_routing = nullptr;
+    // kernel timing
+    int prof_class = -1;
+    std::vector<EventPair> prof_events;
+    size_t prof_used = 0;
+};
+
+namespace {
+
+template <typename T>
+int dalloc(spec_verify_ctx* c, T** p, size_t elems)
+{
+    void* v = nullptr;
+    size_t bytes = std::max<size_t>(elems * sizeof(T), 256);
+    HIP_TRY(hipMalloc(&v, bytes));
+    c->allocs.push_back(v);
+    *p = (T*)v;
+    return SV_OK;
+}
+
+int validate_config(const spec_verify_config& c)
+{
+    auto bad = [](const char* m) { return fail(SV_ERR_UNSUPPORTED, m); };
+    if (c.n_layers < 1 || c.hidden < 64 || c.hidden % 64 || c.hidden > 8192)
+        return bad("hidden must be a multiple of 64 in [64, 8192] and n_layers >= 1");
+    if (c.n_q_heads < 1 || c.n_kv_heads < 1 || c.n_q_heads % c.n_kv_heads)
+        return bad("n_kv_heads must divide n_q_heads");
+    if (c.head_dim != 64 && c.head_dim != 128) return bad("head_dim must be 64 or 128");
+    if (c.vocab < 16 || c.vocab % 16) return bad("vocab must be a positive multiple of 16");
+    if (c.k_draft < 1 || c.k_draft + 1 > 64) return bad("k_draft must be in [1, 63]");
+    if (c.max_batch < 1) return bad("max_batch must be >= 1");
+    if (c.kv_capacity < c.k_draft + 1 || c.kv_capacity % 64)
+        return bad("kv_capacity must be a multiple of 64 and >= K+1");
+    bool f32 = c.weight_dtype == SV_F32;
+    if (f32) {
+        if (c.embed_dtype != SV_F32 || c.kv_dtype != SV_F32)
+            return bad("fp32 weights need fp32 embedding and KV cache");
+    } else if (c.weight_dtype == SV_BF16 || c.weight_dtype == SV_FP8) {
+        if (c.embed_dtype != SV_BF16 || c.kv_dtype != SV_BF16)
+            return bad("bf16/fp8 weights need bf16 embedding and KV cache");
+    } else {
+        return bad("unknown weight dtype");
+    }
+    int step = wsteps(c.weight_dtype);
+    if (c.hidden % step || (c.n_q_heads * c.head_dim) % step)
+        return bad("hidden and n_q*head_dim must be multiples of the weight step");
+    if (c.ffn_kind == SV_FFN_MOE) {
+        if (c.n_experts < 1 || c.n_experts > 256) return bad("n_experts must be in [1, 256]");
+        if (c.top_k < 1 || c.top_k > 8 || c.top_k > c.n_experts) return bad("bad top_k");
+        if (c.expert_inter < 64 || c.expert_inter % 64 || c.expert_inter % step)
+            return bad("expert_inter must be a multiple of 64");
+        if (c.n_shared < 0) return bad("n_shared must be >= 0");
+        if (c.n_experts % 4) return bad("n_experts must be a multiple of 4");
+        long T = (long)c.max_batch * (c.k_draft + 1);
+        if (T * c.n_experts > 32768) return bad("max_batch*(K+1)*n_experts must be <= 32768");
+    } else if (c.ffn_kind == SV_FFN_DENSE) {
+        if (c.dense_inter < 64 || c.dense_inter % 64 || c.dense_inter % step)
+            return bad("dense_inter must be a multiple of 64");
+    } else {
+        return bad("unknown ffn_kind");
+    }
+    return SV_OK;
+}
+
+// ------------------------------------------------------------- GEMM launch
+template <int WT, int MODE>
+void launch_gemm_t(int MF, const GemmArgs& a, dim3 grid, hipStream_t s)
+{
+    switch (MF) {
+    case 1: gemm_kernel<WT, 1, 1, MODE><<<grid, 256, 0, s>>>(a); break;
+    case 2: gemm_kernel<WT, 2, 1, MODE><<<grid, 256, 0, s>>>(a); break;
+    default: gemm_kernel<WT, 4, 1, MODE><<<grid, 256, 0, s>>>(a); break;
+    }
+}
+
+template <int MODE>
+void launch_gemm_m(int wt, int MF, const GemmArgs& a, dim3 grid, hipStream_t s)
+{
+    if (wt == SV_F32) launch_gemm_t<SV_F32, MODE>(MF, a, grid, s);
+    else if (wt == SV_BF16) launch_gemm_t<SV_BF16, MODE>(MF, a, grid, s);
+    else launch_gemm_t<SV_FP8, MODE>(MF, a, grid, s);
+}
+
+void launch_gemm(int wt, int mode, int MF, GemmArgs& a, hipStream_t s)
+{
+    dim3 grid((unsigned)(cdiv(a.NT, 8) * 8 * a.MT), (unsigned)a.ksplit, 1);
+    if (mode == GM_STORE) launch_gemm_m<GM_STORE>(wt, MF, a, grid, s);
+    else if (mode == GM_SWIGLU) launch_gemm_m<GM_SWIGLU>(wt, MF, a, grid, s);
+    else launch_gemm_m<GM_ARGMAX>(wt, MF, a, grid, s);
+}
+
+int rows_mf(int rows) { return rows <= 16 ? 1 : (rows <= 32 ? 2 : 4); }
+
+// K split: enough waves to cover the GPU, each split at least 4 reduction steps
+int pick_ksplit(long waves, int K, int step)
+{
+    int steps = K / step, best = 1;
+    for (int s = 1; s <= KS_MAX; s++) {
+        if (steps % s) continue;
+        if (steps / s < 4) break;
+        best = s;
+        if (waves * s >= 2048) break;
+    }
+    return best;
+}
+
+GemmArgs dense_args(const void* X, long ldx, int M, int N, int K, const void* W, const float* ws)
+{
+    GemmArgs a;
+    memset(&a, 0, sizeof(a));
+    a.X = X;
+    a.ldx = ldx;
+    a.M = M;
+    a.N = N;
+    a.K = K;
+    a.ksplit = 1;
+    a.W = W;
+    a.ws = ws;
+    a.G1 = 1;
+    return a;
+}
+
+// event-timed launch scope
+struct ProfScope {
+    spec_verify_ctx* c;
+    hipStream_t s;
+    bool on;
+    size_t idx;
+    ProfScope(spec_verify_ctx* c_, int kc, hipStream_t s_) : c(c_), s(s_), on(false), idx(0)
+    {
+        if (c->prof_class == kc && c->prof_used < c->prof_events.size()) {
+            on = true;
+            idx = c->prof_used++;
+            (void)hipEventRecord(c->prof_events[idx].a, s);
+        }
+    }
+    ~ProfScope()
+    {
+        if (on) (void)hipEventRecord(c->prof_events[idx].b, s);
+    }
+};
+
+}  // namespace
+
+// ====================================================================== ABI
+extern "C" {
+
+int spec_verify_abi_version(void) { return SPEC_VERIFY_ABI_VERSION; }
+
+const char* spec_verify_status_string(int s)
+{
+    switch (s) {
+    case SV_OK: return "ok";
+    case SV_ERR_INVALID_ARG: return "invalid argument";
+    case SV_ERR_UNSUPPORTED: return "unsupported shape or dtype";
+    case SV_ERR_HIP: return "HIP runtime error";
+    case SV_ERR_NO_DEVICE: return "no usable gfx950 device";
+    case SV_ERR_NOT_SET: return "requested data was never produced";
+    default: return "unknown status";
+    }
+}
+
+int spec_verify_last_error(char* buf, int len)
+{
+    std::lock_guard<std::mutex> lk(g_err_mu);
+    if (buf && len > 0) {
+        size_t n = std::min<size_t>(g_err.size(), (size_t)len - 1);
+        memcpy(buf, g_err.data(), n);
+        buf[n] = 0;
+    }
+    return (int)g_err.size();
+}
+
+void spec_verify_destroy(spec_verify_ctx* c)
+{
+    if (!c) return;
+    (void)hipSetDevice(c->device);
+    for (auto& e : c->prof_events) {
+        (void)hipEventDestroy(e.a);
+        (void)hipEventDestroy(e.b);
+    }
+    for (void* p : c->allocs) (void)hipFree(p);
+    delete c;
+}
+
+int spec_verify_init(const spec_verify_config* cfg, spec_verify_ctx** out)
+{
+    if (!cfg || !out) return fail(SV_ERR_INVALID_ARG, "null config or output pointer");
+    *out = nullptr;
+    int rc = validate_config(*cfg);
+    if (rc) return rc;
+    int ndev = 0;
+    if (hipGetDeviceCount(&ndev) != hipSuccess || ndev < 1)
+        return fail(SV_ERR_NO_DEVICE, "no HIP device visible");
+    int dev = 0;
+    HIP_TRY(hipGetDevice(&dev));
+    hipDeviceProp_t prop;
+    HIP_TRY(hipGetDeviceProperties(&prop, dev));
+    if (strncmp(prop.gcnArchName, "gfx950", 6) != 0)
+        return fail(SV_ERR_NO_DEVICE, std::string("device is ") + prop.gcnArchName + ", not gfx950");
+
+    spec_verify_ctx* c = new spec_verify_ctx();
+    c->c = *cfg;
+    c->device = dev;
+    const spec_verify_config& k = c->c;
+    c->K1 = k.k_draft + 1;
+    c->T_max = k.max_batch * c->K1;
+    c->QD = k.n_q_heads * k.head_dim;
+    c->QKV = (k.n_q_heads + 2 * k.n_kv_heads) * k.head_dim;
+    c->bf = k.weight_dtype != SV_F32;
+    const int T = c->T_max, H = k.hidden;
+    const size_t AES = c->bf ? 2 : 4;
+
+    // attention plan: rows per KV head and chunking
+    int G = k.n_q_heads / k.n_kv_heads;
+    int R = c->K1 * G;
+    int QF = cdiv(R, 16);
+    c->att_QPW = QF >= 2 ? 2 : 1;
+    c->att_QG = cdiv(QF, c->att_QPW);
+    {
+        long work = (long)k.max_batch * k.n_kv_heads * c->att_QG * k.kv_capacity;
+        int ch = 64;
+        while (ch < 512 && work / ch > 2 * 2048) ch *= 2;
+        c->att_CH = ch;
+        c->att_maxch = cdiv(k.kv_capacity, ch);
+        if (c->att_maxch > ATT_MAXCH_CAP) {
+            delete c;
+            return fail(SV_ERR_UNSUPPORTED, "kv_capacity too large for the attention plan");
+        }
+    }
+
+    int E = k.n_experts, tk = k.top_k, S = k.n_shared;
+    long moe_rows = (long)T * tk + (long)S * T;
+    int NT_lm = cdiv(k.vocab, 64);
+    int NT_lg = cdiv(k.vocab, 1024);
+    size_t part_cols = std::max<size_t>({(size_t)c->QKV, (size_t)H, (size_t)(E > 0 ? E : 1)});
+    c->parts_elems = (size_t)KS_MAX * T * part_cols;
+    c->keys_elems = (size_t)std::max(NT_lm, NT_lg) * T;
+
+#define ALLOC(p, n)                                           \
+    do {                                                      \
+        int r_ = dalloc(c, &(p), (n));                        \
+        if (r_) { spec_verify_destroy(c); return r_; }        \
+    } while (0)
+    char* hbuf = nullptr;
+    char* qbuf = nullptr;
+    char* obuf = nullptr;
+    ALLOC(c->x, (size_t)T * H);
+    ALLOC(hbuf, (size_t)T * H * AES);
+    c->h = hbuf;
+    ALLOC(c->parts, c->parts_elems);
+    ALLOC(qbuf, (size_t)T * c->QD * AES);
+    c->q = qbuf;
+    ALLOC(obuf, (size_t)T * c->QD * AES);
+    c->o = obuf;
+    size_t prow = (size_t)k.max_batch * k.n_q_heads * c->K1 * c->att_maxch;
+    ALLOC(c->opart, prow * k.head_dim);
+    ALLOC(c->mlpart, prow * 2);
+    ALLOC(c->rope, (size_t)k.kv_capacity * (k.head_dim / 2));
+    ALLOC(c->keys, c->keys_elems);
+    ALLOC(c->seq_err, (size_t)k.max_batch);
+    ALLOC(c->err_word, 1);
+    if (k.ffn_kind == SV_FFN_MOE) {
+        char* abuf = nullptr;
+        ALLOC(c->probs, (size_t)T * E);
+        ALLOC(c->sel, (size_t)T * tk);
+        ALLOC(c->gate, (size_t)T * tk);
+        ALLOC(c->slot, (size_t)T * tk);
+        ALLOC(c->perm_tok, (size_t)moe_rows);
+        ALLOC(c->tiles, (size_t)3 * (E + moe_rows + 8));
+        ALLOC(c->n_tiles, 1);
+        ALLOC(abuf, (size_t)moe_rows * k.expert_inter * AES);
+        c->act = abuf;
+        ALLOC(c->y, (size_t)moe_rows * H);
+    } else {
+        char* abuf = nullptr;
+        ALLOC(abuf, (size_t)T * k.dense_inter * AES);
+        c->act = abuf;
+    }
+#undef ALLOC
+    // rotary table: angle pos * theta^(-2i/D) in double, stored as fp32 (cos, sin)
+    {
+        int half = k.head_dim / 2;
+        std::vector<float2> tab((size_t)k.kv_capacity * half);
+        for (int p = 0; p < k.kv_capacity; p++)
+            for (int i = 0; i < half; i++) {
+                double ang = (double)p * std::pow((double)k.rope_theta, -2.0 * i / k.head_dim);
+                tab[(size_t)p * half + i] = make_float2((float)std::cos(ang), (float)std::sin(ang));
+            }
+        hipError_t e = hipMemcpy(c->rope, tab.data(), tab.size() * sizeof(float2),
+                                 hipMemcpyHostToDevice);
+        if (e != hipSuccess) {
+            spec_verify_destroy(c);
+            return fail(SV_ERR_HIP, std::string("rope upload: ") + hipGetErrorString(e));
+        }
+    }
+    hipError_t e = hipMemset(c->err_word, 0, sizeof(unsigned));
+    if (e != hipSuccess) {
+        spec_verify_destroy(c);
+        return fail(SV_ERR_HIP, std::string("error word reset: ") + hipGetErrorString(e));
+    }
+    *out = c;
+    return SV_OK;
+}
+
+int spec_verify_set_debug(spec_verify_ctx* c, float* logits, float* hidden, int32_t* target,
+                          int32_t* routing)
+{
+    if (!c) return fail(SV_ERR_INVALID_ARG, "null context");
+    c->dbg_logits = logits;
+    c->dbg_hidden = hidden;
+    c->dbg_target = target;
+    c->dbg_routing = routing;
+    return SV_OK;
+}
+
+int spec_verify_step(spec_verify_ctx* c, const spec_verify_weights* w, void* k_cache,
+                     void* v_cache, const int32_t* committed, const int32_t* drafts,
+                     const int32_t* ctx_in, int32_t* ctx_out, int B, int32_t* accepted,
+                     int32_t* next_tok, void* stream)
+{
+    if (!c || !w) return fail(SV_ERR_INVALID_ARG, "null context or weights");
+    if (B < 1 || B > c->c.max_batch) return fail(SV_ERR_INVALID_ARG, "batch outside [1, max_batch]");
+    if (!k_cache || !v_cache || !committed || !drafts || !ctx_in || !ctx_out || !accepted ||
+        !next_tok)
+        return fail(SV_ERR_INVALID_ARG, "null buffer pointer");
+    const spec_verify_config& k = c->c;
+    if (!w->embed || !w->layers || !w->final_norm || !w->lm_head)
+        return fail(SV_ERR_INVALID_ARG, "null weight pointer");
+    const bool fp8 = k.weight_dtype == SV_FP8;
+    if (fp8 && !w->lm_scale) return fail(SV_ERR_INVALID_ARG, "fp8 weights need lm_scale");
+    for (int l = 0; l < k.n_layers; l++) {
+        const spec_verify_layer& L = w->layers[l];
+        bool ok = L.attn_norm && L.ffn_norm && L.w_qkv && L.w_o && L.w_gate_up && L.w_down;
+        if (k.ffn_kind == SV_FFN_MOE) ok = ok && L.w_router && (k.n_shared == 0 || (L.w_sh_gate_up && L.w_sh_down));
+        if (fp8) {
+            ok = ok && L.s_qkv && L.s_o && L.s_gate_up && L.s_down;
+            if (k.ffn_kind == SV_FFN_MOE)
+                ok = ok && L.s_router && (k.n_shared == 0 || (L.s_sh_gate_up && L.s_sh_down));
+        }
+        if (!ok) return fail(SV_ERR_INVALID_ARG, "null pointer in layer " + std::to_string(l));
+    }
+    HIP_TRY(hipSetDevice(c->device));
+    hipStream_t s = (hipStream_t)stream;
+    const int wt = k.weight_dtype, step = wsteps(wt);
+    const int K1 = c->K1, T = B * K1, H = k.hidden, L = k.n_layers, QKV = c->QKV, QD = c->QD;
+    const bool bf = c->bf;
+    const size_t AES = bf ? 2 : 4;
+    (void)AES;
+
+    RowArgs ra;
+    memset(&ra, 0, sizeof(ra));
+    ra.H = H;
+    ra.K1 = K1;
+    ra.V = k.vocab;
+    ra.cap = k.kv_capacity;
+    ra.E = k.n_experts;
+    ra.topk = k.top_k;
+    ra.n_shared = k.n_shared;
+    ra.T = T;
+    ra.eps = k.rms_eps;
+    ra.committed = committed;
+    ra.drafts = drafts;
+    ra.ctx_in = ctx_in;
+    ra.seq_err = c->seq_err;
+    ra.err_word = c->err_word;
+    ra.embed = w->embed;
+    ra.x = c->x;
+    ra.h = c->h;
+    ra.gain = w->layers[0].attn_norm;
+    if (bf) embed_norm_kernel<true><<<T, 256, 0, s>>>(ra);
+    else embed_norm_kernel<false><<<T, 256, 0, s>>>(ra);
+
+    const int MFd = rows_mf(T);
+    const int MTd = cdiv(T, 16 * MFd);
+    auto dense_gemm = [&](int mode, const void* X, long ldx, int N, int Kd, const void* W,
+                          const float* ws, void* out, long ldo, int allow_split) -> int {
+        GemmArgs a = dense_args(X, ldx, T, N, Kd, W, ws);
+        a.MT = MTd;
+        a.NT = cdiv(N, 64);
+        long waves = (long)a.NT * a.MT * 4;
+        a.ksplit = allow_split ? pick_ksplit(waves, Kd, step) : 1;
+        a.out = out;
+        a.ldo = ldo;
+        a.split_stride = (long)T * ldo;
+        launch_gemm(wt, mode, MFd, a, s);
+        return a.ksplit;
+    };
+
+    AttnArgs at;
+    memset(&at, 0, sizeof(at));
+    at.q = c->q;
+    at.kc = k_cache;
+    at.vc = v_cache;
+    at.ctx_in = ctx_in;
+    at.seq_err = c->seq_err;
+    at.L = L;
+    at.n_q = k.n_q_heads;
+    at.n_kv = k.n_kv_heads;
+    at.D = k.head_dim;
+    at.K1 = K1;
+    at.cap = k.kv_capacity;
+    at.CH = c->att_CH;
+    at.maxch = c->att_maxch;
+    at.QG = c->att_QG;
+    at.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)k.head_dim));
+    at.opart = c->opart;
+    at.mlpart = c->mlpart;
+
+    for (int l = 0; l < L; l++) {
+        const spec_verify_layer& Lw = w->layers[l];
+        // ---- attention half
+        int ks;
+        {
+            ProfScope ps(c, SV_KC_QKV, s);
+            ks = dense_gemm(GM_STORE, c->h, H, QKV, H, Lw.w_qkv, Lw.s_qkv, c->parts, QKV, 1);
+        }
+        RopeArgs rp;
+        rp.qkv = c->parts;
+        rp.nsplit = ks;
+        rp.T = T;
+        rp.K1 = K1;
+        rp.n_q = k.n_q_heads;
+        rp.n_kv = k.n_kv_heads;
+        rp.D = k.head_dim;
+        rp.L = L;
+        rp.layer = l;
+        rp.cap = k.kv_capacity;
+        rp.ctx_in = ctx_in;
+        rp.seq_err = c->seq_err;
+        rp.rope = c->rope;
+        rp.q = c->q;
+        rp.kc = k_cache;
+        rp.vc = v_cache;
+        if (bf) rope_append_kernel<true><<<T, 256, 0, s>>>(rp);
+        else rope_append_kernel<false><<<T, 256, 0, s>>>(rp);
+
+        at.layer = l;
+        {
+            ProfScope ps(c, SV_KC_ATTENTION, s);
+            dim3 grid(c->att_maxch, k.n_kv_heads * c->att_QG, B);
+            if (bf) {
+                if (k.head_dim == 128) {
+                    if (c->att_QPW == 2) attn_split_kernel<true, 2, 128><<<grid, 64, 0, s>>>(at);
+                    else attn_split_kernel<true, 1, 128><<<grid, 64, 0, s>>>(at);
+                } else {
+                    if (c->att_QPW == 2) attn_split_kernel<true, 2, 64><<<grid, 64, 0, s>>>(at);
+                    else attn_split_kernel<true, 1, 64><<<grid, 64, 0, s>>>(at);
+                }
+            } else {
+                if (k.head_dim == 128) {
+                    if (c->att_QPW == 2) attn_split_kernel<false, 2, 128><<<grid, 64, 0, s>>>(at);
+                    else attn_split_kernel<false, 1, 128><<<grid, 64, 0, s>>>(at);
+                } else {
+                    if (c->att_QPW == 2) attn_split_kernel<false, 2, 64><<<grid, 64, 0, s>>>(at);
+                    else attn_split_kernel<false, 1, 64><<<grid, 64, 0, s>>>(at);
+                }
+            }
+        }
+        {
+            int rows = B * k.n_q_heads * K1;
+            if (bf) attn_merge_kernel<true><<<rows, 64, 0, s>>>(at, c->o);
+            else attn_merge_kernel<false><<<rows, 64, 0, s>>>(at, c->o);
+        }
+        ks = dense_gemm(GM_STORE, c->o, QD, H, QD, Lw.w_o, Lw.s_o, c->parts, H, 1);
+        ra.parts = c->parts;
+        ra.nsplit = ks;
+        ra.gain = Lw.ffn_norm;
+        ra.dbg_hidden = nullptr;
+        if (bf) residual_norm_kernel<true, false><<<T, 256, 0, s>>>(ra);
+        else residual_norm_kernel<false, false><<<T, 256, 0, s>>>(ra);
+
+        // ---- feed-forward half
+        const float* next_gain = (l + 1 < L) ? w->layers[l + 1].attn_norm : w->final_norm;
+        float* dbg_h = c->dbg_hidden ? c->dbg_hidden + (size_t)l * T * H : nullptr;
+        if (k.ffn_kind == SV_FFN_MOE) {
+            const int E = k.n_experts, tk = k.top_k, S = k.n_shared, I = k.expert_inter;
+            ks = dense_gemm(GM_STORE, c->h, H, E, H, Lw.w_router, Lw.s_router, c->parts, E, 1);
+            const int avg_rows = std::max(1, T * tk / E);
+            const int MFe = rows_mf(avg_rows);
+            const int BMe = 16 * MFe;
+            const int max_tiles = std::min(E, T * tk) + (T * tk) / BMe + S * cdiv(T, BMe) + 1;
+            RouteArgs ro;
+            ro.logits = c->parts;
+            ro.nsplit = ks;
+            ro.T = T;
+            ro.E = E;
+            ro.topk = tk;
+            ro.n_shared = S;
+            ro.renorm = k.renorm_topk;
+            ro.BM = BMe;
+            ro.max_tiles = max_tiles;
+            ro.probs = c->probs;
+            ro.dbg_sel = c->dbg_routing ? c->dbg_routing + (size_t)l * T * tk : nullptr;
+            ro.sel = c->sel;
+            ro.gate = c->gate;
+            ro.slot = c->slot;
+            ro.perm_tok = c->perm_tok;
+            ro.tiles = c->tiles;
+            ro.n_tiles = c->n_tiles;
+            route_kernel<<<1, 256, (size_t)T * E * sizeof(unsigned short), s>>>(ro);
+
+            GemmArgs g;
+            memset(&g, 0, sizeof(g));
+            g.X = c->h;
+            g.ldx = H;
+            g.gather = c->perm_tok;
+            g.N = I;
+            g.K = H;
+            g.ksplit = 1;
+            g.W = Lw.w_gate_up;
+            g.ws = Lw.s_gate_up;
+            g.w_gstride = (long)2 * I * H;
+            g.s_gstride = 2L * I;
+            g.W2 = Lw.w_sh_gate_up;
+            g.ws2 = Lw.s_sh_gate_up;
+            g.w2_gstride = (long)2 * I * H;
+            g.s2_gstride = 2L * I;
+            g.G1 = E;
+            g.dual_off = I;
+            g.tiles = c->tiles;
+            g.n_tiles = c->n_tiles;
+            g.MT = max_tiles;
+            g.NT = cdiv(I, 64);
+            g.out = c->act;
+            g.ldo = I;
+            {
+                ProfScope ps(c, SV_KC_EXPERT_GATE_UP, s);
+                launch_gemm(wt, GM_SWIGLU, MFe, g, s);
+            }
+            GemmArgs d = g;
+            d.X = c->act;
+            d.ldx = I;
+            d.gather = nullptr;
+            d.N = H;
+            d.K = I;
+            d.W = Lw.w_down;
+            d.ws = Lw.s_down;
+            d.w_gstride = (long)H * I;
+            d.s_gstride = H;
+            d.W2 = Lw.w_sh_down;
+            d.ws2 = Lw.s_sh_down;
+            d.w2_gstride = (long)H * I;
+            d.s2_gstride = H;
+            d.dual_off = 0;
+            d.NT = cdiv(H, 64);
+            d.out = c->y;
+            d.ldo = H;
+            d.split_stride = 0;
+            {
+                ProfScope ps(c, SV_KC_EXPERT_DOWN, s);
+                launch_gemm(wt, GM_STORE, MFe, d, s);
+            }
+            ra.y = c->y;
+            ra.gate = c->gate;
+            ra.slot = c->slot;
+            ra.gain = next_gain;
+            ra.dbg_hidden = dbg_h;
+            if (bf) residual_norm_kernel<true, true><<<T, 256, 0, s>>>(ra);
+            else residual_norm_kernel<false, true><<<T, 256, 0, s>>>(ra);
+        } else {
+            const int I = k.dense_inter;
+            GemmArgs g = dense_args(c->h, H, T, I, H, Lw.w_gate_up, Lw.s_gate_up);
+            g.MT = MTd;
+            g.NT = cdiv(I, 64);
+            g.dual_off = I;
+            g.out = c->act;
+            g.ldo = I;
+            {
+                ProfScope ps(c, SV_KC_EXPERT_GATE_UP, s);
+                launch_gemm(wt, GM_SWIGLU, MFd, g, s);
+            }
+            {
+                ProfScope ps(c, SV_KC_EXPERT_DOWN, s);
+                ks = dense_gemm(GM_STORE, c->act, I, H, I, Lw.w_down, Lw.s_down, c->parts, H, 1);
+            }
+            ra.parts = c->parts;
+            ra.nsplit = ks;
+            ra.gain = next_gain;
+            ra.dbg_hidden = dbg_h;
+            if (bf) residual_norm_kernel<true, false><<<T, 256, 0, s>>>(ra);
+            else residual_norm_kernel<false, false><<<T, 256, 0, s>>>(ra);
+        }
+    }
+
+    // ---- LM head + argmax, acceptance
+    const int NT_lm = cdiv(k.vocab, 64);
+    {
+        GemmArgs a = dense_args(c->h, H, T, k.vocab, H, w->lm_head, w->lm_scale);
+        a.MT = MTd;
+        a.NT = NT_lm;
+        a.keys = c->keys;
+        a.key_ld = T;
+        a.dbg = c->dbg_logits;
+        a.dbg_ld = k.vocab;
+        ProfScope ps(c, SV_KC_LM_HEAD, s);
+        launch_gemm(wt, GM_ARGMAX, MFd, a, s);
+    }
+    AcceptArgs ac;
+    ac.keys = c->keys;
+    ac.NT = NT_lm;
+    ac.T = T;
+    ac.K1 = K1;
+    ac.drafts = drafts;
+    ac.ctx_in = ctx_in;
+    ac.ctx_out = ctx_out;
+    ac.accepted = accepted;
+    ac.next_tok = next_tok;
+    ac.target = c->dbg_target;
+    ac.seq_err = c->seq_err;
+    ac.err_word = c->err_word;
+    accept_kernel<<<B, 64, 0, s>>>(ac);
+    HIP_TRY(hipGetLastError());
+    return SV_OK;
+}
+
+int spec_verify_accept_from_logits(spec_verify_ctx* c, const float* logits, const int32_t* drafts,
+                                   const int32_t* ctx_in, int32_t* ctx_out, int B,
+                                   int32_t* accepted, int32_t* next_tok, int32_t* target,
+                                   void* stream)
+{
+    if (!c) return fail(SV_ERR_INVALID_ARG, "null context");
+    if (B < 1 || B > c->c.max_batch) return fail(SV_ERR_INVALID_ARG, "batch outside [1, max_batch]");
+    if (!logits || !drafts || !ctx_in || !ctx_out || !accepted || !next_tok)
+        return fail(SV_ERR_INVALID_ARG, "null buffer pointer");
+    HIP_TRY(hipSetDevice(c->device));
+    hipStream_t s = (hipStream_t)stream;
+    const int T = B * c->K1, V = c->c.vocab;
+    const int NT = cdiv(V, 1024);
+    logits_keys_kernel<<<dim3(NT, T), 256, 0, s>>>(logits, V, T, c->keys);
+    AcceptArgs ac;
+    ac.keys = c->keys;
+    ac.NT = NT;
+    ac.T = T;
+    ac.K1 = c->K1;
+    ac.drafts = drafts;
+    ac.ctx_in = ctx_in;
+    ac.ctx_out = ctx_out;
+    ac.accepted = accepted;
+    ac.next_tok = next_tok;
+    ac.target = target;
+    ac.seq_err = nullptr;
+    ac.err_word = c->err_word;
+    accept_kernel<<<B, 64, 0, s>>>(ac);
+    HIP_TRY(hipGetLastError());
+    return SV_OK;
+}
+
+int spec_verify_error_word(spec_verify_ctx* c, uint32_t* out, int clear, void* stream)
+{
+    if (!c || !out) return fail(SV_ERR_INVALID_ARG, "null argument");
+    HIP_TRY(hipSetDevice(c->device));
+    hipStream_t s = (hipStream_t)stream;
+    HIP_TRY(hipStreamSynchronize(s));
+    unsigned v = 0;
+    HIP_TRY(hipMemcpy(&v, c->err_word, sizeof(v), hipMemcpyDeviceToHost));
+    *out = v;
+    if (clear) HIP_TRY(hipMemset(c->err_word, 0, sizeof(unsigned)));
+    return SV_OK;
+}
+
+int spec_verify_kernel_time(spec_verify_ctx* c, int kclass, int enable, double* total_ms,
+                            int* launches)
+{
+    if (!c) return fail(SV_ERR_INVALID_ARG, "null context");
+    if (kclass < 0 || kclass >= SV_KC_COUNT) return fail(SV_ERR_INVALID_ARG, "bad kernel class");
+    HIP_TRY(hipSetDevice(c->device));
+    if (total_ms || launches) {
+        if (c->prof_class != kclass && c->prof_used == 0) return fail(SV_ERR_NOT_SET, "not recording");
+        double tot = 0;
+        for (size_t i = 0; i < c->prof_used; i++) {
+            HIP_TRY(hipEventSynchronize(c->prof_events[i].b));
+            float ms = 0;
+            HIP_TRY(hipEventElapsedTime(&ms, c->prof_events[i].a, c->prof_events[i].b));
+            tot += ms;
+        }
+        if (total_ms) *total_ms = tot;
+        if (launches) *launches = (int)c->prof_used;
+    }
+    if (enable == 1) {
+        if (c->prof_events.empty()) {
+            c->prof_events.resize(8192);
+            for (auto& e : c->prof_events) {
+                HIP_TRY(hipEventCreate(&e.a));
+                HIP_TRY(hipEventCreate(&e.b));
+            }
+        }
+        c->prof_class = kclass;
+        c->prof_used = 0;
+    } else if (enable == 0) {
+        c->prof_class = -1;
+    }
+    return SV_OK;
+}
+
+}  // extern "C"

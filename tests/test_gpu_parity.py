@@ -1,0 +1,231 @@
+"""Parity of the HIP verify step with the CPU oracle on seeded inputs.
+
+Every test calls the library through its C ABI (the ctypes binding) and
+compares with the oracle under the rules in gpu_harness.  Sizes: the tiny and
+batch-1 workloads at full size; scaled versions of the batched MoE, the fp8
+dense GQA and the chained long-context workloads that span several tiles,
+chunks and a ragged tail and that the oracle finishes in seconds.
+"""
+import numpy as np
+import pytest
+import torch
+
+import workloads
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def H():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import gpu_harness
+    return gpu_harness
+
+
+def _verify_case(H, cfg, sampled=None, batch=None, check_kv=True, label=""):
+    case = H.Case(cfg)
+    B = cfg.batch if batch is None else batch
+    sampled = list(range(B)) if sampled is None else sampled
+    H.say(f"[{label}] {cfg.name}: B={B} L={cfg.n_layers} H={cfg.hidden} V={cfg.vocab} "
+          f"K={cfg.k_draft} cap={case.cap} ctx={case.ctx[:B].tolist()[:8]} sampled={sampled}")
+    drafts = case.drafts(sampled)
+    run = H.GpuRun(case, batch=B)
+    g = run.step(case.committed[:B], drafts[:B], case.ctx[:B])
+    H.say(f"[{label}] gpu step done: accepted={g['accepted'][:8].tolist()}")
+    orc = case.oracle()
+    stats = {}
+    for b in sampled:
+        kc, vc = case.oracle_kv(b)
+        forced = run.routing_of(g, b)
+        o = orc.verify_step(kc, vc, [int(case.committed[b])], drafts[b:b + 1].numpy(),
+                            [int(case.ctx[b])], want_logits=True, want_layer_hidden=True,
+                            force_sel=forced, want_routing=forced is not None)
+        H.check_routing(cfg, forced, o, stats, label=f"seq {b}")
+        H.compare_sequence(cfg, g, b, o, 0, stats)
+        if check_kv:
+            H.compare_new_kv(cfg, run, b, kc, vc, int(case.ctx[b]), stats)
+    # the step wrote nothing outside the K+1 new slots of each sequence
+    K1 = cfg.k_draft + 1
+    for b in range(B):
+        c = int(case.ctx[b])
+        before = case.k_nat[b].clone()
+        after = run.kc[b].clone()
+        before[:, :, c:c + K1] = 0
+        after[:, :, c:c + K1] = 0
+        assert torch.equal(before, after), f"seq {b}: K cache changed outside the new slots"
+    H.say(f"[{label}] stats {stats}")
+    run.close()
+    return stats, g
+
+
+def test_tiny_fp32_full_size(H):
+    cfg = workloads.get_config("tiny_fp32")
+    stats, _ = _verify_case(H, cfg, label="tiny_fp32")
+    assert stats["max_rel_logit_err"] < 1e-4
+    assert stats["accept_checked"] == 1
+
+
+def test_moe_batch1_full_size(H):
+    cfg = workloads.get_config("moe_b1")
+    stats, _ = _verify_case(H, cfg, label="moe_b1")
+    assert stats["accept_agree"] == 1
+
+
+def test_moe_batched_scaled(H):
+    """The batched MoE stack with fewer layers and a smaller vocabulary; the
+    context range spans several attention chunks and a ragged last tile."""
+    cfg = workloads.scaled(workloads.get_config("moe_b32"), n_layers=3, vocab=8192, batch=12,
+                           ctx=("uniform", 30, 700))
+    stats, _ = _verify_case(H, cfg, label="moe_b32_scaled")
+    assert stats["argmax_agree"] >= 0.9 * stats["positions"]
+
+
+def test_moe_small_shapes(H):
+    """Small MoE shapes: 16 experts, top-4, one shared expert, head_dim 128 with
+    2 heads, contexts from 1 token; norm gains away from 1."""
+    cfg = workloads.scaled(workloads.get_config("moe_b1"), n_layers=2, hidden=256, n_q=2, n_kv=2,
+                           n_experts=16, expert_inter=128, top_k=4, n_shared=1, vocab=2048,
+                           batch=5, ctx=("uniform", 1, 200), norm_gain_std=0.2)
+    _verify_case(H, cfg, label="moe_small_shapes")
+
+
+def test_dense_fp8_gqa_scaled(H):
+    """Block drafts (K = 31) on the dense GQA decoder with e4m3 weights:
+    4 query heads per KV head, 128 query rows per KV head."""
+    cfg = workloads.scaled(workloads.get_config("dense_fp8_b8"), n_layers=2, hidden=512, n_q=8,
+                           n_kv=2, dense_inter=1024, vocab=4096, batch=3,
+                           ctx=("uniform", 100, 900))
+    stats, _ = _verify_case(H, cfg, label="dense_fp8_scaled")
+    assert stats["argmax_agree"] >= 0.8 * stats["positions"]
+
+
+def test_dense_fp8_gqa_full_width_sampled(H):
+    """The full fp8 dense layer width (hidden 2560, 32/8 heads, I 9728, vocab
+    151,936) with 2 layers; two sequences of the batch checked."""
+    cfg = workloads.scaled(workloads.get_config("dense_fp8_b8"), n_layers=2)
+    _verify_case(H, cfg, sampled=[5], label="dense_fp8_wide")
+
+
+def test_deterministic_reruns(H):
+    cfg = workloads.scaled(workloads.get_config("moe_b32"), n_layers=2, vocab=4096, batch=6,
+                           ctx=("uniform", 50, 400))
+    case = H.Case(cfg)
+    H.say("[determinism] two identical steps")
+    outs = []
+    for _ in range(2):
+        run = H.GpuRun(case)
+        outs.append(run.step(case.committed, case.rtok[0], case.ctx))
+        run.close()
+    for k in ("logits", "hidden", "target", "accepted", "next_tok", "ctx_out"):
+        assert np.array_equal(outs[0][k], outs[1][k], equal_nan=True), k
+
+
+def test_chained_steps_scaled(H):
+    """Verify steps chained on the device: ctx_lens_out aliases ctx_lens_in,
+    next_tok becomes the next committed token, and the cache keeps the K/V of
+    accepted positions (rollback by length).  The oracle runs the same chain
+    on its own caches; every step is compared."""
+    cfg = workloads.scaled(workloads.get_config("moe_b64_long"), n_layers=2, vocab=4096,
+                           batch=8, steps=12, ctx=("loguniform", 20, 600))
+    case = H.Case(cfg)
+    B, K = cfg.batch, cfg.k_draft
+    run = H.GpuRun(case)
+    orc = case.oracle()
+    kv = {b: case.oracle_kv(b) for b in range(B)}
+    ctx_dev = case.ctx.to("cuda", torch.int32).clone()
+    com = case.committed.clone()
+    ctx_cpu = case.ctx.clone()
+    stats = {}
+    for s in range(cfg.steps):
+        H.say(f"[chained] step {s} ctx={ctx_cpu.tolist()}")
+        drafts = case.drafts(range(B), step=s, committed=com, ctx=ctx_cpu, kv=kv)
+        g = run.step(com, drafts, ctx_dev, ctx_out=ctx_dev)
+        for b in range(B):
+            kc, vc = kv[b]
+            forced = run.routing_of(g, b)
+            o = orc.verify_step(kc, vc, [int(com[b])], drafts[b:b + 1].numpy(),
+                                [int(ctx_cpu[b])], want_logits=True, force_sel=forced,
+                                want_routing=True)
+            H.check_routing(cfg, forced, o, stats, label=f"step {s} seq {b}")
+            H.compare_sequence(cfg, g, b, o, 0, stats, check_hidden=False)
+            # continue both chains from the oracle's decision
+            com[b] = int(o["next_tok"][0])
+            ctx_cpu[b] = int(o["ctx_out"][0])
+        ctx_dev.copy_(ctx_cpu.to("cuda", torch.int32))
+    H.say(f"[chained] stats {stats}")
+    assert stats["accept_agree"] >= 0.9 * stats["sequences"]
+    assert int(ctx_cpu.min()) > int(case.ctx.min())
+    run.close()
+
+
+def test_accept_from_identical_logits_bit_exact(H):
+    """Acceptance and commit fed the same fp32 logits as the oracle's rule:
+    exact, including ties (lowest index wins) and a NaN position."""
+    import oracle
+    cfg = workloads.scaled(workloads.get_config("tiny_fp32"), batch=7, vocab=50000)
+    case_cap = 4096
+    import speculative_decoding_verify_step_amd as sv
+    B, K, V = cfg.batch, cfg.k_draft, cfg.vocab
+    w = workloads.make_weights(cfg, "cuda")
+    ctx = sv.VerifyContext(cfg, B, case_cap, w)
+    rng = np.random.default_rng(11)
+    logits = rng.standard_normal((B, K + 1, V)).astype(np.float32)
+    g = logits.argmax(-1)
+    # plant ties: a second index with the same maximum value (lower index must win)
+    for b in range(B):
+        for j in range(K + 1):
+            top = g[b, j]
+            other = (top + 1 + b * 7 + j) % V
+            logits[b, j, other] = logits[b, j, top]
+    drafts = np.zeros((B, K), np.int32)
+    want_g = np.array([[oracle.argmax(logits[b, j].astype(np.float64)) for j in range(K + 1)]
+                       for b in range(B)])
+    # sequence b accepts min(b, K) drafts, then a wrong one
+    for b in range(B):
+        for i in range(K):
+            drafts[b, i] = want_g[b, i] if i < min(b, K) else (want_g[b, i] + 1) % V
+    logits[6, 2, 123] = np.nan
+    ctx_in = torch.tensor([100 + b for b in range(B)], dtype=torch.int32, device="cuda")
+    ctx_out = torch.zeros_like(ctx_in)
+    acc = torch.zeros_like(ctx_in)
+    nxt = torch.zeros_like(ctx_in)
+    tgt = torch.zeros((B, K + 1), dtype=torch.int32, device="cuda")
+    H.say("[accept_from_logits] B=7 V=50000 with planted ties and one NaN")
+    ctx.accept_from_logits(torch.from_numpy(logits).cuda(), torch.from_numpy(drafts).cuda(), ctx_in,
+                           ctx_out, acc, nxt, tgt)
+    torch.cuda.synchronize()
+    assert ctx.error_word(clear=True) & sv.SV_DEV_NAN_LOGIT
+    for b in range(B):
+        if b == 6:
+            assert acc[b].item() == -1 and nxt[b].item() == -1 and ctx_out[b].item() == 100 + b
+            continue
+        a, n = oracle.accept(want_g[b], drafts[b])
+        assert np.array_equal(tgt[b].cpu().numpy(), want_g[b])
+        assert (acc[b].item(), nxt[b].item(), ctx_out[b].item()) == (a, n, 100 + b + a + 1)
+    ctx.close()
+
+
+def test_device_side_errors_are_reported_without_writes(H):
+    """A token outside the vocabulary and a context with no room for K+1 new
+    positions: accepted/next = -1, ctx unchanged, error bits set, the cache of
+    the offending sequence untouched; the other sequences are unaffected."""
+    cfg = workloads.scaled(workloads.get_config("tiny_fp32"), batch=3, n_layers=2)
+    case = H.Case(cfg)
+    run = H.GpuRun(case)
+    com = case.committed.clone()
+    com[1] = cfg.vocab + 5
+    ctx = case.ctx.clone()
+    ctx[2] = case.cap - cfg.k_draft          # no room for K+1 positions
+    H.say("[errors] bad token in seq 1, capacity overflow in seq 2")
+    before = run.kc.clone()
+    g = run.step(com, case.rtok[0], ctx)
+    assert g["accepted"][1] == -1 and g["next_tok"][1] == -1 and g["ctx_out"][1] == ctx[1]
+    assert g["accepted"][2] == -1 and g["ctx_out"][2] == ctx[2]
+    assert torch.equal(before[2], run.kc[2])
+    word = run.ctx.error_word(clear=True)
+    import speculative_decoding_verify_step_amd as sv
+    assert word & sv.SV_DEV_BAD_TOKEN and word & sv.SV_DEV_CAPACITY
+    assert g["accepted"][0] >= 0 and g["ctx_out"][0] == ctx[0] + g["accepted"][0] + 1
+    assert run.ctx.error_word() == 0
+    run.close()

@@ -370,3 +370,30 @@ def test_error_status(oracle_mod):
     assert out["ctx_out"][0] == 10
     out = orc.verify_step(kc, vc, [1], [[1, 2, 3]], [cap - 3])
     assert out["status"][0] == oracle_mod.CAPACITY and out["next_tok"][0] == -1
+
+
+def test_routing_hook_forcing_own_choice_is_identity(oracle_mod):
+    """Forcing the oracle's own expert choice reproduces the free run bit for
+    bit; forcing another choice changes the result; the reported router logits
+    give back the reported selection through softmax + top-k."""
+    cfg = workloads.scaled(_small_moe(), n_layers=2, batch=1, k_draft=3)
+    w = workloads.make_weights(cfg)
+    cap = 128
+    k, v = workloads.kv_cache(cfg, capacity=cap)
+    orc = oracle_mod.Oracle(cfg, w, cap)
+    args = ([3], [[10, 20, 30]], [50])
+    kc, vc = orc.kv_np(k, v)
+    free = orc.verify_step(kc, vc, *args, want_logits=True, want_routing=True)
+    kc, vc = orc.kv_np(k, v)
+    same = orc.verify_step(kc, vc, *args, want_logits=True, force_sel=free["sel"])
+    np.testing.assert_array_equal(same["logits"], free["logits"])
+    for l in range(cfg.n_layers):
+        for j in range(4):
+            r = free["router_logits"][0, l, j]
+            np.testing.assert_array_equal(free["sel"][0, l, j],
+                                          oracle_mod.topk(oracle_mod.softmax(r), cfg.top_k))
+    other = free["sel"].copy()
+    other[0, 0, 0] = [e for e in range(cfg.n_experts) if e not in other[0, 0, 0]][:cfg.top_k]
+    kc, vc = orc.kv_np(k, v)
+    diff = orc.verify_step(kc, vc, *args, want_logits=True, force_sel=other)
+    assert np.abs(diff["logits"] - free["logits"]).max() > 1e-6
