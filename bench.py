@@ -1,0 +1,293 @@
+"""Benchmark of the greedy speculative-decoding verify step on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config moe_b1]
+
+A step is one spec_verify_step over a whole batch (every row of the hot
+path: embedding, all decoder layers, LM head + argmax, acceptance + commit).
+Inputs are seeded synthetic tensors resident in HBM before timing starts.
+Drafts follow the workload's rule (copy the target's greedy token with the
+match probability, else a uniform token) and are recorded in untimed passes,
+then replayed, so the timed steps accept exactly what was recorded.
+
+Workloads: single-step ones repeat the same step (same context, same drafts)
+K times; the chained long-context workload runs K consecutive steps in which
+contexts grow by accepted + 1 and the bonus token becomes the next committed
+token, all on the device.
+
+One JSON line is printed: accepted tokens/s (sum over sequences of
+accepted + 1 per step, over the timed wall clock), microseconds per step, the
+roofline of the dominant kernel (algorithmic bytes / its mean duration from
+HIP events recorded around its launches on the launch stream during the timed
+steps) and the CPU oracle's throughput on the host as a reported baseline.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+METRIC = "accepted tokens/s + verify-step µs at batch 1/32/64, K=3, MoE decoder"
+WBYTES = {"f32": 4, "bf16": 2, "fp8": 1}
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+# ------------------------------------------------------------ byte model
+def lm_head_bytes(cfg, T):
+    """Algorithmic HBM bytes of one LM-head launch: the weight matrix (and
+    fp8 row scales) once, the normalised activations once, the argmax
+    partial keys written (one 8-byte key per 64-column tile and row)."""
+    V, H = cfg.vocab, cfg.hidden
+    w = V * H * WBYTES[cfg.wdtype] + (V * 4 if cfg.wdtype == "fp8" else 0)
+    act = T * H * (4 if cfg.wdtype == "f32" else 2)
+    keys = ((V + 63) // 64) * T * 8
+    return w + act + keys
+
+
+def step_bytes(cfg, ctx, distinct_experts):
+    """Algorithmic bytes of one step: every weight the step needs, once
+    (routed experts counted from the actual routing), the cached context read
+    once per (sequence, layer, KV head) and the new K/V written."""
+    H, D, L = cfg.hidden, cfg.head_dim, cfg.n_layers
+    wb = WBYTES[cfg.wdtype]
+    sc = 4 if cfg.wdtype == "fp8" else 0
+    T = cfg.batch * (cfg.k_draft + 1)
+    kvb = 4 if cfg.kvdtype == "f32" else 2
+    per_layer = (cfg.qkv_dim * H + H * cfg.n_q * D) * wb + (cfg.qkv_dim + H) * sc
+    total = 0
+    for l in range(L):
+        total += per_layer
+        if cfg.ffn == "moe":
+            ex = 3 * H * cfg.expert_inter * wb
+            total += cfg.n_experts * H * wb + (distinct_experts[l] + cfg.n_shared) * ex
+        else:
+            total += 3 * H * cfg.dense_inter * wb + (3 * cfg.dense_inter) * sc
+    total += cfg.vocab * H * wb + cfg.vocab * sc                 # LM head
+    total += T * H * (4 if cfg.embdtype == "f32" else 2)        # embedding rows
+    kv_read = sum(int(c) + cfg.k_draft + 1 for c in ctx) * 2 * cfg.n_kv * D * L * kvb
+    kv_write = T * 2 * cfg.n_kv * D * L * kvb
+    return total + kv_read + kv_write
+
+
+# ------------------------------------------------------------- workload
+def setup(cfg, steps):
+    import torch
+
+    import speculative_decoding_verify_step_amd as sv
+    import workloads
+
+    cap = workloads.capacity_for(workloads.scaled(cfg, steps=max(cfg.steps, steps)))
+    w = workloads.make_weights(cfg, "cuda")
+    k, v = workloads.kv_cache(cfg, "cuda", capacity=cap)
+    v = sv.to_library_v_layout(v)
+    torch.cuda.synchronize()
+    ctx = workloads.context_lengths(cfg)
+    com = workloads.committed_tokens(cfg)
+    n_rec = steps if cfg.steps > 1 else 1
+    coins, rtok = workloads.draft_randomness(cfg, steps=n_rec)
+    vc = sv.VerifyContext(cfg, cfg.batch, cap, w)
+    return dict(sv=sv, w=w, k=k, v=v, cap=cap, ctx=ctx, com=com, coins=coins, rtok=rtok, vc=vc,
+                n_rec=n_rec)
+
+
+def record_drafts(cfg, S):
+    """Drafts of every step by the workload's rule, the target's tokens taken
+    from untimed passes of the library itself; returns per-step device
+    tensors plus the routing of the first step (for the byte model)."""
+    import torch
+    sv, vc = S["sv"], S["vc"]
+    B, K = cfg.batch, cfg.k_draft
+    K1 = K + 1
+    dev = "cuda"
+    i32 = dict(dtype=torch.int32, device=dev)
+    target = torch.empty(B, K1, **i32)
+    routing = (torch.empty(cfg.n_layers, B * K1, cfg.top_k, **i32) if cfg.ffn == "moe" else None)
+    vc.set_debug(None, None, target, routing)
+    ctx = S["ctx"].to(**i32)
+    com = S["com"].to(**i32)
+    tmp_ctx, acc, nxt = (torch.empty(B, **i32) for _ in range(3))
+    drafts, first_routing = [], None
+    for s in range(S["n_rec"]):
+        d = S["rtok"][s].to(**i32).clone()
+        coin = S["coins"][s].to(dev).bool()
+        for i in range(K):
+            vc.step(S["k"], S["v"], com, d, ctx, tmp_ctx, acc, nxt)
+            d[:, i] = torch.where(coin[:, i], target[:, i], d[:, i])
+        drafts.append(d)
+        if s == 0 and routing is not None:
+            vc.step(S["k"], S["v"], com, d, ctx, tmp_ctx, acc, nxt)
+            first_routing = routing.clone()
+        if S["n_rec"] > 1:     # advance the chain
+            vc.step(S["k"], S["v"], com, d, ctx, ctx, acc, nxt)
+            com = nxt.clone()
+    vc.set_debug(None, None, None, None)
+    torch.cuda.synchronize()
+    return drafts, first_routing
+
+
+def run_bench(cfg, steps, warmup):
+    import torch
+
+    S = setup(cfg, steps)
+    sv, vc = S["sv"], S["vc"]
+    B, K1 = cfg.batch, cfg.k_draft + 1
+    log(f"[bench] {cfg.name}: B={B} L={cfg.n_layers} cap={S['cap']} recording drafts")
+    drafts, routing = record_drafts(cfg, S)
+    i32 = dict(dtype=torch.int32, device="cuda")
+    ctx0 = S["ctx"].to(**i32)
+    com0 = S["com"].to(**i32)
+    nxt, cout = (torch.empty(B, **i32) for _ in range(2))
+    chained = S["n_rec"] > 1
+    distinct = []
+    if routing is not None:
+        for l in range(cfg.n_layers):
+            distinct.append(int(torch.unique(routing[l]).numel()))
+    acc_all = torch.empty(max(steps, warmup, 1), B, **i32)
+    com_bufs = [com0.clone(), com0.clone()]
+
+    def one(i, ctx):
+        # chained: the bonus token of step i is the committed token of step i+1
+        # (two alternating buffers, no copy); contexts grow in place
+        d = drafts[i % len(drafts)]
+        if chained:
+            vc.step(S["k"], S["v"], com_bufs[i % 2], d, ctx, ctx, acc_all[i], com_bufs[(i + 1) % 2])
+        else:
+            vc.step(S["k"], S["v"], com0, d, ctx, cout, acc_all[i], nxt)
+
+    # warmup (untimed); a chained run restarts from the recorded start state
+    ctx = ctx0.clone()
+    for i in range(warmup):
+        one(i, ctx)
+    torch.cuda.synchronize()
+    ctx = ctx0.clone()
+    com_bufs[0].copy_(com0)
+    ctx_start = ctx.clone()
+    # timed region
+    kc = sv.SV_KC_LM_HEAD
+    vc.kernel_time(kc, enable=1, query=False)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        one(i, ctx)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    acc_sum = acc_all[:steps].to(torch.int64).sum(0)
+    lm_ms, lm_n = vc.kernel_time(kc, enable=0)
+    assert vc.error_word() == 0, "device error during the benchmark"
+    wall = t1 - t0
+    committed_tokens = int(acc_sum.sum().item()) + steps * B
+    ms_step = wall * 1e3 / steps
+    res = {
+        "ms_per_step": ms_step,
+        "tok_s": committed_tokens / wall,
+        "tau": committed_tokens / (steps * B),
+        "lm_ms": lm_ms / max(lm_n, 1),
+        "lm_launches": lm_n,
+        "lm_bytes": lm_head_bytes(cfg, B * K1),
+        "step_bytes": step_bytes(cfg, (ctx_start if not chained else ctx0).tolist(),
+                                 distinct or [0] * cfg.n_layers),
+        "distinct_experts": distinct,
+        "ctx_end": ctx.tolist() if chained else None,
+    }
+    vc.close()
+    return res
+
+
+# ----------------------------------------------------------- CPU baseline
+def cpu_baseline(cfg, budget_s=15.0):
+    """The oracle, as it is, on this host: whole verify steps of sequence 0
+    of the workload (the same shapes and seeds; drafts by the workload's rule
+    through the oracle), repeated until about `budget_s` seconds of work."""
+    import numpy as np
+
+    import oracle
+    import workloads
+
+    c1 = workloads.scaled(cfg, batch=1)
+    cap = workloads.capacity_for(cfg)
+    w = workloads.make_weights(c1, "cpu")
+    k, v = workloads.kv_cache(c1, "cpu", capacity=cap)
+    orc = oracle.Oracle(c1, w, cap)
+    kc, vc = orc.kv_np(k, v)
+    ctx = int(workloads.context_lengths(cfg)[0])
+    com = int(workloads.committed_tokens(cfg)[0])
+    coins, rtok = workloads.draft_randomness(cfg, steps=1)
+    d = orc.make_drafts(kc, vc, 0, ctx, com, coins[0, 0], rtok[0, 0])
+    n, tok, t0 = 0, 0, time.perf_counter()
+    while True:
+        out = orc.verify_step(kc, vc, [com], d[None], [ctx])
+        tok += int(out["accepted"][0]) + 1
+        n += 1
+        el = time.perf_counter() - t0
+        if el >= budget_s or n >= 200:
+            break
+    return {"value": tok / el, "unit": "tokens/s", "cores": oracle.num_threads(),
+            "kind": "oracle",
+            "sample": f"{n} whole verify steps of one sequence of {cfg.name} "
+                      f"(ctx {ctx}, K={cfg.k_draft}, {cfg.n_layers} layer(s)), "
+                      f"{el:.1f} s; per-step {1e3 * el / n:.1f} ms"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=None)
+    ap.add_argument("--warmup", type=int, default=None)
+    ap.add_argument("--config", default="moe_b1")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU; --gpus must be 1",
+                          "n_gpus": args.gpus}))
+        sys.exit(2)
+    import workloads
+    cfg = workloads.get_config(args.config)
+    steps = args.steps if args.steps is not None else (cfg.steps if cfg.steps > 1 else 200)
+    warmup = args.warmup if args.warmup is not None else 10
+    r = run_bench(cfg, steps, warmup)
+    lm_gbs = r["lm_bytes"] / (r["lm_ms"] * 1e-3) / 1e9 if r["lm_ms"] > 0 else None
+    out = {
+        "metric": METRIC,
+        "value": r["tok_s"],
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": steps,
+        "warmup": warmup,
+        "ms_per_step": r["ms_per_step"],
+        "us_per_step": r["ms_per_step"] * 1e3,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if cfg.wdtype == "bf16" else cfg.wdtype,
+        "data": "synthetic (seeded N(0,0.02) weights, seeded KV cache and drafts)",
+        "config": {"workload": cfg.name, "batch": cfg.batch, "k_draft": cfg.k_draft,
+                   "layers": cfg.n_layers, "hidden": cfg.hidden, "vocab": cfg.vocab,
+                   "ctx": list(cfg.ctx), "chained_steps": cfg.steps > 1,
+                   "weight_layout": "tiled16",
+                   "tokens_per_verify": r["tau"]},
+        "roofline": {"bound": "hbm", "kernel": "lm_head_argmax",
+                     "achieved": lm_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": (lm_gbs / HBM_PEAK_GBS) if lm_gbs else None, "traffic": None,
+                     "mean_us": r["lm_ms"] * 1e3, "bytes_per_launch": r["lm_bytes"],
+                     "launches_timed": r["lm_launches"]},
+        "step_roofline": {"bytes_per_step": r["step_bytes"],
+                          "achieved_GBs": r["step_bytes"] / (r["ms_per_step"] * 1e-3) / 1e9,
+                          "frac": r["step_bytes"] / (r["ms_per_step"] * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                          "distinct_experts_per_layer": r["distinct_experts"]},
+    }
+    if not args.no_cpu_baseline:
+        log("[bench] timing the CPU oracle")
+        out["cpu_baseline"] = cpu_baseline(cfg)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -67,6 +67,17 @@
  *   fp8 scales: s_x has one fp32 per row of w_x, laid out like w_x without
  *   its last dimension (e.g. s_gate_up [E][2I]).
  *
+ * Two layouts are accepted for the matrices that feed a matrix product
+ * (w_qkv, w_o, w_router, w_gate_up, w_down, w_sh_gate_up, w_sh_down,
+ * lm_head), chosen by spec_verify_weights.layout:
+ *   SV_LAYOUT_ROW_MAJOR  as above;
+ *   SV_LAYOUT_TILED16    rows grouped in blocks of 16, each block stored step
+ *                        by step along the reduction dimension (exact format
+ *                        at spec_verify_pack_tiled16).  Every 64-lane load of a
+ *                        weight fragment is then one contiguous KiB, which is
+ *                        what lets the weight stream run near the HBM peak.
+ * The embedding is always row-major (it is gathered by row, not multiplied).
+ *
  * KV-cache layout (storage = kv dtype), capacity slots per (sequence, layer,
  * KV head), sequence b occupying one contiguous region:
  *   K cache: [B_max][L][n_kv][capacity][D]   (position-major)
@@ -107,6 +118,10 @@ extern "C" {
 #define SV_DEV_BAD_TOKEN 1u       /* a committed or draft token outside [0, V) */
 #define SV_DEV_CAPACITY 2u        /* ctx < 0 or ctx + K + 1 > capacity */
 #define SV_DEV_NAN_LOGIT 4u       /* a NaN among a position's logits */
+
+/* weight layouts */
+#define SV_LAYOUT_ROW_MAJOR 0
+#define SV_LAYOUT_TILED16 1
 
 /* kernel classes for spec_verify_kernel_time */
 #define SV_KC_LM_HEAD 0           /* final norm output x LM head + argmax partials */
@@ -160,6 +175,7 @@ typedef struct {
     const float* final_norm;
     const void* lm_head;
     const float* lm_scale;             /* SV_FP8 only */
+    int layout;                        /* SV_LAYOUT_ROW_MAJOR or SV_LAYOUT_TILED16 */
 } spec_verify_weights;
 
 /* Validate `cfg` (host), pick the kernel plan, allocate the workspace for
@@ -214,6 +230,26 @@ int spec_verify_accept_from_logits(spec_verify_ctx* ctx, const float* logits,
                                    const int32_t* draft_toks, const int32_t* ctx_lens_in,
                                    int32_t* ctx_lens_out, int batch, int32_t* accepted_len,
                                    int32_t* next_tok, int32_t* target_tok, void* stream);
+
+/*
+ * Repack one row-major matrix W[rows][cols] (device, storage `dtype`) into
+ * the SV_LAYOUT_TILED16 layout at `dst` (device, caller-owned, at least
+ * spec_verify_tiled16_bytes(rows, cols, dtype) bytes, not overlapping src).
+ * Layout: let esize be the element size (4, 2 or 1), KL = 16 / esize and
+ * S = 4 KL (the reduction step: 16, 32 or 64 elements).  Rows are padded with
+ * zeros to a multiple of 16.  Row block r (rows 16r .. 16r+15) and step s
+ * (columns sS .. sS+S-1) occupy the 1024 bytes at offset
+ * (r * cols / S + s) * 1024; inside them, the 16 bytes at offset 16 l
+ * (l = 0..63) hold W[16r + l%16][sS + (l/16) KL .. + KL-1].  cols must be a
+ * multiple of S.  A stack of equally shaped matrices (experts) may be packed
+ * as one tall matrix when each matrix's row count is a multiple of 16.
+ * Enqueued on `stream`.
+ */
+int spec_verify_pack_tiled16(const void* src, void* dst, long rows, int cols, int dtype,
+                             void* stream);
+
+/* Bytes of a matrix in the SV_LAYOUT_TILED16 layout (rows padded to 16). */
+long spec_verify_tiled16_bytes(long rows, int cols, int dtype);
 
 /* Read (host) the sticky device error word (SV_DEV_* bits) accumulated since
  * the last clear; synchronises `stream` first.  clear != 0 resets it. */

@@ -103,6 +103,8 @@ def _load():
         lib.or_argmax.argtypes = [P, c_long]
         lib.or_argmax.restype = c_int
         lib.or_accept.argtypes = [c_int, P, P, P, P]
+        lib.or_num_threads.argtypes = []
+        lib.or_num_threads.restype = c_int
         for f in ("or_matvec", "or_rmsnorm", "or_rope", "or_attend", "or_softmax", "or_topk",
                   "or_ffn", "or_accept"):
             getattr(lib, f).restype = None
@@ -370,3 +372,8 @@ def ffn(orc: Oracle, layer: int, h):
     lay = ctypes.byref(orc._layers[layer])
     _load().or_ffn(ctypes.byref(orc._c), lay, _ptr(h), _ptr(y), None, _ptr(sel), None)
     return y, (sel if orc.cfg.ffn == "moe" else None)
+
+
+def num_threads() -> int:
+    """OpenMP threads the oracle's parallel loops use."""
+    return _load().or_num_threads()

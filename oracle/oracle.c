@@ -48,6 +48,7 @@
  * in the cache storage type (fp32, or bf16 bit patterns).
  */
 #include <math.h>
+#include <omp.h>
 #include <stdint.h>
 #include <stdlib.h>
 #include <string.h>
@@ -570,3 +571,6 @@ void or_make_drafts(const or_config* c, const or_weights* w, void* kc, void* vc,
         prev = drafts[i];
     }
 }
+
+/* Threads the parallel loops use (for reporting). */
+int or_num_threads(void) { return omp_get_max_threads(); }

@@ -21,13 +21,18 @@ SV_F32, SV_BF16, SV_FP8 = 0, 1, 2
 SV_FFN_MOE, SV_FFN_DENSE = 0, 1
 SV_DEV_BAD_TOKEN, SV_DEV_CAPACITY, SV_DEV_NAN_LOGIT = 1, 2, 4
 SV_KC_LM_HEAD, SV_KC_ATTENTION, SV_KC_EXPERT_GATE_UP, SV_KC_EXPERT_DOWN, SV_KC_QKV = range(5)
+SV_LAYOUT_ROW_MAJOR, SV_LAYOUT_TILED16 = 0, 1
+_LAYOUTS = {"row_major": SV_LAYOUT_ROW_MAJOR, "tiled16": SV_LAYOUT_TILED16}
+# matrices that feed a matrix product (packed in the tiled16 layout)
+GEMM_MATRICES = ("w_qkv", "w_o", "w_router", "w_gate_up", "w_down", "w_sh_gate_up", "w_sh_down")
 KERNEL_CLASSES = {"lm_head": 0, "attention": 1, "expert_gate_up": 2, "expert_down": 3, "qkv": 4}
 _DT = {"f32": SV_F32, "bf16": SV_BF16, "fp8": SV_FP8}
 
 # every function include/spec_verify.h declares
 EXPORTS = ("spec_verify_init", "spec_verify_destroy", "spec_verify_step", "spec_verify_set_debug",
            "spec_verify_accept_from_logits", "spec_verify_error_word", "spec_verify_kernel_time",
-           "spec_verify_last_error", "spec_verify_status_string", "spec_verify_abi_version")
+           "spec_verify_last_error", "spec_verify_status_string", "spec_verify_abi_version",
+           "spec_verify_pack_tiled16", "spec_verify_tiled16_bytes")
 
 
 class SpecVerifyConfig(ctypes.Structure):
@@ -49,7 +54,8 @@ class SpecVerifyLayer(ctypes.Structure):
 
 class SpecVerifyWeights(ctypes.Structure):
     _fields_ = [("embed", c_void_p), ("layers", POINTER(SpecVerifyLayer)),
-                ("final_norm", c_void_p), ("lm_head", c_void_p), ("lm_scale", c_void_p)]
+                ("final_norm", c_void_p), ("lm_head", c_void_p), ("lm_scale", c_void_p),
+                ("layout", c_int)]
 
 
 class SpecVerifyError(RuntimeError):
@@ -82,9 +88,12 @@ def load_library() -> ctypes.CDLL:
         lib.spec_verify_status_string.argtypes = [c_int]
         lib.spec_verify_status_string.restype = c_char_p
         lib.spec_verify_abi_version.argtypes = []
+        lib.spec_verify_pack_tiled16.argtypes = [P, P, ctypes.c_long, c_int, c_int, P]
+        lib.spec_verify_tiled16_bytes.argtypes = [ctypes.c_long, c_int, c_int]
         for f in EXPORTS:
             if f not in ("spec_verify_destroy", "spec_verify_status_string"):
                 getattr(lib, f).restype = c_int
+        lib.spec_verify_tiled16_bytes.restype = ctypes.c_long
         _lib = lib
     return _lib
 
@@ -151,9 +160,55 @@ def spec_verify_destroy(ctx: int) -> None:
     load_library().spec_verify_destroy(ctx)
 
 
+def spec_verify_tiled16_bytes(rows: int, cols: int, dtype: int) -> int:
+    return load_library().spec_verify_tiled16_bytes(rows, cols, dtype)
+
+
+def spec_verify_pack_tiled16(src, dst, rows: int, cols: int, dtype: int, stream=None) -> None:
+    _check(load_library().spec_verify_pack_tiled16(_p(src), _p(dst), rows, cols, dtype,
+                                                   _stream(stream)), "spec_verify_pack_tiled16")
+
+
+def _dtype_code(t) -> int:
+    import torch
+    return {torch.float32: SV_F32, torch.bfloat16: SV_BF16, torch.uint8: SV_FP8,
+            torch.float8_e4m3fn: SV_FP8}[t.dtype]
+
+
+def pack_matrix(t, stream=None):
+    """A device tensor [..., cols] (row-major, stacked matrices flattened into
+    one tall matrix) repacked by the library into the tiled16 layout; returns
+    a new uint8 tensor of spec_verify_tiled16_bytes bytes."""
+    import torch
+    cols = t.shape[-1]
+    rows = t.numel() // cols
+    dt = _dtype_code(t)
+    dst = torch.empty(spec_verify_tiled16_bytes(rows, cols, dt), dtype=torch.uint8,
+                      device=t.device)
+    spec_verify_pack_tiled16(t.contiguous(), dst, rows, cols, dt, stream)
+    return dst
+
+
+def pack_weights(weights: dict, stream=None) -> dict:
+    """A copy of a weight dict with every matrix-product weight in the
+    tiled16 layout (norm gains, scales and the embedding unchanged)."""
+    out = dict(weights)
+    out["layers"] = []
+    for L in weights["layers"]:
+        L2 = dict(L)
+        for name in GEMM_MATRICES:
+            if L.get(name) is not None:
+                L2[name] = pack_matrix(L[name], stream)
+        out["layers"].append(L2)
+    out["lm_head"] = pack_matrix(weights["lm_head"], stream)
+    out["layout"] = "tiled16"
+    return out
+
+
 def make_weights(weights: dict, n_layers: int):
     """Weights struct from a dict of device tensors laid out as the header
-    documents; returns (struct, keep-alive list)."""
+    documents (key "layout": "row_major" (default) or "tiled16"); returns
+    (struct, keep-alive list)."""
     keep = []
     layers = (SpecVerifyLayer * n_layers)()
     for l, L in enumerate(weights["layers"]):
@@ -170,6 +225,7 @@ def make_weights(weights: dict, n_layers: int):
     w.lm_head = weights["lm_head"].data_ptr()
     sc = weights.get("lm_scale")
     w.lm_scale = sc.data_ptr() if sc is not None else None
+    w.layout = _LAYOUTS[weights.get("layout", "row_major")]
     keep += [layers, weights]
     return w, keep
 
@@ -229,12 +285,19 @@ def from_library_v_layout(v_cache):
 class VerifyContext:
     """Owns one library context; wraps spec_verify_step for torch tensors."""
 
-    def __init__(self, cfg, max_batch: int, kv_capacity: int, weights: dict):
+    def __init__(self, cfg, max_batch: int, kv_capacity: int, weights: dict,
+                 layout: str = "tiled16"):
+        """`weights`: row-major device tensors (the workload dict).  With
+        layout "tiled16" the matrix-product weights are repacked once by the
+        library into a copy owned by this object."""
         self.cfg = cfg
         self.max_batch = max_batch
         self.kv_capacity = kv_capacity
         self._config = make_config(cfg, max_batch, kv_capacity)
         self.handle = spec_verify_init(self._config)
+        if layout == "tiled16" and weights.get("layout", "row_major") == "row_major":
+            weights = pack_weights(weights)
+        self.weights = weights
         self._w, self._keep = make_weights(weights, cfg.n_layers)
 
     def step(self, k_cache, v_cache, committed, drafts, ctx_in, ctx_out, accepted, next_tok,

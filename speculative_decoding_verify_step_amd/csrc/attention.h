@@ -181,9 +181,13 @@ __global__ __launch_bounds__(64) void attn_split_kernel(AttnArgs a)
 
 // Merge the chunk partials of one (sequence, query head, position) row in
 // chunk order and write the attention output row in the activation type.
+// 128 threads per row: chunk weights exp2(m_c - M) are formed once in shared
+// memory, then thread d sums its channel over the chunks.
 template <bool BF>
-__global__ __launch_bounds__(64) void attn_merge_kernel(AttnArgs a, void* out /* [T][n_q*D] */)
+__global__ __launch_bounds__(128) void attn_merge_kernel(AttnArgs a, void* out /* [T][n_q*D] */)
 {
+    __shared__ float wgt[1024];
+    __shared__ float red[2];
     const int row = blockIdx.x;                     // ((b * n_q + hq) * K1 + j)
     const int K1 = a.K1;
     const int j = row % K1;
@@ -191,23 +195,31 @@ __global__ __launch_bounds__(64) void attn_merge_kernel(AttnArgs a, void* out /*
     const int b = row / (K1 * a.n_q);
     const int ctx = min(max(a.ctx_in[b], 0), a.cap - K1);
     const int nch = (ctx + K1 + a.CH - 1) / a.CH;
-    const float* ml = a.mlpart + (size_t)row * a.maxch * 2;
-    const float* op = a.opart + (size_t)row * a.maxch * a.D;
-    float M = -INFINITY;
-    for (int c = 0; c < nch; c++) M = fmaxf(M, ml[2 * c]);
-    float Lsum = 0.f;
-    for (int c = 0; c < nch; c++) {
-        float mc = ml[2 * c];
-        if (mc != -INFINITY) Lsum += exp2f(mc - M) * ml[2 * c + 1];
-    }
-    float inv = 1.f / Lsum;
-    size_t t = (size_t)b * K1 + j;
-    for (int d = threadIdx.x; d < a.D; d += 64) {
-        float acc = 0.f;
-        for (int c = 0; c < nch; c++) {
+    const float* __restrict__ ml = a.mlpart + (size_t)row * a.maxch * 2;
+    const float* __restrict__ op = a.opart + (size_t)row * a.maxch * a.D;
+    const int tid = threadIdx.x, lane = tid & 63;
+    if (tid < 64) {
+        float M = -INFINITY;
+        for (int c = lane; c < nch; c += 64) M = fmaxf(M, ml[2 * c]);
+#pragma unroll
+        for (int o = 32; o >= 1; o >>= 1) M = fmaxf(M, __shfl_xor(M, o, 64));
+        float L = 0.f;
+        for (int c = lane; c < nch; c += 64) {
             float mc = ml[2 * c];
-            if (mc != -INFINITY) acc += exp2f(mc - M) * op[(size_t)c * a.D + d];
+            float wc = (mc == -INFINITY) ? 0.f : exp2f(mc - M);
+            wgt[c] = wc;
+            L += wc * ml[2 * c + 1];
         }
+        L = wave_sum(L);
+        if (lane == 0) red[0] = L;
+    }
+    __syncthreads();
+    const float inv = 1.f / red[0];
+    const size_t t = (size_t)b * K1 + j;
+    for (int d = tid; d < a.D; d += 128) {
+        float acc = 0.f;
+#pragma unroll 8
+        for (int c = 0; c < nch; c++) acc += wgt[c] * op[(size_t)c * a.D + d];
         float v = acc * inv;
         size_t o = t * (size_t)a.n_q * a.D + (size_t)hq * a.D + d;
         if constexpr (BF) ((uint16_t*)out)[o] = (uint16_t)f32_to_bf16_bits(v);

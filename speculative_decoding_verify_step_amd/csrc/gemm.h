@@ -53,7 +53,7 @@ struct GemmArgs {
     const int* tiles;       // grouped: [max_tiles][3] = (group, row0, nrows); null = dense
     const int* n_tiles;     // grouped: device count of valid tiles
     int MT;                 // row tiles in the grid (dense: ceil(M / BM); grouped: max tiles)
-    int NT;                 // column tiles (64*NF columns each)
+    int NT;                 // column tiles (16*NF*WAVES columns each)
     void* out;              // STORE: fp32 [ksplit][rows][ldo]; SWIGLU: act [rows][ldo]
     long ldo;
     long split_stride;      // STORE: elements between K-split slabs
@@ -87,15 +87,17 @@ SV_DEV f32x4_t mma_step(uint4 w, const uint4* x, f32x4_t c)
     }
 }
 
-template <int WT, int MF, int NF, int MODE>
-__global__ __launch_bounds__(256) void gemm_kernel(GemmArgs a)
+// WAVES waves per workgroup side by side (a 16*NF*WAVES-column tile); UU
+// reduction steps per prefetch stage (0: by row count).
+template <int WT, int MF, int NF, int MODE, int WAVES = 4, int UU = 0, bool PACKED = false>
+__global__ __launch_bounds__(64 * WAVES) void gemm_kernel(GemmArgs a)
 {
     using Tr = WTraits<WT>;
     constexpr int KL = Tr::KL, SK = Tr::SK, XU = Tr::XU, WESZ = Tr::ESZ;
     constexpr int AESZ = ATraits<WT>::ESZ;
     constexpr int NFT = (MODE == GM_SWIGLU) ? 2 * NF : NF;   // weight fragments per wave
     constexpr int BM = 16 * MF;
-    constexpr int U = (MF >= 4) ? 2 : 4;                      // reduction steps per stage
+    constexpr int U = UU ? UU : ((MF >= 4) ? 2 : 4);          // reduction steps per stage
 
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
@@ -132,7 +134,7 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs a)
         sc = a.ws2 ? a.ws2 + (size_t)(group - a.G1) * a.s2_gstride : nullptr;
     }
 
-    const int ncol0 = nt * 64 * NF + wave * 16 * NF;      // this wave's first column
+    const int ncol0 = (nt * WAVES + wave) * 16 * NF;      // this wave's first column
     const int K = a.K;
     const int kspan = K / a.ksplit;
     const int kb = blockIdx.y * kspan;
@@ -146,9 +148,18 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs a)
         int n0 = ncol0 + 16 * f;
         fvalid[f] = n0 < a.N;
         int r = fvalid[f] ? min(n0 + l16, a.N - 1) : 0;   // rows past N read row N-1
-        wrow[f] = Wb + ((size_t)r * K + (size_t)lg * KL) * WESZ;
-        if constexpr (MODE == GM_SWIGLU)
-            wrow[NF + f] = Wb + ((size_t)(r + a.dual_off) * K + (size_t)lg * KL) * WESZ;
+        if constexpr (PACKED) {
+            // 16-row blocks stored step-major: block rb, step s at ((rb * K/SK) + s) KiB,
+            // lane l's 16 bytes at l * 16; the k offset below is in elements of SK per KiB
+            int rb = fvalid[f] ? n0 / 16 : 0;
+            wrow[f] = Wb + (size_t)rb * K * 16 * WESZ + (size_t)lane * 16;
+            if constexpr (MODE == GM_SWIGLU)
+                wrow[NF + f] = Wb + (size_t)(rb + a.dual_off / 16) * K * 16 * WESZ + (size_t)lane * 16;
+        } else {
+            wrow[f] = Wb + ((size_t)r * K + (size_t)lg * KL) * WESZ;
+            if constexpr (MODE == GM_SWIGLU)
+                wrow[NF + f] = Wb + ((size_t)(r + a.dual_off) * K + (size_t)lg * KL) * WESZ;
+        }
     }
     // activation rows of this lane, one per row fragment
     const char* xrow[MF];
@@ -175,7 +186,10 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs a)
             int kk = k + u * SK;
             if (kk < ke) {
 #pragma unroll
-                for (int f = 0; f < NFT; f++) w[u][f] = ldg16_stream(wrow[f] + (size_t)kk * WESZ);
+                for (int f = 0; f < NFT; f++) {
+                    if constexpr (PACKED) w[u][f] = ldg16_stream(wrow[f] + (size_t)(kk / SK) * 1024);
+                    else w[u][f] = ldg16_stream(wrow[f] + (size_t)kk * WESZ);
+                }
 #pragma unroll
                 for (int m = 0; m < MF; m++)
 #pragma unroll
@@ -252,7 +266,7 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs a)
             }
         }
     } else {   // GM_ARGMAX
-        __shared__ unsigned long long red[4][BM];
+        __shared__ unsigned long long red[WAVES][BM];
 #pragma unroll
         for (int m = 0; m < MF; m++) {
             unsigned long long best = 0ull;
@@ -277,8 +291,10 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs a)
             if (lg == 0) red[wave][r] = best;
         }
         __syncthreads();
-        for (int r = threadIdx.x; r < nrows; r += 256) {
-            unsigned long long b = umax64(umax64(red[0][r], red[1][r]), umax64(red[2][r], red[3][r]));
+        for (int r = threadIdx.x; r < nrows; r += 64 * WAVES) {
+            unsigned long long b = red[0][r];
+#pragma unroll
+            for (int w2 = 1; w2 < WAVES; w2++) b = umax64(b, red[w2][r]);
             a.keys[(size_t)nt * a.key_ld + row0 + r] = b;
         }
     }

@@ -13,6 +13,7 @@
 //
 // Nothing here reads device memory back: context lengths, routing and
 // acceptance stay on the device, so a step can be captured in a HIP graph.
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
@@ -48,7 +49,7 @@ int fail(int code, const std::string& msg)
     } while (0)
 
 constexpr int KS_MAX = 16;           // largest K split
-constexpr int ATT_MAXCH_CAP = 4096;  // sanity bound on chunks per sequence
+constexpr int ATT_MAXCH_CAP = 1024;  // chunks per sequence (merge kernel weights in LDS)
 
 inline int cdiv(long a, long b) { return (int)((a + b - 1) / b); }
 
@@ -60,6 +61,19 @@ int wsteps(int wt)
 struct EventPair {
     hipEvent_t a, b;
 };
+
+// Events of the launch being timed (set by ProfScope).  A timed kernel is
+// launched with hipExtLaunchKernelGGL, which stamps the start and end of the
+// kernel itself into the events as part of its dispatch, so timing adds no
+// packets (and no gaps) to the stream.
+thread_local hipEvent_t g_ev_start = nullptr, g_ev_stop = nullptr;
+
+template <typename... KArgs, typename... Args>
+void launch(void (*k)(KArgs...), dim3 grid, dim3 block, size_t shm, hipStream_t s, Args... args)
+{
+    if (g_ev_start) hipExtLaunchKernelGGL(k, grid, block, (uint32_t)shm, s, g_ev_start, g_ev_stop, 0, args...);
+    else hipLaunchKernelGGL(k, grid, block, shm, s, args...);
+}
 
 }  // namespace
 
@@ -162,30 +176,45 @@ int validate_config(const spec_verify_config& c)
 }
 
 // ------------------------------------------------------------- GEMM launch
-template <int WT, int MODE>
+template <int WT, int MODE, bool PK>
 void launch_gemm_t(int MF, const GemmArgs& a, dim3 grid, hipStream_t s)
 {
+    if (a.tiles) {   // grouped (experts): one wave per workgroup, finer balance
+        switch (MF) {
+        case 1: launch(gemm_kernel<WT, 1, 1, MODE, 1, 0, PK>, grid, dim3(64), 0, s, a); break;
+        case 2: launch(gemm_kernel<WT, 2, 1, MODE, 1, 0, PK>, grid, dim3(64), 0, s, a); break;
+        default: launch(gemm_kernel<WT, 4, 1, MODE, 1, 0, PK>, grid, dim3(64), 0, s, a); break;
+        }
+        return;
+    }
     switch (MF) {
-    case 1: gemm_kernel<WT, 1, 1, MODE><<<grid, 256, 0, s>>>(a); break;
-    case 2: gemm_kernel<WT, 2, 1, MODE><<<grid, 256, 0, s>>>(a); break;
-    default: gemm_kernel<WT, 4, 1, MODE><<<grid, 256, 0, s>>>(a); break;
+    case 1: launch(gemm_kernel<WT, 1, 1, MODE, 4, 0, PK>, grid, dim3(256), 0, s, a); break;
+    case 2: launch(gemm_kernel<WT, 2, 1, MODE, 4, 0, PK>, grid, dim3(256), 0, s, a); break;
+    default: launch(gemm_kernel<WT, 4, 1, MODE, 4, 0, PK>, grid, dim3(256), 0, s, a); break;
     }
 }
 
-template <int MODE>
+template <int MODE, bool PK>
 void launch_gemm_m(int wt, int MF, const GemmArgs& a, dim3 grid, hipStream_t s)
 {
-    if (wt == SV_F32) launch_gemm_t<SV_F32, MODE>(MF, a, grid, s);
-    else if (wt == SV_BF16) launch_gemm_t<SV_BF16, MODE>(MF, a, grid, s);
-    else launch_gemm_t<SV_FP8, MODE>(MF, a, grid, s);
+    if (wt == SV_F32) launch_gemm_t<SV_F32, MODE, PK>(MF, a, grid, s);
+    else if (wt == SV_BF16) launch_gemm_t<SV_BF16, MODE, PK>(MF, a, grid, s);
+    else launch_gemm_t<SV_FP8, MODE, PK>(MF, a, grid, s);
 }
 
-void launch_gemm(int wt, int mode, int MF, GemmArgs& a, hipStream_t s)
+template <bool PK>
+void launch_gemm_l(int wt, int mode, int MF, const GemmArgs& a, dim3 grid, hipStream_t s)
+{
+    if (mode == GM_STORE) launch_gemm_m<GM_STORE, PK>(wt, MF, a, grid, s);
+    else if (mode == GM_SWIGLU) launch_gemm_m<GM_SWIGLU, PK>(wt, MF, a, grid, s);
+    else launch_gemm_m<GM_ARGMAX, PK>(wt, MF, a, grid, s);
+}
+
+void launch_gemm(int wt, int mode, int MF, bool packed, GemmArgs& a, hipStream_t s)
 {
     dim3 grid((unsigned)(cdiv(a.NT, 8) * 8 * a.MT), (unsigned)a.ksplit, 1);
-    if (mode == GM_STORE) launch_gemm_m<GM_STORE>(wt, MF, a, grid, s);
-    else if (mode == GM_SWIGLU) launch_gemm_m<GM_SWIGLU>(wt, MF, a, grid, s);
-    else launch_gemm_m<GM_ARGMAX>(wt, MF, a, grid, s);
+    if (packed) launch_gemm_l<true>(wt, mode, MF, a, grid, s);
+    else launch_gemm_l<false>(wt, mode, MF, a, grid, s);
 }
 
 int rows_mf(int rows) { return rows <= 16 ? 1 : (rows <= 32 ? 2 : 4); }
@@ -220,23 +249,17 @@ GemmArgs dense_args(const void* X, long ldx, int M, int N, int K, const void* W,
 }
 
 // event-timed launch scope
+// Times the one kernel launched inside the scope if its class is recorded.
 struct ProfScope {
-    spec_verify_ctx* c;
-    hipStream_t s;
-    bool on;
-    size_t idx;
-    ProfScope(spec_verify_ctx* c_, int kc, hipStream_t s_) : c(c_), s(s_), on(false), idx(0)
+    ProfScope(spec_verify_ctx* c, int kc, hipStream_t)
     {
         if (c->prof_class == kc && c->prof_used < c->prof_events.size()) {
-            on = true;
-            idx = c->prof_used++;
-            (void)hipEventRecord(c->prof_events[idx].a, s);
+            size_t idx = c->prof_used++;
+            g_ev_start = c->prof_events[idx].a;
+            g_ev_stop = c->prof_events[idx].b;
         }
     }
-    ~ProfScope()
-    {
-        if (on) (void)hipEventRecord(c->prof_events[idx].b, s);
-    }
+    ~ProfScope() { g_ev_start = g_ev_stop = nullptr; }
 };
 
 }  // namespace
@@ -439,6 +462,9 @@ int spec_verify_step(spec_verify_ctx* c, const spec_verify_weights* w, void* k_c
         }
         if (!ok) return fail(SV_ERR_INVALID_ARG, "null pointer in layer " + std::to_string(l));
     }
+    if (w->layout != SV_LAYOUT_ROW_MAJOR && w->layout != SV_LAYOUT_TILED16)
+        return fail(SV_ERR_INVALID_ARG, "unknown weight layout");
+    const bool packed = w->layout == SV_LAYOUT_TILED16;
     HIP_TRY(hipSetDevice(c->device));
     hipStream_t s = (hipStream_t)stream;
     const int wt = k.weight_dtype, step = wsteps(wt);
@@ -482,7 +508,7 @@ int spec_verify_step(spec_verify_ctx* c, const spec_verify_weights* w, void* k_c
         a.out = out;
         a.ldo = ldo;
         a.split_stride = (long)T * ldo;
-        launch_gemm(wt, mode, MFd, a, s);
+        launch_gemm(wt, mode, MFd, packed, a, s);
         return a.ksplit;
     };
 
@@ -531,8 +557,11 @@ int spec_verify_step(spec_verify_ctx* c, const spec_verify_weights* w, void* k_c
         rp.q = c->q;
         rp.kc = k_cache;
         rp.vc = v_cache;
-        if (bf) rope_append_kernel<true><<<T, 256, 0, s>>>(rp);
-        else rope_append_kernel<false><<<T, 256, 0, s>>>(rp);
+        {
+            dim3 grid(T, k.n_q_heads + 2 * k.n_kv_heads);
+            if (bf) rope_append_kernel<true><<<grid, 64, 0, s>>>(rp);
+            else rope_append_kernel<false><<<grid, 64, 0, s>>>(rp);
+        }
 
         at.layer = l;
         {
@@ -540,34 +569,34 @@ int spec_verify_step(spec_verify_ctx* c, const spec_verify_weights* w, void* k_c
             dim3 grid(c->att_maxch, k.n_kv_heads * c->att_QG, B);
             if (bf) {
                 if (k.head_dim == 128) {
-                    if (c->att_QPW == 2) attn_split_kernel<true, 2, 128><<<grid, 64, 0, s>>>(at);
-                    else attn_split_kernel<true, 1, 128><<<grid, 64, 0, s>>>(at);
+                    if (c->att_QPW == 2) launch(attn_split_kernel<true, 2, 128>, grid, dim3(64), 0, s, at);
+                    else launch(attn_split_kernel<true, 1, 128>, grid, dim3(64), 0, s, at);
                 } else {
-                    if (c->att_QPW == 2) attn_split_kernel<true, 2, 64><<<grid, 64, 0, s>>>(at);
-                    else attn_split_kernel<true, 1, 64><<<grid, 64, 0, s>>>(at);
+                    if (c->att_QPW == 2) launch(attn_split_kernel<true, 2, 64>, grid, dim3(64), 0, s, at);
+                    else launch(attn_split_kernel<true, 1, 64>, grid, dim3(64), 0, s, at);
                 }
             } else {
                 if (k.head_dim == 128) {
-                    if (c->att_QPW == 2) attn_split_kernel<false, 2, 128><<<grid, 64, 0, s>>>(at);
-                    else attn_split_kernel<false, 1, 128><<<grid, 64, 0, s>>>(at);
+                    if (c->att_QPW == 2) launch(attn_split_kernel<false, 2, 128>, grid, dim3(64), 0, s, at);
+                    else launch(attn_split_kernel<false, 1, 128>, grid, dim3(64), 0, s, at);
                 } else {
-                    if (c->att_QPW == 2) attn_split_kernel<false, 2, 64><<<grid, 64, 0, s>>>(at);
-                    else attn_split_kernel<false, 1, 64><<<grid, 64, 0, s>>>(at);
+                    if (c->att_QPW == 2) launch(attn_split_kernel<false, 2, 64>, grid, dim3(64), 0, s, at);
+                    else launch(attn_split_kernel<false, 1, 64>, grid, dim3(64), 0, s, at);
                 }
             }
         }
         {
             int rows = B * k.n_q_heads * K1;
-            if (bf) attn_merge_kernel<true><<<rows, 64, 0, s>>>(at, c->o);
-            else attn_merge_kernel<false><<<rows, 64, 0, s>>>(at, c->o);
+            if (bf) attn_merge_kernel<true><<<rows, 128, 0, s>>>(at, c->o);
+            else attn_merge_kernel<false><<<rows, 128, 0, s>>>(at, c->o);
         }
         ks = dense_gemm(GM_STORE, c->o, QD, H, QD, Lw.w_o, Lw.s_o, c->parts, H, 1);
         ra.parts = c->parts;
         ra.nsplit = ks;
         ra.gain = Lw.ffn_norm;
         ra.dbg_hidden = nullptr;
-        if (bf) residual_norm_kernel<true, false><<<T, 256, 0, s>>>(ra);
-        else residual_norm_kernel<false, false><<<T, 256, 0, s>>>(ra);
+        if (bf) residual_norm_kernel<true, false><<<T, 1024, 0, s>>>(ra);
+        else residual_norm_kernel<false, false><<<T, 1024, 0, s>>>(ra);
 
         // ---- feed-forward half
         const float* next_gain = (l + 1 < L) ? w->layers[l + 1].attn_norm : w->final_norm;
@@ -597,7 +626,8 @@ int spec_verify_step(spec_verify_ctx* c, const spec_verify_weights* w, void* k_c
             ro.perm_tok = c->perm_tok;
             ro.tiles = c->tiles;
             ro.n_tiles = c->n_tiles;
-            route_kernel<<<1, 256, (size_t)T * E * sizeof(unsigned short), s>>>(ro);
+            route_topk_kernel<<<cdiv(T, 4), 256, 0, s>>>(ro);
+            route_permute_kernel<<<1, 256, (size_t)T * (E + tk) * sizeof(unsigned short), s>>>(ro);
 
             GemmArgs g;
             memset(&g, 0, sizeof(g));
@@ -620,12 +650,12 @@ int spec_verify_step(spec_verify_ctx* c, const spec_verify_weights* w, void* k_c
             g.tiles = c->tiles;
             g.n_tiles = c->n_tiles;
             g.MT = max_tiles;
-            g.NT = cdiv(I, 64);
+            g.NT = cdiv(I, 16);   // one-wave workgroups
             g.out = c->act;
             g.ldo = I;
             {
                 ProfScope ps(c, SV_KC_EXPERT_GATE_UP, s);
-                launch_gemm(wt, GM_SWIGLU, MFe, g, s);
+                launch_gemm(wt, GM_SWIGLU, MFe, packed, g, s);
             }
             GemmArgs d = g;
             d.X = c->act;
@@ -642,21 +672,21 @@ int spec_verify_step(spec_verify_ctx* c, const spec_verify_weights* w, void* k_c
             d.w2_gstride = (long)H * I;
             d.s2_gstride = H;
             d.dual_off = 0;
-            d.NT = cdiv(H, 64);
+            d.NT = cdiv(H, 16);
             d.out = c->y;
             d.ldo = H;
             d.split_stride = 0;
             {
                 ProfScope ps(c, SV_KC_EXPERT_DOWN, s);
-                launch_gemm(wt, GM_STORE, MFe, d, s);
+                launch_gemm(wt, GM_STORE, MFe, packed, d, s);
             }
             ra.y = c->y;
             ra.gate = c->gate;
             ra.slot = c->slot;
             ra.gain = next_gain;
             ra.dbg_hidden = dbg_h;
-            if (bf) residual_norm_kernel<true, true><<<T, 256, 0, s>>>(ra);
-            else residual_norm_kernel<false, true><<<T, 256, 0, s>>>(ra);
+            if (bf) residual_norm_kernel<true, true><<<T, 1024, 0, s>>>(ra);
+            else residual_norm_kernel<false, true><<<T, 1024, 0, s>>>(ra);
         } else {
             const int I = k.dense_inter;
             GemmArgs g = dense_args(c->h, H, T, I, H, Lw.w_gate_up, Lw.s_gate_up);
@@ -667,7 +697,7 @@ int spec_verify_step(spec_verify_ctx* c, const spec_verify_weights* w, void* k_c
             g.ldo = I;
             {
                 ProfScope ps(c, SV_KC_EXPERT_GATE_UP, s);
-                launch_gemm(wt, GM_SWIGLU, MFd, g, s);
+                launch_gemm(wt, GM_SWIGLU, MFd, packed, g, s);
             }
             {
                 ProfScope ps(c, SV_KC_EXPERT_DOWN, s);
@@ -677,8 +707,8 @@ int spec_verify_step(spec_verify_ctx* c, const spec_verify_weights* w, void* k_c
             ra.nsplit = ks;
             ra.gain = next_gain;
             ra.dbg_hidden = dbg_h;
-            if (bf) residual_norm_kernel<true, false><<<T, 256, 0, s>>>(ra);
-            else residual_norm_kernel<false, false><<<T, 256, 0, s>>>(ra);
+            if (bf) residual_norm_kernel<true, false><<<T, 1024, 0, s>>>(ra);
+            else residual_norm_kernel<false, false><<<T, 1024, 0, s>>>(ra);
         }
     }
 
@@ -693,7 +723,7 @@ int spec_verify_step(spec_verify_ctx* c, const spec_verify_weights* w, void* k_c
         a.dbg = c->dbg_logits;
         a.dbg_ld = k.vocab;
         ProfScope ps(c, SV_KC_LM_HEAD, s);
-        launch_gemm(wt, GM_ARGMAX, MFd, a, s);
+        launch_gemm(wt, GM_ARGMAX, MFd, packed, a, s);
     }
     AcceptArgs ac;
     ac.keys = c->keys;
@@ -708,7 +738,7 @@ int spec_verify_step(spec_verify_ctx* c, const spec_verify_weights* w, void* k_c
     ac.target = c->dbg_target;
     ac.seq_err = c->seq_err;
     ac.err_word = c->err_word;
-    accept_kernel<<<B, 64, 0, s>>>(ac);
+    accept_kernel<<<B, 256, 0, s>>>(ac);
     HIP_TRY(hipGetLastError());
     return SV_OK;
 }
@@ -740,7 +770,31 @@ int spec_verify_accept_from_logits(spec_verify_ctx* c, const float* logits, cons
     ac.target = target;
     ac.seq_err = nullptr;
     ac.err_word = c->err_word;
-    accept_kernel<<<B, 64, 0, s>>>(ac);
+    accept_kernel<<<B, 256, 0, s>>>(ac);
+    HIP_TRY(hipGetLastError());
+    return SV_OK;
+}
+
+long spec_verify_tiled16_bytes(long rows, int cols, int dtype)
+{
+    if (rows < 1 || cols < 1 || dtype < SV_F32 || dtype > SV_FP8) return -1;
+    long es = dtype == SV_F32 ? 4 : (dtype == SV_BF16 ? 2 : 1);
+    return (rows + 15) / 16 * 16 * (long)cols * es;
+}
+
+int spec_verify_pack_tiled16(const void* src, void* dst, long rows, int cols, int dtype,
+                             void* stream)
+{
+    if (!src || !dst) return fail(SV_ERR_INVALID_ARG, "null matrix pointer");
+    if (rows < 1 || cols < 1 || dtype < SV_F32 || dtype > SV_FP8)
+        return fail(SV_ERR_INVALID_ARG, "bad matrix shape or dtype");
+    int es = dtype == SV_F32 ? 4 : (dtype == SV_BF16 ? 2 : 1);
+    int S = 4 * (16 / es);
+    if (cols % S) return fail(SV_ERR_UNSUPPORTED, "cols must be a multiple of the reduction step");
+    hipStream_t s = (hipStream_t)stream;
+    long chunks = (rows + 15) / 16 * (cols / S) * 64;
+    long blocks = std::min<long>((chunks + 255) / 256, 65536);
+    pack_tiled16_kernel<<<(unsigned)blocks, 256, 0, s>>>((const char*)src, (char*)dst, rows, cols, es);
     HIP_TRY(hipGetLastError());
     return SV_OK;
 }

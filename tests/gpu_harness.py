@@ -94,11 +94,11 @@ class Case:
 class GpuRun:
     """One library context with debug outputs for a case."""
 
-    def __init__(self, case: Case, batch: int | None = None, debug=True):
+    def __init__(self, case: Case, batch: int | None = None, debug=True, layout="tiled16"):
         cfg = case.cfg
         self.case = case
         self.B = cfg.batch if batch is None else batch
-        self.ctx = sv.VerifyContext(cfg, self.B, case.cap, case.w_gpu)
+        self.ctx = sv.VerifyContext(cfg, self.B, case.cap, case.w_gpu, layout=layout)
         self.kc = case.k_nat[: self.B].clone()
         self.vc = sv.to_library_v_layout(case.v_nat[: self.B])
         K1 = cfg.k_draft + 1

@@ -13,7 +13,7 @@ HEADER = os.path.join(ROOT, "include", "spec_verify.h")
 def _declared():
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(spec_verify_[a-z_]+)\s*\(", text)))
+    return sorted(set(re.findall(r"\b(spec_verify_[a-z0-9_]+)\s*\(", text)))
 
 
 @pytest.fixture(scope="module")
@@ -43,10 +43,18 @@ def test_status_strings_and_version(sv):
 
 
 def test_struct_sizes_match_header(sv):
-    # 21 four-byte fields; layer = 16 pointers; weights = 5 pointers
+    # 21 four-byte fields; layer = 16 pointers; weights = 5 pointers + int (padded)
     assert ctypes.sizeof(sv.SpecVerifyConfig) == 21 * 4
     assert ctypes.sizeof(sv.SpecVerifyLayer) == 16 * 8
-    assert ctypes.sizeof(sv.SpecVerifyWeights) == 5 * 8
+    assert ctypes.sizeof(sv.SpecVerifyWeights) == 6 * 8
+
+
+def test_tiled16_sizes(sv):
+    assert sv.spec_verify_tiled16_bytes(129280, 1280, sv.SV_BF16) == 129280 * 1280 * 2
+    assert sv.spec_verify_tiled16_bytes(8, 256, sv.SV_F32) == 16 * 256 * 4      # padded rows
+    assert sv.spec_verify_tiled16_bytes(0, 256, sv.SV_F32) == -1
+    lib = sv.load_library()
+    assert lib.spec_verify_pack_tiled16(None, None, 16, 64, 1, None) == sv.SV_ERR_INVALID_ARG
 
 
 def _cfg(sv, **kw):

@@ -229,3 +229,54 @@ def test_device_side_errors_are_reported_without_writes(H):
     assert g["accepted"][0] >= 0 and g["ctx_out"][0] == ctx[0] + g["accepted"][0] + 1
     assert run.ctx.error_word() == 0
     run.close()
+
+
+def _tiled16_reference(W: torch.Tensor, esize: int) -> torch.Tensor:
+    """The documented tiled16 layout built with torch reshapes: rows padded to
+    16, block r and step s at KiB (r * steps + s), lane l = (row l%16, slice
+    l/16) of the step, KL = 16 / esize elements per slice."""
+    rows, cols = W.shape
+    KL = 16 // esize
+    S = 4 * KL
+    pad = (-rows) % 16
+    if pad:
+        W = torch.cat([W, torch.zeros(pad, cols, dtype=W.dtype, device=W.device)])
+    nb = W.shape[0] // 16
+    t = W.reshape(nb, 16, cols // S, 4, KL)          # block, row, step, slice, elem
+    t = t.permute(0, 2, 3, 1, 4).contiguous()        # block, step, slice, row, elem
+    return t.view(torch.uint8).reshape(-1)
+
+
+@pytest.mark.parametrize("dtype,rows,cols", [("f32", 24, 64), ("bf16", 48, 96), ("fp8", 40, 128),
+                                             ("bf16", 1792, 1280)])
+def test_pack_tiled16_layout(H, dtype, rows, cols):
+    import speculative_decoding_verify_step_amd as sv
+    g = torch.Generator(device="cuda").manual_seed(3)
+    W = torch.randn(rows, cols, generator=g, device="cuda")
+    if dtype == "bf16":
+        W = W.to(torch.bfloat16)
+    elif dtype == "fp8":
+        W = W.to(torch.float8_e4m3fn).view(torch.uint8)
+    esize = W.element_size()
+    H.say(f"[pack] {dtype} {rows}x{cols}")
+    got = sv.pack_matrix(W)
+    torch.cuda.synchronize()
+    want = _tiled16_reference(W.view(torch.uint8).view(W.dtype) if dtype != "fp8" else W, esize)
+    assert got.numel() == want.numel()
+    assert torch.equal(got, want)
+
+
+def test_row_major_and_tiled16_layouts_agree_bitwise(H):
+    """The two weight layouts feed the same values in the same order to the
+    same arithmetic: every output is bit-identical."""
+    cfg = workloads.scaled(workloads.get_config("moe_b32"), n_layers=2, vocab=4096, batch=5,
+                           ctx=("uniform", 40, 300))
+    case = H.Case(cfg)
+    outs = []
+    for layout in ("row_major", "tiled16"):
+        H.say(f"[layouts] {layout}")
+        run = H.GpuRun(case, layout=layout)
+        outs.append(run.step(case.committed, case.rtok[0], case.ctx))
+        run.close()
+    for k in ("logits", "hidden", "target", "accepted", "next_tok", "ctx_out", "routing"):
+        assert np.array_equal(outs[0][k], outs[1][k], equal_nan=True), k
