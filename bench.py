@@ -32,6 +32,33 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
+
+# HBM traffic of the dominant kernel from rocprofv3 counter runs (see
+# profiles/lm_head_argmax_moe_b1.md): KiB per dispatch, scaled by what the same
+# counter reads for a plain copy of known size.  Valid only for the kernel
+# sources it was measured on (SHA-256 prefix of common.h + gemm.h +
+# spec_verify.hip).
+MEASURED_TRAFFIC = {
+    "moe_b1": {"source_sha": "825f170976cf83ce", "fetch_kib": 161672.8, "fetch_scale": 2.000,
+               "write_kib": 63.1, "write_scale": 1.000},
+}
+
+
+def kernel_source_sha() -> str:
+    import hashlib
+    h = hashlib.sha256()
+    d = os.path.join(ROOT, "speculative_decoding_verify_step_amd", "csrc")
+    for f in ("common.h", "gemm.h", "spec_verify.hip"):
+        with open(os.path.join(d, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(workload: str):
+    m = MEASURED_TRAFFIC.get(workload)
+    if m is None or m["source_sha"] != kernel_source_sha():
+        return None
+    return (m["fetch_kib"] * m["fetch_scale"] + m["write_kib"] * m["write_scale"]) * 1024
 METRIC = "accepted tokens/s + verify-step µs at batch 1/32/64, K=3, MoE decoder"
 WBYTES = {"f32": 4, "bf16": 2, "fp8": 1}
 
@@ -236,6 +263,20 @@ def cpu_baseline(cfg, budget_s=15.0):
                       f"{el:.1f} s; per-step {1e3 * el / n:.1f} ms"}
 
 
+def copy_calibration(nbytes: int, reps: int):
+    """A plain device-to-device copy of `nbytes`, `reps` times: the reference
+    against which HBM byte counters (FETCH_SIZE, WRITE_SIZE) are scaled --
+    each copy must read and write exactly nbytes."""
+    import torch
+    src = torch.empty(nbytes, dtype=torch.uint8, device="cuda").fill_(7)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(reps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes": nbytes, "reps": reps}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -243,7 +284,12 @@ def main():
     ap.add_argument("--warmup", type=int, default=None)
     ap.add_argument("--config", default="moe_b1")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
+                    help="only run a plain device copy of BYTES (counter calibration)")
     args = ap.parse_args()
+    if args.copy_calibration:
+        copy_calibration(args.copy_calibration, args.steps or 5)
+        return
     if args.gpus != 1:
         print(json.dumps({"error": "this build runs on one GPU; --gpus must be 1",
                           "n_gpus": args.gpus}))
@@ -275,7 +321,8 @@ def main():
                    "tokens_per_verify": r["tau"]},
         "roofline": {"bound": "hbm", "kernel": "lm_head_argmax",
                      "achieved": lm_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": (lm_gbs / HBM_PEAK_GBS) if lm_gbs else None, "traffic": None,
+                     "frac": (lm_gbs / HBM_PEAK_GBS) if lm_gbs else None,
+                     "traffic": measured_traffic(cfg.name),
                      "mean_us": r["lm_ms"] * 1e3, "bytes_per_launch": r["lm_bytes"],
                      "launches_timed": r["lm_launches"]},
         "step_roofline": {"bytes_per_step": r["step_bytes"],
