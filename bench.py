@@ -114,7 +114,7 @@ def setup(cfg, steps):
     cap = workloads.capacity_for(workloads.scaled(cfg, steps=max(cfg.steps, steps)))
     w = workloads.make_weights(cfg, "cuda")
     k, v = workloads.kv_cache(cfg, "cuda", capacity=cap)
-    v = sv.to_library_v_layout(v)
+    k, v = sv.kv_to_library(k, v)
     torch.cuda.synchronize()
     ctx = workloads.context_lengths(cfg)
     com = workloads.committed_tokens(cfg)

@@ -78,13 +78,26 @@
  *                        what lets the weight stream run near the HBM peak.
  * The embedding is always row-major (it is gathered by row, not multiplied).
  *
- * KV-cache layout (storage = kv dtype), capacity slots per (sequence, layer,
- * KV head), sequence b occupying one contiguous region:
- *   K cache: [B_max][L][n_kv][capacity][D]   (position-major)
- *   V cache: [B_max][L][n_kv][D][capacity]   (channel-major: transposed)
- * Positions 0 .. ctx_lens_in[b]-1 hold the cached context.  The step writes
- * positions ctx .. ctx+K; after the commit, slots at or past ctx_lens_out[b]
- * are dead and will be overwritten by the next step (rollback is by length).
+ * KV-cache layout (storage = kv dtype).  Each (sequence b, layer l, KV head h)
+ * owns one contiguous region of capacity * D elements at offset
+ * ((b * L + l) * n_kv + h) * capacity * D, for both the K and the V cache;
+ * sequence b's regions are contiguous.  Inside a region, positions are grouped
+ * in tiles of KT keys (KL = 16 / element size: 8 for bf16, 4 for fp32;
+ * KT = 4 KL) and every tile is KT * D contiguous elements, made of 1 KiB
+ * pieces of 64 lanes x KL elements, the exact operands of the attention's
+ * matrix instructions:
+ *   K: piece (blk, s) of tile t (blk < KL/4, s < D/(4 KL)) is at element
+ *      ((t * KL/4 + blk) * D/(4 KL) + s) * 64 KL; lane l = q4 + 16 g (q4 < 16,
+ *      g < 4) holds K[pos][d] for pos = t KT + KL (q4 / 4) + 4 blk + q4 % 4 and
+ *      d = s 4 KL + g KL + e, e < KL.
+ *   V: piece f of tile t (f < D/16) is at element (t * D/16 + f) * 64 KL; lane
+ *      l = c + 16 g holds V[pos][d] for pos = t KT + g KL + e (e < KL) and
+ *      d = 16 f + c.
+ * A cache built in the natural order [pos][d] per region can be converted
+ * with a pure permutation (the Python binding provides one).  Positions
+ * 0 .. ctx_lens_in[b]-1 hold the cached context.  The step writes positions
+ * ctx .. ctx+K; after the commit, slots at or past ctx_lens_out[b] are dead
+ * and are overwritten by the next step (rollback is by length).
  */
 #ifndef SPEC_VERIFY_H
 #define SPEC_VERIFY_H

@@ -272,14 +272,32 @@ def spec_verify_kernel_time(ctx: int, kclass: int, enable: int = -1, query: bool
 
 
 # --------------------------------------------------------------- helpers
-def to_library_v_layout(v_cache):
-    """The V cache in the library's channel-major layout [B][L][n_kv][D][cap]
-    from the natural [B][L][n_kv][cap][D]."""
-    return v_cache.transpose(-1, -2).contiguous()
+def _kv_shape(t):
+    esize = t.element_size()
+    KL = 16 // esize
+    B, L, H, cap, D = t.shape
+    if cap % (4 * KL) or D % (4 * KL):
+        raise ValueError("capacity and head_dim must be multiples of the key tile")
+    return B, L, H, cap, D, KL, KL // 4, D // (4 * KL), cap // (4 * KL)
 
 
-def from_library_v_layout(v_cache):
-    return v_cache.transpose(-1, -2).contiguous()
+def kv_to_library(k_cache, v_cache):
+    """Caches in the natural order [B][L][n_kv][capacity][D] -> the library's
+    tiled layout (a pure permutation; see include/spec_verify.h)."""
+    B, L, H, cap, D, KL, NB, DS, NT = _kv_shape(k_cache)
+    # K: key r = q*4NB + blk*4 + m, channel d = s*4KL + g*KL + e
+    k = k_cache.reshape(B, L, H, NT, 4, NB, 4, DS, 4, KL).permute(0, 1, 2, 3, 5, 7, 8, 4, 6, 9)
+    # V: key r = g*KL + e, channel d = 16f + c
+    v = v_cache.reshape(B, L, H, NT, 4, KL, D // 16, 16).permute(0, 1, 2, 3, 6, 4, 7, 5)
+    return (k.contiguous().reshape(B, L, H, cap, D), v.contiguous().reshape(B, L, H, cap, D))
+
+
+def kv_from_library(k_cache, v_cache):
+    """Inverse of kv_to_library."""
+    B, L, H, cap, D, KL, NB, DS, NT = _kv_shape(k_cache)
+    k = k_cache.reshape(B, L, H, NT, NB, DS, 4, 4, 4, KL).permute(0, 1, 2, 3, 7, 4, 8, 5, 6, 9)
+    v = v_cache.reshape(B, L, H, NT, D // 16, 4, 16, KL).permute(0, 1, 2, 3, 5, 7, 4, 6)
+    return (k.contiguous().reshape(B, L, H, cap, D), v.contiguous().reshape(B, L, H, cap, D))
 
 
 class VerifyContext:

@@ -14,20 +14,20 @@
 // Tile shapes (KL = elements per 16-byte slice: 8 for bf16, 4 for fp32):
 //   scores   S^T[key][row] = K[key][:] . Q[row][:]  -- key tile = A operand,
 //            query fragment = B operand (held in registers for the chunk);
-//   output   O^T[d][row] += V^T[d][keys] . P^T[keys][row] -- the V cache is
-//            stored channel-major (V^T[d][pos]) so a lane's A slice is 16
-//            contiguous bytes, and the probabilities a lane produced by the
-//            score product are exactly its B slice (no shuffles):
+//   output   O^T[d][row] += V^T[d][keys] . P^T[keys][row] -- the probabilities
+//            a lane produced by the score product are exactly its B slice:
 // a 4*KL-key tile is computed as KL/4 score blocks of 16 keys whose slot s
 // maps to key KL*(s/4) + 4*blk + s%4, so that lane group g ends up holding
-// keys KL*g .. KL*g + KL-1 for its row.
+// keys KL*g .. KL*g + KL-1 for its row.  The cache stores every tile as the
+// 1 KiB operand pieces of exactly these instructions (layout documented with
+// the C ABI), so each fragment load is 64 lanes x 16 contiguous bytes.
 #pragma once
 #include "common.h"
 
 struct AttnArgs {
     const void* q;            // [T][n_q][D] activations (rotary applied)
-    const void* kc;           // K cache [B_max][L][n_kv][cap][D]
-    const void* vc;           // V cache [B_max][L][n_kv][D][cap]
+    const void* kc;           // K cache, tiled (see the C ABI)
+    const void* vc;           // V cache, tiled
     const int* ctx_in;        // [B]
     const int* seq_err;       // [B]
     int layer, L, n_q, n_kv, D, K1, cap, CH, maxch, QG;
@@ -58,8 +58,9 @@ __global__ __launch_bounds__(64) void attn_split_kernel(AttnArgs a)
     const int c1 = min(c0 + a.CH, total);
 
     const size_t head = ((size_t)b * a.L + a.layer) * a.n_kv + hkv;
-    const char* kbase = (const char*)a.kc + head * (size_t)a.cap * DH * ESZ;
-    const char* vbase = (const char*)a.vc + head * (size_t)DH * a.cap * ESZ;
+    const char* kbase = (const char*)a.kc + head * (size_t)a.cap * DH * ESZ + lane * 16;
+    const char* vbase = (const char*)a.vc + head * (size_t)a.cap * DH * ESZ + lane * 16;
+    constexpr size_t TILE = (size_t)KT * DH * ESZ;     // bytes per key tile
 
     // query fragments (B operand): lane supplies row l16, slice lg of each step
     uint4 qf[QPW][DS];
@@ -88,26 +89,18 @@ __global__ __launch_bounds__(64) void attn_split_kernel(AttnArgs a)
         for (int d = 0; d < DF; d++) o[f][d] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     }
 
-    const int cap = a.cap;
     for (int kt = c0; kt < c1; kt += KT) {
-        // key tile (A operand of the score product)
+        const size_t toff = (size_t)(kt / KT) * TILE;
+        // key tile (A operand of the score product): lane (slot l16, slice lg)
         uint4 kf[NB][DS];
 #pragma unroll
-        for (int blk = 0; blk < NB; blk++) {
-            int key = kt + KL * (l16 >> 2) + 4 * blk + (l16 & 3);
-            key = min(key, cap - 1);
-            const char* kp = kbase + ((size_t)key * DH + lg * KL) * ESZ;
+        for (int blk = 0; blk < NB; blk++)
 #pragma unroll
-            for (int s = 0; s < DS; s++) kf[blk][s] = ldg16(kp + (size_t)s * 4 * KL * ESZ);
-        }
-        // V^T tile (A operand of the output product): d = 16 df + l16, keys KL*lg ..
+            for (int s = 0; s < DS; s++) kf[blk][s] = ldg16(kbase + toff + (size_t)(blk * DS + s) * 1024);
+        // value tile (A operand of the output product): lane (channel 16 df + l16, keys KL lg ..)
         uint4 vf[DF];
-        {
-            int key = min(kt + KL * lg, cap - KL);
 #pragma unroll
-            for (int d = 0; d < DF; d++)
-                vf[d] = ldg16(vbase + ((size_t)(16 * d + l16) * cap + key) * ESZ);
-        }
+        for (int d = 0; d < DF; d++) vf[d] = ldg16(vbase + toff + (size_t)d * 1024);
 #pragma unroll
         for (int f = 0; f < QPW; f++) {
             float s[KL];

@@ -72,6 +72,33 @@ template <> struct WTraits<SV_FP8> { static constexpr int KL = 16, SK = 64, XU =
 // activation element size: fp32 with fp32 weights, bf16 otherwise
 template <int WT> struct ATraits { static constexpr int ESZ = (WT == SV_F32) ? 4 : 2; };
 
+// A weight slice in MFMA operand form: one 16-byte operand (fp32, bf16) or
+// two bf16 operands widened from 16 e4m3 codes (fp8) -- converted once per
+// fragment and reused for every row fragment.
+template <int WT> struct WOp { uint4 v[WT == SV_FP8 ? 2 : 1]; };
+
+template <int WT>
+SV_DEV WOp<WT> wprep(uint4 w)
+{
+    WOp<WT> o;
+    if constexpr (WT == SV_FP8) e4m3x16_to_bf16(w, o.v[0], o.v[1]);
+    else o.v[0] = w;
+    return o;
+}
+
+template <int WT>
+SV_DEV f32x4_t mma_op(const WOp<WT>& w, const uint4* x, f32x4_t c)
+{
+    if constexpr (WT == SV_F32) {
+        return mma_f32x4(w.v[0], x[0], c);
+    } else if constexpr (WT == SV_BF16) {
+        return mma_bf16(w.v[0], x[0], c);
+    } else {
+        c = mma_bf16(w.v[0], x[0], c);
+        return mma_bf16(w.v[1], x[1], c);
+    }
+}
+
 template <int WT>
 SV_DEV f32x4_t mma_step(uint4 w, const uint4* x, f32x4_t c)
 {
@@ -84,6 +111,96 @@ SV_DEV f32x4_t mma_step(uint4 w, const uint4* x, f32x4_t c)
         e4m3x16_to_bf16(w, lo, hi);
         c = mma_bf16(lo, x[0], c);
         return mma_bf16(hi, x[1], c);
+    }
+}
+
+// Epilogue shared by the GEMM kernels.  The lane holds columns
+// ncol0 + 16 f + 4 lg + e (e = 0..3) of rows row0 + 16 m + l16; `red` is
+// WAVES * 16 MF keys of shared memory (argmax mode only).
+template <int WT, int MF, int NF, int MODE, int WAVES>
+SV_DEV void gemm_epilogue(const GemmArgs& a, f32x4_t (&acc)[MF][(MODE == GM_SWIGLU) ? 2 * NF : NF],
+                          int row0, int nrows, int ncol0, int nt, const float* sc,
+                          const bool (&fvalid)[NF], unsigned long long* red)
+{
+    constexpr int AESZ = ATraits<WT>::ESZ;
+    constexpr int BM = 16 * MF;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int l16 = lane & 15, lg = lane >> 4;
+    if constexpr (MODE == GM_STORE) {
+        float* out = (float*)a.out + (size_t)blockIdx.y * a.split_stride;
+#pragma unroll
+        for (int f = 0; f < NF; f++) {
+            int n = ncol0 + 16 * f + 4 * lg;
+            if (!fvalid[f] || n >= a.N) continue;
+            float s0 = 1.f, s1 = 1.f, s2 = 1.f, s3 = 1.f;
+            if constexpr (WT == SV_FP8) { s0 = sc[n]; s1 = sc[n + 1]; s2 = sc[n + 2]; s3 = sc[n + 3]; }
+#pragma unroll
+            for (int m = 0; m < MF; m++) {
+                int r = 16 * m + l16;
+                if (r >= nrows) continue;
+                float4 v = make_float4(acc[m][f][0] * s0, acc[m][f][1] * s1, acc[m][f][2] * s2,
+                                       acc[m][f][3] * s3);
+                *reinterpret_cast<float4*>(out + (size_t)(row0 + r) * a.ldo + n) = v;
+            }
+        }
+    } else if constexpr (MODE == GM_SWIGLU) {
+#pragma unroll
+        for (int f = 0; f < NF; f++) {
+            int n = ncol0 + 16 * f + 4 * lg;
+            if (!fvalid[f] || n >= a.N) continue;
+            float gs[4] = {1.f, 1.f, 1.f, 1.f}, us[4] = {1.f, 1.f, 1.f, 1.f};
+            if constexpr (WT == SV_FP8) {
+#pragma unroll
+                for (int r = 0; r < 4; r++) { gs[r] = sc[n + r]; us[r] = sc[a.dual_off + n + r]; }
+            }
+#pragma unroll
+            for (int m = 0; m < MF; m++) {
+                int r = 16 * m + l16;
+                if (r >= nrows) continue;
+                float v[4];
+#pragma unroll
+                for (int e = 0; e < 4; e++)
+                    v[e] = silu_f32(acc[m][f][e] * gs[e]) * (acc[m][NF + f][e] * us[e]);
+                size_t o = (size_t)(row0 + r) * a.ldo + n;
+                if constexpr (AESZ == 2) {
+                    uint2 p = make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
+                    *reinterpret_cast<uint2*>((uint16_t*)a.out + o) = p;
+                } else {
+                    *reinterpret_cast<float4*>((float*)a.out + o) = make_float4(v[0], v[1], v[2], v[3]);
+                }
+            }
+        }
+    } else {   // GM_ARGMAX
+#pragma unroll
+        for (int m = 0; m < MF; m++) {
+            unsigned long long best = 0ull;
+            int r = 16 * m + l16;
+#pragma unroll
+            for (int f = 0; f < NF; f++) {
+                int n = ncol0 + 16 * f + 4 * lg;
+                if (!fvalid[f] || n >= a.N) continue;
+                float v[4];
+#pragma unroll
+                for (int e = 0; e < 4; e++) {
+                    v[e] = acc[m][f][e];
+                    if constexpr (WT == SV_FP8) v[e] *= sc[n + e];
+                    best = umax64(best, argmax_key(v[e], (uint32_t)(n + e)));
+                }
+                if (a.dbg && r < nrows)
+                    *reinterpret_cast<float4*>(a.dbg + (size_t)(row0 + r) * a.dbg_ld + n) =
+                        make_float4(v[0], v[1], v[2], v[3]);
+            }
+            best = umax64(best, shfl_xor_u64(best, 16));
+            best = umax64(best, shfl_xor_u64(best, 32));
+            if (lg == 0) red[wave * BM + r] = best;
+        }
+        __syncthreads();
+        for (int r = threadIdx.x; r < nrows; r += 64 * WAVES) {
+            unsigned long long b = red[r];
+#pragma unroll
+            for (int w2 = 1; w2 < WAVES; w2++) b = umax64(b, red[w2 * BM + r]);
+            a.keys[(size_t)nt * a.key_ld + row0 + r] = b;
+        }
     }
 }
 
@@ -203,9 +320,11 @@ __global__ __launch_bounds__(64 * WAVES) void gemm_kernel(GemmArgs a)
         for (int u = 0; u < U; u++) {
             if (k + u * SK < ke) {
 #pragma unroll
-                for (int m = 0; m < MF; m++)
+                for (int f = 0; f < NFT; f++) {
+                    const WOp<WT> wo = wprep<WT>(w[u][f]);
 #pragma unroll
-                    for (int f = 0; f < NFT; f++) acc[m][f] = mma_step<WT>(w[u][f], x[u][m], acc[m][f]);
+                    for (int m = 0; m < MF; m++) acc[m][f] = mma_op<WT>(wo, x[u][m], acc[m][f]);
+                }
             }
         }
     };
@@ -220,82 +339,150 @@ __global__ __launch_bounds__(64 * WAVES) void gemm_kernel(GemmArgs a)
     }
 
     // ------------------------------------------------------------ epilogue
-    // lane holds columns n0 + 4*lg + r (r = 0..3) of row 16*m + l16
-    if constexpr (MODE == GM_STORE) {
-        float* out = (float*)a.out + (size_t)blockIdx.y * a.split_stride;
+    if constexpr (MODE == GM_ARGMAX) {
+        __shared__ unsigned long long red[WAVES * BM];
+        gemm_epilogue<WT, MF, NF, MODE, WAVES>(a, acc, row0, nrows, ncol0, nt, sc, fvalid, red);
+    } else {
+        gemm_epilogue<WT, MF, NF, MODE, WAVES>(a, acc, row0, nrows, ncol0, nt, sc, fvalid, nullptr);
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Large-row variant (dense mode, 64 .. 256 rows).  The small-row kernel above
+// re-reads every activation fragment from cache for each 16x16 product; with
+// 16 row fragments per wave that traffic exceeds what the vector cache can
+// deliver.  Here the workgroup stages a K-chunk of all its rows in LDS once,
+// in operand order (row block, step, lane: one 1 KiB piece per fragment, read
+// back with one conflict-free 16-byte access per lane), double-buffered with
+// one barrier per chunk; each wave streams NF (x2 for SwiGLU) distinct weight
+// fragments from HBM one chunk ahead and applies every activation fragment to
+// all of them.
+template <int WT, int MF, int NF, int MODE, bool PACKED>
+__global__ __launch_bounds__(256) void gemm_bigm_kernel(GemmArgs a)
+{
+    using Tr = WTraits<WT>;
+    constexpr int KL = Tr::KL, SK = Tr::SK, XU = Tr::XU, WESZ = Tr::ESZ;
+    constexpr int AESZ = ATraits<WT>::ESZ;
+    constexpr int NFT = (MODE == GM_SWIGLU) ? 2 * NF : NF;
+    constexpr int BM = 16 * MF;
+    constexpr int CS = 2;                        // reduction steps per chunk
+    constexpr int KC = CS * SK;                  // chunk length
+    constexpr int PIECES = MF * CS * XU;         // 1 KiB activation pieces per chunk
+    static_assert(PIECES % 4 == 0, "pieces split over 4 waves");
+    constexpr int PPW = PIECES / 4;              // pieces each wave stages
+    __shared__ uint4 xs[2][PIECES][64];
+
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int l16 = lane & 15, lg = lane >> 4;
+    const int id = blockIdx.x, xcd = id & 7, q = id >> 3;
+    const int mt = q % a.MT;
+    const int nt = (q / a.MT) * 8 + xcd;
+    if (nt >= a.NT) return;
+    const int row0 = mt * BM;
+    const int nrows = min(BM, a.M - row0);
+    if (nrows <= 0) return;
+    const char* Wb = (const char*)a.W;
+    const float* sc = a.ws;
+    const int ncol0 = (nt * 4 + wave) * 16 * NF;
+    const int K = a.K;
+    const int kspan = K / a.ksplit;
+    const int kb = blockIdx.y * kspan;
+    const int nchunk = kspan / KC;
+
+    const char* wrow[NFT];
+    bool fvalid[NF];
 #pragma unroll
-        for (int f = 0; f < NF; f++) {
-            int n = ncol0 + 16 * f + 4 * lg;
-            if (!fvalid[f] || n >= a.N) continue;
-            float s0 = 1.f, s1 = 1.f, s2 = 1.f, s3 = 1.f;
-            if constexpr (WT == SV_FP8) { s0 = sc[n]; s1 = sc[n + 1]; s2 = sc[n + 2]; s3 = sc[n + 3]; }
+    for (int f = 0; f < NF; f++) {
+        int n0 = ncol0 + 16 * f;
+        fvalid[f] = n0 < a.N;
+        int r = fvalid[f] ? min(n0 + l16, a.N - 1) : 0;
+        if constexpr (PACKED) {
+            int rb = fvalid[f] ? n0 / 16 : 0;
+            wrow[f] = Wb + (size_t)rb * K * 16 * WESZ + (size_t)lane * 16;
+            if constexpr (MODE == GM_SWIGLU)
+                wrow[NF + f] = Wb + (size_t)(rb + a.dual_off / 16) * K * 16 * WESZ + (size_t)lane * 16;
+        } else {
+            wrow[f] = Wb + ((size_t)r * K + (size_t)lg * KL) * WESZ;
+            if constexpr (MODE == GM_SWIGLU)
+                wrow[NF + f] = Wb + ((size_t)(r + a.dual_off) * K + (size_t)lg * KL) * WESZ;
+        }
+    }
+    // activation pieces this wave stages: piece p = (m * CS + s) * XU + v
+    const char* xsrc[PPW];
+#pragma unroll
+    for (int i = 0; i < PPW; i++) {
+        int p = wave * PPW + i;
+        int v = p % XU, s = (p / XU) % CS, m = p / (XU * CS);
+        int r = 16 * m + l16;
+        r = (r < nrows) ? row0 + r : row0;
+        xsrc[i] = (const char*)a.X + ((size_t)r * a.ldx + (size_t)s * SK + (size_t)lg * KL + 8 * v) * AESZ;
+    }
+    auto wload = [&](int k, uint4 (&w)[CS][NFT]) {
+#pragma unroll
+        for (int s = 0; s < CS; s++)
+#pragma unroll
+            for (int f = 0; f < NFT; f++) {
+                int kk = k + s * SK;
+                if constexpr (PACKED) w[s][f] = ldg16_stream(wrow[f] + (size_t)(kk / SK) * 1024);
+                else w[s][f] = ldg16_stream(wrow[f] + (size_t)kk * WESZ);
+            }
+    };
+    auto xload = [&](int k, uint4 (&st)[PPW]) {
+#pragma unroll
+        for (int i = 0; i < PPW; i++) st[i] = ldg16(xsrc[i] + (size_t)k * AESZ);
+    };
+
+    f32x4_t acc[MF][NFT];
+#pragma unroll
+    for (int m = 0; m < MF; m++)
+#pragma unroll
+        for (int f = 0; f < NFT; f++) acc[m][f] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+    uint4 wcur[CS][NFT], wnext[CS][NFT], stage[PPW];
+    xload(kb, stage);
+    wload(kb, wcur);
+#pragma unroll
+    for (int i = 0; i < PPW; i++) xs[0][wave * PPW + i][lane] = stage[i];
+    __syncthreads();
+    for (int c = 0; c < nchunk; c++) {
+        const int buf = c & 1;
+        const int kn = kb + (c + 1) * KC;
+        const bool more = c + 1 < nchunk;
+        if (more) {
+            xload(kn, stage);
+            wload(kn, wnext);
+        }
+#pragma unroll
+        for (int s = 0; s < CS; s++) {
+            WOp<WT> wo[NFT];
+#pragma unroll
+            for (int f = 0; f < NFT; f++) wo[f] = wprep<WT>(wcur[s][f]);
 #pragma unroll
             for (int m = 0; m < MF; m++) {
-                int r = 16 * m + l16;
-                if (r >= nrows) continue;
-                float4 v = make_float4(acc[m][f][0] * s0, acc[m][f][1] * s1, acc[m][f][2] * s2,
-                                       acc[m][f][3] * s3);
-                *reinterpret_cast<float4*>(out + (size_t)(row0 + r) * a.ldo + n) = v;
+                uint4 xf[XU];
+#pragma unroll
+                for (int v = 0; v < XU; v++) xf[v] = xs[buf][(m * CS + s) * XU + v][lane];
+#pragma unroll
+                for (int f = 0; f < NFT; f++) acc[m][f] = mma_op<WT>(wo[f], xf, acc[m][f]);
             }
         }
-    } else if constexpr (MODE == GM_SWIGLU) {
+        if (more) {
 #pragma unroll
-        for (int f = 0; f < NF; f++) {
-            int n = ncol0 + 16 * f + 4 * lg;
-            if (!fvalid[f] || n >= a.N) continue;
-            float gs[4] = {1.f, 1.f, 1.f, 1.f}, us[4] = {1.f, 1.f, 1.f, 1.f};
-            if constexpr (WT == SV_FP8) {
+            for (int i = 0; i < PPW; i++) xs[buf ^ 1][wave * PPW + i][lane] = stage[i];
 #pragma unroll
-                for (int r = 0; r < 4; r++) { gs[r] = sc[n + r]; us[r] = sc[a.dual_off + n + r]; }
-            }
+            for (int s = 0; s < CS; s++)
 #pragma unroll
-            for (int m = 0; m < MF; m++) {
-                int r = 16 * m + l16;
-                if (r >= nrows) continue;
-                float v[4];
-#pragma unroll
-                for (int e = 0; e < 4; e++)
-                    v[e] = silu_f32(acc[m][f][e] * gs[e]) * (acc[m][NF + f][e] * us[e]);
-                size_t o = (size_t)(row0 + r) * a.ldo + n;
-                if constexpr (AESZ == 2) {
-                    uint2 p = make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
-                    *reinterpret_cast<uint2*>((uint16_t*)a.out + o) = p;
-                } else {
-                    *reinterpret_cast<float4*>((float*)a.out + o) = make_float4(v[0], v[1], v[2], v[3]);
-                }
-            }
-        }
-    } else {   // GM_ARGMAX
-        __shared__ unsigned long long red[WAVES][BM];
-#pragma unroll
-        for (int m = 0; m < MF; m++) {
-            unsigned long long best = 0ull;
-            int r = 16 * m + l16;
-#pragma unroll
-            for (int f = 0; f < NF; f++) {
-                int n = ncol0 + 16 * f + 4 * lg;
-                if (!fvalid[f] || n >= a.N) continue;
-                float v[4];
-#pragma unroll
-                for (int e = 0; e < 4; e++) {
-                    v[e] = acc[m][f][e];
-                    if constexpr (WT == SV_FP8) v[e] *= sc[n + e];
-                    best = umax64(best, argmax_key(v[e], (uint32_t)(n + e)));
-                }
-                if (a.dbg && r < nrows)
-                    *reinterpret_cast<float4*>(a.dbg + (size_t)(row0 + r) * a.dbg_ld + n) =
-                        make_float4(v[0], v[1], v[2], v[3]);
-            }
-            best = umax64(best, shfl_xor_u64(best, 16));
-            best = umax64(best, shfl_xor_u64(best, 32));
-            if (lg == 0) red[wave][r] = best;
+                for (int f = 0; f < NFT; f++) wcur[s][f] = wnext[s][f];
         }
         __syncthreads();
-        for (int r = threadIdx.x; r < nrows; r += 64 * WAVES) {
-            unsigned long long b = red[0][r];
-#pragma unroll
-            for (int w2 = 1; w2 < WAVES; w2++) b = umax64(b, red[w2][r]);
-            a.keys[(size_t)nt * a.key_ld + row0 + r] = b;
-        }
+    }
+
+    if constexpr (MODE == GM_ARGMAX) {
+        // the activation buffers are no longer needed: reuse them for the reduction
+        unsigned long long* red = reinterpret_cast<unsigned long long*>(&xs[0][0][0]);
+        static_assert(sizeof(xs) >= 4 * BM * sizeof(unsigned long long), "reduction space");
+        gemm_epilogue<WT, MF, NF, MODE, 4>(a, acc, row0, nrows, ncol0, nt, sc, fvalid, red);
+    } else {
+        gemm_epilogue<WT, MF, NF, MODE, 4>(a, acc, row0, nrows, ncol0, nt, sc, fvalid, nullptr);
     }
 }

@@ -177,6 +177,29 @@ struct RopeArgs {
     void* vc;                   // V cache (channel-major)
 };
 
+// Element offsets of (pos, d) inside one (sequence, layer, KV head) region of
+// the tiled caches (layout documented with the C ABI).
+template <bool BF>
+SV_DEV size_t k_cache_index(int pos, int d, int D)
+{
+    constexpr int KL = BF ? 8 : 4, KT = 4 * KL, NB = KL / 4;
+    const int DS = D / (4 * KL);
+    const int t = pos / KT, r = pos % KT;
+    const int rem = r % KL;
+    const int slot = 4 * (r / KL) + (rem & 3), blk = rem >> 2;
+    const int s = d / (4 * KL), g = (d % (4 * KL)) / KL, e = d % KL;
+    return ((((size_t)t * NB + blk) * DS + s) * 64 + slot + 16 * g) * KL + e;
+}
+
+template <bool BF>
+SV_DEV size_t v_cache_index(int pos, int d, int D)
+{
+    constexpr int KL = BF ? 8 : 4, KT = 4 * KL;
+    const int t = pos / KT, r = pos % KT;
+    const int g = r / KL, e = r % KL;
+    return (((size_t)t * (D / 16) + d / 16) * 64 + (d % 16) + 16 * g) * KL + e;
+}
+
 // rotary on q and k (pair (i, i + D/2) turned by pos * theta^(-2i/D)), then q
 // to the attention input and k, v to the caches at position ctx + j.  One
 // wave per (row, head); grid (T, n_q + 2 n_kv).
@@ -205,18 +228,17 @@ __global__ __launch_bounds__(64) void rope_append_kernel(RopeArgs a)
                 Act<BF>::st(qo, i + half, r1);
             } else if (write_cache) {
                 int kh = hh - a.n_q;
-                size_t base = (((size_t)b * a.L + a.layer) * a.n_kv + kh) * (size_t)a.cap;
-                AT* kp = (AT*)a.kc + (base + pos) * D;
-                Act<BF>::st(kp, i, r0);
-                Act<BF>::st(kp, i + half, r1);
+                AT* kp = (AT*)a.kc + (((size_t)b * a.L + a.layer) * a.n_kv + kh) * (size_t)a.cap * D;
+                Act<BF>::st(kp, k_cache_index<BF>(pos, i, D), r0);
+                Act<BF>::st(kp, k_cache_index<BF>(pos, i + half, D), r1);
             }
         }
     } else if (write_cache) {
         int vh = hh - a.n_q - a.n_kv;
+        AT* vp = (AT*)a.vc + (((size_t)b * a.L + a.layer) * a.n_kv + vh) * (size_t)a.cap * D;
         for (int d = lane; d < D; d += 64) {
             float v = sum_strided(src + d, a.nsplit, sstride);
-            size_t base = ((((size_t)b * a.L + a.layer) * a.n_kv + vh) * D + d) * (size_t)a.cap;
-            Act<BF>::st((AT*)a.vc, base + pos, v);
+            Act<BF>::st(vp, v_cache_index<BF>(pos, d, D), v);
         }
     }
 }

@@ -217,6 +217,31 @@ void launch_gemm(int wt, int mode, int MF, bool packed, GemmArgs& a, hipStream_t
     else launch_gemm_l<false>(wt, mode, MF, a, grid, s);
 }
 
+// Large-row path: 128-row workgroup tiles (MF 8) of 128 columns (NF 2).
+constexpr int BIG_MF = 8, BIG_NF = 2, BIG_CHUNK_STEPS = 2;
+
+template <int MODE, bool PK>
+void launch_big_m(int wt, const GemmArgs& a, dim3 grid, hipStream_t s)
+{
+    if (wt == SV_F32) launch(gemm_bigm_kernel<SV_F32, BIG_MF, BIG_NF, MODE, PK>, grid, dim3(256), 0, s, a);
+    else if (wt == SV_BF16) launch(gemm_bigm_kernel<SV_BF16, BIG_MF, BIG_NF, MODE, PK>, grid, dim3(256), 0, s, a);
+    else launch(gemm_bigm_kernel<SV_FP8, BIG_MF, BIG_NF, MODE, PK>, grid, dim3(256), 0, s, a);
+}
+
+void launch_gemm_big(int wt, int mode, bool packed, GemmArgs& a, hipStream_t s)
+{
+    dim3 grid((unsigned)(cdiv(a.NT, 8) * 8 * a.MT), (unsigned)a.ksplit, 1);
+    if (packed) {
+        if (mode == GM_STORE) launch_big_m<GM_STORE, true>(wt, a, grid, s);
+        else if (mode == GM_SWIGLU) launch_big_m<GM_SWIGLU, true>(wt, a, grid, s);
+        else launch_big_m<GM_ARGMAX, true>(wt, a, grid, s);
+    } else {
+        if (mode == GM_STORE) launch_big_m<GM_STORE, false>(wt, a, grid, s);
+        else if (mode == GM_SWIGLU) launch_big_m<GM_SWIGLU, false>(wt, a, grid, s);
+        else launch_big_m<GM_ARGMAX, false>(wt, a, grid, s);
+    }
+}
+
 int rows_mf(int rows) { return rows <= 16 ? 1 : (rows <= 32 ? 2 : 4); }
 
 // K split: enough waves to cover the GPU, each split at least 4 reduction steps
@@ -498,16 +523,42 @@ int spec_verify_step(spec_verify_ctx* c, const spec_verify_weights* w, void* k_c
 
     const int MFd = rows_mf(T);
     const int MTd = cdiv(T, 16 * MFd);
+    // rows >= 64: the large-row kernel (activation chunks staged in LDS)
+    const bool big = T >= 64 && wt != SV_F32;
+    const int MTb = cdiv(T, 16 * BIG_MF);
+    // dense GEMM (or the dense SwiGLU / argmax variants); returns the K split used
     auto dense_gemm = [&](int mode, const void* X, long ldx, int N, int Kd, const void* W,
                           const float* ws, void* out, long ldo, int allow_split) -> int {
         GemmArgs a = dense_args(X, ldx, T, N, Kd, W, ws);
+        a.out = out;
+        a.ldo = ldo;
+        a.split_stride = (long)T * ldo;
+        a.keys = c->keys;
+        a.key_ld = T;
+        a.dbg = c->dbg_logits;
+        a.dbg_ld = k.vocab;
+        if (mode == GM_SWIGLU) a.dual_off = N;
+        const int chunk = BIG_CHUNK_STEPS * step;
+        if (big && Kd % chunk == 0) {
+            a.MT = MTb;
+            a.NT = cdiv(N, 16 * 4 * BIG_NF);
+            long wgs = (long)a.NT * a.MT;
+            a.ksplit = 1;
+            if (allow_split) {   // enough workgroups for the 256 CUs, each split >= 4 chunks
+                int steps = Kd / chunk;
+                for (int sp = 2; sp <= KS_MAX; sp++) {
+                    if (steps % sp || steps / sp < 4) continue;
+                    if (wgs * a.ksplit >= 512) break;
+                    a.ksplit = sp;
+                }
+            }
+            launch_gemm_big(wt, mode, packed, a, s);
+            return a.ksplit;
+        }
         a.MT = MTd;
         a.NT = cdiv(N, 64);
         long waves = (long)a.NT * a.MT * 4;
         a.ksplit = allow_split ? pick_ksplit(waves, Kd, step) : 1;
-        a.out = out;
-        a.ldo = ldo;
-        a.split_stride = (long)T * ldo;
         launch_gemm(wt, mode, MFd, packed, a, s);
         return a.ksplit;
     };
@@ -689,15 +740,9 @@ int spec_verify_step(spec_verify_ctx* c, const spec_verify_weights* w, void* k_c
             else residual_norm_kernel<false, true><<<T, 1024, 0, s>>>(ra);
         } else {
             const int I = k.dense_inter;
-            GemmArgs g = dense_args(c->h, H, T, I, H, Lw.w_gate_up, Lw.s_gate_up);
-            g.MT = MTd;
-            g.NT = cdiv(I, 64);
-            g.dual_off = I;
-            g.out = c->act;
-            g.ldo = I;
             {
                 ProfScope ps(c, SV_KC_EXPERT_GATE_UP, s);
-                launch_gemm(wt, GM_SWIGLU, MFd, packed, g, s);
+                dense_gemm(GM_SWIGLU, c->h, H, I, H, Lw.w_gate_up, Lw.s_gate_up, c->act, I, 0);
             }
             {
                 ProfScope ps(c, SV_KC_EXPERT_DOWN, s);
@@ -713,17 +758,12 @@ int spec_verify_step(spec_verify_ctx* c, const spec_verify_weights* w, void* k_c
     }
 
     // ---- LM head + argmax, acceptance
-    const int NT_lm = cdiv(k.vocab, 64);
+    // column tiles of the argmax keys: 64 columns (small-row) or 128 (large-row)
+    const int NT_lm = (big && H % (BIG_CHUNK_STEPS * step) == 0) ? cdiv(k.vocab, 16 * 4 * BIG_NF)
+                                                                  : cdiv(k.vocab, 64);
     {
-        GemmArgs a = dense_args(c->h, H, T, k.vocab, H, w->lm_head, w->lm_scale);
-        a.MT = MTd;
-        a.NT = NT_lm;
-        a.keys = c->keys;
-        a.key_ld = T;
-        a.dbg = c->dbg_logits;
-        a.dbg_ld = k.vocab;
         ProfScope ps(c, SV_KC_LM_HEAD, s);
-        launch_gemm(wt, GM_ARGMAX, MFd, packed, a, s);
+        dense_gemm(GM_ARGMAX, c->h, H, k.vocab, H, w->lm_head, w->lm_scale, nullptr, 0, 0);
     }
     AcceptArgs ac;
     ac.keys = c->keys;

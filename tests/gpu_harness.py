@@ -99,8 +99,7 @@ class GpuRun:
         self.case = case
         self.B = cfg.batch if batch is None else batch
         self.ctx = sv.VerifyContext(cfg, self.B, case.cap, case.w_gpu, layout=layout)
-        self.kc = case.k_nat[: self.B].clone()
-        self.vc = sv.to_library_v_layout(case.v_nat[: self.B])
+        self.kc, self.vc = sv.kv_to_library(case.k_nat[: self.B], case.v_nat[: self.B])
         K1 = cfg.k_draft + 1
         T = self.B * K1
         dev = "cuda"
@@ -193,8 +192,9 @@ def compare_new_kv(cfg, run: GpuRun, b: int, kc_or, vc_or, ctx_b: int, stats: di
     """The K+1 slots the step wrote, every layer, against the oracle's cache."""
     tol = TOL[cfg.wdtype]
     K1 = cfg.k_draft + 1
-    kg = run.kc[b, :, :, ctx_b:ctx_b + K1].float().cpu().numpy()
-    vg = run.vc[b, :, :, :, ctx_b:ctx_b + K1].float().cpu().numpy().swapaxes(-1, -2)
+    kn, vn = sv.kv_from_library(run.kc[b:b + 1], run.vc[b:b + 1])
+    kg = kn[0, :, :, ctx_b:ctx_b + K1].float().cpu().numpy()
+    vg = vn[0, :, :, ctx_b:ctx_b + K1].float().cpu().numpy()
     conv = (lambda a: a.astype(np.float64)) if cfg.kvdtype == "f32" else (
         lambda a: (a.astype(np.uint32) << 16).view(np.float32).astype(np.float64))
     ko = conv(kc_or[0, :, :, ctx_b:ctx_b + K1])

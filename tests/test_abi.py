@@ -93,3 +93,34 @@ def test_init_without_gpu_reports_no_device(sv):
     lib = sv.load_library()
     h = ctypes.c_void_p()
     assert lib.spec_verify_init(ctypes.byref(_cfg(sv)), ctypes.byref(h)) == sv.SV_ERR_NO_DEVICE
+
+
+@pytest.mark.parametrize("dtype,D", [("bf16", 128), ("bf16", 64), ("f32", 64)])
+def test_kv_layout_permutation_matches_documented_formulas(sv, dtype, D):
+    """kv_to_library places K[pos][d] and V[pos][d] at the element offsets the
+    header documents, and kv_from_library inverts it."""
+    import torch
+    tdt = {"bf16": torch.bfloat16, "f32": torch.float32}[dtype]
+    KL = 8 if dtype == "bf16" else 4
+    KT, NB, DS = 4 * KL, KL // 4, D // (4 * KL)
+    cap = 128
+    # integer tags of the same element size: K holds pos * D + d, V its negative - 1
+    itype = torch.int16 if dtype == "bf16" else torch.int32
+    idx = torch.arange(cap * D, dtype=torch.int64).reshape(1, 1, 1, cap, D)
+    k_lib, v_lib = sv.kv_to_library(idx.to(itype), (-idx - 1).to(itype))
+    kf, vf = k_lib.reshape(-1), v_lib.reshape(-1)
+    for pos in (0, 1, 5, 8, 13, 31, 32, 77, cap - 1):
+        for d in (0, 1, 7, 8, 15, 16, 33, D - 1):
+            t, r = pos // KT, pos % KT
+            rem = r % KL
+            q4, blk = 4 * (r // KL) + rem % 4, rem // 4
+            s_, g, e = d // (4 * KL), (d % (4 * KL)) // KL, d % KL
+            ko = (((t * NB + blk) * DS + s_) * 64 + q4 + 16 * g) * KL + e
+            assert kf[ko].item() == pos * D + d
+            g2, e2 = r // KL, r % KL
+            vo = ((t * (D // 16) + d // 16) * 64 + d % 16 + 16 * g2) * KL + e2
+            assert vf[vo].item() == -(pos * D + d) - 1
+    x = torch.randn(2, 3, 2, cap, D).to(tdt)
+    y = torch.randn(2, 3, 2, cap, D).to(tdt)
+    k2, v2 = sv.kv_from_library(*sv.kv_to_library(x, y))
+    assert torch.equal(k2, x) and torch.equal(v2, y)
