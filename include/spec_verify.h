@@ -68,8 +68,9 @@
  *   its last dimension (e.g. s_gate_up [E][2I]).
  *
  * Two layouts are accepted for the matrices that feed a matrix product
- * (w_qkv, w_o, w_router, w_gate_up, w_down, w_sh_gate_up, w_sh_down,
- * lm_head), chosen by spec_verify_weights.layout:
+ * (w_qkv, w_o, w_gate_up, w_down, w_sh_gate_up, w_sh_down, lm_head), chosen
+ * by spec_verify_weights.layout (the router w_router is always row-major: it
+ * is applied inside the normalisation kernel, one row of logits per token):
  *   SV_LAYOUT_ROW_MAJOR  as above;
  *   SV_LAYOUT_TILED16    rows grouped in blocks of 16, each block stored step
  *                        by step along the reduction dimension (exact format
@@ -156,7 +157,7 @@ typedef struct {
     int n_experts;      /* E (MoE), multiple of 4, <= 256 */
     int expert_inter;   /* I (MoE), multiple of 64 */
     int top_k;          /* k (MoE), 1 <= k <= min(E, 8) */
-    int n_shared;       /* shared experts (MoE), >= 0 */
+    int n_shared;       /* shared experts (MoE), 0..8 */
     int renorm_topk;    /* 1: gates renormalised to sum 1 over the selected experts */
     int dense_inter;    /* I_d (dense), multiple of 64 */
     int vocab;          /* V, multiple of 16 */

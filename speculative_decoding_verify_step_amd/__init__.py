@@ -24,7 +24,7 @@ SV_KC_LM_HEAD, SV_KC_ATTENTION, SV_KC_EXPERT_GATE_UP, SV_KC_EXPERT_DOWN, SV_KC_Q
 SV_LAYOUT_ROW_MAJOR, SV_LAYOUT_TILED16 = 0, 1
 _LAYOUTS = {"row_major": SV_LAYOUT_ROW_MAJOR, "tiled16": SV_LAYOUT_TILED16}
 # matrices that feed a matrix product (packed in the tiled16 layout)
-GEMM_MATRICES = ("w_qkv", "w_o", "w_router", "w_gate_up", "w_down", "w_sh_gate_up", "w_sh_down")
+GEMM_MATRICES = ("w_qkv", "w_o", "w_gate_up", "w_down", "w_sh_gate_up", "w_sh_down")
 KERNEL_CLASSES = {"lm_head": 0, "attention": 1, "expert_gate_up": 2, "expert_down": 3, "qkv": 4}
 _DT = {"f32": SV_F32, "bf16": SV_BF16, "fp8": SV_FP8}
 

@@ -214,7 +214,7 @@ __global__ __launch_bounds__(64 * WAVES) void gemm_kernel(GemmArgs a)
     constexpr int AESZ = ATraits<WT>::ESZ;
     constexpr int NFT = (MODE == GM_SWIGLU) ? 2 * NF : NF;   // weight fragments per wave
     constexpr int BM = 16 * MF;
-    constexpr int U = UU ? UU : ((MF >= 4) ? 2 : 4);          // reduction steps per stage
+    constexpr int U = UU ? UU : ((MF >= 4) ? 2 : (MF == 2 ? 4 : 8));   // reduction steps per stage
 
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
@@ -348,7 +348,7 @@ __global__ __launch_bounds__(64 * WAVES) void gemm_kernel(GemmArgs a)
 }
 
 // ---------------------------------------------------------------------------
-// Large-row variant (dense mode, 64 .. 256 rows).  The small-row kernel above
+// Large-row variant (dense mode with 64 .. 256 rows, or grouped mode).  The small-row kernel above
 // re-reads every activation fragment from cache for each 16x16 product; with
 // 16 row fragments per wave that traffic exceeds what the vector cache can
 // deliver.  Here the workgroup stages a K-chunk of all its rows in LDS once,
@@ -368,9 +368,8 @@ __global__ __launch_bounds__(256) void gemm_bigm_kernel(GemmArgs a)
     constexpr int CS = 2;                        // reduction steps per chunk
     constexpr int KC = CS * SK;                  // chunk length
     constexpr int PIECES = MF * CS * XU;         // 1 KiB activation pieces per chunk
-    static_assert(PIECES % 4 == 0, "pieces split over 4 waves");
-    constexpr int PPW = PIECES / 4;              // pieces each wave stages
-    __shared__ uint4 xs[2][PIECES][64];
+    constexpr int PPW = (PIECES + 3) / 4;        // pieces each wave stages (the last may idle)
+    __shared__ uint4 xs[2][PIECES < 4 ? 4 : PIECES][64];
 
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int l16 = lane & 15, lg = lane >> 4;
@@ -378,11 +377,26 @@ __global__ __launch_bounds__(256) void gemm_bigm_kernel(GemmArgs a)
     const int mt = q % a.MT;
     const int nt = (q / a.MT) * 8 + xcd;
     if (nt >= a.NT) return;
-    const int row0 = mt * BM;
-    const int nrows = min(BM, a.M - row0);
+    int group = 0, row0, nrows;
+    if (a.tiles) {
+        if (mt >= *a.n_tiles) return;
+        group = a.tiles[3 * mt];
+        row0 = a.tiles[3 * mt + 1];
+        nrows = a.tiles[3 * mt + 2];
+    } else {
+        row0 = mt * BM;
+        nrows = min(BM, a.M - row0);
+    }
     if (nrows <= 0) return;
-    const char* Wb = (const char*)a.W;
-    const float* sc = a.ws;
+    const char* Wb;
+    const float* sc;
+    if (group < a.G1) {
+        Wb = (const char*)a.W + (size_t)group * a.w_gstride * WESZ;
+        sc = a.ws ? a.ws + (size_t)group * a.s_gstride : nullptr;
+    } else {
+        Wb = (const char*)a.W2 + (size_t)(group - a.G1) * a.w2_gstride * WESZ;
+        sc = a.ws2 ? a.ws2 + (size_t)(group - a.G1) * a.s2_gstride : nullptr;
+    }
     const int ncol0 = (nt * 4 + wave) * 16 * NF;
     const int K = a.K;
     const int kspan = K / a.ksplit;
@@ -411,12 +425,14 @@ __global__ __launch_bounds__(256) void gemm_bigm_kernel(GemmArgs a)
     const char* xsrc[PPW];
 #pragma unroll
     for (int i = 0; i < PPW; i++) {
-        int p = wave * PPW + i;
+        int p = min(wave * PPW + i, PIECES - 1);
         int v = p % XU, s = (p / XU) % CS, m = p / (XU * CS);
         int r = 16 * m + l16;
         r = (r < nrows) ? row0 + r : row0;
-        xsrc[i] = (const char*)a.X + ((size_t)r * a.ldx + (size_t)s * SK + (size_t)lg * KL + 8 * v) * AESZ;
+        int xr = a.gather ? a.gather[r] : r;
+        xsrc[i] = (const char*)a.X + ((size_t)xr * a.ldx + (size_t)s * SK + (size_t)lg * KL + 8 * v) * AESZ;
     }
+    auto staged = [&](int i) { return wave * PPW + i < PIECES; };
     auto wload = [&](int k, uint4 (&w)[CS][NFT]) {
 #pragma unroll
         for (int s = 0; s < CS; s++)
@@ -429,7 +445,8 @@ __global__ __launch_bounds__(256) void gemm_bigm_kernel(GemmArgs a)
     };
     auto xload = [&](int k, uint4 (&st)[PPW]) {
 #pragma unroll
-        for (int i = 0; i < PPW; i++) st[i] = ldg16(xsrc[i] + (size_t)k * AESZ);
+        for (int i = 0; i < PPW; i++)
+            if (staged(i)) st[i] = ldg16(xsrc[i] + (size_t)k * AESZ);
     };
 
     f32x4_t acc[MF][NFT];
@@ -442,7 +459,8 @@ __global__ __launch_bounds__(256) void gemm_bigm_kernel(GemmArgs a)
     xload(kb, stage);
     wload(kb, wcur);
 #pragma unroll
-    for (int i = 0; i < PPW; i++) xs[0][wave * PPW + i][lane] = stage[i];
+    for (int i = 0; i < PPW; i++)
+        if (staged(i)) xs[0][wave * PPW + i][lane] = stage[i];
     __syncthreads();
     for (int c = 0; c < nchunk; c++) {
         const int buf = c & 1;
@@ -468,7 +486,8 @@ __global__ __launch_bounds__(256) void gemm_bigm_kernel(GemmArgs a)
         }
         if (more) {
 #pragma unroll
-            for (int i = 0; i < PPW; i++) xs[buf ^ 1][wave * PPW + i][lane] = stage[i];
+            for (int i = 0; i < PPW; i++)
+                if (staged(i)) xs[buf ^ 1][wave * PPW + i][lane] = stage[i];
 #pragma unroll
             for (int s = 0; s < CS; s++)
 #pragma unroll

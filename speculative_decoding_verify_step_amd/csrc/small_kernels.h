@@ -60,13 +60,21 @@ struct RowArgs {
     const float* gate;          // [T][topk]
     const int* slot;            // [T][topk]
     float* dbg_hidden;          // optional [T][H] copy of x after the update
+    // router fused into the norm (MoE, after attention): W_r [E][H] row-major
+    const void* w_router;
+    const float* s_router;      // fp8 per-row scales
+    int wdtype;
+    int renorm;
+    int* sel;                   // [T][topk] out
+    float* gate_out;            // [T][topk] out
+    int* dbg_sel;               // optional copy of sel
 };
 
 // token block + embedding gather + RMSNorm (one workgroup per row)
 template <bool BF>
 __global__ __launch_bounds__(256) void embed_norm_kernel(RowArgs a)
 {
-    __shared__ float xs[8192];
+    __shared__ __align__(16) float xs[8192];
     __shared__ float sh4[4];
     const int t = blockIdx.x, K1 = a.K1, K = K1 - 1;
     const int b = t / K1, j = t % K1;
@@ -123,11 +131,141 @@ SV_DEV float block_sum(float v, float* shw)
 // shared-expert outputs); then RMSNorm into h.  One 1024-thread workgroup per
 // row, so a thread owns one or two columns and issues all of a column's loads
 // (every split, or every rank and shared expert) before consuming any.
-template <bool BF, bool MOE>
+// Router of one token (after the attention half's norm): logits r = W_r h
+// over the stored (activation-typed) h, softmax over all E in fp32, top-k by
+// probability with the lower expert index first on ties, gates = the selected
+// probabilities (optionally renormalised).  Waves take experts round-robin;
+// wave 0 then does the softmax and selection.
+template <bool BF>
+SV_DEV void route_row(const RowArgs& a, int t, const float* hs)
+{
+    __shared__ float logit[256];
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, NW = blockDim.x >> 6;
+    const int E = a.E, H = a.H, k = a.topk;
+    // lane l covers elements [EPL l + 64 EPL j, + EPL) of a row (EPL = elements
+    // per 16-byte load); four experts per pass keep four rows of loads in flight
+    const int EPL = a.wdtype == SV_F32 ? 4 : (a.wdtype == SV_BF16 ? 8 : 16);
+    const int esz = 16 / EPL;
+    for (int e0 = w; e0 < E; e0 += 4 * NW) {
+        float acc[4] = {0.f, 0.f, 0.f, 0.f};
+        // up to 4 row chunks x 4 experts of loads issued before any is used
+        for (int i00 = EPL * lane; i00 < H; i00 += 4 * 64 * EPL) {
+            uint4 wv[4][4];
+#pragma unroll
+            for (int c = 0; c < 4; c++) {
+                const int i0 = i00 + c * 64 * EPL;
+#pragma unroll
+                for (int u = 0; u < 4; u++) {
+                    int e = min(e0 + u * NW, E - 1);
+                    wv[c][u] = i0 < H ? ldg16((const char*)a.w_router + ((size_t)e * H + i0) * esz)
+                                      : make_uint4(0, 0, 0, 0);
+                }
+            }
+#pragma unroll
+            for (int c = 0; c < 4; c++) {
+                const int i0 = i00 + c * 64 * EPL;
+                if (i0 >= H) break;
+                // this lane's EPL activation values, read once (16-byte LDS reads)
+                float hv[16];
+                const float4* h4 = reinterpret_cast<const float4*>(hs + i0);
+#pragma unroll
+                for (int q = 0; q < 4; q++) {
+                    if (q * 4 < EPL) {
+                        float4 t = h4[q];
+                        hv[4 * q] = t.x; hv[4 * q + 1] = t.y; hv[4 * q + 2] = t.z; hv[4 * q + 3] = t.w;
+                    }
+                }
+#pragma unroll
+                for (int u = 0; u < 4; u++) {
+                    const uint32_t wd[4] = {wv[c][u].x, wv[c][u].y, wv[c][u].z, wv[c][u].w};
+                    if (a.wdtype == SV_F32) {
+#pragma unroll
+                        for (int q = 0; q < 4; q++) acc[u] += __uint_as_float(wd[q]) * hv[q];
+                    } else if (a.wdtype == SV_BF16) {
+#pragma unroll
+                        for (int q = 0; q < 4; q++) {
+                            acc[u] += bf16_bits_to_f32(wd[q] & 0xffffu) * hv[2 * q];
+                            acc[u] += bf16_bits_to_f32(wd[q] >> 16) * hv[2 * q + 1];
+                        }
+                    } else {
+#pragma unroll
+                        for (int q = 0; q < 4; q++)
+#pragma unroll
+                            for (int bb = 0; bb < 4; bb++)
+                                acc[u] += e4m3_to_f32((wd[q] >> (8 * bb)) & 0xffu) * hv[4 * q + bb];
+                    }
+                }
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < 4; u++) {
+            int e = e0 + u * NW;
+            float v = wave_sum(acc[u]);
+            if (e < E && lane == 0) logit[e] = (a.wdtype == SV_FP8) ? v * a.s_router[e] : v;
+        }
+    }
+    __syncthreads();
+    if (w != 0) return;
+    float p[4];
+    float m = -INFINITY;
+#pragma unroll
+    for (int q = 0; q < 4; q++) {
+        int e = lane + 64 * q;
+        p[q] = e < E ? logit[e] : -INFINITY;
+        m = fmaxf(m, p[q]);
+    }
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) m = fmaxf(m, __shfl_xor(m, o, 64));
+    float sum = 0.f;
+#pragma unroll
+    for (int q = 0; q < 4; q++) {
+        p[q] = (lane + 64 * q < E) ? __expf(p[q] - m) : 0.f;
+        sum += p[q];
+    }
+    sum = wave_sum(sum);
+    const float inv = 1.f / sum;
+#pragma unroll
+    for (int q = 0; q < 4; q++) p[q] *= inv;
+    bool taken[4] = {false, false, false, false};
+    float gsum = 0.f, chosen_p[8];
+    int chosen[8];
+    for (int rr = 0; rr < k; rr++) {
+        unsigned long long best = 0ull;
+#pragma unroll
+        for (int q = 0; q < 4; q++) {
+            int e = lane + 64 * q;
+            if (e < E && !taken[q]) best = umax64(best, argmax_key(p[q], (uint32_t)e));
+        }
+#pragma unroll
+        for (int o = 32; o >= 1; o >>= 1) best = umax64(best, shfl_xor_u64(best, o));
+        const int e = (int)(0xffffffffu - (uint32_t)(best & 0xffffffffull));
+        const int qq = e >> 6;   // expert e lives in register qq of lane e % 64
+#pragma unroll
+        for (int q = 0; q < 4; q++)
+            if ((e & 63) == lane && q == qq) taken[q] = true;
+        float v0 = __shfl(p[0], e & 63, 64), v1 = __shfl(p[1], e & 63, 64);
+        float v2 = __shfl(p[2], e & 63, 64), v3 = __shfl(p[3], e & 63, 64);
+        float pe = qq == 0 ? v0 : (qq == 1 ? v1 : (qq == 2 ? v2 : v3));
+        chosen[rr] = e;
+        chosen_p[rr] = pe;
+        gsum += pe;
+    }
+    if (lane < k) {
+        float pe = 0.f;
+        int e = 0;
+        for (int rr = 0; rr < k; rr++)
+            if (rr == lane) { pe = chosen_p[rr]; e = chosen[rr]; }
+        a.sel[t * k + lane] = e;
+        if (a.dbg_sel) a.dbg_sel[t * k + lane] = e;
+        a.gate_out[t * k + lane] = a.renorm ? pe / gsum : pe;
+    }
+}
+
+template <bool BF, bool MOE, bool ROUTE = false>
 __global__ __launch_bounds__(1024) void residual_norm_kernel(RowArgs a)
 {
     constexpr int RT = 1024;
-    __shared__ float xs[8192];
+    __shared__ __align__(16) float xs[8192];
     __shared__ float shw[RT / 64];
     const int t = blockIdx.x, H = a.H, T = a.T;
     float* __restrict__ xr = a.x + (size_t)t * H;
@@ -163,7 +301,15 @@ __global__ __launch_bounds__(1024) void residual_norm_kernel(RowArgs a)
     ss = block_sum<RT>(ss, shw);
     const float r = rsqrtf(ss / (float)H + a.eps);
     typename Act<BF>::T* h = (typename Act<BF>::T*)a.h + (size_t)t * H;
-    for (int i = threadIdx.x; i < H; i += RT) Act<BF>::st(h, i, xs[i] * r * a.gain[i]);
+    for (int i = threadIdx.x; i < H; i += RT) {
+        float v = xs[i] * r * a.gain[i];
+        Act<BF>::st(h, i, v);
+        if constexpr (ROUTE) xs[i] = Act<BF>::ld(h, i);   // the value the experts will read
+    }
+    if constexpr (ROUTE) {
+        __syncthreads();
+        route_row<BF>(a, t, xs);
+    }
 }
 
 struct RopeArgs {
@@ -256,128 +402,93 @@ struct RouteArgs {
     int* dbg_sel;               // optional copy of sel
 };
 
-// Router, part 1: softmax over the E router logits of every row (fp32), top-k
-// by probability with the lower expert index first on ties, gates = the
-// selected probabilities (optionally renormalised).  One wave per row; lane l
-// holds experts l, l+64, l+128, l+192.
-__global__ __launch_bounds__(256) void route_topk_kernel(RouteArgs a)
-{
-    const int lane = threadIdx.x & 63;
-    const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
-    if (t >= a.T) return;
-    const int E = a.E, k = a.topk, T = a.T;
-    float p[4];
-    float m = -INFINITY;
-#pragma unroll
-    for (int q = 0; q < 4; q++) {
-        int e = lane + 64 * q;
-        p[q] = e < E ? sum_strided(a.logits + (size_t)t * E + e, a.nsplit, (size_t)T * E) : -INFINITY;
-        m = fmaxf(m, p[q]);
-    }
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) m = fmaxf(m, __shfl_xor(m, o, 64));
-    float sum = 0.f;
-#pragma unroll
-    for (int q = 0; q < 4; q++) {
-        p[q] = (lane + 64 * q < E) ? __expf(p[q] - m) : 0.f;
-        sum += p[q];
-    }
-    sum = wave_sum(sum);
-    const float inv = 1.f / sum;
-#pragma unroll
-    for (int q = 0; q < 4; q++) p[q] *= inv;
-    bool taken[4] = {false, false, false, false};
-    float gsum = 0.f, chosen_p[8];
-    int chosen[8];
-    for (int r = 0; r < k; r++) {
-        unsigned long long best = 0ull;
-#pragma unroll
-        for (int q = 0; q < 4; q++) {
-            int e = lane + 64 * q;
-            if (e < E && !taken[q]) best = umax64(best, argmax_key(p[q], (uint32_t)e));
-        }
-#pragma unroll
-        for (int o = 32; o >= 1; o >>= 1) best = umax64(best, shfl_xor_u64(best, o));
-        int e = (int)(0xffffffffu - (uint32_t)(best & 0xffffffffull));
-        const int qq = e >> 6;   // expert e lives in register qq of lane e % 64
-#pragma unroll
-        for (int q = 0; q < 4; q++)
-            if ((e & 63) == lane && q == qq) taken[q] = true;
-        float v0 = __shfl(p[0], e & 63, 64), v1 = __shfl(p[1], e & 63, 64);
-        float v2 = __shfl(p[2], e & 63, 64), v3 = __shfl(p[3], e & 63, 64);
-        float pe = qq == 0 ? v0 : (qq == 1 ? v1 : (qq == 2 ? v2 : v3));
-        chosen[r] = e;
-        chosen_p[r] = pe;
-        gsum += pe;
-    }
-    if (lane < k) {
-        float pe = 0.f;
-        int e = 0;
-        for (int r = 0; r < k; r++)
-            if (r == lane) { pe = chosen_p[r]; e = chosen[r]; }
-        a.sel[t * k + lane] = e;
-        if (a.dbg_sel) a.dbg_sel[t * k + lane] = e;
-        a.gate[t * k + lane] = a.renorm ? pe / gsum : pe;
-    }
-}
-
-// Router, part 2: a stable counting sort of the T*topk assignments by expert
-// -- assignment (t, r) of expert e goes to offset[e] + (number of rows t' < t
-// that also chose e) -- followed by the shared-expert rows (every token, in
-// order), and the list of BM-row tiles per group for the grouped GEMMs.  One
-// workgroup; deterministic.
+// Router permutation: a stable counting sort of the T*topk assignments by
+// expert -- assignment (t, r) of expert e goes to offset[e] + (number of rows
+// t' < t that also chose e) -- followed by the shared-expert rows (every
+// token, in order), and the list of BM-row tiles per group for the grouped
+// GEMMs.  One 256-thread workgroup, deterministic:
+//   * flags[t][e] = 1 if row t chose e;
+//   * 4 threads per expert each scan a quarter of the rows, then add the
+//     totals of the earlier quarters (exclusive ranks within the expert);
+//   * one wave scans the per-group tile counts; each group writes its tiles.
 __global__ __launch_bounds__(256) void route_permute_kernel(RouteArgs a)
 {
-    extern __shared__ unsigned short cnt[];          // [T][E], then sel [T][topk] as shorts
-    __shared__ int total[256], offset[257];
-    const int T = a.T, E = a.E, k = a.topk;
+    extern __shared__ unsigned short cnt[];          // [T][E] flags -> ranks, then sel [T][topk]
+    __shared__ int total[256 * 4], offset[257], tile0[257 + 8];
+    const int T = a.T, E = a.E, k = a.topk, tid = threadIdx.x;
     unsigned short* sel = cnt + (size_t)T * E;
-    for (int i = threadIdx.x; i < T * E; i += 256) cnt[i] = 0;
-    for (int i = threadIdx.x; i < T * k; i += 256) sel[i] = (unsigned short)a.sel[i];
+    for (int i = tid; i < T * E; i += 256) cnt[i] = 0;
+    for (int i = tid; i < T * k; i += 256) sel[i] = (unsigned short)a.sel[i];
     __syncthreads();
-    for (int t = threadIdx.x; t < T; t += 256)
-        for (int r = 0; r < k; r++) cnt[t * E + sel[t * k + r]] = 1;
+    for (int i = tid; i < T * k; i += 256) cnt[(i / k) * E + sel[i]] = 1;
     __syncthreads();
-    // exclusive scan over tokens, one expert per thread
-    for (int e = threadIdx.x; e < E; e += 256) {
+    // ranks: thread (e, quarter) scans rows [quarter * T/4, ...) of expert e
+    const int QT = (T + 3) / 4;
+    for (int job = tid; job < E * 4; job += 256) {
+        const int e = job >> 2, qtr = job & 3;
         int run = 0;
-        for (int t = 0; t < T; t++) {
+        const int t1 = min(T, (qtr + 1) * QT);
+        for (int t = qtr * QT; t < t1; t++) {
             int c = cnt[t * E + e];
             cnt[t * E + e] = (unsigned short)run;
             run += c;
         }
-        total[e] = run;
+        total[job] = run;
     }
     __syncthreads();
-    if (threadIdx.x == 0) {
-        int off = 0, nt = 0;
-        for (int e = 0; e < E; e++) {
-            offset[e] = off;
-            for (int r0 = 0; r0 < total[e]; r0 += a.BM) {
-                if (nt < a.max_tiles) {
-                    a.tiles[3 * nt] = e;
-                    a.tiles[3 * nt + 1] = off + r0;
-                    a.tiles[3 * nt + 2] = min(a.BM, total[e] - r0);
-                }
-                nt++;
-            }
-            off += total[e];
+    for (int job = tid; job < E * 4; job += 256) {
+        const int e = job >> 2, qtr = job & 3;
+        int add = 0;
+        for (int q = 0; q < qtr; q++) add += total[e * 4 + q];
+        if (add) {
+            const int t1 = min(T, (qtr + 1) * QT);
+            for (int t = qtr * QT; t < t1; t++) cnt[t * E + e] = (unsigned short)(cnt[t * E + e] + add);
         }
-        offset[E] = off;
-        for (int sx = 0; sx < a.n_shared; sx++) {
-            for (int r0 = 0; r0 < T; r0 += a.BM) {
-                if (nt < a.max_tiles) {
-                    a.tiles[3 * nt] = E + sx;
-                    a.tiles[3 * nt + 1] = T * k + sx * T + r0;
-                    a.tiles[3 * nt + 2] = min(a.BM, T - r0);
-                }
-                nt++;
-            }
-        }
-        *a.n_tiles = min(nt, a.max_tiles);
     }
     __syncthreads();
-    for (int t = threadIdx.x; t < T; t += 256) {
+    // per-group rows and tiles (groups: E routed experts, then n_shared shared)
+    const int G = E + a.n_shared;
+    if (tid < 64) {
+        int run_rows = 0, run_tiles = 0;
+        for (int g0 = 0; g0 < G; g0 += 64) {
+            const int g = g0 + tid;
+            int rows = 0;
+            if (g < E) rows = total[g * 4] + total[g * 4 + 1] + total[g * 4 + 2] + total[g * 4 + 3];
+            else if (g < G) rows = T;
+            int tiles = (rows + a.BM - 1) / a.BM;
+            // inclusive wave scans of rows (routed only) and tiles
+            int sr = g < E ? rows : 0, st = tiles;
+#pragma unroll
+            for (int o = 1; o < 64; o <<= 1) {
+                int vr = __shfl_up(sr, o, 64), vt = __shfl_up(st, o, 64);
+                if (tid >= o) { sr += vr; st += vt; }
+            }
+            if (g < G) {
+                if (g < E) offset[g] = run_rows + sr - rows;
+                tile0[g] = run_tiles + st - tiles;
+            }
+            run_rows += __shfl(sr, 63, 64);
+            run_tiles += __shfl(st, 63, 64);
+        }
+        if (tid == 0) {
+            offset[E] = run_rows;
+            tile0[G] = run_tiles;
+            *a.n_tiles = min(run_tiles, a.max_tiles);
+        }
+    }
+    __syncthreads();
+    for (int g = tid; g < G; g += 256) {
+        const int rows = g < E ? offset[g + 1 < E ? g + 1 : E] - offset[g] : T;
+        const int first = g < E ? offset[g] : T * k + (g - E) * T;
+        for (int r0 = 0, ti = tile0[g]; r0 < rows; r0 += a.BM, ti++) {
+            if (ti < a.max_tiles) {
+                a.tiles[3 * ti] = g;
+                a.tiles[3 * ti + 1] = first + r0;
+                a.tiles[3 * ti + 2] = min(a.BM, rows - r0);
+            }
+        }
+    }
+    for (int t = tid; t < T; t += 256) {
         for (int r = 0; r < k; r++) {
             int e = sel[t * k + r];
             int sl = offset[e] + cnt[t * E + e];

@@ -162,7 +162,7 @@ int validate_config(const spec_verify_config& c)
         if (c.top_k < 1 || c.top_k > 8 || c.top_k > c.n_experts) return bad("bad top_k");
         if (c.expert_inter < 64 || c.expert_inter % 64 || c.expert_inter % step)
             return bad("expert_inter must be a multiple of 64");
-        if (c.n_shared < 0) return bad("n_shared must be >= 0");
+        if (c.n_shared < 0 || c.n_shared > 8) return bad("n_shared must be in [0, 8]");
         if (c.n_experts % 4) return bad("n_experts must be a multiple of 4");
         long T = (long)c.max_batch * (c.k_draft + 1);
         if (T * c.n_experts > 32768) return bad("max_batch*(K+1)*n_experts must be <= 32768");
@@ -226,6 +226,34 @@ void launch_big_m(int wt, const GemmArgs& a, dim3 grid, hipStream_t s)
     if (wt == SV_F32) launch(gemm_bigm_kernel<SV_F32, BIG_MF, BIG_NF, MODE, PK>, grid, dim3(256), 0, s, a);
     else if (wt == SV_BF16) launch(gemm_bigm_kernel<SV_BF16, BIG_MF, BIG_NF, MODE, PK>, grid, dim3(256), 0, s, a);
     else launch(gemm_bigm_kernel<SV_FP8, BIG_MF, BIG_NF, MODE, PK>, grid, dim3(256), 0, s, a);
+}
+
+// Grouped (expert) GEMMs on the large-row kernel: MF row fragments per tile.
+template <int MODE, bool PK, int MF>
+void launch_grouped_mf(int wt, const GemmArgs& a, dim3 grid, hipStream_t s)
+{
+    if (wt == SV_BF16) launch(gemm_bigm_kernel<SV_BF16, MF, BIG_NF, MODE, PK>, grid, dim3(256), 0, s, a);
+    else launch(gemm_bigm_kernel<SV_FP8, MF, BIG_NF, MODE, PK>, grid, dim3(256), 0, s, a);
+}
+
+template <int MODE, bool PK>
+void launch_grouped_m(int wt, int MF, const GemmArgs& a, dim3 grid, hipStream_t s)
+{
+    if (MF == 1) launch_grouped_mf<MODE, PK, 1>(wt, a, grid, s);
+    else if (MF == 2) launch_grouped_mf<MODE, PK, 2>(wt, a, grid, s);
+    else launch_grouped_mf<MODE, PK, 4>(wt, a, grid, s);
+}
+
+void launch_grouped_big(int wt, int mode, int MF, bool packed, GemmArgs& a, hipStream_t s)
+{
+    dim3 grid((unsigned)(cdiv(a.NT, 8) * 8 * a.MT), 1, 1);
+    if (packed) {
+        if (mode == GM_SWIGLU) launch_grouped_m<GM_SWIGLU, true>(wt, MF, a, grid, s);
+        else launch_grouped_m<GM_STORE, true>(wt, MF, a, grid, s);
+    } else {
+        if (mode == GM_SWIGLU) launch_grouped_m<GM_SWIGLU, false>(wt, MF, a, grid, s);
+        else launch_grouped_m<GM_STORE, false>(wt, MF, a, grid, s);
+    }
 }
 
 void launch_gemm_big(int wt, int mode, bool packed, GemmArgs& a, hipStream_t s)
@@ -646,22 +674,34 @@ int spec_verify_step(spec_verify_ctx* c, const spec_verify_weights* w, void* k_c
         ra.nsplit = ks;
         ra.gain = Lw.ffn_norm;
         ra.dbg_hidden = nullptr;
-        if (bf) residual_norm_kernel<true, false><<<T, 1024, 0, s>>>(ra);
-        else residual_norm_kernel<false, false><<<T, 1024, 0, s>>>(ra);
+        if (k.ffn_kind == SV_FFN_MOE) {
+            // residual + norm + router logits, softmax and top-k in one kernel
+            ra.w_router = Lw.w_router;
+            ra.s_router = Lw.s_router;
+            ra.wdtype = wt;
+            ra.renorm = k.renorm_topk;
+            ra.sel = c->sel;
+            ra.gate_out = c->gate;
+            ra.dbg_sel = c->dbg_routing ? c->dbg_routing + (size_t)l * T * k.top_k : nullptr;
+            if (bf) residual_norm_kernel<true, false, true><<<T, 1024, 0, s>>>(ra);
+            else residual_norm_kernel<false, false, true><<<T, 1024, 0, s>>>(ra);
+        } else {
+            if (bf) residual_norm_kernel<true, false><<<T, 1024, 0, s>>>(ra);
+            else residual_norm_kernel<false, false><<<T, 1024, 0, s>>>(ra);
+        }
 
         // ---- feed-forward half
         const float* next_gain = (l + 1 < L) ? w->layers[l + 1].attn_norm : w->final_norm;
         float* dbg_h = c->dbg_hidden ? c->dbg_hidden + (size_t)l * T * H : nullptr;
         if (k.ffn_kind == SV_FFN_MOE) {
             const int E = k.n_experts, tk = k.top_k, S = k.n_shared, I = k.expert_inter;
-            ks = dense_gemm(GM_STORE, c->h, H, E, H, Lw.w_router, Lw.s_router, c->parts, E, 1);
             const int avg_rows = std::max(1, T * tk / E);
             const int MFe = rows_mf(avg_rows);
             const int BMe = 16 * MFe;
             const int max_tiles = std::min(E, T * tk) + (T * tk) / BMe + S * cdiv(T, BMe) + 1;
             RouteArgs ro;
-            ro.logits = c->parts;
-            ro.nsplit = ks;
+            ro.logits = nullptr;
+            ro.nsplit = 0;
             ro.T = T;
             ro.E = E;
             ro.topk = tk;
@@ -670,14 +710,13 @@ int spec_verify_step(spec_verify_ctx* c, const spec_verify_weights* w, void* k_c
             ro.BM = BMe;
             ro.max_tiles = max_tiles;
             ro.probs = c->probs;
-            ro.dbg_sel = c->dbg_routing ? c->dbg_routing + (size_t)l * T * tk : nullptr;
+            ro.dbg_sel = nullptr;
             ro.sel = c->sel;
             ro.gate = c->gate;
             ro.slot = c->slot;
             ro.perm_tok = c->perm_tok;
             ro.tiles = c->tiles;
             ro.n_tiles = c->n_tiles;
-            route_topk_kernel<<<cdiv(T, 4), 256, 0, s>>>(ro);
             route_permute_kernel<<<1, 256, (size_t)T * (E + tk) * sizeof(unsigned short), s>>>(ro);
 
             GemmArgs g;
@@ -701,12 +740,17 @@ int spec_verify_step(spec_verify_ctx* c, const spec_verify_weights* w, void* k_c
             g.tiles = c->tiles;
             g.n_tiles = c->n_tiles;
             g.MT = max_tiles;
-            g.NT = cdiv(I, 16);   // one-wave workgroups
+            // many rows (T >= 64): 4-wave tiles sharing an LDS activation tile;
+            // few rows: one-wave tiles streaming weights (finer balance)
+            const bool big_e = big && H % (BIG_CHUNK_STEPS * step) == 0 &&
+                               I % (BIG_CHUNK_STEPS * step) == 0;
+            g.NT = big_e ? cdiv(I, 16 * 4 * BIG_NF) : cdiv(I, 16);
             g.out = c->act;
             g.ldo = I;
             {
                 ProfScope ps(c, SV_KC_EXPERT_GATE_UP, s);
-                launch_gemm(wt, GM_SWIGLU, MFe, packed, g, s);
+                if (big_e) launch_grouped_big(wt, GM_SWIGLU, MFe, packed, g, s);
+                else launch_gemm(wt, GM_SWIGLU, MFe, packed, g, s);
             }
             GemmArgs d = g;
             d.X = c->act;
@@ -723,13 +767,14 @@ int spec_verify_step(spec_verify_ctx* c, const spec_verify_weights* w, void* k_c
             d.w2_gstride = (long)H * I;
             d.s2_gstride = H;
             d.dual_off = 0;
-            d.NT = cdiv(H, 16);
+            d.NT = big_e ? cdiv(H, 16 * 4 * BIG_NF) : cdiv(H, 16);
             d.out = c->y;
             d.ldo = H;
             d.split_stride = 0;
             {
                 ProfScope ps(c, SV_KC_EXPERT_DOWN, s);
-                launch_gemm(wt, GM_STORE, MFe, packed, d, s);
+                if (big_e) launch_grouped_big(wt, GM_STORE, MFe, packed, d, s);
+                else launch_gemm(wt, GM_STORE, MFe, packed, d, s);
             }
             ra.y = c->y;
             ra.gate = c->gate;

@@ -83,13 +83,15 @@ def test_moe_batched_scaled(H):
     assert stats["argmax_agree"] >= 0.9 * stats["positions"]
 
 
-def test_moe_small_shapes(H):
-    """Small MoE shapes: 16 experts, top-4, one shared expert, head_dim 128 with
-    2 heads, contexts from 1 token; norm gains away from 1."""
+@pytest.mark.parametrize("batch,n_experts,top_k", [(5, 16, 4), (20, 16, 4), (16, 8, 6)])
+def test_moe_small_shapes(H, batch, n_experts, top_k):
+    """Small MoE shapes: head_dim 128 with 2 heads, one shared expert, contexts
+    from 1 token, norm gains away from 1.  Rows per expert ~1 (one-wave expert
+    tiles), ~20 (32-row tiles of the large-row kernel) and ~48 (64-row tiles)."""
     cfg = workloads.scaled(workloads.get_config("moe_b1"), n_layers=2, hidden=256, n_q=2, n_kv=2,
-                           n_experts=16, expert_inter=128, top_k=4, n_shared=1, vocab=2048,
-                           batch=5, ctx=("uniform", 1, 200), norm_gain_std=0.2)
-    _verify_case(H, cfg, label="moe_small_shapes")
+                           n_experts=n_experts, expert_inter=128, top_k=top_k, n_shared=1,
+                           vocab=2048, batch=batch, ctx=("uniform", 1, 200), norm_gain_std=0.2)
+    _verify_case(H, cfg, label=f"moe_small_shapes_b{batch}_e{n_experts}_k{top_k}")
 
 
 def test_dense_fp8_gqa_scaled(H):
