@@ -165,20 +165,20 @@ __global__ __launch_bounds__(64) void attn_split_kernel(AttnArgs a)
         for (int d = 0; d < DF; d++)
             *reinterpret_cast<float4*>(op + 16 * d + 4 * lg) =
                 make_float4(o[f][d][0], o[f][d][1], o[f][d][2], o[f][d][3]);
-        if (lg == 0) {
-            a.mlpart[slot * 2] = m_run[f];
-            a.mlpart[slot * 2 + 1] = l;
-        }
+        if (lg == 0) *reinterpret_cast<float2*>(a.mlpart + slot * 2) = make_float2(m_run[f], l);
     }
 }
 
 // Merge the chunk partials of one (sequence, query head, position) row in
 // chunk order and write the attention output row in the activation type.
-// 128 threads per row: chunk weights exp2(m_c - M) are formed once in shared
-// memory, then thread d sums its channel over the chunks.
+// 128 threads per row, thread d owns channel d (D <= 128).  The partial
+// outputs of the first CB chunks are loaded together with the chunk (max,
+// sum) pairs, so one memory round trip follows the context-length read; wave
+// 0 forms the chunk weights exp2(m_c - M) in shared memory.
 template <bool BF>
 __global__ __launch_bounds__(128) void attn_merge_kernel(AttnArgs a, void* out /* [T][n_q*D] */)
 {
+    constexpr int CB = 32;                           // chunks per batch of loads
     __shared__ float wgt[1024];
     __shared__ float red[2];
     const int row = blockIdx.x;                     // ((b * n_q + hq) * K1 + j)
@@ -187,35 +187,56 @@ __global__ __launch_bounds__(128) void attn_merge_kernel(AttnArgs a, void* out /
     const int hq = (row / K1) % a.n_q;
     const int b = row / (K1 * a.n_q);
     const int ctx = min(max(a.ctx_in[b], 0), a.cap - K1);
-    const int nch = (ctx + K1 + a.CH - 1) / a.CH;
-    const float* __restrict__ ml = a.mlpart + (size_t)row * a.maxch * 2;
+    const int nch = (ctx + K1 + a.CH - 1) / a.CH;   // <= maxch <= 1024
+    const float2* __restrict__ ml = reinterpret_cast<const float2*>(a.mlpart) + (size_t)row * a.maxch;
     const float* __restrict__ op = a.opart + (size_t)row * a.maxch * a.D;
     const int tid = threadIdx.x, lane = tid & 63;
+    const int d = tid;
+    const bool dok = d < a.D;
+    // loads without conditions (clamped indices; the extra values are unused)
+    const int dc = min(d, a.D - 1);
+    float ov[CB];
+#pragma unroll
+    for (int c = 0; c < CB; c++) ov[c] = op[(size_t)min(c, nch - 1) * a.D + dc];
     if (tid < 64) {
+        float2 mv[16];                               // chunks lane + 64 i
+#pragma unroll
+        for (int i = 0; i < 16; i++) mv[i] = ml[min(lane + 64 * i, nch - 1)];
+#pragma unroll
+        for (int i = 0; i < 16; i++) mv[i] = lane + 64 * i < nch ? mv[i] : make_float2(-INFINITY, 0.f);
         float M = -INFINITY;
-        for (int c = lane; c < nch; c += 64) M = fmaxf(M, ml[2 * c]);
+#pragma unroll
+        for (int i = 0; i < 16; i++) M = fmaxf(M, mv[i].x);
 #pragma unroll
         for (int o = 32; o >= 1; o >>= 1) M = fmaxf(M, __shfl_xor(M, o, 64));
         float L = 0.f;
-        for (int c = lane; c < nch; c += 64) {
-            float mc = ml[2 * c];
-            float wc = (mc == -INFINITY) ? 0.f : exp2f(mc - M);
-            wgt[c] = wc;
-            L += wc * ml[2 * c + 1];
+#pragma unroll
+        for (int i = 0; i < 16; i++) {
+            const int c = lane + 64 * i;
+            const float wc = (mv[i].x == -INFINITY) ? 0.f : exp2f(mv[i].x - M);
+            if (c < nch) wgt[c] = wc;
+            L += wc * mv[i].y;
         }
         L = wave_sum(L);
         if (lane == 0) red[0] = L;
     }
     __syncthreads();
     const float inv = 1.f / red[0];
-    const size_t t = (size_t)b * K1 + j;
-    for (int d = tid; d < a.D; d += 128) {
-        float acc = 0.f;
-#pragma unroll 8
-        for (int c = 0; c < nch; c++) acc += wgt[c] * op[(size_t)c * a.D + d];
-        float v = acc * inv;
-        size_t o = t * (size_t)a.n_q * a.D + (size_t)hq * a.D + d;
-        if constexpr (BF) ((uint16_t*)out)[o] = (uint16_t)f32_to_bf16_bits(v);
-        else ((float*)out)[o] = v;
+    float acc = 0.f;
+#pragma unroll
+    for (int c = 0; c < CB; c++)
+        if (c < nch) acc += wgt[c] * ov[c];
+    for (int c0 = CB; c0 < nch; c0 += CB) {
+#pragma unroll
+        for (int c = 0; c < CB; c++) ov[c] = op[(size_t)min(c0 + c, nch - 1) * a.D + dc];
+#pragma unroll
+        for (int c = 0; c < CB; c++)
+            if (c0 + c < nch) acc += wgt[c0 + c] * ov[c];
     }
+    if (!dok) return;
+    const float v = acc * inv;
+    const size_t t = (size_t)b * K1 + j;
+    const size_t o = t * (size_t)a.n_q * a.D + (size_t)hq * a.D + d;
+    if constexpr (BF) ((uint16_t*)out)[o] = (uint16_t)f32_to_bf16_bits(v);
+    else ((float*)out)[o] = v;
 }

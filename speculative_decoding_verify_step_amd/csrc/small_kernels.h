@@ -11,105 +11,14 @@ template <> struct Act<true> {
     typedef uint16_t T;
     static SV_DEV float ld(const T* p, size_t i) { return bf16_bits_to_f32(p[i]); }
     static SV_DEV void st(T* p, size_t i, float v) { p[i] = (uint16_t)f32_to_bf16_bits(v); }
+    static SV_DEV float round(float v) { return bf16_bits_to_f32((uint16_t)f32_to_bf16_bits(v)); }
 };
 template <> struct Act<false> {
     typedef float T;
     static SV_DEV float ld(const T* p, size_t i) { return p[i]; }
     static SV_DEV void st(T* p, size_t i, float v) { p[i] = v; }
+    static SV_DEV float round(float v) { return v; }
 };
-
-// Block-wide sum over 256 threads (deterministic: fixed butterfly, then a
-// fixed-order sum of the four wave totals).
-SV_DEV float block_sum256(float v, float* sh4)
-{
-    v = wave_sum(v);
-    const int w = threadIdx.x >> 6;
-    if ((threadIdx.x & 63) == 0) sh4[w] = v;
-    __syncthreads();
-    float s = (sh4[0] + sh4[1]) + (sh4[2] + sh4[3]);
-    __syncthreads();
-    return s;
-}
-
-// x[H] (fp32 in `xs`, shared) -> h = x / sqrt(mean(x^2) + eps) * g, stored as act
-template <bool BF>
-SV_DEV void rms_store(const float* xs, int H, const float* g, float eps, typename Act<BF>::T* h,
-                      float* sh4)
-{
-    float ss = 0.f;
-    for (int i = threadIdx.x; i < H; i += 256) ss += xs[i] * xs[i];
-    ss = block_sum256(ss, sh4);
-    float r = rsqrtf(ss / (float)H + eps);
-    for (int i = threadIdx.x; i < H; i += 256) Act<BF>::st(h, i, xs[i] * r * g[i]);
-}
-
-struct RowArgs {
-    int H, K1, V, cap, E, topk, n_shared, T, nsplit;
-    float eps;
-    const int* committed;       // [B]
-    const int* drafts;          // [B][K]
-    const int* ctx_in;          // [B]
-    int* seq_err;               // [B]
-    unsigned* err_word;         // sticky
-    const void* embed;          // [V][H]
-    float* x;                   // [T][H] residual
-    void* h;                    // [T][H] normalised activations
-    const float* gain;          // [H] gain of the norm that follows
-    const float* parts;         // [nsplit][T][H] partial sums to add (or null)
-    const float* y;             // MoE expert outputs [rows][H]
-    const float* gate;          // [T][topk]
-    const int* slot;            // [T][topk]
-    float* dbg_hidden;          // optional [T][H] copy of x after the update
-    // router fused into the norm (MoE, after attention): W_r [E][H] row-major
-    const void* w_router;
-    const float* s_router;      // fp8 per-row scales
-    int wdtype;
-    int renorm;
-    int* sel;                   // [T][topk] out
-    float* gate_out;            // [T][topk] out
-    int* dbg_sel;               // optional copy of sel
-};
-
-// token block + embedding gather + RMSNorm (one workgroup per row)
-template <bool BF>
-__global__ __launch_bounds__(256) void embed_norm_kernel(RowArgs a)
-{
-    __shared__ __align__(16) float xs[8192];
-    __shared__ float sh4[4];
-    const int t = blockIdx.x, K1 = a.K1, K = K1 - 1;
-    const int b = t / K1, j = t % K1;
-    int tok = (j == 0) ? a.committed[b] : a.drafts[(size_t)b * K + j - 1];
-    bool bad = tok < 0 || tok >= a.V;
-    if (j == 0 && threadIdx.x == 0) {
-        unsigned e = 0;
-        for (int i = 0; i < K1; i++) {
-            int ti = (i == 0) ? a.committed[b] : a.drafts[(size_t)b * K + i - 1];
-            if (ti < 0 || ti >= a.V) e |= SV_DEV_BAD_TOKEN;
-        }
-        int c = a.ctx_in[b];
-        if (c < 0 || c + K1 > a.cap) e |= SV_DEV_CAPACITY;
-        a.seq_err[b] = (int)e;
-        if (e) atomicOr(a.err_word, e);
-    }
-    if (bad) tok = 0;
-    const typename Act<BF>::T* er = (const typename Act<BF>::T*)a.embed + (size_t)tok * a.H;
-    for (int i = threadIdx.x; i < a.H; i += 256) {
-        float v = Act<BF>::ld(er, i);
-        xs[i] = v;
-        a.x[(size_t)t * a.H + i] = v;
-    }
-    __syncthreads();
-    rms_store<BF>(xs, a.H, a.gain, a.eps, (typename Act<BF>::T*)a.h + (size_t)t * a.H, sh4);
-}
-
-// Sum of `n` fp32 values `stride` apart, loads issued together.
-SV_DEV float sum_strided(const float* __restrict__ p, int n, size_t stride)
-{
-    float acc = 0.f;
-#pragma unroll 8
-    for (int s = 0; s < n; s++) acc += p[(size_t)s * stride];
-    return acc;
-}
 
 // Block-wide sum over RT threads (deterministic: butterfly within waves, then
 // the wave totals in wave order).
@@ -127,40 +36,171 @@ SV_DEV float block_sum(float v, float* shw)
     return s;
 }
 
-// x += (sum of K-split partials) or (sum over ranks of gate * expert output +
-// shared-expert outputs); then RMSNorm into h.  One 1024-thread workgroup per
-// row, so a thread owns one or two columns and issues all of a column's loads
-// (every split, or every rank and shared expert) before consuming any.
-// Router of one token (after the attention half's norm): logits r = W_r h
-// over the stored (activation-typed) h, softmax over all E in fp32, top-k by
-// probability with the lower expert index first on ties, gates = the selected
-// probabilities (optionally renormalised).  Waves take experts round-robin;
-// wave 0 then does the softmax and selection.
+struct RowArgs {
+    int H, K1, V, cap, E, topk, n_shared, T, nsplit;
+    float eps;
+    const int* committed;       // [B]
+    const int* drafts;          // [B][K]
+    const int* ctx_in;          // [B]
+    int* seq_err;               // [B]
+    unsigned* err_word;         // sticky
+    const void* embed;          // [V][H]
+    const float* x;             // [T][H] residual read
+    float* x_out;               // [T][H] residual written (may equal x when one workgroup owns a row)
+    void* h;                    // [T][H] normalised activations
+    const float* gain;          // [H] gain of the norm that follows
+    const float* parts;         // [nsplit][T][H] partial sums to add (or null)
+    const float* y;             // MoE expert outputs [rows][H]
+    const float* gate;          // [T][topk]
+    const int* slot;            // [T][topk]
+    float* dbg_hidden;          // optional [T][H] copy of x after the update
+    // router after the attention half's norm: W_r [E][H] row-major
+    const void* w_router;
+    const float* s_router;      // fp8 per-row scales
+    int wdtype;
+    int renorm;
+    int* sel;                   // [T][topk] out
+    float* gate_out;            // [T][topk] out
+    int* dbg_sel;               // optional copy of sel
+    // the router's experts shared out over S workgroups per row
+    int S;
+    float* logits_g;            // [T][E] router logits (S > 1)
+    // permutation (stable counting sort by expert) and expert tile list
+    int BM, max_tiles;
+    int* slot_out;              // [T][topk] row of (t, rank) in the permuted order
+    int* perm_tok;              // [T*topk + n_shared*T] token of every permuted row
+    int* tiles;                 // [max_tiles][3] = (group, first row, rows)
+    int* n_tiles;               // [1]
+};
+
+// token block + embedding gather + RMSNorm (one 1024-thread workgroup per
+// row; a thread owns up to 8 columns and issues all of their loads -- embedding
+// and gain -- before using any)
 template <bool BF>
-SV_DEV void route_row(const RowArgs& a, int t, const float* hs)
+__global__ __launch_bounds__(1024) void embed_norm_kernel(RowArgs a)
 {
-    __shared__ float logit[256];
-    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, NW = blockDim.x >> 6;
-    const int E = a.E, H = a.H, k = a.topk;
-    // lane l covers elements [EPL l + 64 EPL j, + EPL) of a row (EPL = elements
-    // per 16-byte load); four experts per pass keep four rows of loads in flight
-    const int EPL = a.wdtype == SV_F32 ? 4 : (a.wdtype == SV_BF16 ? 8 : 16);
-    const int esz = 16 / EPL;
-    for (int e0 = w; e0 < E; e0 += 4 * NW) {
-        float acc[4] = {0.f, 0.f, 0.f, 0.f};
-        // up to 4 row chunks x 4 experts of loads issued before any is used
+    constexpr int RT = 1024, EPT = 8;      // H <= 8192
+    __shared__ float shw[RT / 64];
+    const int t = blockIdx.x, K1 = a.K1, K = K1 - 1, tid = threadIdx.x;
+    const int b = t / K1, j = t % K1;
+    int tok = (j == 0) ? a.committed[b] : a.drafts[(size_t)b * K + j - 1];
+    if (j == 0 && tid < 64) {
+        // one lane per token of the block (K1 <= 64), flags combined by a wave vote
+        int ti = 0;
+        if (tid < K1) ti = (tid == 0) ? a.committed[b] : a.drafts[(size_t)b * K + tid - 1];
+        const int c = a.ctx_in[b];
+        unsigned e = 0;
+        if (__any(tid < K1 && (ti < 0 || ti >= a.V))) e |= SV_DEV_BAD_TOKEN;
+        if (c < 0 || c + K1 > a.cap) e |= SV_DEV_CAPACITY;
+        if (tid == 0) {
+            a.seq_err[b] = (int)e;
+            if (e) atomicOr(a.err_word, e);
+        }
+    }
+    if (tok < 0 || tok >= a.V) tok = 0;
+    const typename Act<BF>::T* er = (const typename Act<BF>::T*)a.embed + (size_t)tok * a.H;
+    float v[EPT], g[EPT];
+#pragma unroll
+    for (int u = 0; u < EPT; u++) {
+        const int i = min(tid + u * RT, a.H - 1);
+        v[u] = Act<BF>::ld(er, i);
+        g[u] = a.gain[i];
+    }
+#pragma unroll
+    for (int u = 0; u < EPT; u++) v[u] = tid + u * RT < a.H ? v[u] : 0.f;
+    float ss = 0.f;
+#pragma unroll
+    for (int u = 0; u < EPT; u++) {
+        const int i = tid + u * RT;
+        if (i < a.H) a.x_out[(size_t)t * a.H + i] = v[u];
+        ss += v[u] * v[u];
+    }
+    ss = block_sum<RT>(ss, shw);
+    const float r = rsqrtf(ss / (float)a.H + a.eps);
+    typename Act<BF>::T* h = (typename Act<BF>::T*)a.h + (size_t)t * a.H;
+#pragma unroll
+    for (int u = 0; u < EPT; u++) {
+        const int i = tid + u * RT;
+        if (i < a.H) Act<BF>::st(h, i, v[u] * r * g[u]);
+    }
+}
+
+// Loads that must be in flight together are written without conditions:
+// indices are clamped into range and the unwanted values replaced afterwards.
+// (A load inside a branch lets the compiler move its first use into the
+// branch, which puts a wait on it before the next load issues.)
+//
+// n (<= NMAX) fp32 values `stride` apart into v[] (slots past n read as 0);
+// p must be readable even when n == 0.
+template <int NMAX>
+SV_DEV void load_strided(const float* __restrict__ p, int n, size_t stride, float (&v)[NMAX])
+{
+    const int last = max(n, 1) - 1;
+#pragma unroll
+    for (int s = 0; s < NMAX; s++) v[s] = p[(size_t)min(s, last) * stride];
+#pragma unroll
+    for (int s = 0; s < NMAX; s++) v[s] = s < n ? v[s] : 0.f;
+}
+
+// fp32 at a wave-uniform base plus a 32-bit byte offset (one offset register
+// serves every load that shares it; the base stays in scalar registers)
+SV_DEV float ld_at(const float* base, unsigned byte_off)
+{
+    return *reinterpret_cast<const float*>(reinterpret_cast<const char*>(base) + byte_off);
+}
+
+template <int NMAX>
+SV_DEV float sum_in_order(const float (&v)[NMAX])
+{
+    float acc = 0.f;
+#pragma unroll
+    for (int s = 0; s < NMAX; s++) acc += v[s];
+    return acc;
+}
+
+// Router weight slices of one pass: wave w, pass (e0, i00) covers experts
+// e0 + 16 u (u < UPW, clamped below eend) and row chunks i00 + 64 EPL c (c < 4)
+// of 16 bytes per lane.
+SV_DEV int router_epl(int wdtype) { return wdtype == SV_F32 ? 4 : (wdtype == SV_BF16 ? 8 : 16); }
+
+// e0 is wave-uniform; the row bases are formed as uniform pointers so that each
+// load is (uniform base + 32-bit lane offset)
+template <int UPW>
+SV_DEV void router_loads(const RowArgs& a, int e0, int i00, int eend, uint4 (&wv)[4][UPW])
+{
+    const int EPL = router_epl(a.wdtype), esz = 16 / EPL;
+    e0 = __builtin_amdgcn_readfirstlane(e0);
+#pragma unroll
+    for (int u = 0; u < UPW; u++) {
+        const int e = min(e0 + u * 16, eend - 1);
+        const char* row = (const char*)a.w_router + (size_t)e * a.H * esz;
+#pragma unroll
+        for (int c = 0; c < 4; c++) {
+            // columns past H re-read the row's last slice; the consumer skips them
+            const unsigned i0 = (unsigned)min(i00 + c * 64 * EPL, a.H - EPL);
+            wv[c][u] = ldg16(row + i0 * esz);
+        }
+    }
+}
+
+// Router logits r[e] = W_r[e] . h for experts [ebeg, eend) over the stored
+// (activation-typed) row h in shared memory: the 16 waves take experts
+// round-robin, UPW at a time; `wv` arrives holding the first pass's weight
+// slices (loaded at kernel entry).  Results go to logit[e].
+template <int UPW>
+SV_DEV void router_logits(const RowArgs& a, const float* hs, uint4 (&wv)[4][UPW], int ebeg, int eend,
+                          float* logit)
+{
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const int H = a.H, EPL = router_epl(a.wdtype);
+    bool first = true;
+    for (int e0 = ebeg + w; e0 < eend; e0 += 16 * UPW) {
+        float acc[UPW];
+#pragma unroll
+        for (int u = 0; u < UPW; u++) acc[u] = 0.f;
         for (int i00 = EPL * lane; i00 < H; i00 += 4 * 64 * EPL) {
-            uint4 wv[4][4];
-#pragma unroll
-            for (int c = 0; c < 4; c++) {
-                const int i0 = i00 + c * 64 * EPL;
-#pragma unroll
-                for (int u = 0; u < 4; u++) {
-                    int e = min(e0 + u * NW, E - 1);
-                    wv[c][u] = i0 < H ? ldg16((const char*)a.w_router + ((size_t)e * H + i0) * esz)
-                                      : make_uint4(0, 0, 0, 0);
-                }
-            }
+            if (!first) router_loads<UPW>(a, e0, i00, eend, wv);   // later passes reuse the registers
+            first = false;
 #pragma unroll
             for (int c = 0; c < 4; c++) {
                 const int i0 = i00 + c * 64 * EPL;
@@ -176,7 +216,7 @@ SV_DEV void route_row(const RowArgs& a, int t, const float* hs)
                     }
                 }
 #pragma unroll
-                for (int u = 0; u < 4; u++) {
+                for (int u = 0; u < UPW; u++) {
                     const uint32_t wd[4] = {wv[c][u].x, wv[c][u].y, wv[c][u].z, wv[c][u].w};
                     if (a.wdtype == SV_F32) {
 #pragma unroll
@@ -198,22 +238,29 @@ SV_DEV void route_row(const RowArgs& a, int t, const float* hs)
             }
         }
 #pragma unroll
-        for (int u = 0; u < 4; u++) {
-            int e = e0 + u * NW;
-            float v = wave_sum(acc[u]);
-            if (e < E && lane == 0) logit[e] = (a.wdtype == SV_FP8) ? v * a.s_router[e] : v;
+        for (int u = 0; u < UPW; u++) {
+            const int e = e0 + u * 16;
+            const float v = wave_sum(acc[u]);
+            if (e < eend && lane == 0) logit[e] = (a.wdtype == SV_FP8) ? v * a.s_router[e] : v;
         }
     }
-    __syncthreads();
-    if (w != 0) return;
-    float p[4];
+}
+
+// Softmax over the E logits of row t (lane l holds experts l + 64 q) in fp32,
+// top-k by probability with the lower expert index first on ties, gates = the
+// selected probabilities (optionally renormalised).  One wave.  Selection by
+// rank: with key(e) = (probability, then lower index) as an order-preserving
+// 64-bit key, the rank of e is the number of experts with a larger key (equal
+// keys -- NaN only -- ordered by index), and e is the rank-th choice when
+// rank < k.  `kbuf`: 256 keys + 8 floats of this wave's shared memory.
+SV_DEV void router_select(const RowArgs& a, int t, float (&p)[4], unsigned long long* kbuf,
+                          unsigned short* sel_lds = nullptr)
+{
+    const int lane = threadIdx.x & 63, E = a.E, k = a.topk;
+    const int NQ = (E + 63) >> 6;
     float m = -INFINITY;
 #pragma unroll
-    for (int q = 0; q < 4; q++) {
-        int e = lane + 64 * q;
-        p[q] = e < E ? logit[e] : -INFINITY;
-        m = fmaxf(m, p[q]);
-    }
+    for (int q = 0; q < 4; q++) m = fmaxf(m, p[q]);
 #pragma unroll
     for (int o = 32; o >= 1; o >>= 1) m = fmaxf(m, __shfl_xor(m, o, 64));
     float sum = 0.f;
@@ -224,207 +271,73 @@ SV_DEV void route_row(const RowArgs& a, int t, const float* hs)
     }
     sum = wave_sum(sum);
     const float inv = 1.f / sum;
+    float* pbuf = reinterpret_cast<float*>(kbuf + 256);   // selected probabilities by rank
+    unsigned long long key[4];
 #pragma unroll
-    for (int q = 0; q < 4; q++) p[q] *= inv;
-    bool taken[4] = {false, false, false, false};
-    float gsum = 0.f, chosen_p[8];
-    int chosen[8];
-    for (int rr = 0; rr < k; rr++) {
-        unsigned long long best = 0ull;
-#pragma unroll
-        for (int q = 0; q < 4; q++) {
-            int e = lane + 64 * q;
-            if (e < E && !taken[q]) best = umax64(best, argmax_key(p[q], (uint32_t)e));
-        }
-#pragma unroll
-        for (int o = 32; o >= 1; o >>= 1) best = umax64(best, shfl_xor_u64(best, o));
-        const int e = (int)(0xffffffffu - (uint32_t)(best & 0xffffffffull));
-        const int qq = e >> 6;   // expert e lives in register qq of lane e % 64
-#pragma unroll
-        for (int q = 0; q < 4; q++)
-            if ((e & 63) == lane && q == qq) taken[q] = true;
-        float v0 = __shfl(p[0], e & 63, 64), v1 = __shfl(p[1], e & 63, 64);
-        float v2 = __shfl(p[2], e & 63, 64), v3 = __shfl(p[3], e & 63, 64);
-        float pe = qq == 0 ? v0 : (qq == 1 ? v1 : (qq == 2 ? v2 : v3));
-        chosen[rr] = e;
-        chosen_p[rr] = pe;
-        gsum += pe;
+    for (int q = 0; q < 4; q++) {
+        p[q] *= inv;
+        const int e = lane + 64 * q;
+        key[q] = argmax_key(p[q], (uint32_t)e);
+        if (q < NQ && e < E) kbuf[e] = key[q];
     }
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+    for (int q = 0; q < NQ; q++) {
+        const int e = lane + 64 * q;
+        int r = 0;
+#pragma unroll 4
+        for (int j = 0; j < E; j += 2) {     // E is a multiple of 4
+            const ulonglong2 kk = *reinterpret_cast<const ulonglong2*>(kbuf + j);
+            r += (kk.x > key[q]) | ((kk.x == key[q]) & (j < e));
+            r += (kk.y > key[q]) | ((kk.y == key[q]) & (j + 1 < e));
+        }
+        if (e < E && r < k) {
+            a.sel[t * k + r] = e;
+            if (sel_lds) sel_lds[t * k + r] = (unsigned short)e;
+            if (a.dbg_sel) a.dbg_sel[t * k + r] = e;
+            pbuf[r] = p[q];
+        }
+    }
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
     if (lane < k) {
-        float pe = 0.f;
-        int e = 0;
-        for (int rr = 0; rr < k; rr++)
-            if (rr == lane) { pe = chosen_p[rr]; e = chosen[rr]; }
-        a.sel[t * k + lane] = e;
-        if (a.dbg_sel) a.dbg_sel[t * k + lane] = e;
+        float gsum = 0.f;
+        for (int rr = 0; rr < k; rr++) gsum += pbuf[rr];   // in rank order
+        const float pe = pbuf[lane];
         a.gate_out[t * k + lane] = a.renorm ? pe / gsum : pe;
     }
 }
 
-template <bool BF, bool MOE, bool ROUTE = false>
-__global__ __launch_bounds__(1024) void residual_norm_kernel(RowArgs a)
-{
-    constexpr int RT = 1024;
-    __shared__ __align__(16) float xs[8192];
-    __shared__ float shw[RT / 64];
-    const int t = blockIdx.x, H = a.H, T = a.T;
-    float* __restrict__ xr = a.x + (size_t)t * H;
-    const float* __restrict__ y = a.y;
-    int slot[8];
-    float gate[8];
-    if constexpr (MOE) {
-#pragma unroll
-        for (int r = 0; r < 8; r++) {
-            slot[r] = r < a.topk ? a.slot[t * a.topk + r] : 0;
-            gate[r] = r < a.topk ? a.gate[t * a.topk + r] : 0.f;
-        }
-    }
-    float ss = 0.f;
-    for (int i = threadIdx.x; i < H; i += RT) {
-        float d = 0.f;
-        if constexpr (MOE) {
-            float v[8];
-#pragma unroll
-            for (int r = 0; r < 8; r++) v[r] = r < a.topk ? y[(size_t)slot[r] * H + i] : 0.f;
-#pragma unroll
-            for (int r = 0; r < 8; r++) d += gate[r] * v[r];
-            d += sum_strided(y + ((size_t)T * a.topk + t) * H + i, a.n_shared, (size_t)T * H);
-        } else {
-            d = sum_strided(a.parts + (size_t)t * H + i, a.nsplit, (size_t)T * H);
-        }
-        float v = xr[i] + d;
-        xr[i] = v;
-        xs[i] = v;
-        ss += v * v;
-        if (a.dbg_hidden) a.dbg_hidden[(size_t)t * H + i] = v;
-    }
-    ss = block_sum<RT>(ss, shw);
-    const float r = rsqrtf(ss / (float)H + a.eps);
-    typename Act<BF>::T* h = (typename Act<BF>::T*)a.h + (size_t)t * H;
-    for (int i = threadIdx.x; i < H; i += RT) {
-        float v = xs[i] * r * a.gain[i];
-        Act<BF>::st(h, i, v);
-        if constexpr (ROUTE) xs[i] = Act<BF>::ld(h, i);   // the value the experts will read
-    }
-    if constexpr (ROUTE) {
-        __syncthreads();
-        route_row<BF>(a, t, xs);
-    }
-}
-
-struct RopeArgs {
-    const float* qkv;           // [nsplit][T][(n_q + 2 n_kv) D] partial sums
-    int nsplit, T, K1, n_q, n_kv, D, L, layer, cap;
-    const int* ctx_in;
-    const int* seq_err;
-    const float2* rope;         // [cap][D/2] (cos, sin)
-    void* q;                    // [T][n_q][D] act
-    void* kc;                   // K cache
-    void* vc;                   // V cache (channel-major)
-};
-
-// Element offsets of (pos, d) inside one (sequence, layer, KV head) region of
-// the tiled caches (layout documented with the C ABI).
-template <bool BF>
-SV_DEV size_t k_cache_index(int pos, int d, int D)
-{
-    constexpr int KL = BF ? 8 : 4, KT = 4 * KL, NB = KL / 4;
-    const int DS = D / (4 * KL);
-    const int t = pos / KT, r = pos % KT;
-    const int rem = r % KL;
-    const int slot = 4 * (r / KL) + (rem & 3), blk = rem >> 2;
-    const int s = d / (4 * KL), g = (d % (4 * KL)) / KL, e = d % KL;
-    return ((((size_t)t * NB + blk) * DS + s) * 64 + slot + 16 * g) * KL + e;
-}
-
-template <bool BF>
-SV_DEV size_t v_cache_index(int pos, int d, int D)
-{
-    constexpr int KL = BF ? 8 : 4, KT = 4 * KL;
-    const int t = pos / KT, r = pos % KT;
-    const int g = r / KL, e = r % KL;
-    return (((size_t)t * (D / 16) + d / 16) * 64 + (d % 16) + 16 * g) * KL + e;
-}
-
-// rotary on q and k (pair (i, i + D/2) turned by pos * theta^(-2i/D)), then q
-// to the attention input and k, v to the caches at position ctx + j.  One
-// wave per (row, head); grid (T, n_q + 2 n_kv).
-template <bool BF>
-__global__ __launch_bounds__(64) void rope_append_kernel(RopeArgs a)
-{
-    const int t = blockIdx.x, hh = blockIdx.y, lane = threadIdx.x;
-    const int K1 = a.K1, D = a.D, half = D / 2;
-    const int b = t / K1, j = t % K1;
-    const int QKV = (a.n_q + 2 * a.n_kv) * D;
-    const bool write_cache = a.seq_err[b] == 0;
-    const int pos = min(max(a.ctx_in[b], 0), a.cap - K1) + j;
-    typedef typename Act<BF>::T AT;
-    const float* __restrict__ src = a.qkv + (size_t)t * QKV + (size_t)hh * D;
-    const size_t sstride = (size_t)a.T * QKV;
-    if (hh < a.n_q + a.n_kv) {
-        for (int i = lane; i < half; i += 64) {
-            float2 cs = a.rope[(size_t)pos * half + i];
-            float x0 = sum_strided(src + i, a.nsplit, sstride);
-            float x1 = sum_strided(src + i + half, a.nsplit, sstride);
-            float r0 = x0 * cs.x - x1 * cs.y;
-            float r1 = x1 * cs.x + x0 * cs.y;
-            if (hh < a.n_q) {
-                AT* qo = (AT*)a.q + ((size_t)t * a.n_q + hh) * D;
-                Act<BF>::st(qo, i, r0);
-                Act<BF>::st(qo, i + half, r1);
-            } else if (write_cache) {
-                int kh = hh - a.n_q;
-                AT* kp = (AT*)a.kc + (((size_t)b * a.L + a.layer) * a.n_kv + kh) * (size_t)a.cap * D;
-                Act<BF>::st(kp, k_cache_index<BF>(pos, i, D), r0);
-                Act<BF>::st(kp, k_cache_index<BF>(pos, i + half, D), r1);
-            }
-        }
-    } else if (write_cache) {
-        int vh = hh - a.n_q - a.n_kv;
-        AT* vp = (AT*)a.vc + (((size_t)b * a.L + a.layer) * a.n_kv + vh) * (size_t)a.cap * D;
-        for (int d = lane; d < D; d += 64) {
-            float v = sum_strided(src + d, a.nsplit, sstride);
-            Act<BF>::st(vp, v_cache_index<BF>(pos, d, D), v);
-        }
-    }
-}
-
-struct RouteArgs {
-    const float* logits;        // [nsplit][T][E] partial router logits
-    int nsplit, T, E, topk, n_shared, renorm, BM, max_tiles;
-    float* probs;               // [T][E] workspace: routing probabilities
-    int* sel;                   // [T][topk]
-    float* gate;                // [T][topk]
-    int* slot;                  // [T][topk] row of (t, rank) in the permuted order
-    int* perm_tok;              // [T*topk + n_shared*T] token of every permuted row
-    int* tiles;                 // [max_tiles][3]
-    int* n_tiles;               // [1]
-    int* dbg_sel;               // optional copy of sel
-};
-
-// Router permutation: a stable counting sort of the T*topk assignments by
-// expert -- assignment (t, r) of expert e goes to offset[e] + (number of rows
-// t' < t that also chose e) -- followed by the shared-expert rows (every
-// token, in order), and the list of BM-row tiles per group for the grouped
-// GEMMs.  One 256-thread workgroup, deterministic:
+// Router permutation over all T rows (the selections already in shared
+// memory, `lds` layout below): a stable
+// counting sort of the T*topk assignments by expert -- assignment (t, r) of
+// expert e goes to offset[e] + (number of rows t' < t that also chose e) --
+// followed by the shared-expert rows (every token, in order), and the list of
+// BM-row tiles per group for the grouped GEMMs.  Run by one workgroup,
+// deterministic:
 //   * flags[t][e] = 1 if row t chose e;
 //   * 4 threads per expert each scan a quarter of the rows, then add the
 //     totals of the earlier quarters (exclusive ranks within the expert);
 //   * one wave scans the per-group tile counts; each group writes its tiles.
-__global__ __launch_bounds__(256) void route_permute_kernel(RouteArgs a)
+// `lds`: T (E + topk) 2 bytes (16-aligned) + 6.2 KB of shared memory.
+SV_DEV unsigned short* perm_sel_lds(const RowArgs& a, char* lds)
 {
-    extern __shared__ unsigned short cnt[];          // [T][E] flags -> ranks, then sel [T][topk]
-    __shared__ int total[256 * 4], offset[257], tile0[257 + 8];
-    const int T = a.T, E = a.E, k = a.topk, tid = threadIdx.x;
-    unsigned short* sel = cnt + (size_t)T * E;
-    for (int i = tid; i < T * E; i += 256) cnt[i] = 0;
-    for (int i = tid; i < T * k; i += 256) sel[i] = (unsigned short)a.sel[i];
+    return reinterpret_cast<unsigned short*>(lds) + (size_t)a.T * a.E;
+}
+
+SV_DEV void permute_rows(const RowArgs& a, char* lds)
+{
+    const int T = a.T, E = a.E, k = a.topk, tid = threadIdx.x, NT = blockDim.x;
+    unsigned short* cnt = reinterpret_cast<unsigned short*>(lds);   // [T][E] flags -> ranks
+    unsigned short* sel = perm_sel_lds(a, lds);                       // [T][k], filled by the caller
+    int* total = reinterpret_cast<int*>(lds + (((size_t)T * (E + k) * 2 + 15) & ~(size_t)15));   // [E][4]
+    int* offset = total + 1024;                                       // [E + 1]
+    int* tile0 = offset + 260;                                        // [E + n_shared + 1]
+    for (int i = tid; i < T * E; i += NT) cnt[i] = 0;
     __syncthreads();
-    for (int i = tid; i < T * k; i += 256) cnt[(i / k) * E + sel[i]] = 1;
+    for (int i = tid; i < T * k; i += NT) cnt[(i / k) * E + sel[i]] = 1;
     __syncthreads();
     // ranks: thread (e, quarter) scans rows [quarter * T/4, ...) of expert e
     const int QT = (T + 3) / 4;
-    for (int job = tid; job < E * 4; job += 256) {
+    for (int job = tid; job < E * 4; job += NT) {
         const int e = job >> 2, qtr = job & 3;
         int run = 0;
         const int t1 = min(T, (qtr + 1) * QT);
@@ -436,7 +349,7 @@ __global__ __launch_bounds__(256) void route_permute_kernel(RouteArgs a)
         total[job] = run;
     }
     __syncthreads();
-    for (int job = tid; job < E * 4; job += 256) {
+    for (int job = tid; job < E * 4; job += NT) {
         const int e = job >> 2, qtr = job & 3;
         int add = 0;
         for (int q = 0; q < qtr; q++) add += total[e * 4 + q];
@@ -477,7 +390,7 @@ __global__ __launch_bounds__(256) void route_permute_kernel(RouteArgs a)
         }
     }
     __syncthreads();
-    for (int g = tid; g < G; g += 256) {
+    for (int g = tid; g < G; g += NT) {
         const int rows = g < E ? offset[g + 1 < E ? g + 1 : E] - offset[g] : T;
         const int first = g < E ? offset[g] : T * k + (g - E) * T;
         for (int r0 = 0, ti = tile0[g]; r0 < rows; r0 += a.BM, ti++) {
@@ -488,14 +401,256 @@ __global__ __launch_bounds__(256) void route_permute_kernel(RouteArgs a)
             }
         }
     }
-    for (int t = tid; t < T; t += 256) {
+    for (int t = tid; t < T; t += NT) {
         for (int r = 0; r < k; r++) {
             int e = sel[t * k + r];
             int sl = offset[e] + cnt[t * E + e];
-            a.slot[t * k + r] = sl;
+            a.slot_out[t * k + r] = sl;
             a.perm_tok[sl] = t;
         }
         for (int sx = 0; sx < a.n_shared; sx++) a.perm_tok[T * k + sx * T + t] = t;
+    }
+}
+
+// x_out = x + (sum of K-split partials) or x + (sum over ranks of gate * expert
+// output + shared-expert outputs); then RMSNorm into h.  One 1024-thread
+// workgroup per row; a thread owns up to two columns per pass and issues every
+// load of the pass -- residual, gain and all splits (or ranks and shared
+// experts) of both columns -- before consuming any, so a pass costs one memory
+// round trip.  ROUTE (MoE, after attention): S workgroups per row each
+// recompute the update and the norm (workgroup 0 writes them) and take E/S of
+// the router's experts; with S > 1 they write the logits for the selection in
+// route_finish_kernel, with S = 1 the row selects its experts here.
+template <bool BF, bool MOE, bool ROUTE = false, int UPW = 4>
+__global__ __launch_bounds__(1024) void residual_norm_kernel(RowArgs a)
+{
+    constexpr int RT = 1024, EPT = 2, NS = ROUTE ? 4 : 16;
+    __shared__ __align__(16) float smem[2 * 8192];   // row update, gains
+    __shared__ float shw[RT / 64];
+    __shared__ float logit[256];
+    float* xs = smem;
+    float* gs = smem + 8192;
+    const int t = blockIdx.x, H = a.H, T = a.T, tid = threadIdx.x;
+    const int sidx = ROUTE ? blockIdx.y : 0;
+    const bool writer = sidx == 0;
+    const float* xr = a.x + (size_t)t * H;
+    float* xo = a.x_out + (size_t)t * H;
+    const float* __restrict__ y = a.y;
+    int slot[8];
+    float gate[8];
+    if constexpr (MOE) {
+#pragma unroll
+        for (int r = 0; r < 8; r++) {
+            const int rc = min(r, a.topk - 1);
+            slot[r] = a.slot[t * a.topk + rc];
+            gate[r] = a.gate[t * a.topk + rc];
+        }
+#pragma unroll
+        for (int r = 0; r < 8; r++) gate[r] = r < a.topk ? gate[r] : 0.f;
+    }
+    // uniform row bases; every load below is (uniform base + 32-bit byte offset)
+    const float* __restrict__ prow = a.parts + (size_t)t * H;
+    const size_t pstride = (size_t)T * H;
+    const float* __restrict__ shrow =
+        (MOE && a.n_shared > 0) ? y + ((size_t)T * a.topk + t) * H : y;
+    const int nlast = MOE ? max(a.n_shared, 1) - 1 : max(a.nsplit, 1) - 1;
+    float xv[EPT], gv[EPT], pv[EPT][16];
+    auto loads = [&](int i0) {
+#pragma unroll
+        for (int u = 0; u < EPT; u++) {
+            const unsigned off = 4u * (unsigned)min(i0 + u * RT, H - 1);
+            xv[u] = ld_at(xr, off);
+            gv[u] = ld_at(a.gain, off);
+            if constexpr (MOE) {
+#pragma unroll
+                for (int r = 0; r < 8; r++) pv[u][r] = ld_at(y + (size_t)slot[r] * H, off);
+#pragma unroll
+                for (int sx = 0; sx < 8; sx++)
+                    pv[u][8 + sx] = ld_at(shrow + (size_t)min(sx, nlast) * pstride, off);
+            } else {
+#pragma unroll
+                for (int sp = 0; sp < NS; sp++) pv[u][sp] = ld_at(prow + (size_t)min(sp, nlast) * pstride, off);
+            }
+        }
+    };
+    float ss = 0.f;
+    auto consume = [&](int i0) {
+#pragma unroll
+        for (int u = 0; u < EPT; u++) {
+            const int i = i0 + u * RT;
+            float d = 0.f;
+            if constexpr (MOE) {     // clamped re-reads are dropped here
+#pragma unroll
+                for (int r = 0; r < 8; r++) d += gate[r] * (r < a.topk ? pv[u][r] : 0.f);
+                float sh = 0.f;
+#pragma unroll
+                for (int sx = 0; sx < 8; sx++) sh += sx < a.n_shared ? pv[u][8 + sx] : 0.f;
+                d += sh;
+            } else {
+#pragma unroll
+                for (int sp = 0; sp < NS; sp++) d += sp < a.nsplit ? pv[u][sp] : 0.f;
+            }
+            if (i >= H) continue;
+            const float v = xv[u] + d;
+            if (writer) {
+                xo[i] = v;
+                if (a.dbg_hidden) a.dbg_hidden[(size_t)t * H + i] = v;
+            }
+            xs[i] = v;
+            gs[i] = gv[u];
+            ss += v * v;
+        }
+    };
+    // first pass: its loads, then the router's first weight slices (still in
+    // flight while the residual is summed and normalised), then the rest
+    const int EP = ROUTE ? a.E / a.S : 0, ebeg = sidx * EP, eend = ebeg + EP;
+    loads(tid);
+    uint4 wv[4][UPW];
+    if constexpr (ROUTE) router_loads<UPW>(a, ebeg + (tid >> 6), router_epl(a.wdtype) * (tid & 63), eend, wv);
+    consume(tid);
+    for (int i0 = tid + EPT * RT; i0 < H; i0 += EPT * RT) {
+        loads(i0);
+        consume(i0);
+    }
+    ss = block_sum<RT>(ss, shw);
+    const float r = rsqrtf(ss / (float)H + a.eps);
+    typename Act<BF>::T* h = (typename Act<BF>::T*)a.h + (size_t)t * H;
+    for (int i = tid; i < H; i += RT) {   // each thread rereads only the columns it wrote
+        float v = xs[i] * r * gs[i];
+        if (writer) Act<BF>::st(h, i, v);
+        if constexpr (ROUTE) xs[i] = Act<BF>::round(v);   // the value the experts will read
+    }
+    if constexpr (ROUTE) {
+        __syncthreads();
+        router_logits<UPW>(a, xs, wv, ebeg, eend, logit);
+        __syncthreads();
+        if (tid < 64) {
+            const int lane = tid, E = a.E;
+            if (a.S > 1) {
+                // this workgroup's share of the row's logits; selection follows
+#pragma unroll
+                for (int q = 0; q < 4; q++) {
+                    const int e = lane + 64 * q;
+                    if (e >= ebeg && e < eend) a.logits_g[(size_t)t * E + e] = logit[e];
+                }
+            } else {
+                float p[4];
+#pragma unroll
+                for (int q = 0; q < 4; q++)
+                    p[q] = lane + 64 * q < E ? logit[min(lane + 64 * q, E - 1)] : -INFINITY;
+                // the row buffer is free after the logits: wave 0's key scratch
+                router_select(a, t, p, reinterpret_cast<unsigned long long*>(smem));
+            }
+        }
+    }
+}
+
+// Routing, second half (one 1024-thread workgroup): when the router was
+// shared out (S > 1), each wave selects the experts of rows w, w + 16, ...
+// from the published logits; otherwise the rows' selections are read back.
+// Then the permutation and tile list of every row.
+__global__ __launch_bounds__(1024) void route_finish_kernel(RowArgs a)
+{
+    __shared__ __align__(16) char lds[81920];
+    __shared__ __align__(16) unsigned long long kscr[16][256 + 8];   // per-wave selection scratch
+    const int T = a.T, E = a.E, k = a.topk, tid = threadIdx.x, lane = tid & 63;
+    unsigned short* sel = perm_sel_lds(a, lds);
+    if (a.S > 1) {
+        for (int row = tid >> 6; row < T; row += 16) {
+            float p[4];
+#pragma unroll
+            for (int q = 0; q < 4; q++) p[q] = a.logits_g[(size_t)row * E + min(lane + 64 * q, E - 1)];
+#pragma unroll
+            for (int q = 0; q < 4; q++) p[q] = lane + 64 * q < E ? p[q] : -INFINITY;
+            router_select(a, row, p, kscr[tid >> 6], sel);
+        }
+    } else {
+        for (int i = tid; i < T * k; i += 1024) sel[i] = (unsigned short)a.sel[i];
+    }
+    __syncthreads();
+    permute_rows(a, lds);
+}
+
+struct RopeArgs {
+    const float* qkv;           // [nsplit][T][(n_q + 2 n_kv) D] partial sums
+    int nsplit, T, K1, n_q, n_kv, D, L, layer, cap;
+    const int* ctx_in;
+    const int* seq_err;
+    const float2* rope;         // [cap][D/2] (cos, sin)
+    void* q;                    // [T][n_q][D] act
+    void* kc;                   // K cache
+    void* vc;                   // V cache
+};
+
+// Element offsets of (pos, d) inside one (sequence, layer, KV head) region of
+// the tiled caches (layout documented with the C ABI).
+template <bool BF>
+SV_DEV size_t k_cache_index(int pos, int d, int D)
+{
+    constexpr int KL = BF ? 8 : 4, KT = 4 * KL, NB = KL / 4;
+    const int DS = D / (4 * KL);
+    const int t = pos / KT, r = pos % KT;
+    const int rem = r % KL;
+    const int slot = 4 * (r / KL) + (rem & 3), blk = rem >> 2;
+    const int s = d / (4 * KL), g = (d % (4 * KL)) / KL, e = d % KL;
+    return ((((size_t)t * NB + blk) * DS + s) * 64 + slot + 16 * g) * KL + e;
+}
+
+template <bool BF>
+SV_DEV size_t v_cache_index(int pos, int d, int D)
+{
+    constexpr int KL = BF ? 8 : 4, KT = 4 * KL;
+    const int t = pos / KT, r = pos % KT;
+    const int g = r / KL, e = r % KL;
+    return (((size_t)t * (D / 16) + d / 16) * 64 + (d % 16) + 16 * g) * KL + e;
+}
+
+// rotary on q and k (pair (i, i + D/2) turned by pos * theta^(-2i/D)), then q
+// to the attention input and k, v to the caches at position ctx + j.  One
+// wave per (row, head); grid (T, n_q + 2 n_kv).  A lane owns one rotary pair
+// (q, k heads) or two channels (v heads) and issues the loads of every K-split
+// partial of them at once; the rotary table read waits only for ctx.
+template <bool BF>
+__global__ __launch_bounds__(64) void rope_append_kernel(RopeArgs a)
+{
+    const int t = blockIdx.x, hh = blockIdx.y, lane = threadIdx.x;
+    const int K1 = a.K1, D = a.D, half = D / 2;     // D in {64, 128}: half <= 64
+    const int b = t / K1, j = t % K1;
+    const int QKV = (a.n_q + 2 * a.n_kv) * D;
+    typedef typename Act<BF>::T AT;
+    const float* __restrict__ src = a.qkv + (size_t)t * QKV + (size_t)hh * D;
+    const size_t sstride = (size_t)a.T * QKV;
+    float p0[16], p1[16];
+    const bool rot = hh < a.n_q + a.n_kv;
+    // rotary heads: channels lane and lane + half; value heads: lane and lane + 64
+    const int i0 = lane, i1 = rot ? lane + half : lane + 64;
+    const bool ok0 = rot ? lane < half : lane < D, ok1 = rot ? lane < half : lane + 64 < D;
+    load_strided<16>(src + (ok0 ? i0 : 0), ok0 ? a.nsplit : 0, sstride, p0);
+    load_strided<16>(src + (ok1 ? i1 : 0), ok1 ? a.nsplit : 0, sstride, p1);
+    const int ctx = a.ctx_in[b];
+    const bool write_cache = a.seq_err[b] == 0;
+    const int pos = min(max(ctx, 0), a.cap - K1) + j;
+    const float x0 = sum_in_order(p0), x1 = sum_in_order(p1);
+    if (rot) {
+        if (!ok0) return;
+        const float2 cs = a.rope[(size_t)pos * half + lane];
+        const float r0 = x0 * cs.x - x1 * cs.y;
+        const float r1 = x1 * cs.x + x0 * cs.y;
+        if (hh < a.n_q) {
+            AT* qo = (AT*)a.q + ((size_t)t * a.n_q + hh) * D;
+            Act<BF>::st(qo, lane, r0);
+            Act<BF>::st(qo, lane + half, r1);
+        } else if (write_cache) {
+            const int kh = hh - a.n_q;
+            AT* kp = (AT*)a.kc + (((size_t)b * a.L + a.layer) * a.n_kv + kh) * (size_t)a.cap * D;
+            Act<BF>::st(kp, k_cache_index<BF>(pos, lane, D), r0);
+            Act<BF>::st(kp, k_cache_index<BF>(pos, lane + half, D), r1);
+        }
+    } else if (write_cache) {
+        const int vh = hh - a.n_q - a.n_kv;
+        AT* vp = (AT*)a.vc + (((size_t)b * a.L + a.layer) * a.n_kv + vh) * (size_t)a.cap * D;
+        if (ok0) Act<BF>::st(vp, v_cache_index<BF>(pos, i0, D), x0);
+        if (ok1) Act<BF>::st(vp, v_cache_index<BF>(pos, i1, D), x1);
     }
 }
 
@@ -514,56 +669,73 @@ struct AcceptArgs {
 
 // Greedy token per position (max over the column-tile keys), then the longest
 // prefix of drafts equal to the target's tokens, the bonus token, and the new
-// context length.  One workgroup of 4 waves per sequence; wave w reduces the
-// positions j = w, w+4, ...
-__global__ __launch_bounds__(256) void accept_kernel(AcceptArgs a)
+// context length.  One 1024-thread workgroup per sequence: the 16 waves are
+// shared out over the K+1 positions (WPP waves per position when K+1 <= 16,
+// else positions round-robin), every lane keeps 16 key loads in flight, and
+// the drafts are staged in shared memory alongside; the first mismatch is
+// found with a wave vote.
+__global__ __launch_bounds__(1024) void accept_kernel(AcceptArgs a)
 {
+    constexpr int NW = 16, KB = 16;
+    __shared__ unsigned long long part[64][NW];     // [position][wave part], K1 <= 64
+    __shared__ int dr[64];
     __shared__ int g[64];
-    __shared__ int nan_seen[64];
-    const int b = blockIdx.x, K1 = a.K1, K = K1 - 1;
-    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-    for (int j = w; j < K1; j += 4) {
-        const int t = b * K1 + j;
-        const unsigned long long* __restrict__ kp = a.keys + t;
-        unsigned long long part[8] = {0ull, 0ull, 0ull, 0ull, 0ull, 0ull, 0ull, 0ull};
-        int n = lane;
-        for (; n + 7 * 64 < a.NT; n += 8 * 64) {
+    const int b = blockIdx.x, K1 = a.K1, K = K1 - 1, tid = threadIdx.x;
+    const int lane = tid & 63, w = tid >> 6;
+    // this sequence's drafts: loaded now, stored to shared memory after the key loads
+    const int dv = a.drafts[(size_t)b * K + min(tid, K - 1)];
+    const int WPP = K1 >= NW ? 1 : NW / K1;          // waves per position
+    const int NG = NW / WPP;                         // position groups
+    const int gi = w / WPP, pi = w % WPP;
+    if (gi < NG) {
+        for (int j = gi; j < K1; j += NG) {
+            const unsigned long long* __restrict__ kp = a.keys + (size_t)b * K1 + j;
+            unsigned long long best = 0ull;
+            for (int n0 = pi * 64 + lane; n0 < a.NT; n0 += KB * 64 * WPP) {
+                unsigned long long v[KB];
 #pragma unroll
-            for (int u = 0; u < 8; u++) part[u] = umax64(part[u], kp[(size_t)(n + u * 64) * a.T]);
-        }
-        for (; n < a.NT; n += 64) part[0] = umax64(part[0], kp[(size_t)n * a.T]);
-        unsigned long long best = part[0];
+                for (int u = 0; u < KB; u++) {   // clamped: a repeated key leaves the maximum
+                    const int n = min(n0 + u * 64 * WPP, a.NT - 1);
+                    v[u] = kp[(size_t)n * a.T];
+                }
 #pragma unroll
-        for (int u = 1; u < 8; u++) best = umax64(best, part[u]);
+                for (int u = 0; u < KB; u++) best = umax64(best, v[u]);
+            }
 #pragma unroll
-        for (int m = 32; m >= 1; m >>= 1) best = umax64(best, shfl_xor_u64(best, m));
-        if (lane == 0) {
-            nan_seen[j] = best == ~0ull;
-            g[j] = (int)(0xffffffffu - (uint32_t)(best & 0xffffffffull));
+            for (int m = 32; m >= 1; m >>= 1) best = umax64(best, shfl_xor_u64(best, m));
+            if (lane == 0) part[j][pi] = best;
         }
     }
+    if (tid < K) dr[tid] = dv;
     __syncthreads();
-    if (threadIdx.x == 0) {
+    if (w != 0) return;
+    // wave 0: lane j < K1 finishes position j
+    unsigned long long best = 0ull;
+    if (lane < K1)
+        for (int p = 0; p < WPP; p++) best = umax64(best, part[lane][p]);
+    const bool nan_here = lane < K1 && best == ~0ull;
+    const int gj = (int)(0xffffffffu - (uint32_t)(best & 0xffffffffull));
+    if (lane < K1) g[lane] = gj;
+    const bool nan_any = __any(nan_here);
+    const unsigned long long miss = __ballot(lane < K && dr[lane] != gj);
+    const int n = miss ? (__ffsll((long long)miss) - 1) : K;
+    const int gn = __shfl(gj, n, 64);
+    if (a.target && lane < K1) a.target[(size_t)b * K1 + lane] = gj;
+    if (lane == 0) {
         unsigned e = a.seq_err ? (unsigned)a.seq_err[b] : 0u;
-        int nan_any = 0;
-        for (int j = 0; j < K1; j++) nan_any |= nan_seen[j];
         if (nan_any) e |= SV_DEV_NAN_LOGIT;
-        int c = a.ctx_in[b];
+        const int c = a.ctx_in[b];
         if (e) {
             if (a.seq_err == nullptr || nan_any) atomicOr(a.err_word, e);
             a.accepted[b] = -1;
             a.next_tok[b] = -1;
             a.ctx_out[b] = c;
         } else {
-            int n = 0;
-            while (n < K && a.drafts[(size_t)b * K + n] == g[n]) n++;
             a.accepted[b] = n;
-            a.next_tok[b] = g[n];
+            a.next_tok[b] = gn;
             a.ctx_out[b] = c + n + 1;
         }
     }
-    if (a.target)
-        for (int j = threadIdx.x; j < K1; j += 256) a.target[(size_t)b * K1 + j] = g[j];
 }
 
 // fp32 logits [T][V] -> per-(column tile, row) argmax keys, for acceptance

@@ -86,6 +86,7 @@ struct spec_verify_ctx {
     // workspace
     std::vector<void*> allocs;
     float* x = nullptr;
+    float* x2 = nullptr;        // residual after the attention half (MoE: written by the router kernel)
     void* h = nullptr;
     float* parts = nullptr;
     size_t parts_elems = 0;
@@ -94,7 +95,7 @@ struct spec_verify_ctx {
     float* opart = nullptr;
     float* mlpart = nullptr;
     float2* rope = nullptr;
-    float* probs = nullptr;
+    float* logits_g = nullptr;  // router logits shared between a row's workgroups
     int* sel = nullptr;
     float* gate = nullptr;
     int* slot = nullptr;
@@ -166,6 +167,9 @@ int validate_config(const spec_verify_config& c)
         if (c.n_experts % 4) return bad("n_experts must be a multiple of 4");
         long T = (long)c.max_batch * (c.k_draft + 1);
         if (T * c.n_experts > 32768) return bad("max_batch*(K+1)*n_experts must be <= 32768");
+        // the permutation's shared memory: T (E + top_k) 2 bytes + 6.2 KB <= 80 KB
+        if (((T * (c.n_experts + c.top_k) * 2 + 15) & ~15L) + 1024 * 4 + 525 * 4 > 81920)
+            return bad("max_batch*(K+1)*(n_experts+top_k) too large for the routing permutation");
     } else if (c.ffn_kind == SV_FFN_DENSE) {
         if (c.dense_inter < 64 || c.dense_inter % 64 || c.dense_inter % step)
             return bad("dense_inter must be a multiple of 64");
@@ -273,10 +277,10 @@ void launch_gemm_big(int wt, int mode, bool packed, GemmArgs& a, hipStream_t s)
 int rows_mf(int rows) { return rows <= 16 ? 1 : (rows <= 32 ? 2 : 4); }
 
 // K split: enough waves to cover the GPU, each split at least 4 reduction steps
-int pick_ksplit(long waves, int K, int step)
+int pick_ksplit(long waves, int K, int step, int smax = KS_MAX)
 {
     int steps = K / step, best = 1;
-    for (int s = 1; s <= KS_MAX; s++) {
+    for (int s = 1; s <= smax; s++) {
         if (steps % s) continue;
         if (steps / s < 4) break;
         best = s;
@@ -421,6 +425,7 @@ int spec_verify_init(const spec_verify_config* cfg, spec_verify_ctx** out)
     char* qbuf = nullptr;
     char* obuf = nullptr;
     ALLOC(c->x, (size_t)T * H);
+    ALLOC(c->x2, (size_t)T * H);
     ALLOC(hbuf, (size_t)T * H * AES);
     c->h = hbuf;
     ALLOC(c->parts, c->parts_elems);
@@ -437,7 +442,7 @@ int spec_verify_init(const spec_verify_config* cfg, spec_verify_ctx** out)
     ALLOC(c->err_word, 1);
     if (k.ffn_kind == SV_FFN_MOE) {
         char* abuf = nullptr;
-        ALLOC(c->probs, (size_t)T * E);
+        ALLOC(c->logits_g, (size_t)T * E);
         ALLOC(c->sel, (size_t)T * tk);
         ALLOC(c->gate, (size_t)T * tk);
         ALLOC(c->slot, (size_t)T * tk);
@@ -544,10 +549,11 @@ int spec_verify_step(spec_verify_ctx* c, const spec_verify_weights* w, void* k_c
     ra.err_word = c->err_word;
     ra.embed = w->embed;
     ra.x = c->x;
+    ra.x_out = c->x;
     ra.h = c->h;
     ra.gain = w->layers[0].attn_norm;
-    if (bf) embed_norm_kernel<true><<<T, 256, 0, s>>>(ra);
-    else embed_norm_kernel<false><<<T, 256, 0, s>>>(ra);
+    if (bf) embed_norm_kernel<true><<<T, 1024, 0, s>>>(ra);
+    else embed_norm_kernel<false><<<T, 1024, 0, s>>>(ra);
 
     const int MFd = rows_mf(T);
     const int MTd = cdiv(T, 16 * MFd);
@@ -555,6 +561,7 @@ int spec_verify_step(spec_verify_ctx* c, const spec_verify_weights* w, void* k_c
     const bool big = T >= 64 && wt != SV_F32;
     const int MTb = cdiv(T, 16 * BIG_MF);
     // dense GEMM (or the dense SwiGLU / argmax variants); returns the K split used
+    // allow_split: largest K split the consumer accepts (0 or 1: none)
     auto dense_gemm = [&](int mode, const void* X, long ldx, int N, int Kd, const void* W,
                           const float* ws, void* out, long ldo, int allow_split) -> int {
         GemmArgs a = dense_args(X, ldx, T, N, Kd, W, ws);
@@ -572,9 +579,9 @@ int spec_verify_step(spec_verify_ctx* c, const spec_verify_weights* w, void* k_c
             a.NT = cdiv(N, 16 * 4 * BIG_NF);
             long wgs = (long)a.NT * a.MT;
             a.ksplit = 1;
-            if (allow_split) {   // enough workgroups for the 256 CUs, each split >= 4 chunks
+            if (allow_split > 1) {   // enough workgroups for the 256 CUs, each split >= 4 chunks
                 int steps = Kd / chunk;
-                for (int sp = 2; sp <= KS_MAX; sp++) {
+                for (int sp = 2; sp <= allow_split; sp++) {
                     if (steps % sp || steps / sp < 4) continue;
                     if (wgs * a.ksplit >= 512) break;
                     a.ksplit = sp;
@@ -586,7 +593,7 @@ int spec_verify_step(spec_verify_ctx* c, const spec_verify_weights* w, void* k_c
         a.MT = MTd;
         a.NT = cdiv(N, 64);
         long waves = (long)a.NT * a.MT * 4;
-        a.ksplit = allow_split ? pick_ksplit(waves, Kd, step) : 1;
+        a.ksplit = allow_split > 1 ? pick_ksplit(waves, Kd, step, allow_split) : 1;
         launch_gemm(wt, mode, MFd, packed, a, s);
         return a.ksplit;
     };
@@ -617,7 +624,7 @@ int spec_verify_step(spec_verify_ctx* c, const spec_verify_weights* w, void* k_c
         int ks;
         {
             ProfScope ps(c, SV_KC_QKV, s);
-            ks = dense_gemm(GM_STORE, c->h, H, QKV, H, Lw.w_qkv, Lw.s_qkv, c->parts, QKV, 1);
+            ks = dense_gemm(GM_STORE, c->h, H, QKV, H, Lw.w_qkv, Lw.s_qkv, c->parts, QKV, KS_MAX);
         }
         RopeArgs rp;
         rp.qkv = c->parts;
@@ -669,13 +676,23 @@ int spec_verify_step(spec_verify_ctx* c, const spec_verify_weights* w, void* k_c
             if (bf) attn_merge_kernel<true><<<rows, 128, 0, s>>>(at, c->o);
             else attn_merge_kernel<false><<<rows, 128, 0, s>>>(at, c->o);
         }
-        ks = dense_gemm(GM_STORE, c->o, QD, H, QD, Lw.w_o, Lw.s_o, c->parts, H, 1);
+        // the MoE consumer (residual + norm + router) takes at most 4 splits
+        ks = dense_gemm(GM_STORE, c->o, QD, H, QD, Lw.w_o, Lw.s_o, c->parts, H,
+                        k.ffn_kind == SV_FFN_MOE ? 4 : KS_MAX);
         ra.parts = c->parts;
         ra.nsplit = ks;
         ra.gain = Lw.ffn_norm;
         ra.dbg_hidden = nullptr;
+        ra.x = c->x;
         if (k.ffn_kind == SV_FFN_MOE) {
-            // residual + norm + router logits, softmax and top-k in one kernel
+            // residual + norm + router (experts shared out over S workgroups per
+            // row when rows are few; the updated residual goes to x2 since a
+            // row's workgroups all read x), then selection + permutation
+            const int E = k.n_experts, tk = k.top_k;
+            const int S = (E % 16 == 0 && E >= 32 && T <= 64) ? E / 16 : 1;
+            const int avg_rows = std::max(1, T * tk / E);
+            const int BMe = 16 * rows_mf(avg_rows);
+            ra.x_out = c->x2;
             ra.w_router = Lw.w_router;
             ra.s_router = Lw.s_router;
             ra.wdtype = wt;
@@ -683,9 +700,25 @@ int spec_verify_step(spec_verify_ctx* c, const spec_verify_weights* w, void* k_c
             ra.sel = c->sel;
             ra.gate_out = c->gate;
             ra.dbg_sel = c->dbg_routing ? c->dbg_routing + (size_t)l * T * k.top_k : nullptr;
-            if (bf) residual_norm_kernel<true, false, true><<<T, 1024, 0, s>>>(ra);
-            else residual_norm_kernel<false, false, true><<<T, 1024, 0, s>>>(ra);
+            ra.S = S;
+            ra.logits_g = c->logits_g;
+            ra.BM = BMe;
+            ra.max_tiles = std::min(E, T * tk) + (T * tk) / BMe + k.n_shared * cdiv(T, BMe) + 1;
+            ra.slot_out = c->slot;
+            ra.perm_tok = c->perm_tok;
+            ra.tiles = c->tiles;
+            ra.n_tiles = c->n_tiles;
+            dim3 grid(T, S);
+            if (S > 1) {
+                if (bf) residual_norm_kernel<true, false, true, 1><<<grid, 1024, 0, s>>>(ra);
+                else residual_norm_kernel<false, false, true, 1><<<grid, 1024, 0, s>>>(ra);
+            } else {
+                if (bf) residual_norm_kernel<true, false, true, 4><<<grid, 1024, 0, s>>>(ra);
+                else residual_norm_kernel<false, false, true, 4><<<grid, 1024, 0, s>>>(ra);
+            }
+            route_finish_kernel<<<1, 1024, 0, s>>>(ra);
         } else {
+            ra.x_out = c->x;
             if (bf) residual_norm_kernel<true, false><<<T, 1024, 0, s>>>(ra);
             else residual_norm_kernel<false, false><<<T, 1024, 0, s>>>(ra);
         }
@@ -699,25 +732,6 @@ int spec_verify_step(spec_verify_ctx* c, const spec_verify_weights* w, void* k_c
             const int MFe = rows_mf(avg_rows);
             const int BMe = 16 * MFe;
             const int max_tiles = std::min(E, T * tk) + (T * tk) / BMe + S * cdiv(T, BMe) + 1;
-            RouteArgs ro;
-            ro.logits = nullptr;
-            ro.nsplit = 0;
-            ro.T = T;
-            ro.E = E;
-            ro.topk = tk;
-            ro.n_shared = S;
-            ro.renorm = k.renorm_topk;
-            ro.BM = BMe;
-            ro.max_tiles = max_tiles;
-            ro.probs = c->probs;
-            ro.dbg_sel = nullptr;
-            ro.sel = c->sel;
-            ro.gate = c->gate;
-            ro.slot = c->slot;
-            ro.perm_tok = c->perm_tok;
-            ro.tiles = c->tiles;
-            ro.n_tiles = c->n_tiles;
-            route_permute_kernel<<<1, 256, (size_t)T * (E + tk) * sizeof(unsigned short), s>>>(ro);
 
             GemmArgs g;
             memset(&g, 0, sizeof(g));
@@ -781,6 +795,8 @@ int spec_verify_step(spec_verify_ctx* c, const spec_verify_weights* w, void* k_c
             ra.slot = c->slot;
             ra.gain = next_gain;
             ra.dbg_hidden = dbg_h;
+            ra.x = c->x2;
+            ra.x_out = c->x;
             if (bf) residual_norm_kernel<true, true><<<T, 1024, 0, s>>>(ra);
             else residual_norm_kernel<false, true><<<T, 1024, 0, s>>>(ra);
         } else {
@@ -791,12 +807,14 @@ int spec_verify_step(spec_verify_ctx* c, const spec_verify_weights* w, void* k_c
             }
             {
                 ProfScope ps(c, SV_KC_EXPERT_DOWN, s);
-                ks = dense_gemm(GM_STORE, c->act, I, H, I, Lw.w_down, Lw.s_down, c->parts, H, 1);
+                ks = dense_gemm(GM_STORE, c->act, I, H, I, Lw.w_down, Lw.s_down, c->parts, H, KS_MAX);
             }
             ra.parts = c->parts;
             ra.nsplit = ks;
             ra.gain = next_gain;
             ra.dbg_hidden = dbg_h;
+            ra.x = c->x;
+            ra.x_out = c->x;
             if (bf) residual_norm_kernel<true, false><<<T, 1024, 0, s>>>(ra);
             else residual_norm_kernel<false, false><<<T, 1024, 0, s>>>(ra);
         }
@@ -823,7 +841,7 @@ int spec_verify_step(spec_verify_ctx* c, const spec_verify_weights* w, void* k_c
     ac.target = c->dbg_target;
     ac.seq_err = c->seq_err;
     ac.err_word = c->err_word;
-    accept_kernel<<<B, 256, 0, s>>>(ac);
+    accept_kernel<<<B, 1024, 0, s>>>(ac);
     HIP_TRY(hipGetLastError());
     return SV_OK;
 }
@@ -855,7 +873,7 @@ int spec_verify_accept_from_logits(spec_verify_ctx* c, const float* logits, cons
     ac.target = target;
     ac.seq_err = nullptr;
     ac.err_word = c->err_word;
-    accept_kernel<<<B, 256, 0, s>>>(ac);
+    accept_kernel<<<B, 1024, 0, s>>>(ac);
     HIP_TRY(hipGetLastError());
     return SV_OK;
 }
