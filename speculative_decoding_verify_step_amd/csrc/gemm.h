@@ -204,11 +204,16 @@ SV_DEV void gemm_epilogue(const GemmArgs& a, f32x4_t (&acc)[MF][(MODE == GM_SWIG
     }
 }
 
-// WAVES waves per workgroup side by side (a 16*NF*WAVES-column tile); UU
-// reduction steps per prefetch stage (0: by row count).
-template <int WT, int MF, int NF, int MODE, int WAVES = 4, int UU = 0, bool PACKED = false>
+// WAVES waves per workgroup side by side (a 16*NF*WAVES-column tile), or with
+// KW the WAVES waves share one 16*NF-column tile and each takes a contiguous
+// share of the reduction steps (more loads in flight per column tile; wave 0
+// adds the other waves' partial sums from shared memory in wave order, then
+// runs the epilogue; STORE and SWIGLU only).  UU reduction steps per prefetch
+// stage (0: by row count).
+template <int WT, int MF, int NF, int MODE, int WAVES = 4, int UU = 0, bool PACKED = false, bool KW = false>
 __global__ __launch_bounds__(64 * WAVES) void gemm_kernel(GemmArgs a)
 {
+    static_assert(!KW || MODE != GM_ARGMAX, "K-split waves: STORE and SWIGLU epilogues only");
     using Tr = WTraits<WT>;
     constexpr int KL = Tr::KL, SK = Tr::SK, XU = Tr::XU, WESZ = Tr::ESZ;
     constexpr int AESZ = ATraits<WT>::ESZ;
@@ -251,11 +256,20 @@ __global__ __launch_bounds__(64 * WAVES) void gemm_kernel(GemmArgs a)
         sc = a.ws2 ? a.ws2 + (size_t)(group - a.G1) * a.s2_gstride : nullptr;
     }
 
-    const int ncol0 = (nt * WAVES + wave) * 16 * NF;      // this wave's first column
+    const int ncol0 = KW ? nt * 16 * NF : (nt * WAVES + wave) * 16 * NF;   // this wave's first column
     const int K = a.K;
     const int kspan = K / a.ksplit;
-    const int kb = blockIdx.y * kspan;
-    const int ke = kb + kspan;
+    int kb = blockIdx.y * kspan;
+    int ke = kb + kspan;
+    if constexpr (KW) {   // wave w: reduction steps [w S / WAVES, (w + 1) S / WAVES) of the split
+        // (the wave index made explicitly uniform: scalar loop bounds, as in the
+        // one-wave case; derived from the lane id the loop became exec-masked and
+        // its sums came out wrong)
+        const int wu = __builtin_amdgcn_readfirstlane(wave);
+        const int steps = kspan / SK;
+        ke = kb + (wu + 1) * steps / WAVES * SK;
+        kb = kb + wu * steps / WAVES * SK;
+    }
 
     // weight rows of this lane, one per fragment (invalid fragments read row 0)
     const char* wrow[NFT];
@@ -330,12 +344,32 @@ __global__ __launch_bounds__(64 * WAVES) void gemm_kernel(GemmArgs a)
     };
 
     constexpr int STAGE = U * SK;
-    load(kb, wA, xA);
+    if (kb < ke) load(kb, wA, xA);
     for (int k = kb; k < ke; k += 2 * STAGE) {
         if (k + STAGE < ke) load(k + STAGE, wB, xB);
         compute(k, wA, xA);
         if (k + 2 * STAGE < ke) load(k + 2 * STAGE, wA, xA);
         if (k + STAGE < ke) compute(k + STAGE, wB, xB);
+    }
+    if constexpr (KW) {
+        // partial sums of waves 1.. through shared memory, added by wave 0 in wave order
+        __shared__ f32x4_t part[WAVES > 1 ? WAVES - 1 : 1][MF][NFT][64];
+        if (wave > 0) {
+#pragma unroll
+            for (int m = 0; m < MF; m++)
+#pragma unroll
+                for (int f = 0; f < NFT; f++) part[wave - 1][m][f][lane] = acc[m][f];
+        }
+        __syncthreads();
+        if (wave > 0) return;
+#pragma unroll
+        for (int w = 0; w < WAVES - 1; w++)
+#pragma unroll
+            for (int m = 0; m < MF; m++)
+#pragma unroll
+                for (int f = 0; f < NFT; f++) acc[m][f] += part[w][m][f][lane];
+        gemm_epilogue<WT, MF, NF, MODE, 1>(a, acc, row0, nrows, ncol0, nt, sc, fvalid, nullptr);
+        return;
     }
 
     // ------------------------------------------------------------ epilogue

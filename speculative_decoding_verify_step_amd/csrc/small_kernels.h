@@ -52,7 +52,7 @@ struct RowArgs {
     const float* parts;         // [nsplit][T][H] partial sums to add (or null)
     const float* y;             // MoE expert outputs [rows][H]
     const float* gate;          // [T][topk]
-    const int* slot;            // [T][topk]
+    const int* slot;            // [T][topk] expert-output row of (t, rank)
     float* dbg_hidden;          // optional [T][H] copy of x after the update
     // router after the attention half's norm: W_r [E][H] row-major
     const void* w_router;

@@ -28,6 +28,7 @@
 #include "common.h"
 #include "gemm.h"
 #include "small_kernels.h"
+#include "qkv_rope.h"
 
 namespace {
 
@@ -183,11 +184,21 @@ int validate_config(const spec_verify_config& c)
 template <int WT, int MODE, bool PK>
 void launch_gemm_t(int MF, const GemmArgs& a, dim3 grid, hipStream_t s)
 {
-    if (a.tiles) {   // grouped (experts): one wave per workgroup, finer balance
-        switch (MF) {
-        case 1: launch(gemm_kernel<WT, 1, 1, MODE, 1, 0, PK>, grid, dim3(64), 0, s, a); break;
-        case 2: launch(gemm_kernel<WT, 2, 1, MODE, 1, 0, PK>, grid, dim3(64), 0, s, a); break;
-        default: launch(gemm_kernel<WT, 4, 1, MODE, 1, 0, PK>, grid, dim3(64), 0, s, a); break;
+    if (a.tiles) {
+        // grouped (experts): one 16-column tile per workgroup; gate/up one wave,
+        // down (K = expert_inter, shorter rows) its reduction shared by 2 waves
+        if constexpr (MODE == GM_SWIGLU) {
+            switch (MF) {
+            case 1: launch(gemm_kernel<WT, 1, 1, MODE, 1, 0, PK>, grid, dim3(64), 0, s, a); break;
+            case 2: launch(gemm_kernel<WT, 2, 1, MODE, 1, 0, PK>, grid, dim3(64), 0, s, a); break;
+            default: launch(gemm_kernel<WT, 4, 1, MODE, 1, 0, PK>, grid, dim3(64), 0, s, a); break;
+            }
+        } else if constexpr (MODE == GM_STORE) {
+            switch (MF) {
+            case 1: launch(gemm_kernel<WT, 1, 1, MODE, 2, 8, PK, true>, grid, dim3(128), 0, s, a); break;
+            case 2: launch(gemm_kernel<WT, 2, 1, MODE, 2, 4, PK, true>, grid, dim3(128), 0, s, a); break;
+            default: launch(gemm_kernel<WT, 4, 1, MODE, 2, 2, PK, true>, grid, dim3(128), 0, s, a); break;
+            }
         }
         return;
     }
@@ -275,6 +286,38 @@ void launch_gemm_big(int wt, int mode, bool packed, GemmArgs& a, hipStream_t s)
 }
 
 int rows_mf(int rows) { return rows <= 16 ? 1 : (rows <= 32 ? 2 : 4); }
+
+// Fused attention input (few rows): 8 waves split each column pair's
+// reduction; 5 steps per prefetch stage for one row fragment (one stage at
+// hidden 1280 bf16), fewer stages and, for four fragments, 4 waves (registers).
+constexpr int QKV_W = 8;
+
+template <int WT, bool PK, bool EMB>
+void launch_qkv_rope_t(int MF, const QkvArgs& a, dim3 grid, hipStream_t s)
+{
+    switch (MF) {
+    case 1: launch(qkv_rope_kernel<WT, 1, QKV_W, 5, PK, EMB>, grid, dim3(64 * QKV_W), 0, s, a); break;
+    case 2: launch(qkv_rope_kernel<WT, 2, QKV_W, 3, PK, EMB>, grid, dim3(64 * QKV_W), 0, s, a); break;
+    default: launch(qkv_rope_kernel<WT, 4, 4, 2, PK, EMB>, grid, dim3(256), 0, s, a); break;   // registers
+    }
+}
+
+void launch_qkv_rope(int wt, int MF, bool packed, bool embed, const QkvArgs& a, hipStream_t s)
+{
+    dim3 grid((unsigned)(cdiv(a.NT, 8) * 8 * a.MT));
+#define QKV_CASE(WT)                                                              \
+    if (packed) {                                                                 \
+        if (embed) launch_qkv_rope_t<WT, true, true>(MF, a, grid, s);             \
+        else launch_qkv_rope_t<WT, true, false>(MF, a, grid, s);                  \
+    } else {                                                                      \
+        if (embed) launch_qkv_rope_t<WT, false, true>(MF, a, grid, s);            \
+        else launch_qkv_rope_t<WT, false, false>(MF, a, grid, s);                 \
+    }
+    if (wt == SV_F32) { QKV_CASE(SV_F32) }
+    else if (wt == SV_BF16) { QKV_CASE(SV_BF16) }
+    else { QKV_CASE(SV_FP8) }
+#undef QKV_CASE
+}
 
 // K split: enough waves to cover the GPU, each split at least 4 reduction steps
 int pick_ksplit(long waves, int K, int step, int smax = KS_MAX)
@@ -552,13 +595,43 @@ int spec_verify_step(spec_verify_ctx* c, const spec_verify_weights* w, void* k_c
     ra.x_out = c->x;
     ra.h = c->h;
     ra.gain = w->layers[0].attn_norm;
-    if (bf) embed_norm_kernel<true><<<T, 1024, 0, s>>>(ra);
-    else embed_norm_kernel<false><<<T, 1024, 0, s>>>(ra);
-
     const int MFd = rows_mf(T);
     const int MTd = cdiv(T, 16 * MFd);
-    // rows >= 64: the large-row kernel (activation chunks staged in LDS)
+    // rows >= 64: the large-row kernel (activation chunks staged in LDS);
+    // fewer rows: the attention input (embedding + norm for the first layer,
+    // QKV, rotary, cache append) is one kernel
     const bool big = T >= 64 && wt != SV_F32;
+    if (big) {
+        if (bf) embed_norm_kernel<true><<<T, 1024, 0, s>>>(ra);
+        else embed_norm_kernel<false><<<T, 1024, 0, s>>>(ra);
+    }
+    QkvArgs qa;
+    memset(&qa, 0, sizeof(qa));
+    qa.X = c->h;
+    qa.embed = w->embed;
+    qa.gain = w->layers[0].attn_norm;
+    qa.committed = committed;
+    qa.drafts = drafts;
+    qa.ctx_in = ctx_in;
+    qa.seq_err = c->seq_err;
+    qa.err_word = c->err_word;
+    qa.x_out = c->x;
+    qa.rope = c->rope;
+    qa.q = c->q;
+    qa.kc = k_cache;
+    qa.vc = v_cache;
+    qa.V = k.vocab;
+    qa.cap = k.kv_capacity;
+    qa.K1 = K1;
+    qa.T = T;
+    qa.H = H;
+    qa.n_q = k.n_q_heads;
+    qa.n_kv = k.n_kv_heads;
+    qa.D = k.head_dim;
+    qa.L = L;
+    qa.MT = MTd;
+    qa.NT = (k.n_q_heads + 2 * k.n_kv_heads) * (k.head_dim / 32);
+    qa.eps = k.rms_eps;
     const int MTb = cdiv(T, 16 * BIG_MF);
     // dense GEMM (or the dense SwiGLU / argmax variants); returns the K split used
     // allow_split: largest K split the consumer accepts (0 or 1: none)
@@ -622,28 +695,34 @@ int spec_verify_step(spec_verify_ctx* c, const spec_verify_weights* w, void* k_c
         const spec_verify_layer& Lw = w->layers[l];
         // ---- attention half
         int ks;
-        {
+        if (!big) {
+            qa.W = Lw.w_qkv;
+            qa.ws = Lw.s_qkv;
+            qa.layer = l;
             ProfScope ps(c, SV_KC_QKV, s);
-            ks = dense_gemm(GM_STORE, c->h, H, QKV, H, Lw.w_qkv, Lw.s_qkv, c->parts, QKV, KS_MAX);
-        }
-        RopeArgs rp;
-        rp.qkv = c->parts;
-        rp.nsplit = ks;
-        rp.T = T;
-        rp.K1 = K1;
-        rp.n_q = k.n_q_heads;
-        rp.n_kv = k.n_kv_heads;
-        rp.D = k.head_dim;
-        rp.L = L;
-        rp.layer = l;
-        rp.cap = k.kv_capacity;
-        rp.ctx_in = ctx_in;
-        rp.seq_err = c->seq_err;
-        rp.rope = c->rope;
-        rp.q = c->q;
-        rp.kc = k_cache;
-        rp.vc = v_cache;
-        {
+            launch_qkv_rope(wt, MFd, packed, l == 0, qa, s);
+        } else {
+            {
+                ProfScope ps(c, SV_KC_QKV, s);
+                ks = dense_gemm(GM_STORE, c->h, H, QKV, H, Lw.w_qkv, Lw.s_qkv, c->parts, QKV, KS_MAX);
+            }
+            RopeArgs rp;
+            rp.qkv = c->parts;
+            rp.nsplit = ks;
+            rp.T = T;
+            rp.K1 = K1;
+            rp.n_q = k.n_q_heads;
+            rp.n_kv = k.n_kv_heads;
+            rp.D = k.head_dim;
+            rp.L = L;
+            rp.layer = l;
+            rp.cap = k.kv_capacity;
+            rp.ctx_in = ctx_in;
+            rp.seq_err = c->seq_err;
+            rp.rope = c->rope;
+            rp.q = c->q;
+            rp.kc = k_cache;
+            rp.vc = v_cache;
             dim3 grid(T, k.n_q_heads + 2 * k.n_kv_heads);
             if (bf) rope_append_kernel<true><<<grid, 64, 0, s>>>(rp);
             else rope_append_kernel<false><<<grid, 64, 0, s>>>(rp);
