@@ -89,6 +89,10 @@ __global__ __launch_bounds__(64) void attn_split_kernel(AttnArgs a)
         for (int d = 0; d < DF; d++) o[f][d] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     }
 
+    // a tile read by one workgroup only (QG == 1) is streamed past the caches;
+    // with several query groups per KV head the later readers hit in L2
+    const bool stream = a.QG == 1;
+    auto kvload = [&](const char* p) { return stream ? ldg16_stream(p) : ldg16(p); };
     for (int kt = c0; kt < c1; kt += KT) {
         const size_t toff = (size_t)(kt / KT) * TILE;
         // key tile (A operand of the score product): lane (slot l16, slice lg)
@@ -96,11 +100,11 @@ __global__ __launch_bounds__(64) void attn_split_kernel(AttnArgs a)
 #pragma unroll
         for (int blk = 0; blk < NB; blk++)
 #pragma unroll
-            for (int s = 0; s < DS; s++) kf[blk][s] = ldg16(kbase + toff + (size_t)(blk * DS + s) * 1024);
+            for (int s = 0; s < DS; s++) kf[blk][s] = kvload(kbase + toff + (size_t)(blk * DS + s) * 1024);
         // value tile (A operand of the output product): lane (channel 16 df + l16, keys KL lg ..)
         uint4 vf[DF];
 #pragma unroll
-        for (int d = 0; d < DF; d++) vf[d] = ldg16(vbase + toff + (size_t)d * 1024);
+        for (int d = 0; d < DF; d++) vf[d] = kvload(vbase + toff + (size_t)d * 1024);
 #pragma unroll
         for (int f = 0; f < QPW; f++) {
             float s[KL];
