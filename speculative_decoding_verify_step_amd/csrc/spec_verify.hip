@@ -243,12 +243,16 @@ void launch_big_m(int wt, const GemmArgs& a, dim3 grid, hipStream_t s)
     else launch(gemm_bigm_kernel<SV_FP8, BIG_MF, BIG_NF, MODE, PK>, grid, dim3(256), 0, s, a);
 }
 
-// Grouped (expert) GEMMs on the large-row kernel: MF row fragments per tile.
+// Grouped (expert) GEMMs on the large-row kernel: MF row fragments per tile,
+// one column fragment per wave (64-column workgroup tiles: twice the
+// workgroups of the dense tiles, measured 7-8% faster at 12-row experts).
+constexpr int GROUPED_NF = 1;
+
 template <int MODE, bool PK, int MF>
 void launch_grouped_mf(int wt, const GemmArgs& a, dim3 grid, hipStream_t s)
 {
-    if (wt == SV_BF16) launch(gemm_bigm_kernel<SV_BF16, MF, BIG_NF, MODE, PK>, grid, dim3(256), 0, s, a);
-    else launch(gemm_bigm_kernel<SV_FP8, MF, BIG_NF, MODE, PK>, grid, dim3(256), 0, s, a);
+    if (wt == SV_BF16) launch(gemm_bigm_kernel<SV_BF16, MF, GROUPED_NF, MODE, PK>, grid, dim3(256), 0, s, a);
+    else launch(gemm_bigm_kernel<SV_FP8, MF, GROUPED_NF, MODE, PK>, grid, dim3(256), 0, s, a);
 }
 
 template <int MODE, bool PK>
@@ -837,7 +841,7 @@ int spec_verify_step(spec_verify_ctx* c, const spec_verify_weights* w, void* k_c
             // few rows: one-wave tiles streaming weights (finer balance)
             const bool big_e = big && H % (BIG_CHUNK_STEPS * step) == 0 &&
                                I % (BIG_CHUNK_STEPS * step) == 0;
-            g.NT = big_e ? cdiv(I, 16 * 4 * BIG_NF) : cdiv(I, 16);
+            g.NT = big_e ? cdiv(I, 16 * 4 * GROUPED_NF) : cdiv(I, 16);
             g.out = c->act;
             g.ldo = I;
             {
@@ -860,7 +864,7 @@ int spec_verify_step(spec_verify_ctx* c, const spec_verify_weights* w, void* k_c
             d.w2_gstride = (long)H * I;
             d.s2_gstride = H;
             d.dual_off = 0;
-            d.NT = big_e ? cdiv(H, 16 * 4 * BIG_NF) : cdiv(H, 16);
+            d.NT = big_e ? cdiv(H, 16 * 4 * GROUPED_NF) : cdiv(H, 16);
             d.out = c->y;
             d.ldo = H;
             d.split_stride = 0;
