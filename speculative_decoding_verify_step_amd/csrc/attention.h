@@ -36,7 +36,10 @@ struct AttnArgs {
     float* mlpart;            // [B][n_q][K1][maxch][2]  (max in log2 units, sum)
 };
 
-template <bool BF, int QPW, int DH>
+// STREAM: the K/V tiles are read by this workgroup only (one query group per
+// KV head) and are loaded with streaming (nontemporal) loads; with several
+// query groups the later readers of a tile hit in L2, so normal loads stay.
+template <bool BF, int QPW, int DH, bool STREAM>
 __global__ __launch_bounds__(64) void attn_split_kernel(AttnArgs a)
 {
     constexpr int ESZ = BF ? 2 : 4;
@@ -89,10 +92,10 @@ __global__ __launch_bounds__(64) void attn_split_kernel(AttnArgs a)
         for (int d = 0; d < DF; d++) o[f][d] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     }
 
-    // a tile read by one workgroup only (QG == 1) is streamed past the caches;
-    // with several query groups per KV head the later readers hit in L2
-    const bool stream = a.QG == 1;
-    auto kvload = [&](const char* p) { return stream ? ldg16_stream(p) : ldg16(p); };
+    auto kvload = [&](const char* p) {
+        if constexpr (STREAM) return ldg16_stream(p);
+        else return ldg16(p);
+    };
     for (int kt = c0; kt < c1; kt += KT) {
         const size_t toff = (size_t)(kt / KT) * TILE;
         // key tile (A operand of the score product): lane (slot l16, slice lg)

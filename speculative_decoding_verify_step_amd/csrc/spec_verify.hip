@@ -291,6 +291,27 @@ void launch_gemm_big(int wt, int mode, bool packed, GemmArgs& a, hipStream_t s)
 
 int rows_mf(int rows) { return rows <= 16 ? 1 : (rows <= 32 ? 2 : 4); }
 
+template <bool BF, int DH, bool ST>
+void launch_attention_t(int QPW, dim3 grid, const AttnArgs& at, hipStream_t s)
+{
+    if (QPW == 2) launch(attn_split_kernel<BF, 2, DH, ST>, grid, dim3(64), 0, s, at);
+    else launch(attn_split_kernel<BF, 1, DH, ST>, grid, dim3(64), 0, s, at);
+}
+
+// split-KV attention; streaming K/V loads when each tile has one reader
+void launch_attention(bool bf, int D, int QPW, bool stream, dim3 grid, const AttnArgs& at, hipStream_t s)
+{
+#define ATT_CASE(BF, DH)                                                     \
+    if (stream) launch_attention_t<BF, DH, true>(QPW, grid, at, s);          \
+    else launch_attention_t<BF, DH, false>(QPW, grid, at, s);
+    if (bf) {
+        if (D == 128) { ATT_CASE(true, 128) } else { ATT_CASE(true, 64) }
+    } else {
+        if (D == 128) { ATT_CASE(false, 128) } else { ATT_CASE(false, 64) }
+    }
+#undef ATT_CASE
+}
+
 // Fused attention input (few rows): 8 waves split each column pair's
 // reduction; 5 steps per prefetch stage for one row fragment (one stage at
 // hidden 1280 bf16), fewer stages and, for four fragments, 4 waves (registers).
@@ -736,23 +757,7 @@ int spec_verify_step(spec_verify_ctx* c, const spec_verify_weights* w, void* k_c
         {
             ProfScope ps(c, SV_KC_ATTENTION, s);
             dim3 grid(c->att_maxch, k.n_kv_heads * c->att_QG, B);
-            if (bf) {
-                if (k.head_dim == 128) {
-                    if (c->att_QPW == 2) launch(attn_split_kernel<true, 2, 128>, grid, dim3(64), 0, s, at);
-                    else launch(attn_split_kernel<true, 1, 128>, grid, dim3(64), 0, s, at);
-                } else {
-                    if (c->att_QPW == 2) launch(attn_split_kernel<true, 2, 64>, grid, dim3(64), 0, s, at);
-                    else launch(attn_split_kernel<true, 1, 64>, grid, dim3(64), 0, s, at);
-                }
-            } else {
-                if (k.head_dim == 128) {
-                    if (c->att_QPW == 2) launch(attn_split_kernel<false, 2, 128>, grid, dim3(64), 0, s, at);
-                    else launch(attn_split_kernel<false, 1, 128>, grid, dim3(64), 0, s, at);
-                } else {
-                    if (c->att_QPW == 2) launch(attn_split_kernel<false, 2, 64>, grid, dim3(64), 0, s, at);
-                    else launch(attn_split_kernel<false, 1, 64>, grid, dim3(64), 0, s, at);
-                }
-            }
+            launch_attention(bf, k.head_dim, c->att_QPW, c->att_QG == 1, grid, at, s);
         }
         {
             int rows = B * k.n_q_heads * K1;
