@@ -214,8 +214,7 @@ __global__ __launch_bounds__(128) void attn_merge_kernel(AttnArgs a, void* out /
         float M = -INFINITY;
 #pragma unroll
         for (int i = 0; i < 16; i++) M = fmaxf(M, mv[i].x);
-#pragma unroll
-        for (int o = 32; o >= 1; o >>= 1) M = fmaxf(M, __shfl_xor(M, o, 64));
+        M = wave_max(M);
         float L = 0.f;
 #pragma unroll
         for (int i = 0; i < 16; i++) {

@@ -113,11 +113,67 @@ SV_DEV unsigned long long shfl_xor_u64(unsigned long long v, int m)
     return ((unsigned long long)hi << 32) | lo;
 }
 
+// Wave-wide reductions with DPP (row_shr 1, 2, 4, 8 inside each 16-lane row,
+// then row_bcast15 / row_bcast31 across rows, then a read of lane 63): no LDS
+// round trips (a __shfl_xor butterfly compiles to one ds_bpermute per step).
+// Fixed order, so deterministic; the result is returned in every lane.
+template <int CTRL, int RM>
+SV_DEV float dpp_f32(float old, float v)
+{
+    return __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(old), __float_as_int(v), CTRL, RM, 0xf, false));
+}
+
+template <int CTRL, int RM>
+SV_DEV uint32_t dpp_u32(uint32_t old, uint32_t v)
+{
+    return (uint32_t)__builtin_amdgcn_update_dpp((int)old, (int)v, CTRL, RM, 0xf, false);
+}
+
+enum { DPP_SHR1 = 0x111, DPP_SHR2 = 0x112, DPP_SHR4 = 0x114, DPP_SHR8 = 0x118,
+       DPP_BCAST15 = 0x142, DPP_BCAST31 = 0x143 };
+
+SV_DEV float lane63(float v) { return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63)); }
+
 SV_DEV float wave_sum(float v)
 {
-#pragma unroll
-    for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m, 64);
-    return v;
+    v += dpp_f32<DPP_SHR1, 0xf>(0.f, v);
+    v += dpp_f32<DPP_SHR2, 0xf>(0.f, v);
+    v += dpp_f32<DPP_SHR4, 0xf>(0.f, v);
+    v += dpp_f32<DPP_SHR8, 0xf>(0.f, v);
+    v += dpp_f32<DPP_BCAST15, 0xa>(0.f, v);
+    v += dpp_f32<DPP_BCAST31, 0xc>(0.f, v);
+    return lane63(v);
+}
+
+SV_DEV float wave_max(float v)
+{
+    v = fmaxf(v, dpp_f32<DPP_SHR1, 0xf>(-INFINITY, v));
+    v = fmaxf(v, dpp_f32<DPP_SHR2, 0xf>(-INFINITY, v));
+    v = fmaxf(v, dpp_f32<DPP_SHR4, 0xf>(-INFINITY, v));
+    v = fmaxf(v, dpp_f32<DPP_SHR8, 0xf>(-INFINITY, v));
+    v = fmaxf(v, dpp_f32<DPP_BCAST15, 0xa>(-INFINITY, v));
+    v = fmaxf(v, dpp_f32<DPP_BCAST31, 0xc>(-INFINITY, v));
+    return lane63(v);
+}
+
+template <int CTRL, int RM>
+SV_DEV unsigned long long dpp_max_u64(unsigned long long v)
+{
+    const uint32_t lo = dpp_u32<CTRL, RM>(0u, (uint32_t)v), hi = dpp_u32<CTRL, RM>(0u, (uint32_t)(v >> 32));
+    return umax64(v, ((unsigned long long)hi << 32) | lo);
+}
+
+SV_DEV unsigned long long wave_max_u64(unsigned long long v)
+{
+    v = dpp_max_u64<DPP_SHR1, 0xf>(v);
+    v = dpp_max_u64<DPP_SHR2, 0xf>(v);
+    v = dpp_max_u64<DPP_SHR4, 0xf>(v);
+    v = dpp_max_u64<DPP_SHR8, 0xf>(v);
+    v = dpp_max_u64<DPP_BCAST15, 0xa>(v);
+    v = dpp_max_u64<DPP_BCAST31, 0xc>(v);
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)v, 63);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(v >> 32), 63);
+    return ((unsigned long long)hi << 32) | lo;
 }
 
 SV_DEV float silu_f32(float z) { return z / (1.0f + __expf(-z)); }

@@ -261,8 +261,7 @@ SV_DEV void router_select(const RowArgs& a, int t, float (&p)[4], unsigned long 
     float m = -INFINITY;
 #pragma unroll
     for (int q = 0; q < 4; q++) m = fmaxf(m, p[q]);
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) m = fmaxf(m, __shfl_xor(m, o, 64));
+    m = wave_max(m);
     float sum = 0.f;
 #pragma unroll
     for (int q = 0; q < 4; q++) {
@@ -284,7 +283,7 @@ SV_DEV void router_select(const RowArgs& a, int t, float (&p)[4], unsigned long 
     for (int q = 0; q < NQ; q++) {
         const int e = lane + 64 * q;
         int r = 0;
-#pragma unroll 4
+#pragma unroll 8
         for (int j = 0; j < E; j += 2) {     // E is a multiple of 4
             const ulonglong2 kk = *reinterpret_cast<const ulonglong2*>(kbuf + j);
             r += (kk.x > key[q]) | ((kk.x == key[q]) & (j < e));
@@ -545,10 +544,74 @@ __global__ __launch_bounds__(1024) void residual_norm_kernel(RowArgs a)
     }
 }
 
+// Permutation for few assignments (T*topk <= 64, T <= BM: every expert's rows
+// fit one tile), by one wave without barriers; the same result as
+// permute_rows.  Lane i holds assignment i = (t = i / k, rank): its expert's
+// offset is the number of assignments with a lower expert, its rank inside the
+// expert the number of earlier assignments with the same expert (row order);
+// the expert's tile index is the number of distinct lower experts (a bitmask
+// of the experts present).  The assignments are read from shared memory four
+// at a time (register compares, no cross-lane round trips).
+SV_DEV void permute_rows_wave(const RowArgs& a, const unsigned short* sel, unsigned* mask)
+{
+    const int lane = threadIdx.x & 63, T = a.T, k = a.topk, A = T * k;
+    if (lane < 8) mask[lane] = 0u;
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+    const bool act = lane < A;
+    const int e = act ? sel[lane] : 0x7fffffff;
+    if (act) atomicOr(&mask[e >> 5], 1u << (e & 31));
+    int off = 0, rank = 0, cnt = 0;
+#pragma unroll 4
+    for (int j0 = 0; j0 < A; j0 += 4) {
+        const uint2 q = *reinterpret_cast<const uint2*>(sel + j0);
+        const int ej[4] = {(int)(q.x & 0xffffu), (int)(q.x >> 16), (int)(q.y & 0xffffu), (int)(q.y >> 16)};
+#pragma unroll
+        for (int u = 0; u < 4; u++) {
+            const int j = j0 + u;
+            if (j < A) {
+                off += ej[u] < e;
+                rank += (ej[u] == e) & (j < lane);
+                cnt += ej[u] == e;
+            }
+        }
+    }
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+    const bool first = act && rank == 0;
+    int tile = 0, distinct = 0;
+#pragma unroll
+    for (int w = 0; w < 8; w++) {
+        const unsigned mw = mask[w];
+        distinct += __popc(mw);
+        if (act) tile += w < (e >> 5) ? __popc(mw) : (w == (e >> 5) ? __popc(mw & ((1u << (e & 31)) - 1u)) : 0);
+    }
+    if (act) {
+        const int slot = off + rank;
+        a.slot_out[lane] = slot;
+        a.perm_tok[slot] = lane / k;
+    }
+    if (first && tile < a.max_tiles) {
+        a.tiles[3 * tile] = e;
+        a.tiles[3 * tile + 1] = off;
+        a.tiles[3 * tile + 2] = cnt;
+    }
+    // shared experts: every token, one tile each (T <= BM)
+    for (int i = lane; i < a.n_shared * T; i += 64) a.perm_tok[A + i] = i % T;
+    if (lane < a.n_shared) {
+        const int ti = distinct + lane;
+        if (ti < a.max_tiles) {
+            a.tiles[3 * ti] = a.E + lane;
+            a.tiles[3 * ti + 1] = A + lane * T;
+            a.tiles[3 * ti + 2] = T;
+        }
+    }
+    if (lane == 0) *a.n_tiles = min(distinct + a.n_shared, a.max_tiles);
+}
+
 // Routing, second half (one 1024-thread workgroup): when the router was
 // shared out (S > 1), each wave selects the experts of rows w, w + 16, ...
 // from the published logits; otherwise the rows' selections are read back.
-// Then the permutation and tile list of every row.
+// Then the permutation and tile list of every row (by one wave when the
+// assignments are few).
 __global__ __launch_bounds__(1024) void route_finish_kernel(RowArgs a)
 {
     __shared__ __align__(16) char lds[81920];
@@ -568,6 +631,12 @@ __global__ __launch_bounds__(1024) void route_finish_kernel(RowArgs a)
         for (int i = tid; i < T * k; i += 1024) sel[i] = (unsigned short)a.sel[i];
     }
     __syncthreads();
+    if (T * k <= 64 && T <= a.BM) {
+        // the mask lives in the space permute_rows would use for its totals
+        unsigned* mask = reinterpret_cast<unsigned*>(lds + (((size_t)T * (E + k) * 2 + 15) & ~(size_t)15));
+        if (tid < 64) permute_rows_wave(a, sel, mask);
+        return;
+    }
     permute_rows(a, lds);
 }
 
@@ -701,8 +770,7 @@ __global__ __launch_bounds__(1024) void accept_kernel(AcceptArgs a)
 #pragma unroll
                 for (int u = 0; u < KB; u++) best = umax64(best, v[u]);
             }
-#pragma unroll
-            for (int m = 32; m >= 1; m >>= 1) best = umax64(best, shfl_xor_u64(best, m));
+            best = wave_max_u64(best);
             if (lane == 0) part[j][pi] = best;
         }
     }
@@ -748,8 +816,7 @@ __global__ __launch_bounds__(256) void logits_keys_kernel(const float* logits, i
     unsigned long long best = 0ull;
     for (int n = nt * 1024 + threadIdx.x; n < min(V, (nt + 1) * 1024); n += 256)
         best = umax64(best, argmax_key(logits[(size_t)t * V + n], (uint32_t)n));
-#pragma unroll
-    for (int m = 32; m >= 1; m >>= 1) best = umax64(best, shfl_xor_u64(best, m));
+    best = wave_max_u64(best);
     if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = best;
     __syncthreads();
     if (threadIdx.x == 0)
