@@ -84,6 +84,7 @@ struct spec_verify_ctx {
     int T_max = 0, K1 = 0, QKV = 0, QD = 0;
     bool bf = true;
     int att_CH = 256, att_maxch = 1, att_QPW = 1, att_QG = 1;
+    bool att_stream = false;
     // workspace
     std::vector<void*> allocs;
     float* x = nullptr;
@@ -470,6 +471,12 @@ int spec_verify_init(const spec_verify_config* cfg, spec_verify_ctx** out)
         while (ch < 512 && work / ch > 2 * 2048) ch *= 2;
         c->att_CH = ch;
         c->att_maxch = cdiv(k.kv_capacity, ch);
+        // streaming K/V loads only when every tile has one reader (one query
+        // group per KV head) and the caches are far larger than the 256 MB
+        // Infinity Cache; a smaller cache stays resident from step to step
+        const double kv_bytes = 2.0 * k.max_batch * k.n_layers * k.n_kv_heads * (double)k.kv_capacity *
+                                k.head_dim * (k.kv_dtype == SV_F32 ? 4 : 2);
+        c->att_stream = c->att_QG == 1 && kv_bytes > 1024.0 * 1024 * 1024;
         if (c->att_maxch > ATT_MAXCH_CAP) {
             delete c;
             return fail(SV_ERR_UNSUPPORTED, "kv_capacity too large for the attention plan");
@@ -757,7 +764,7 @@ int spec_verify_step(spec_verify_ctx* c, const spec_verify_weights* w, void* k_c
         {
             ProfScope ps(c, SV_KC_ATTENTION, s);
             dim3 grid(c->att_maxch, k.n_kv_heads * c->att_QG, B);
-            launch_attention(bf, k.head_dim, c->att_QPW, c->att_QG == 1, grid, at, s);
+            launch_attention(bf, k.head_dim, c->att_QPW, c->att_stream, grid, at, s);
         }
         {
             int rows = B * k.n_q_heads * K1;
