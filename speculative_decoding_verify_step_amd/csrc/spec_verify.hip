@@ -468,7 +468,7 @@ int spec_verify_init(const spec_verify_config* cfg, spec_verify_ctx** out)
     {
         long work = (long)k.max_batch * k.n_kv_heads * c->att_QG * k.kv_capacity;
         int ch = 64;
-        while (ch < 512 && work / ch > 2 * 2048) ch *= 2;
+        while (ch < 1024 && work / ch > 2 * 2048) ch *= 2;
         c->att_CH = ch;
         c->att_maxch = cdiv(k.kv_capacity, ch);
         // streaming K/V loads only when every tile has one reader (one query
