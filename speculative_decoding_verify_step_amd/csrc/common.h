@@ -30,33 +30,35 @@ SV_DEV uint32_t pack_bf16x2(float lo, float hi)
 // One OCP e4m3fn byte -> the fp32 with the same value.  The 7 magnitude bits
 // are placed at the bottom of the fp32 exponent field and the top of its
 // mantissa, which reads as 2^(e-127) * 1.mmm (or 2^-126 * 0.mmm when e = 0);
-// multiplying by 2^120 rebases the exponent from bias 127 to bias 7.  Exact.
+// multiplying by 2^120 rebases the exponent from bias 127 to bias 7.  Exact;
+// the two NaN codes (magnitude 0x7f) give NaN.
 SV_DEV float e4m3_to_f32(uint32_t c)
 {
     float f = __uint_as_float(((c & 0x7fu) << 20) | ((c & 0x80u) << 24));
-    return f * 0x1p120f;
+    return (c & 0x7fu) == 0x7fu ? __builtin_nanf("") : f * 0x1p120f;
 }
 
-// Two e4m3fn bytes (bits 0-7 and 8-15 of w) -> two packed bf16 (exact: every
-// e4m3fn value has at most 4 significant bits).
+// Two e4m3fn bytes (bits 0-7 and 8-15 of w, or 16-31 with HI) -> two packed
+// bf16.  gfx950 converts OCP fp8 in one instruction; with a unit scale the
+// result is exact (every e4m3fn value has at most 4 significant bits) and the
+// NaN codes stay NaN.
+template <bool HI>
 SV_DEV uint32_t e4m3x2_to_bf16x2(uint32_t w)
 {
-    uint32_t lo = __float_as_uint(e4m3_to_f32(w & 0xffu));
-    uint32_t hi = __float_as_uint(e4m3_to_f32((w >> 8) & 0xffu));
-    return (lo >> 16) | (hi & 0xffff0000u);
+    return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, HI));
 }
 
 // 16 e4m3fn bytes -> 16 bf16 as two 16-byte operands (elements 0-7, 8-15).
 SV_DEV void e4m3x16_to_bf16(uint4 w, uint4& lo, uint4& hi)
 {
-    lo.x = e4m3x2_to_bf16x2(w.x);
-    lo.y = e4m3x2_to_bf16x2(w.x >> 16);
-    lo.z = e4m3x2_to_bf16x2(w.y);
-    lo.w = e4m3x2_to_bf16x2(w.y >> 16);
-    hi.x = e4m3x2_to_bf16x2(w.z);
-    hi.y = e4m3x2_to_bf16x2(w.z >> 16);
-    hi.z = e4m3x2_to_bf16x2(w.w);
-    hi.w = e4m3x2_to_bf16x2(w.w >> 16);
+    lo.x = e4m3x2_to_bf16x2<false>(w.x);
+    lo.y = e4m3x2_to_bf16x2<true>(w.x);
+    lo.z = e4m3x2_to_bf16x2<false>(w.y);
+    lo.w = e4m3x2_to_bf16x2<true>(w.y);
+    hi.x = e4m3x2_to_bf16x2<false>(w.z);
+    hi.y = e4m3x2_to_bf16x2<true>(w.z);
+    hi.z = e4m3x2_to_bf16x2<false>(w.w);
+    hi.w = e4m3x2_to_bf16x2<true>(w.w);
 }
 
 // ------------------------------------------------------------------- MFMA
