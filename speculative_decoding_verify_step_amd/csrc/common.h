@@ -73,6 +73,17 @@ SV_DEV f32x4_t mma_bf16(uint4 a, uint4 b, f32x4_t c)
                                                    __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
 }
 
+// 32x32 output tiles (16-step reduction), fp32 accumulate.  Operand lane l
+// supplies row l%32 of A (column l%32 of B) and reduction elements
+// 8*(l/32) .. +7 of its 16-byte slice; register r of lane l holds output row
+// 8*(r/4) + 4*(l/32) + r%4 of column l%32.
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+SV_DEV f32x16_t mma32_bf16(uint4 a, uint4 b, f32x16_t c)
+{
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                   __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
+}
+
 // four 16x16x4 fp32 products, element e of each lane's 16-byte slice in step e
 SV_DEV f32x4_t mma_f32x4(uint4 a, uint4 b, f32x4_t c)
 {

@@ -490,8 +490,11 @@ __global__ __launch_bounds__(256) void gemm_bigm_kernel(GemmArgs a)
         for (int f = 0; f < NFT; f++) acc[m][f] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
     uint4 wcur[CS][NFT], wnext[CS][NFT], stage[PPW];
-    xload(kb, stage);
+    // weights first: the wait for the staged activations then also covers
+    // them, so no load is still counted when the loop starts (a pending load
+    // on entry would make every iteration wait for the next chunk's loads)
     wload(kb, wcur);
+    xload(kb, stage);
 #pragma unroll
     for (int i = 0; i < PPW; i++)
         if (staged(i)) xs[0][wave * PPW + i][lane] = stage[i];
@@ -537,5 +540,255 @@ __global__ __launch_bounds__(256) void gemm_bigm_kernel(GemmArgs a)
         gemm_epilogue<WT, MF, NF, MODE, 4>(a, acc, row0, nrows, ncol0, nt, sc, fvalid, red);
     } else {
         gemm_epilogue<WT, MF, NF, MODE, 4>(a, acc, row0, nrows, ncol0, nt, sc, fvalid, nullptr);
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Wide large-row variant: dense GEMMs with 64 .. 256 rows and bf16 or fp8
+// weights in the tiled16 layout, on 32x32x16 MFMA tiles.  The activation
+// chunk read from shared memory per product is what limits the large-row
+// kernel above (one 1 KiB fragment per 16 columns); here a wave owns 32*MW
+// rows x 32*NW columns, so every activation fragment read from LDS feeds NW
+// 32-column products (half the LDS bytes per flop of a 32-column wave), and
+// the WAVES waves of a workgroup sit side by side in columns sharing one
+// staged chunk.  SwiGLU: the first NW/2 fragments are gate columns, the
+// others the matching up columns.
+//
+// Reduction mapping.  A tiled16 piece holds 16 weight rows x SK elements as
+// 64 16-byte slots (slot 16*g + r: row r, elements KL*g ..); one 16-byte
+// load per lane takes row l%32 of a 32-row fragment from the piece pair of
+// its two 16-row blocks, slot group g = 2u + l/32 (u = 0, 1), and yields XU
+// MFMA operands (fp8: two, widened).  Operand (u, h) of lane l therefore
+// carries elements KL*(2u + l/32) + 8h .. +7 of the step, and the activation
+// operand staged for it carries the same elements of row l%32: every
+// reduction index is used exactly once, in a fixed order.
+//
+// Staging: each thread loads 16-byte segments of activation rows and stores
+// each where its operand lane reads it; chunks are double-buffered with one
+// barrier per chunk, weights are loaded one chunk ahead into registers.
+template <int WT, int MW, int NW, int MODE, int WAVES>
+__global__ __launch_bounds__(64 * WAVES) void gemm_wide_kernel(GemmArgs a)
+{
+    static_assert(WT == SV_BF16 || WT == SV_FP8, "bf16 or fp8 weights");
+    static_assert(MODE != GM_SWIGLU || NW % 2 == 0, "gate/up fragment pairs");
+    constexpr int WESZ = (WT == SV_FP8) ? 1 : 2;
+    constexpr int KL = 16 / WESZ;                // weight elements per 16-byte slot
+    constexpr int SK = 4 * KL;                   // elements per tiled16 piece
+    constexpr int XU = (WT == SV_FP8) ? 2 : 1;   // operands per 16-byte weight load
+    constexpr int CS = 2;                        // steps per chunk
+    constexpr int KC = CS * SK;                  // chunk length
+    constexpr int BM = 32 * MW;
+    constexpr int NWO = (MODE == GM_SWIGLU) ? NW / 2 : NW;   // output column fragments
+    constexpr int PIECES = MW * CS * 2 * XU;     // 1 KiB activation operands per chunk
+    constexpr int RSEG = KC / 8;                 // 16-byte segments of a row per chunk
+    constexpr int SPT = BM * RSEG / (64 * WAVES);
+    static_assert(SPT * 64 * WAVES == BM * RSEG, "staging split");
+    __shared__ uint4 xs[2][PIECES][64];
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int l32 = lane & 31, lh = lane >> 5;
+    const int id = blockIdx.x, xcd = id & 7, q = id >> 3;
+    const int mt = q % a.MT;
+    const int nt = (q / a.MT) * 8 + xcd;
+    if (nt >= a.NT) return;
+    const int row0 = mt * BM;
+    const int nrows = min(BM, a.M - row0);
+    if (nrows <= 0) return;
+    const char* Wb = (const char*)a.W;
+    const float* sc = a.ws;
+    const int K = a.K;
+    const int kspan = K / a.ksplit;
+    const int kb = blockIdx.y * kspan;
+    const int nchunk = kspan / KC;
+    const int ncol0 = (nt * WAVES + wave) * 32 * NWO;
+    const int nrb = a.N / 16;                    // 16-row weight blocks
+
+    // weight fragment bases: lane row l32 of the fragment, slot group lh
+    const char* wrow[NW];
+    bool fvalid[NWO];
+#pragma unroll
+    for (int f = 0; f < NW; f++) {
+        const int fo = (MODE == GM_SWIGLU) ? f % NWO : f;
+        const int n0 = ncol0 + 32 * fo;
+        const bool ok = n0 < a.N;
+        if (f < NWO) fvalid[f] = ok;
+        int rb = ok ? min(n0 / 16 + (l32 >> 4), nrb - 1) : 0;
+        if (MODE == GM_SWIGLU && f >= NWO) rb += a.dual_off / 16;
+        wrow[f] = Wb + (size_t)rb * K * 16 * WESZ + (size_t)(16 * lh + (l32 & 15)) * 16;
+    }
+    // activation segments this thread stages: segment it = tid + 64 WAVES j
+    const char* xsrc[SPT];
+    int xdst[SPT];
+#pragma unroll
+    for (int j = 0; j < SPT; j++) {
+        // a wave covers 16 rows x 4 segments: each 16-lane write phase then
+        // stores 16 rows (distinct LDS banks), each row read is 64 bytes
+        const int it = tid + 64 * WAVES * j, wi = it >> 6, li = it & 63;
+        const int m = 16 * (wi / (RSEG / 4)) + (li & 15), qs = 4 * (wi % (RSEG / 4)) + (li >> 4);
+        const int s = qs / (SK / 8), qq = qs % (SK / 8);
+        const int sl = qq / XU, h = qq % XU;      // slot of the step, operand half
+        const int u = sl >> 1, g = sl & 1;
+        const int piece = (((m >> 5) * CS + s) * 2 + u) * XU + h;
+        xdst[j] = piece * 64 + 32 * g + (m & 31);
+        const int r = row0 + min(m, nrows - 1);
+        xsrc[j] = (const char*)a.X + ((size_t)r * a.ldx + (size_t)s * SK + (size_t)qq * 8) * 2;
+    }
+    uint4* xsf = &xs[0][0][0];
+    auto xload = [&](int k, uint4 (&st)[SPT]) {
+#pragma unroll
+        for (int j = 0; j < SPT; j++) st[j] = ldg16(xsrc[j] + (size_t)k * 2);
+    };
+    auto xstore = [&](int buf, const uint4 (&st)[SPT]) {
+#pragma unroll
+        for (int j = 0; j < SPT; j++) xsf[buf * PIECES * 64 + xdst[j]] = st[j];
+    };
+    auto wload = [&](int k, uint4 (&w)[CS][NW][2]) {
+#pragma unroll
+        for (int s = 0; s < CS; s++)
+#pragma unroll
+            for (int f = 0; f < NW; f++)
+#pragma unroll
+                for (int u = 0; u < 2; u++)
+                    w[s][f][u] = ldg16(wrow[f] + (size_t)((k + s * SK) / SK) * 1024 + u * 512);
+    };
+
+    f32x16_t acc[MW][NW];
+#pragma unroll
+    for (int m = 0; m < MW; m++)
+#pragma unroll
+        for (int f = 0; f < NW; f++)
+#pragma unroll
+            for (int r = 0; r < 16; r++) acc[m][f][r] = 0.f;
+
+    uint4 wcur[CS][NW][2], wnext[CS][NW][2], stage[SPT];
+    wload(kb, wcur);         // weights first (see the large-row kernel)
+    xload(kb, stage);
+    xstore(0, stage);
+    __syncthreads();
+    for (int c = 0; c < nchunk; c++) {
+        const int buf = c & 1;
+        const bool more = c + 1 < nchunk;
+        if (more) {
+            const int kn = kb + (c + 1) * KC;
+            xload(kn, stage);
+            wload(kn, wnext);
+        }
+        const uint4* xb = xsf + buf * PIECES * 64 + lane;
+#pragma unroll
+        for (int s = 0; s < CS; s++)
+#pragma unroll
+            for (int u = 0; u < 2; u++) {
+                WOp<WT> wo[NW];
+#pragma unroll
+                for (int f = 0; f < NW; f++) wo[f] = wprep<WT>(wcur[s][f][u]);
+#pragma unroll
+                for (int h = 0; h < XU; h++)
+#pragma unroll
+                    for (int m = 0; m < MW; m++) {
+                        const uint4 xf = xb[((((m * CS + s) * 2 + u) * XU) + h) * 64];
+#pragma unroll
+                        for (int f = 0; f < NW; f++) acc[m][f] = mma32_bf16(wo[f].v[h], xf, acc[m][f]);
+                    }
+            }
+        if (more) {
+            xstore(buf ^ 1, stage);
+#pragma unroll
+            for (int s = 0; s < CS; s++)
+#pragma unroll
+                for (int f = 0; f < NW; f++)
+#pragma unroll
+                    for (int u = 0; u < 2; u++) wcur[s][f][u] = wnext[s][f][u];
+        }
+        __syncthreads();
+    }
+
+    // epilogue: lane holds rows row0 + 32 m + l32, columns n0 + 8 j + 4 lh + e
+    // (register 4 j + e) of each fragment
+    if constexpr (MODE == GM_STORE) {
+        float* out = (float*)a.out + (size_t)blockIdx.y * a.split_stride;
+#pragma unroll
+        for (int f = 0; f < NW; f++) {
+            if (!fvalid[f]) continue;
+#pragma unroll
+            for (int j = 0; j < 4; j++) {
+                const int n = ncol0 + 32 * f + 8 * j + 4 * lh;
+                if (n >= a.N) continue;
+                float s4[4] = {1.f, 1.f, 1.f, 1.f};
+                if constexpr (WT == SV_FP8) {
+#pragma unroll
+                    for (int e = 0; e < 4; e++) s4[e] = sc[n + e];
+                }
+#pragma unroll
+                for (int m = 0; m < MW; m++) {
+                    const int r = 32 * m + l32;
+                    if (r >= nrows) continue;
+                    *reinterpret_cast<float4*>(out + (size_t)(row0 + r) * a.ldo + n) =
+                        make_float4(acc[m][f][4 * j] * s4[0], acc[m][f][4 * j + 1] * s4[1],
+                                    acc[m][f][4 * j + 2] * s4[2], acc[m][f][4 * j + 3] * s4[3]);
+                }
+            }
+        }
+    } else if constexpr (MODE == GM_SWIGLU) {
+#pragma unroll
+        for (int f = 0; f < NWO; f++) {
+            if (!fvalid[f]) continue;
+#pragma unroll
+            for (int j = 0; j < 4; j++) {
+                const int n = ncol0 + 32 * f + 8 * j + 4 * lh;
+                if (n >= a.N) continue;
+                float gs[4] = {1.f, 1.f, 1.f, 1.f}, us[4] = {1.f, 1.f, 1.f, 1.f};
+                if constexpr (WT == SV_FP8) {
+#pragma unroll
+                    for (int e = 0; e < 4; e++) { gs[e] = sc[n + e]; us[e] = sc[a.dual_off + n + e]; }
+                }
+#pragma unroll
+                for (int m = 0; m < MW; m++) {
+                    const int r = 32 * m + l32;
+                    if (r >= nrows) continue;
+                    float v[4];
+#pragma unroll
+                    for (int e = 0; e < 4; e++)
+                        v[e] = silu_f32(acc[m][f][4 * j + e] * gs[e]) * (acc[m][NWO + f][4 * j + e] * us[e]);
+                    *reinterpret_cast<uint2*>((uint16_t*)a.out + (size_t)(row0 + r) * a.ldo + n) =
+                        make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
+                }
+            }
+        }
+    } else {   // GM_ARGMAX: per row, the largest key over the workgroup's columns
+        unsigned long long* red = reinterpret_cast<unsigned long long*>(xsf);
+        static_assert(sizeof(xs) >= WAVES * BM * sizeof(unsigned long long), "reduction space");
+#pragma unroll
+        for (int m = 0; m < MW; m++) {
+            const int r = 32 * m + l32;
+            unsigned long long best = 0ull;
+#pragma unroll
+            for (int f = 0; f < NW; f++) {
+                if (!fvalid[f]) continue;
+#pragma unroll
+                for (int j = 0; j < 4; j++) {
+                    const int n = ncol0 + 32 * f + 8 * j + 4 * lh;
+                    if (n >= a.N) continue;
+                    float v[4];
+#pragma unroll
+                    for (int e = 0; e < 4; e++) {
+                        v[e] = acc[m][f][4 * j + e];
+                        if constexpr (WT == SV_FP8) v[e] *= sc[n + e];
+                        best = umax64(best, argmax_key(v[e], (uint32_t)(n + e)));
+                    }
+                    if (a.dbg && r < nrows)
+                        *reinterpret_cast<float4*>(a.dbg + (size_t)(row0 + r) * a.dbg_ld + n) =
+                            make_float4(v[0], v[1], v[2], v[3]);
+                }
+            }
+            best = umax64(best, shfl_xor_u64(best, 32));
+            if (lh == 0) red[wave * BM + r] = best;
+        }
+        __syncthreads();
+        for (int r = tid; r < nrows; r += 64 * WAVES) {
+            unsigned long long b = red[r];
+#pragma unroll
+            for (int w2 = 1; w2 < WAVES; w2++) b = umax64(b, red[w2 * BM + r]);
+            a.keys[(size_t)nt * a.key_ld + row0 + r] = b;
+        }
     }
 }
