@@ -319,7 +319,8 @@ int rows_mf(int rows) { return rows <= 16 ? 1 : (rows <= 32 ? 2 : 4); }
 template <bool BF, int DH, bool ST>
 void launch_attention_t(int QPW, dim3 grid, const AttnArgs& at, hipStream_t s)
 {
-    if (QPW == 2) launch(attn_split_kernel<BF, 2, DH, ST>, grid, dim3(64), 0, s, at);
+    if (QPW == 4) launch(attn_split_kernel<BF, 4, DH, ST>, grid, dim3(64), 0, s, at);
+    else if (QPW == 2) launch(attn_split_kernel<BF, 2, DH, ST>, grid, dim3(64), 0, s, at);
     else launch(attn_split_kernel<BF, 1, DH, ST>, grid, dim3(64), 0, s, at);
 }
 
@@ -487,12 +488,15 @@ int spec_verify_init(const spec_verify_config* cfg, spec_verify_ctx** out)
     int G = k.n_q_heads / k.n_kv_heads;
     int R = c->K1 * G;
     int QF = cdiv(R, 16);
-    c->att_QPW = QF >= 2 ? 2 : 1;
+    // more query fragments per wave reuse each loaded K/V tile more often:
+    // dense GQA verify (128 rows per KV head) 78 -> 62 us per layer with four
+    c->att_QPW = QF >= 4 ? 4 : (QF >= 2 ? 2 : 1);
     c->att_QG = cdiv(QF, c->att_QPW);
     {
         long work = (long)k.max_batch * k.n_kv_heads * c->att_QG * k.kv_capacity;
         int ch = 64;
-        while (ch < 1024 && work / ch > 2 * 2048) ch *= 2;
+        const long waves_target = c->att_QPW >= 4 ? 2048 : 2 * 2048;   // busier waves: fewer of them
+        while (ch < 1024 && work / ch > waves_target) ch *= 2;
         c->att_CH = ch;
         c->att_maxch = cdiv(k.kv_capacity, ch);
         // streaming K/V loads only when every tile has one reader (one query
