@@ -178,71 +178,90 @@ __global__ __launch_bounds__(64) void attn_split_kernel(AttnArgs a)
 
 // Merge the chunk partials of one (sequence, query head, position) row in
 // chunk order and write the attention output row in the activation type.
-// 128 threads per row, thread d owns channel d (D <= 128).  The partial
-// outputs of the first CB chunks are loaded together with the chunk (max,
-// sum) pairs, so one memory round trip follows the context-length read; wave
-// 0 forms the chunk weights exp2(m_c - M) in shared memory.
-template <bool BF>
-__global__ __launch_bounds__(128) void attn_merge_kernel(AttnArgs a, void* out /* [T][n_q*D] */)
+// One wave merges two rows, a half-wave each; lane i of a half owns channels
+// 4i .. 4i+3 (D/4 lanes) and chunk weights i, i + 32, ...  The partial
+// outputs of the first CB chunks (16-byte loads, indices clamped so that the
+// loads carry no conditions) are issued together with the chunk (max, sum)
+// pairs, so one memory round trip follows the context-length read.  CB and
+// NI (= ceil(maxch / 32)) are chosen from the chunk count at launch.
+SV_DEV float half_max(float v)
 {
-    constexpr int CB = 32;                           // chunks per batch of loads
-    __shared__ float wgt[1024];
-    __shared__ float red[2];
-    const int row = blockIdx.x;                     // ((b * n_q + hq) * K1 + j)
-    const int K1 = a.K1;
+#pragma unroll
+    for (int m = 16; m >= 1; m >>= 1) v = fmaxf(v, __shfl_xor(v, m, 64));
+    return v;
+}
+
+SV_DEV float half_sum(float v)
+{
+#pragma unroll
+    for (int m = 16; m >= 1; m >>= 1) v += __shfl_xor(v, m, 64);   // fixed pairing order
+    return v;
+}
+
+template <bool BF, int CB, int NI>
+__global__ __launch_bounds__(64) void attn_merge_kernel(AttnArgs a, void* out /* [T][n_q*D] */, int rows)
+{
+    __shared__ float wgt[2][32 * NI];
+    const int lane = threadIdx.x, half = lane >> 5, l32 = lane & 31;
+    const int row = min(blockIdx.x * 2 + half, rows - 1);   // ((b * n_q + hq) * K1 + j)
+    const bool live = blockIdx.x * 2 + half < rows;
+    const int K1 = a.K1, D = a.D;
     const int j = row % K1;
     const int hq = (row / K1) % a.n_q;
     const int b = row / (K1 * a.n_q);
     const int ctx = min(max(a.ctx_in[b], 0), a.cap - K1);
-    const int nch = (ctx + K1 + a.CH - 1) / a.CH;   // <= maxch <= 1024
+    const int nch = (ctx + K1 + a.CH - 1) / a.CH;   // 1 .. maxch <= 32 NI
     const float2* __restrict__ ml = reinterpret_cast<const float2*>(a.mlpart) + (size_t)row * a.maxch;
-    const float* __restrict__ op = a.opart + (size_t)row * a.maxch * a.D;
-    const int tid = threadIdx.x, lane = tid & 63;
-    const int d = tid;
-    const bool dok = d < a.D;
-    // loads without conditions (clamped indices; the extra values are unused)
-    const int dc = min(d, a.D - 1);
-    float ov[CB];
-#pragma unroll
-    for (int c = 0; c < CB; c++) ov[c] = op[(size_t)min(c, nch - 1) * a.D + dc];
-    if (tid < 64) {
-        float2 mv[16];                               // chunks lane + 64 i
-#pragma unroll
-        for (int i = 0; i < 16; i++) mv[i] = ml[min(lane + 64 * i, nch - 1)];
-#pragma unroll
-        for (int i = 0; i < 16; i++) mv[i] = lane + 64 * i < nch ? mv[i] : make_float2(-INFINITY, 0.f);
-        float M = -INFINITY;
-#pragma unroll
-        for (int i = 0; i < 16; i++) M = fmaxf(M, mv[i].x);
-        M = wave_max(M);
-        float L = 0.f;
-#pragma unroll
-        for (int i = 0; i < 16; i++) {
-            const int c = lane + 64 * i;
-            const float wc = (mv[i].x == -INFINITY) ? 0.f : exp2f(mv[i].x - M);
-            if (c < nch) wgt[c] = wc;
-            L += wc * mv[i].y;
-        }
-        L = wave_sum(L);
-        if (lane == 0) red[0] = L;
-    }
-    __syncthreads();
-    const float inv = 1.f / red[0];
-    float acc = 0.f;
+    const float* __restrict__ op = a.opart + (size_t)row * a.maxch * D;
+    const int cg = min(l32, D / 4 - 1);             // channel group (lanes past D/4 repeat the last)
+    float4 ov[CB];
 #pragma unroll
     for (int c = 0; c < CB; c++)
-        if (c < nch) acc += wgt[c] * ov[c];
+        ov[c] = *reinterpret_cast<const float4*>(op + (size_t)min(c, nch - 1) * D + 4 * cg);
+    float2 mv[NI];
+#pragma unroll
+    for (int i = 0; i < NI; i++) mv[i] = ml[min(l32 + 32 * i, nch - 1)];
+#pragma unroll
+    for (int i = 0; i < NI; i++) mv[i] = l32 + 32 * i < nch ? mv[i] : make_float2(-INFINITY, 0.f);
+    float M = -INFINITY;
+#pragma unroll
+    for (int i = 0; i < NI; i++) M = fmaxf(M, mv[i].x);
+    M = half_max(M);
+    float L = 0.f;
+#pragma unroll
+    for (int i = 0; i < NI; i++) {
+        const float wc = (mv[i].x == -INFINITY) ? 0.f : exp2f(mv[i].x - M);
+        wgt[half][l32 + 32 * i] = wc;
+        L += wc * mv[i].y;
+    }
+    L = half_sum(L);
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    const float* w = wgt[half];
+    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+    for (int c = 0; c < CB; c++) {
+        const float wc = c < nch ? w[c] : 0.f;
+        acc.x += wc * ov[c].x; acc.y += wc * ov[c].y; acc.z += wc * ov[c].z; acc.w += wc * ov[c].w;
+    }
     for (int c0 = CB; c0 < nch; c0 += CB) {
 #pragma unroll
-        for (int c = 0; c < CB; c++) ov[c] = op[(size_t)min(c0 + c, nch - 1) * a.D + dc];
-#pragma unroll
         for (int c = 0; c < CB; c++)
-            if (c0 + c < nch) acc += wgt[c0 + c] * ov[c];
+            ov[c] = *reinterpret_cast<const float4*>(op + (size_t)min(c0 + c, nch - 1) * D + 4 * cg);
+#pragma unroll
+        for (int c = 0; c < CB; c++) {
+            const float wc = c0 + c < nch ? w[c0 + c] : 0.f;
+            acc.x += wc * ov[c].x; acc.y += wc * ov[c].y; acc.z += wc * ov[c].z; acc.w += wc * ov[c].w;
+        }
     }
-    if (!dok) return;
-    const float v = acc * inv;
+    if (!live || l32 >= D / 4) return;
+    const float inv = 1.f / L;
     const size_t t = (size_t)b * K1 + j;
-    const size_t o = t * (size_t)a.n_q * a.D + (size_t)hq * a.D + d;
-    if constexpr (BF) ((uint16_t*)out)[o] = (uint16_t)f32_to_bf16_bits(v);
-    else ((float*)out)[o] = v;
+    const size_t o = t * (size_t)a.n_q * D + (size_t)hq * D + 4 * cg;
+    if constexpr (BF) {
+        *reinterpret_cast<uint2*>((uint16_t*)out + o) =
+            make_uint2(pack_bf16x2(acc.x * inv, acc.y * inv), pack_bf16x2(acc.z * inv, acc.w * inv));
+    } else {
+        *reinterpret_cast<float4*>((float*)out + o) = make_float4(acc.x * inv, acc.y * inv, acc.z * inv, acc.w * inv);
+    }
 }

@@ -314,6 +314,25 @@ void launch_gemm_wide(int wt, int mode, GemmArgs& a, hipStream_t s)
     else launch_wide_t<SV_FP8>(mode, a, grid, s);
 }
 
+// merge: CB partials per load batch, NI = ceil(maxch / 32) chunk weights per lane
+template <bool BF>
+void launch_merge_t(int maxch, const AttnArgs& at, void* out, int rows, hipStream_t s)
+{
+    dim3 grid((unsigned)cdiv(rows, 2)), blk(64);
+    if (maxch <= 8) launch(attn_merge_kernel<BF, 8, 1>, grid, blk, 0, s, at, out, rows);
+    else if (maxch <= 16) launch(attn_merge_kernel<BF, 16, 1>, grid, blk, 0, s, at, out, rows);
+    else if (maxch <= 32) launch(attn_merge_kernel<BF, 32, 1>, grid, blk, 0, s, at, out, rows);
+    else if (maxch <= 64) launch(attn_merge_kernel<BF, 32, 2>, grid, blk, 0, s, at, out, rows);
+    else if (maxch <= 256) launch(attn_merge_kernel<BF, 32, 8>, grid, blk, 0, s, at, out, rows);
+    else launch(attn_merge_kernel<BF, 32, 32>, grid, blk, 0, s, at, out, rows);
+}
+
+void launch_merge(bool bf, int maxch, const AttnArgs& at, void* out, int rows, hipStream_t s)
+{
+    if (bf) launch_merge_t<true>(maxch, at, out, rows, s);
+    else launch_merge_t<false>(maxch, at, out, rows, s);
+}
+
 int rows_mf(int rows) { return rows <= 16 ? 1 : (rows <= 32 ? 2 : 4); }
 
 template <bool BF, int DH, bool ST>
@@ -801,11 +820,7 @@ int spec_verify_step(spec_verify_ctx* c, const spec_verify_weights* w, void* k_c
             dim3 grid(c->att_maxch, k.n_kv_heads * c->att_QG, B);
             launch_attention(bf, k.head_dim, c->att_QPW, c->att_stream, grid, at, s);
         }
-        {
-            int rows = B * k.n_q_heads * K1;
-            if (bf) attn_merge_kernel<true><<<rows, 128, 0, s>>>(at, c->o);
-            else attn_merge_kernel<false><<<rows, 128, 0, s>>>(at, c->o);
-        }
+        launch_merge(bf, c->att_maxch, at, c->o, B * k.n_q_heads * K1, s);
         // the MoE consumer (residual + norm + router) takes at most 4 splits
         ks = dense_gemm(GM_STORE, c->o, QD, H, QD, Lw.w_o, Lw.s_o, c->parts, H,
                         k.ffn_kind == SV_FFN_MOE ? 4 : KS_MAX);
