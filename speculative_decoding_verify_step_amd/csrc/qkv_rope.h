@@ -100,102 +100,30 @@ __global__ __launch_bounds__(64 * W) void qkv_rope_kernel(QkvArgs a)
         return (tok < 0 || tok >= a.V) ? 0 : tok;
     };
 
-    if constexpr (EMBED) {
-        for (int r = tid; r < BM; r += NTH) rflag[r] = 0u;
-        for (int i = tid; i < H; i += NTH) gs[i] = a.gain[i];
-        __syncthreads();
-        // validity of every row's sequence: one thread per (row, token of its block)
-        for (int idx = tid; idx < nrows * K1; idx += NTH) {
-            const int r = idx / K1, i = idx % K1, b = (row0 + r) / K1;
-            const int ti = i == 0 ? a.committed[b] : a.drafts[(size_t)b * K + i - 1];
-            unsigned e = (ti < 0 || ti >= a.V) ? (unsigned)SV_DEV_BAD_TOKEN : 0u;
-            if (i == 0) {
-                const int c = a.ctx_in[b];
-                if (c < 0 || c + K1 > a.cap) e |= SV_DEV_CAPACITY;
-            }
-            if (e) atomicOr(&rflag[r], e);
-        }
-        // sum of squares of each row: TPR threads per row, 16-byte slices in a
-        // fixed assignment, then a butterfly inside the TPR lanes
-        constexpr int EPC = 16 / AESZ, NB = 8;
-        const int r = tid / TPR, sl = tid % TPR;
-        float ss = 0.f;
-        if (r < nrows) {
-            const int t = row0 + r;
-            const char* er = (const char*)a.embed + (size_t)row_token(t) * H * AESZ;
-            float* xo = a.x_out + (size_t)t * H;
-            for (int c00 = sl * EPC; c00 < H; c00 += TPR * EPC * NB) {
-                uint4 v[NB];
-#pragma unroll
-                for (int u = 0; u < NB; u++) v[u] = ldg16(er + (size_t)min(c00 + u * TPR * EPC, H - EPC) * AESZ);
-#pragma unroll
-                for (int u = 0; u < NB; u++) {
-                    const int c = c00 + u * TPR * EPC;
-                    if (c >= H) break;
-                    float f[8];
-                    const uint32_t wd[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
-                    if constexpr (BF) {
-#pragma unroll
-                        for (int q = 0; q < 4; q++) { f[2 * q] = bf16_bits_to_f32(wd[q] & 0xffffu); f[2 * q + 1] = bf16_bits_to_f32(wd[q] >> 16); }
-                    } else {
-#pragma unroll
-                        for (int q = 0; q < 4; q++) f[q] = __uint_as_float(wd[q]);
-                    }
-#pragma unroll
-                    for (int e = 0; e < EPC; e++) ss += f[e] * f[e];
-                    if (nt == 0) {   // the residual stream, once per row
-#pragma unroll
-                        for (int e = 0; e < EPC; e += 4)
-                            *reinterpret_cast<float4*>(xo + c + e) = make_float4(f[e], f[e + 1], f[e + 2], f[e + 3]);
-                    }
-                }
-            }
-        }
-#pragma unroll
-        for (int o = TPR / 2; o >= 1; o >>= 1) ss += __shfl_xor(ss, o, 64);
-        __syncthreads();   // rflag complete
-        if (r < nrows && sl == 0) {
-            rs[r] = rsqrtf(ss / (float)H + a.eps);
-            const int t = row0 + r;
-            if (nt == 0 && t % K1 == 0) {   // the sequence's flags, once
-                const unsigned e = rflag[r];
-                a.seq_err[t / K1] = (int)e;
-                if (e) atomicOr(a.err_word, e);
-            }
-        }
-        __syncthreads();
-    }
-
-    // activation rows of this lane, one per row fragment
+    // activation rows of this lane (one per row fragment) and the epilogue
+    // inputs: position and rotary (cos, sin) of each of the lane's rows for
+    // channels i0 .. i0 + 3.  All of these loads, the embedding loads of the
+    // normalisation pass and the first activation stage are issued before
+    // anything waits, so the prologue costs two memory round trips (token,
+    // embedding row) and one barrier.
     const char* xrow[MF];
-    float rsd[MF];
-#pragma unroll
-    for (int m = 0; m < MF; m++) {
-        int r = 16 * m + l16;
-        const bool ok = r < nrows;
-        r = ok ? r : 0;
-        if constexpr (EMBED) {
-            xrow[m] = (const char*)a.embed + ((size_t)row_token(row0 + r) * H + (size_t)lg * KL) * AESZ;
-            rsd[m] = rs[r];
-        } else {
-            xrow[m] = (const char*)a.X + ((size_t)(row0 + r) * H + (size_t)lg * KL) * AESZ;
-            rsd[m] = 1.f;
-        }
-    }
-    // epilogue inputs, loaded now: position and rotary (cos, sin) of each of the
-    // lane's rows, for channels i0 .. i0 + 3
     const int i0 = 16 * a16 + 4 * lg;
     const bool rot = hh < a.n_q + a.n_kv;
     int pos[MF];
     float4 csa[MF], csb[MF];
 #pragma unroll
     for (int m = 0; m < MF; m++) {
-        const int t = row0 + min(16 * m + l16, nrows - 1), b = t / K1, j = t % K1;
+        const int r = min(16 * m + l16, nrows - 1), t = row0 + r, b = t / K1, j = t % K1;
+        if constexpr (EMBED) xrow[m] = (const char*)a.embed + ((size_t)row_token(t) * H + (size_t)lg * KL) * AESZ;
+        else xrow[m] = (const char*)a.X + ((size_t)t * H + (size_t)lg * KL) * AESZ;
         pos[m] = min(max(a.ctx_in[b], 0), a.cap - K1) + j;
         const float4* cp = reinterpret_cast<const float4*>(a.rope + (size_t)pos[m] * half + (rot ? i0 : 0));
         csa[m] = cp[0];
         csb[m] = cp[1];
     }
+    float rsd[MF];   // 1 / rms of the lane's rows (first layer; set after the prologue)
+#pragma unroll
+    for (int m = 0; m < MF; m++) rsd[m] = 1.f;
     uint4 xA[U][MF][XU], xB[U][MF][XU];
     auto xload = [&](int k, uint4 (&x)[U][MF][XU]) {
 #pragma unroll
@@ -258,6 +186,79 @@ __global__ __launch_bounds__(64 * W) void qkv_rope_kernel(QkvArgs a)
     };
     constexpr int STAGE = U * SK;
     if (kb < ke) xload(kb, xA);
+
+    if constexpr (EMBED) {
+        // per row r (TPR threads each): the sequence's validity (this thread's
+        // share of its K1 tokens, and the context length), the sum of squares
+        // over 16-byte slices in a fixed assignment, then butterflies inside
+        // the TPR lanes; the gain is copied to shared memory meanwhile
+        constexpr int EPC = 16 / AESZ, NB = 8, GPT = 8192 / NTH;
+        const int r = tid / TPR, sl = tid % TPR;
+        const bool rv = r < nrows;
+        const int t = row0 + (rv ? r : 0), b = t / K1;
+        unsigned e = 0u;
+        if (sl == 0) {
+            const int c = a.ctx_in[b];
+            if (c < 0 || c + K1 > a.cap) e |= SV_DEV_CAPACITY;
+        }
+        for (int i = sl; i < K1; i += TPR) {
+            const int ti = i == 0 ? a.committed[b] : a.drafts[(size_t)b * K + i - 1];
+            if (ti < 0 || ti >= a.V) e |= SV_DEV_BAD_TOKEN;
+        }
+        float gv[GPT];
+#pragma unroll
+        for (int i = 0; i < GPT; i++) gv[i] = a.gain[min(tid + NTH * i, H - 1)];
+        float ss = 0.f;
+        if (rv) {
+            const char* er = (const char*)a.embed + (size_t)row_token(t) * H * AESZ;
+            float* xo = a.x_out + (size_t)t * H;
+            for (int c00 = sl * EPC; c00 < H; c00 += TPR * EPC * NB) {
+                uint4 v[NB];
+#pragma unroll
+                for (int u = 0; u < NB; u++) v[u] = ldg16(er + (size_t)min(c00 + u * TPR * EPC, H - EPC) * AESZ);
+#pragma unroll
+                for (int u = 0; u < NB; u++) {
+                    const int c = c00 + u * TPR * EPC;
+                    if (c >= H) break;
+                    float f[8];
+                    const uint32_t wd[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
+                    if constexpr (BF) {
+#pragma unroll
+                        for (int q = 0; q < 4; q++) { f[2 * q] = bf16_bits_to_f32(wd[q] & 0xffffu); f[2 * q + 1] = bf16_bits_to_f32(wd[q] >> 16); }
+                    } else {
+#pragma unroll
+                        for (int q = 0; q < 4; q++) f[q] = __uint_as_float(wd[q]);
+                    }
+#pragma unroll
+                    for (int q = 0; q < EPC; q++) ss += f[q] * f[q];
+                    if (nt == 0) {   // the residual stream, once per row
+#pragma unroll
+                        for (int q = 0; q < EPC; q += 4)
+                            *reinterpret_cast<float4*>(xo + c + q) = make_float4(f[q], f[q + 1], f[q + 2], f[q + 3]);
+                    }
+                }
+            }
+        }
+#pragma unroll
+        for (int o = TPR / 2; o >= 1; o >>= 1) {
+            ss += __shfl_xor(ss, o, 64);
+            e |= (unsigned)__shfl_xor((int)e, o, 64);
+        }
+#pragma unroll
+        for (int i = 0; i < GPT; i++)
+            if (tid + NTH * i < H) gs[tid + NTH * i] = gv[i];
+        if (rv && sl == 0) {
+            rs[r] = rsqrtf(ss / (float)H + a.eps);
+            rflag[r] = e;
+            if (nt == 0 && t % K1 == 0) {   // the sequence's flags, once
+                a.seq_err[b] = (int)e;
+                if (e) atomicOr(a.err_word, e);
+            }
+        }
+        __syncthreads();
+#pragma unroll
+        for (int m = 0; m < MF; m++) rsd[m] = rs[min(16 * m + l16, nrows - 1)];
+    }
     for (int k = kb; k < ke; k += 2 * STAGE) {
         if (k + STAGE < ke) { wload(k + STAGE, wB); xload(k + STAGE, xB); }
         compute(k, wA, xA);
