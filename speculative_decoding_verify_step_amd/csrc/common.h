@@ -189,4 +189,65 @@ SV_DEV unsigned long long wave_max_u64(unsigned long long v)
     return ((unsigned long long)hi << 32) | lo;
 }
 
+template <int CTRL, int RM>
+SV_DEV unsigned long long dpp_or_u64(unsigned long long v)
+{
+    const uint32_t lo = dpp_u32<CTRL, RM>(0u, (uint32_t)v), hi = dpp_u32<CTRL, RM>(0u, (uint32_t)(v >> 32));
+    return v | (((unsigned long long)hi << 32) | lo);
+}
+
+SV_DEV unsigned long long wave_or_u64(unsigned long long v)
+{
+    v = dpp_or_u64<DPP_SHR1, 0xf>(v);
+    v = dpp_or_u64<DPP_SHR2, 0xf>(v);
+    v = dpp_or_u64<DPP_SHR4, 0xf>(v);
+    v = dpp_or_u64<DPP_SHR8, 0xf>(v);
+    v = dpp_or_u64<DPP_BCAST15, 0xa>(v);
+    v = dpp_or_u64<DPP_BCAST31, 0xc>(v);
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)v, 63);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(v >> 32), 63);
+    return ((unsigned long long)hi << 32) | lo;
+}
+
+// Routing implied by the selections (few assignments: A = T * topk <= 64,
+// E <= 64), without a permutation pass.  The permuted order is the stable
+// counting sort of the assignments by expert: assignment j with expert e sits
+// at slot (number of assignments with a smaller expert) + (number of earlier
+// assignments with expert e); tile i is the i-th expert present in ascending
+// order, then one tile per shared expert over all T rows.  `sv` is lane l's
+// selection (any value for l >= A).
+struct ImpliedTile { int group, row0, nrows; unsigned long long members; };
+
+SV_DEV ImpliedTile implied_tile(int sv, int A, int T, int E, int n_shared, int tile)
+{
+    const int lane = threadIdx.x & 63;
+    const bool act = lane < A;
+    const unsigned long long present = wave_or_u64(act ? 1ull << sv : 0ull);
+    const int distinct = __popcll(present);
+    ImpliedTile r{0, 0, 0, 0ull};
+    if (tile < distinct) {
+        const bool bit = (present >> lane) & 1ull;
+        const int pre = __popcll(present & ((1ull << lane) - 1ull));
+        const int e = __builtin_ctzll(__ballot(bit && pre == tile));
+        r.group = e;
+        r.row0 = __popcll(__ballot(act && sv < e));
+        r.members = __ballot(act && sv == e);
+        r.nrows = __popcll(r.members);
+    } else if (tile < distinct + n_shared) {
+        r.group = E + (tile - distinct);
+        r.row0 = A + (tile - distinct) * T;
+        r.nrows = T;
+    }
+    return r;
+}
+
+// slot of assignment j (uniform) given every lane's selection
+SV_DEV int implied_slot(int sv, int A, int j)
+{
+    const int lane = threadIdx.x & 63;
+    const bool act = lane < A;
+    const int e = __builtin_amdgcn_readlane(sv, j);
+    return __popcll(__ballot(act && sv < e)) + __popcll(__ballot(act && sv == e && lane < j));
+}
+
 SV_DEV float silu_f32(float z) { return z / (1.0f + __expf(-z)); }

@@ -52,6 +52,9 @@ struct GemmArgs {
     int dual_off;           // SWIGLU: row offset of the "up" rows
     const int* tiles;       // grouped: [max_tiles][3] = (group, row0, nrows); null = dense
     const int* n_tiles;     // grouped: device count of valid tiles
+    const int* sel;         // grouped, few rows: tiles implied by the selections [T][topk]
+                            // (then tiles/n_tiles/gather are unused; see implied_tile)
+    int sel_T, sel_k, sel_E, sel_S;
     int MT;                 // row tiles in the grid (dense: ceil(M / BM); grouped: max tiles)
     int NT;                 // column tiles (16*NF*WAVES columns each)
     void* out;              // STORE: fp32 [ksplit][rows][ldo]; SWIGLU: act [rows][ldo]
@@ -235,7 +238,24 @@ __global__ __launch_bounds__(64 * WAVES) void gemm_kernel(GemmArgs a)
     if (nt >= a.NT) return;
 
     int group = 0, row0, nrows;
-    if (a.tiles) {
+    int xtok = -1;   // implied tiles: activation row of this lane's row l16 (MF == 1)
+    if (a.sel) {
+        const int A = a.sel_T * a.sel_k;
+        const int sv = min(max(a.sel[min(lane, A - 1)], 0), a.sel_E - 1);
+        const ImpliedTile it = implied_tile(sv, A, a.sel_T, a.sel_E, a.sel_S, mt);
+        group = it.group;
+        row0 = it.row0;
+        nrows = it.nrows;
+        if (group < a.sel_E) {
+            // row i of an expert tile is its i-th member assignment: send each
+            // member's token to lane i (non-members to lane 63, never a row)
+            const bool mem = (it.members >> lane) & 1ull;
+            const int dst = mem ? __popcll(it.members & ((1ull << lane) - 1ull)) : 63;
+            xtok = __builtin_amdgcn_ds_permute(4 * dst, lane / a.sel_k);
+        } else {
+            xtok = l16;   // shared expert: row i is token i
+        }
+    } else if (a.tiles) {
         if (mt >= *a.n_tiles) return;
         group = a.tiles[3 * mt];
         row0 = a.tiles[3 * mt + 1];
@@ -298,7 +318,9 @@ __global__ __launch_bounds__(64 * WAVES) void gemm_kernel(GemmArgs a)
     for (int m = 0; m < MF; m++) {
         int r = 16 * m + l16;
         r = (r < nrows) ? row0 + r : row0;
-        int xr = a.gather ? a.gather[r] : r;
+        int xr;
+        if (a.sel) xr = a.gather ? __shfl(xtok, min(16 * m + l16, nrows - 1), 64) : r;   // (MF == 1)
+        else xr = a.gather ? a.gather[r] : r;
         xrow[m] = (const char*)a.X + ((size_t)xr * a.ldx + (size_t)lg * KL) * AESZ;
     }
 

@@ -71,6 +71,7 @@ struct RowArgs {
     int* perm_tok;              // [T*topk + n_shared*T] token of every permuted row
     int* tiles;                 // [max_tiles][3] = (group, first row, rows)
     int* n_tiles;               // [1]
+    int implied;                // combine: slots implied by `sel` (few assignments, see implied_slot)
 };
 
 // token block + embedding gather + RMSNorm (one 1024-thread workgroup per
@@ -438,12 +439,17 @@ __global__ __launch_bounds__(1024) void residual_norm_kernel(RowArgs a)
     int slot[8];
     float gate[8];
     if constexpr (MOE) {
+        if (a.implied) {
+            const int A = T * a.topk;
+            const int sv = min(max(a.sel[min(tid & 63, A - 1)], 0), a.E - 1);
 #pragma unroll
-        for (int r = 0; r < 8; r++) {
-            const int rc = min(r, a.topk - 1);
-            slot[r] = a.slot[t * a.topk + rc];
-            gate[r] = a.gate[t * a.topk + rc];
+            for (int r = 0; r < 8; r++) slot[r] = implied_slot(sv, A, t * a.topk + min(r, a.topk - 1));
+        } else {
+#pragma unroll
+            for (int r = 0; r < 8; r++) slot[r] = a.slot[t * a.topk + min(r, a.topk - 1)];
         }
+#pragma unroll
+        for (int r = 0; r < 8; r++) gate[r] = a.gate[t * a.topk + min(r, a.topk - 1)];
 #pragma unroll
         for (int r = 0; r < 8; r++) gate[r] = r < a.topk ? gate[r] : 0.f;
     }
@@ -611,7 +617,7 @@ SV_DEV void permute_rows_wave(const RowArgs& a, const unsigned short* sel, unsig
 // shared out (S > 1), each wave selects the experts of rows w, w + 16, ...
 // from the published logits; otherwise the rows' selections are read back.
 // Then the permutation and tile list of every row (by one wave when the
-// assignments are few).
+// assignments are few), unless the consumers derive them from the selections.
 __global__ __launch_bounds__(1024) void route_finish_kernel(RowArgs a)
 {
     __shared__ __align__(16) char lds[81920];
@@ -630,6 +636,7 @@ __global__ __launch_bounds__(1024) void route_finish_kernel(RowArgs a)
     } else {
         for (int i = tid; i < T * k; i += 1024) sel[i] = (unsigned short)a.sel[i];
     }
+    if (a.implied) return;   // the consumers derive tiles and slots from the selections
     __syncthreads();
     if (T * k <= 64 && T <= a.BM) {
         // the mask lives in the space permute_rows would use for its totals

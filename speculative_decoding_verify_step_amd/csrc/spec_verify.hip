@@ -834,6 +834,9 @@ int spec_verify_step(spec_verify_ctx* c, const spec_verify_weights* w, void* k_c
             // row when rows are few; the updated residual goes to x2 since a
             // row's workgroups all read x), then selection + permutation
             const int E = k.n_experts, tk = k.top_k;
+            // few assignments: the grouped GEMMs and the combine derive tiles and
+            // slots from the selections (no permutation pass)
+            const bool implied = !big && T <= 16 && T * tk <= 64 && E <= 64;
             const int S = (E % 16 == 0 && E >= 32 && T <= 64) ? E / 16 : 1;
             const int avg_rows = std::max(1, T * tk / E);
             const int BMe = 16 * rows_mf(avg_rows);
@@ -861,7 +864,8 @@ int spec_verify_step(spec_verify_ctx* c, const spec_verify_weights* w, void* k_c
                 if (bf) residual_norm_kernel<true, false, true, 4><<<grid, 1024, 0, s>>>(ra);
                 else residual_norm_kernel<false, false, true, 4><<<grid, 1024, 0, s>>>(ra);
             }
-            route_finish_kernel<<<1, 1024, 0, s>>>(ra);
+            ra.implied = implied;
+            if (!implied || S > 1) route_finish_kernel<<<1, 1024, 0, s>>>(ra);   // selection only when implied
         } else {
             ra.x_out = c->x;
             if (bf) residual_norm_kernel<true, false><<<T, 1024, 0, s>>>(ra);
@@ -873,8 +877,9 @@ int spec_verify_step(spec_verify_ctx* c, const spec_verify_weights* w, void* k_c
         float* dbg_h = c->dbg_hidden ? c->dbg_hidden + (size_t)l * T * H : nullptr;
         if (k.ffn_kind == SV_FFN_MOE) {
             const int E = k.n_experts, tk = k.top_k, S = k.n_shared, I = k.expert_inter;
+            const bool implied = !big && T <= 16 && T * tk <= 64 && E <= 64;   // as in the routing
             const int avg_rows = std::max(1, T * tk / E);
-            const int MFe = rows_mf(avg_rows);
+            const int MFe = implied ? 1 : rows_mf(avg_rows);
             const int BMe = 16 * MFe;
             const int max_tiles = std::min(E, T * tk) + (T * tk) / BMe + S * cdiv(T, BMe) + 1;
 
@@ -898,6 +903,11 @@ int spec_verify_step(spec_verify_ctx* c, const spec_verify_weights* w, void* k_c
             g.dual_off = I;
             g.tiles = c->tiles;
             g.n_tiles = c->n_tiles;
+            g.sel = implied ? c->sel : nullptr;
+            g.sel_T = T;
+            g.sel_k = tk;
+            g.sel_E = E;
+            g.sel_S = S;
             g.MT = max_tiles;
             // many rows (T >= 64): 4-wave tiles sharing an LDS activation tile;
             // few rows: one-wave tiles streaming weights (finer balance)
