@@ -198,7 +198,8 @@ def pack_weights(weights: dict, stream=None) -> dict:
         L2 = dict(L)
         for name in GEMM_MATRICES:
             if L.get(name) is not None:
-                L2[name] = pack_matrix(L[name], stream)
+                # an empty stack (no shared experts) stays empty: nothing to pack
+                L2[name] = pack_matrix(L[name], stream) if L[name].numel() else L[name]
         out["layers"].append(L2)
     out["lm_head"] = pack_matrix(weights["lm_head"], stream)
     out["layout"] = "tiled16"

@@ -94,6 +94,18 @@ def test_moe_small_shapes(H, batch, n_experts, top_k):
     _verify_case(H, cfg, label=f"moe_small_shapes_b{batch}_e{n_experts}_k{top_k}")
 
 
+@pytest.mark.parametrize("batch,n_experts,top_k,n_shared", [(4, 32, 4, 2), (1, 64, 8, 0)])
+def test_moe_few_assignments(H, batch, n_experts, top_k, n_shared):
+    """Few assignments (T <= 16, T * top_k <= 64, at most 64 experts): the
+    grouped GEMMs and the combine take expert tiles and slots from the
+    selections.  Covers all 64 lanes holding an assignment (16 rows x top-4),
+    two shared experts, and none."""
+    cfg = workloads.scaled(workloads.get_config("moe_b1"), n_layers=2, hidden=256, n_q=2, n_kv=2,
+                           n_experts=n_experts, expert_inter=128, top_k=top_k, n_shared=n_shared,
+                           vocab=2048, batch=batch, ctx=("uniform", 1, 200), norm_gain_std=0.2)
+    _verify_case(H, cfg, label=f"moe_few_b{batch}_e{n_experts}_k{top_k}_s{n_shared}")
+
+
 def test_dense_fp8_gqa_scaled(H):
     """Block drafts (K = 31) on the dense GQA decoder with e4m3 weights:
     4 query heads per KV head, 128 query rows per KV head."""
