@@ -14,17 +14,18 @@ typedef float f32x4_t __attribute__((ext_vector_type(4)));
 SV_DEV float bf16_bits_to_f32(uint32_t b) { return __uint_as_float(b << 16); }
 
 // fp32 -> bf16 bits, round to nearest even; NaN stays a quiet NaN.
+// fp32 -> bf16, round to nearest even (one v_cvt_pk_bf16_f32 per pair on
+// gfx950); NaN stays NaN.
 SV_DEV uint32_t f32_to_bf16_bits(float f)
 {
-    uint32_t u = __float_as_uint(f);
-    if ((u & 0x7fffffffu) > 0x7f800000u) return 0x7fc0u;
-    u += 0x7fffu + ((u >> 16) & 1u);
-    return u >> 16;
+    return __builtin_bit_cast(uint16_t, (__bf16)f);
 }
 
 SV_DEV uint32_t pack_bf16x2(float lo, float hi)
 {
-    return f32_to_bf16_bits(lo) | (f32_to_bf16_bits(hi) << 16);
+    typedef __bf16 bf16x2_v __attribute__((ext_vector_type(2)));
+    const bf16x2_v v = {(__bf16)lo, (__bf16)hi};
+    return __builtin_bit_cast(uint32_t, v);
 }
 
 // One OCP e4m3fn byte -> the fp32 with the same value.  The 7 magnitude bits
