@@ -307,16 +307,14 @@ SV_DEV void router_select(const RowArgs& a, int t, float (&p)[4], unsigned long 
 }
 
 // Router permutation over all T rows (the selections already in shared
-// memory, `lds` layout below): a stable
-// counting sort of the T*topk assignments by expert -- assignment (t, r) of
-// expert e goes to offset[e] + (number of rows t' < t that also chose e) --
-// followed by the shared-expert rows (every token, in order), and the list of
-// BM-row tiles per group for the grouped GEMMs.  Run by one workgroup,
-// deterministic:
-//   * flags[t][e] = 1 if row t chose e;
-//   * 4 threads per expert each scan a quarter of the rows, then add the
-//     totals of the earlier quarters (exclusive ranks within the expert);
-//   * one wave scans the per-group tile counts; each group writes its tiles.
+// memory, `lds` layout below): a stable counting sort of the T*topk
+// assignments by expert -- assignment (t, r) of expert e goes to offset[e] +
+// (number of rows t' < t that also chose e) -- followed by the shared-expert
+// rows (every token, in order), and the list of BM-row tiles per group for
+// the grouped GEMMs.  Run by one workgroup, deterministic:
+//   * each wave takes whole experts and ranks their tokens with a wave vote
+//     over 64 tokens at a time (no serial scans);
+//   * one wave scans the per-group row and tile counts; each group writes its tiles.
 // `lds`: T (E + topk) 2 bytes (16-aligned) + 6.2 KB of shared memory.
 SV_DEV unsigned short* perm_sel_lds(const RowArgs& a, char* lds)
 {
@@ -326,37 +324,28 @@ SV_DEV unsigned short* perm_sel_lds(const RowArgs& a, char* lds)
 SV_DEV void permute_rows(const RowArgs& a, char* lds)
 {
     const int T = a.T, E = a.E, k = a.topk, tid = threadIdx.x, NT = blockDim.x;
-    unsigned short* cnt = reinterpret_cast<unsigned short*>(lds);   // [T][E] flags -> ranks
+    const int lane = tid & 63, wave = tid >> 6, NW = NT >> 6;
+    unsigned short* rank = reinterpret_cast<unsigned short*>(lds);   // [T][k] rank inside the expert
     unsigned short* sel = perm_sel_lds(a, lds);                       // [T][k], filled by the caller
-    int* total = reinterpret_cast<int*>(lds + (((size_t)T * (E + k) * 2 + 15) & ~(size_t)15));   // [E][4]
+    int* total = reinterpret_cast<int*>(lds + (((size_t)T * (E + k) * 2 + 15) & ~(size_t)15));   // [E]
     int* offset = total + 1024;                                       // [E + 1]
     int* tile0 = offset + 260;                                        // [E + n_shared + 1]
-    for (int i = tid; i < T * E; i += NT) cnt[i] = 0;
-    __syncthreads();
-    for (int i = tid; i < T * k; i += NT) cnt[(i / k) * E + sel[i]] = 1;
-    __syncthreads();
-    // ranks: thread (e, quarter) scans rows [quarter * T/4, ...) of expert e
-    const int QT = (T + 3) / 4;
-    for (int job = tid; job < E * 4; job += NT) {
-        const int e = job >> 2, qtr = job & 3;
+    // ranks: wave w takes experts w, w + NW, ...; a token chooses an expert
+    // at most once, so the rank of (t, e) is the number of tokens before t
+    // that chose e: a wave vote over 64 tokens at a time
+    for (int e = wave; e < E; e += NW) {
         int run = 0;
-        const int t1 = min(T, (qtr + 1) * QT);
-        for (int t = qtr * QT; t < t1; t++) {
-            int c = cnt[t * E + e];
-            cnt[t * E + e] = (unsigned short)run;
-            run += c;
+        for (int t0 = 0; t0 < T; t0 += 64) {
+            const int t = t0 + lane;
+            int rsel = -1;
+            if (t < T)
+                for (int r = 0; r < k; r++)
+                    if (sel[t * k + r] == e) rsel = r;
+            const unsigned long long m = __ballot(rsel >= 0);
+            if (rsel >= 0) rank[t * k + rsel] = (unsigned short)(run + __popcll(m & ((1ull << lane) - 1ull)));
+            run += __popcll(m);
         }
-        total[job] = run;
-    }
-    __syncthreads();
-    for (int job = tid; job < E * 4; job += NT) {
-        const int e = job >> 2, qtr = job & 3;
-        int add = 0;
-        for (int q = 0; q < qtr; q++) add += total[e * 4 + q];
-        if (add) {
-            const int t1 = min(T, (qtr + 1) * QT);
-            for (int t = qtr * QT; t < t1; t++) cnt[t * E + e] = (unsigned short)(cnt[t * E + e] + add);
-        }
+        if (lane == 0) total[e] = run;
     }
     __syncthreads();
     // per-group rows and tiles (groups: E routed experts, then n_shared shared)
@@ -366,7 +355,7 @@ SV_DEV void permute_rows(const RowArgs& a, char* lds)
         for (int g0 = 0; g0 < G; g0 += 64) {
             const int g = g0 + tid;
             int rows = 0;
-            if (g < E) rows = total[g * 4] + total[g * 4 + 1] + total[g * 4 + 2] + total[g * 4 + 3];
+            if (g < E) rows = total[g];
             else if (g < G) rows = T;
             int tiles = (rows + a.BM - 1) / a.BM;
             // inclusive wave scans of rows (routed only) and tiles
@@ -401,15 +390,12 @@ SV_DEV void permute_rows(const RowArgs& a, char* lds)
             }
         }
     }
-    for (int t = tid; t < T; t += NT) {
-        for (int r = 0; r < k; r++) {
-            int e = sel[t * k + r];
-            int sl = offset[e] + cnt[t * E + e];
-            a.slot_out[t * k + r] = sl;
-            a.perm_tok[sl] = t;
-        }
-        for (int sx = 0; sx < a.n_shared; sx++) a.perm_tok[T * k + sx * T + t] = t;
+    for (int i = tid; i < T * k; i += NT) {
+        const int sl = offset[sel[i]] + rank[i];
+        a.slot_out[i] = sl;
+        a.perm_tok[sl] = i / k;
     }
+    for (int i = tid; i < a.n_shared * T; i += NT) a.perm_tok[T * k + i] = i % T;
 }
 
 // x_out = x + (sum of K-split partials) or x + (sum over ranks of gate * expert
