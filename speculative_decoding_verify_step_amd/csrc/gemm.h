@@ -586,9 +586,10 @@ __global__ __launch_bounds__(256) void gemm_bigm_kernel(GemmArgs a)
 // reduction index is used exactly once, in a fixed order.
 //
 // Staging: each thread loads 16-byte segments of activation rows and stores
-// each where its operand lane reads it; chunks are double-buffered with one
-// barrier per chunk, weights are loaded one chunk ahead into registers.
-template <int WT, int MW, int NW, int MODE, int WAVES>
+// each where its operand lane reads it; chunks of CS steps are double-buffered
+// with one barrier per chunk, weights are loaded one chunk ahead into
+// registers.
+template <int WT, int MW, int NW, int MODE, int WAVES, int CS = 2>
 __global__ __launch_bounds__(64 * WAVES) void gemm_wide_kernel(GemmArgs a)
 {
     static_assert(WT == SV_BF16 || WT == SV_FP8, "bf16 or fp8 weights");
@@ -597,8 +598,7 @@ __global__ __launch_bounds__(64 * WAVES) void gemm_wide_kernel(GemmArgs a)
     constexpr int KL = 16 / WESZ;                // weight elements per 16-byte slot
     constexpr int SK = 4 * KL;                   // elements per tiled16 piece
     constexpr int XU = (WT == SV_FP8) ? 2 : 1;   // operands per 16-byte weight load
-    constexpr int CS = 2;                        // steps per chunk
-    constexpr int KC = CS * SK;                  // chunk length
+    constexpr int KC = CS * SK;                  // chunk length (CS steps)
     constexpr int BM = 32 * MW;
     constexpr int NWO = (MODE == GM_SWIGLU) ? NW / 2 : NW;   // output column fragments
     constexpr int PIECES = MW * CS * 2 * XU;     // 1 KiB activation operands per chunk
