@@ -1,6 +1,6 @@
 /*
- * spec_verify.h -- C ABI of the MI355X (gfx950) greedy speculative-decoding
- * verify step.
+ * spec_verify.h -- C ABI of the MI355X (gfx950) speculative-decoding verify
+ * step: greedy, and sampled (rejection sampling, spec_verify_step_sampled).
  *
  * One call runs the target decoder over the K+1 positions of every sequence
  * of a batch (the last committed token plus K draft tokens) against the
@@ -109,7 +109,7 @@
 extern "C" {
 #endif
 
-#define SPEC_VERIFY_ABI_VERSION 1
+#define SPEC_VERIFY_ABI_VERSION 2
 
 /* status codes */
 #define SV_OK 0
@@ -244,6 +244,57 @@ int spec_verify_accept_from_logits(spec_verify_ctx* ctx, const float* logits,
                                    const int32_t* draft_toks, const int32_t* ctx_lens_in,
                                    int32_t* ctx_lens_out, int batch, int32_t* accepted_len,
                                    int32_t* next_tok, int32_t* target_tok, void* stream);
+
+/*
+ * Sampled (stochastic) verification: the same forward pass, then speculative
+ * sampling instead of the greedy comparison.  "Architecture and acceleration
+ * of an end-to-end OCR expert model", section 6.1, names the property:
+ * verification by rejection sampling leaves the output distributed exactly
+ * as the target's own decoding; section 7 gives the loop (keep the agreeing
+ * prefix, the target resamples at the first disagreement).  The rule is the
+ * standard one (Leviathan et al. 2023; Chen et al. 2023):
+ *   p_j = softmax(logits_j / temperature), j = 0..K, the target after
+ *   position j; q_i the distribution draft d_i was drawn from (i = 1..K).
+ *   Draft d_i is kept while accept_u[i-1] * q_i(d_i) < p_{i-1}(d_i) (fp32),
+ *   i.e. with probability min(1, p/q).  At the first failure (accepted_len =
+ *   a < K) next_tok is drawn from max(0, p_a - q_{a+1}) normalised (from p_a
+ *   if rounding leaves no positive entry); with every draft kept (a = K)
+ *   next_tok is drawn from p_K.  ctx_lens_out = ctx_lens_in + a + 1.
+ * Draws: Gumbel-max with Philox4x32-10 noise (Salmon et al., SC 2011): key =
+ * seed (low 32 bits first), counter = (v / 4, position j, sequence b,
+ * offset), output word v % 4 -> uniform ((w >> 9) + 0.5) * 2^-23 -> noise
+ * -log(-log(uniform)); the draw is the entry with the largest fp32
+ * log-weight + noise, the lower index on ties.  Pass a fresh (seed, offset)
+ * every step.
+ *   draft_probs  [batch][K][V] fp32, q_i of every draft position (device)
+ *   accept_u     [batch][K]    fp32 uniforms in [0, 1) (device)
+ *   temperature  > 0, applied to the target's logits only
+ * Other arguments, outputs and per-sequence errors as in spec_verify_step
+ * (a NaN logit, or a draft outside [0, V), sets the sequence's outputs to -1).
+ * The LM head writes fp32 logits [batch (K+1)][V] into the context's
+ * workspace (or into the debug logits buffer when one is set); the debug
+ * target_tok buffer is not written.  Needs vocab <= 262144 (SV_ERR_UNSUPPORTED
+ * otherwise); a temperature that is not positive and finite, or whose
+ * inverse overflows, is SV_ERR_INVALID_ARG.
+ */
+int spec_verify_step_sampled(spec_verify_ctx* ctx, const spec_verify_weights* w, void* k_cache,
+                             void* v_cache, const int32_t* committed_tok,
+                             const int32_t* draft_toks, const float* draft_probs,
+                             const float* accept_u, float temperature, uint64_t seed,
+                             uint32_t offset, const int32_t* ctx_lens_in, int32_t* ctx_lens_out,
+                             int batch, int32_t* accepted_len, int32_t* next_tok, void* stream);
+
+/*
+ * The sampled acceptance and commit alone, from given target logits
+ * [batch][K+1][V] fp32 (device, before the temperature); arguments and
+ * outputs as in spec_verify_step_sampled.
+ */
+int spec_verify_sample_from_logits(spec_verify_ctx* ctx, const float* logits,
+                                   const int32_t* draft_toks, const float* draft_probs,
+                                   const float* accept_u, float temperature, uint64_t seed,
+                                   uint32_t offset, const int32_t* ctx_lens_in,
+                                   int32_t* ctx_lens_out, int batch, int32_t* accepted_len,
+                                   int32_t* next_tok, void* stream);
 
 /*
  * Repack one row-major matrix W[rows][cols] (device, storage `dtype`) into

@@ -119,7 +119,16 @@ def log_softmax(z):
     return z - (m + np.log(np.exp(z - m).sum()))
 
 
-def sampled_verify(logits, drafts, q, u, tau: float, seed: int, offset: int) -> dict:
+def _certain(key_lo, key_hi, best):
+    """The entry `best` wins for every choice of keys inside [key_lo, key_hi]."""
+    if best < 0:
+        return bool(np.all(key_hi == -np.inf))
+    others = np.delete(key_hi, best)
+    return bool(key_lo[best] > (others.max() if others.size else -np.inf))
+
+
+def sampled_verify(logits, drafts, q, u, tau: float, seed: int, offset: int,
+                   delta: float = 0.0, key_slack: float = 0.0) -> dict:
     """Stochastic verify for a batch.
 
     logits [B][K+1][V] target logits (before the temperature), drafts [B][K]
@@ -128,7 +137,11 @@ def sampled_verify(logits, drafts, q, u, tau: float, seed: int, offset: int) -> 
     accept_margin [B] (smallest |p - u q| over the deciding comparisons,
     relative to p + u q) and key_gap [B] (gap between the two largest keys of
     the final draw), plus the row ("row") and kind ("residual", "bonus",
-    "fallback") of the final draw."""
+    "fallback") of the final draw.  With delta > 0 it also reports whether the
+    outcome is certain when every target probability may be off by a
+    relative delta and every key by key_slack: accept_certain [B] (every
+    acceptance comparison keeps its side) and draw_certain [B] (the final
+    draw keeps its winner)."""
     logits = np.asarray(logits, dtype=np.float64)
     B, K1, V = logits.shape
     K = K1 - 1
@@ -137,7 +150,8 @@ def sampled_verify(logits, drafts, q, u, tau: float, seed: int, offset: int) -> 
     u = np.asarray(u, dtype=np.float64).reshape(B, K)
     out = {"accepted": np.zeros(B, np.int32), "next_tok": np.zeros(B, np.int32),
            "accept_margin": np.full(B, np.inf), "key_gap": np.zeros(B),
-           "row": np.zeros(B, np.int32), "kind": [""] * B}
+           "row": np.zeros(B, np.int32), "kind": [""] * B,
+           "accept_certain": np.ones(B, bool), "draw_certain": np.ones(B, bool)}
     for b in range(B):
         logp = np.stack([log_softmax(logits[b, j] / tau) for j in range(K1)])
         a = K
@@ -148,7 +162,12 @@ def sampled_verify(logits, drafts, q, u, tau: float, seed: int, offset: int) -> 
             den = p + uq
             if den > 0:
                 out["accept_margin"][b] = min(out["accept_margin"][b], abs(p - uq) / den)
-            if not (_f32(uq) < _f32(p)):
+            kept = bool(_f32(uq) < _f32(p))
+            if kept and not p * (1 - delta) > uq * (1 + 1e-6):
+                out["accept_certain"][b] = False
+            if not kept and not p * (1 + delta) < uq * (1 - 1e-6):
+                out["accept_certain"][b] = False
+            if not kept:
                 a = i - 1
                 break
         g = gumbel_noise(seed, offset, b, a, V)
@@ -164,6 +183,23 @@ def sampled_verify(logits, drafts, q, u, tau: float, seed: int, offset: int) -> 
                 kind = "fallback"
         else:
             tok, gap = gumbel_argmax(logp[a], g)
+        if delta > 0 or key_slack > 0:
+            if a < K:
+                pa = np.exp(logp[a])
+                with np.errstate(divide="ignore", invalid="ignore"):
+                    r_lo, r_hi = pa * (1 - delta) - q[b, a], pa * (1 + delta) - q[b, a]
+                    k_lo = np.where(r_lo > 0, np.log(np.maximum(r_lo, 1e-300)) + g - key_slack, -np.inf)
+                    k_hi = np.where(r_hi > 0, np.log(np.maximum(r_hi, 1e-300)) + g + key_slack, -np.inf)
+                if kind == "fallback":
+                    sure = bool(np.all(r_hi <= 0))
+                    w = np.log1p(delta) + key_slack
+                    sure = sure and _certain(logp[a] + g - w, logp[a] + g + w, tok)
+                else:
+                    sure = _certain(k_lo, k_hi, tok)
+            else:
+                w = np.log1p(delta) + key_slack
+                sure = _certain(logp[a] + g - w, logp[a] + g + w, tok)
+            out["draw_certain"][b] = sure
         out["accepted"][b] = a
         out["next_tok"][b] = tok
         out["key_gap"][b] = gap

@@ -32,7 +32,8 @@ _DT = {"f32": SV_F32, "bf16": SV_BF16, "fp8": SV_FP8}
 EXPORTS = ("spec_verify_init", "spec_verify_destroy", "spec_verify_step", "spec_verify_set_debug",
            "spec_verify_accept_from_logits", "spec_verify_error_word", "spec_verify_kernel_time",
            "spec_verify_last_error", "spec_verify_status_string", "spec_verify_abi_version",
-           "spec_verify_pack_tiled16", "spec_verify_tiled16_bytes")
+           "spec_verify_pack_tiled16", "spec_verify_tiled16_bytes", "spec_verify_step_sampled",
+           "spec_verify_sample_from_logits")
 
 
 class SpecVerifyConfig(ctypes.Structure):
@@ -82,6 +83,11 @@ def load_library() -> ctypes.CDLL:
         lib.spec_verify_step.argtypes = [P, P, P, P, P, P, P, P, c_int, P, P, P]
         lib.spec_verify_set_debug.argtypes = [P, P, P, P, P]
         lib.spec_verify_accept_from_logits.argtypes = [P, P, P, P, P, c_int, P, P, P, P]
+        U64, U32 = ctypes.c_uint64, ctypes.c_uint32
+        lib.spec_verify_step_sampled.argtypes = [P, P, P, P, P, P, P, P, c_float, U64, U32, P, P,
+                                                 c_int, P, P, P]
+        lib.spec_verify_sample_from_logits.argtypes = [P, P, P, P, P, c_float, U64, U32, P, P,
+                                                       c_int, P, P, P]
         lib.spec_verify_error_word.argtypes = [P, P, c_int, P]
         lib.spec_verify_kernel_time.argtypes = [P, c_int, c_int, P, P]
         lib.spec_verify_last_error.argtypes = [c_char_p, c_int]
@@ -255,6 +261,28 @@ def spec_verify_accept_from_logits(ctx: int, logits, draft_toks, ctx_lens_in, ct
         "spec_verify_accept_from_logits")
 
 
+def spec_verify_step_sampled(ctx: int, weights: SpecVerifyWeights, k_cache, v_cache,
+                             committed_tok, draft_toks, draft_probs, accept_u, temperature: float,
+                             seed: int, offset: int, ctx_lens_in, ctx_lens_out, batch: int,
+                             accepted_len, next_tok, stream=None) -> None:
+    _check(load_library().spec_verify_step_sampled(
+        ctx, ctypes.byref(weights), _p(k_cache), _p(v_cache), _p(committed_tok), _p(draft_toks),
+        _p(draft_probs), _p(accept_u), float(temperature), int(seed) & (2 ** 64 - 1),
+        int(offset) & 0xFFFFFFFF, _p(ctx_lens_in), _p(ctx_lens_out), int(batch),
+        _p(accepted_len), _p(next_tok), _stream(stream)), "spec_verify_step_sampled")
+
+
+def spec_verify_sample_from_logits(ctx: int, logits, draft_toks, draft_probs, accept_u,
+                                   temperature: float, seed: int, offset: int, ctx_lens_in,
+                                   ctx_lens_out, batch: int, accepted_len, next_tok,
+                                   stream=None) -> None:
+    _check(load_library().spec_verify_sample_from_logits(
+        ctx, _p(logits), _p(draft_toks), _p(draft_probs), _p(accept_u), float(temperature),
+        int(seed) & (2 ** 64 - 1), int(offset) & 0xFFFFFFFF, _p(ctx_lens_in), _p(ctx_lens_out),
+        int(batch), _p(accepted_len), _p(next_tok), _stream(stream)),
+        "spec_verify_sample_from_logits")
+
+
 def spec_verify_error_word(ctx: int, clear: bool = False, stream=None) -> int:
     v = c_uint32()
     _check(load_library().spec_verify_error_word(ctx, ctypes.byref(v), int(clear),
@@ -333,6 +361,20 @@ class VerifyContext:
                            target_tok=None, stream=None):
         spec_verify_accept_from_logits(self.handle, logits, drafts, ctx_in, ctx_out,
                                        drafts.shape[0], accepted, next_tok, target_tok, stream)
+
+    def step_sampled(self, k_cache, v_cache, committed, drafts, draft_probs, accept_u,
+                     temperature, seed, offset, ctx_in, ctx_out, accepted, next_tok,
+                     batch=None, stream=None):
+        B = committed.shape[0] if batch is None else batch
+        spec_verify_step_sampled(self.handle, self._w, k_cache, v_cache, committed, drafts,
+                                 draft_probs, accept_u, temperature, seed, offset, ctx_in,
+                                 ctx_out, B, accepted, next_tok, stream)
+
+    def sample_from_logits(self, logits, drafts, draft_probs, accept_u, temperature, seed,
+                           offset, ctx_in, ctx_out, accepted, next_tok, stream=None):
+        spec_verify_sample_from_logits(self.handle, logits, drafts, draft_probs, accept_u,
+                                       temperature, seed, offset, ctx_in, ctx_out,
+                                       drafts.shape[0], accepted, next_tok, stream)
 
     def error_word(self, clear=False, stream=None) -> int:
         return spec_verify_error_word(self.handle, clear, stream)

@@ -10,6 +10,8 @@
 //                      -> grouped down -> combine + residual + norm
 //              -> dense: gate/up (SwiGLU) -> down -> residual + norm
 //   LM-head GEMM with argmax epilogue -> acceptance + commit
+//   (sampled verification: the LM head also writes fp32 logits, then tile
+//   statistics -> residual draws -> acceptance + commit, sampling.h)
 //
 // Nothing here reads device memory back: context lengths, routing and
 // acceptance stay on the device, so a step can be captured in a HIP graph.
@@ -29,6 +31,7 @@
 #include "gemm.h"
 #include "small_kernels.h"
 #include "qkv_rope.h"
+#include "sampling.h"
 
 namespace {
 
@@ -110,6 +113,12 @@ struct spec_verify_ctx {
     size_t keys_elems = 0;
     int* seq_err = nullptr;
     unsigned* err_word = nullptr;
+    // sampled verification (sampling.h); s_ntile = 0: vocabulary too large for it
+    int s_ntile = 0;
+    float* slogits = nullptr;
+    float2* sstats = nullptr;
+    unsigned long long* spkeys = nullptr;
+    unsigned long long* srkeys = nullptr;
     // debug outputs
     float* dbg_logits = nullptr;
     float* dbg_hidden = nullptr;
@@ -441,6 +450,68 @@ struct ProfScope {
     ~ProfScope() { g_ev_start = g_ev_stop = nullptr; }
 };
 
+struct SampleIn {
+    const float* q;
+    const float* u;
+    float inv_tau;
+    uint64_t seed;
+    uint32_t offset;
+};
+
+int sample_in(const spec_verify_ctx* c, const float* q, const float* u, float temperature,
+              uint64_t seed, uint32_t offset, SampleIn* out)
+{
+    if (!c) return fail(SV_ERR_INVALID_ARG, "null context");
+    if (c->s_ntile == 0)
+        return fail(SV_ERR_UNSUPPORTED, "sampled verification needs vocab <= " +
+                                            std::to_string(SAMPLE_MAX_TILES * SAMPLE_TILE));
+    if (!q || !u) return fail(SV_ERR_INVALID_ARG, "null draft distribution or uniforms");
+    if (!(temperature > 0.f) || !std::isfinite(temperature) || !std::isfinite(1.0f / temperature))
+        return fail(SV_ERR_INVALID_ARG, "temperature must be positive and finite, with a finite inverse");
+    out->q = q;
+    out->u = u;
+    out->inv_tau = 1.0f / temperature;
+    out->seed = seed;
+    out->offset = offset;
+    return SV_OK;
+}
+
+// Tile statistics, residual draws, acceptance + commit (sampling.h).
+int launch_sampling(spec_verify_ctx* c, const SampleIn& smp, const float* logits,
+                    const int32_t* drafts, const int32_t* ctx_in, int32_t* ctx_out, int B,
+                    int32_t* accepted, int32_t* next_tok, const int* seq_err, hipStream_t s)
+{
+    const int K1 = c->K1, K = K1 - 1, T = B * K1, nt = c->s_ntile;
+    SampleArgs a;
+    memset(&a, 0, sizeof(a));
+    a.logits = logits;
+    a.drafts = drafts;
+    a.q = smp.q;
+    a.u = smp.u;
+    a.inv_tau = smp.inv_tau;
+    a.key0 = (uint32_t)smp.seed;
+    a.key1 = (uint32_t)(smp.seed >> 32);
+    a.offset = smp.offset;
+    a.V = c->c.vocab;
+    a.T = T;
+    a.K1 = K1;
+    a.ntile = nt;
+    a.stats = c->sstats;
+    a.pkeys = c->spkeys;
+    a.rkeys = c->srkeys;
+    a.ctx_in = ctx_in;
+    a.ctx_out = ctx_out;
+    a.accepted = accepted;
+    a.next_tok = next_tok;
+    a.seq_err = seq_err;
+    a.err_word = c->err_word;
+    sample_stats_kernel<<<dim3(nt, T), 256, 0, s>>>(a);
+    sample_residual_kernel<<<dim3(nt, B * K), 256, 0, s>>>(a);
+    sample_accept_kernel<<<B, 64, 0, s>>>(a);
+    HIP_TRY(hipGetLastError());
+    return SV_OK;
+}
+
 }  // namespace
 
 // ====================================================================== ABI
@@ -571,6 +642,13 @@ int spec_verify_init(const spec_verify_config* cfg, spec_verify_ctx** out)
     ALLOC(c->keys, c->keys_elems);
     ALLOC(c->seq_err, (size_t)k.max_batch);
     ALLOC(c->err_word, 1);
+    if (k.vocab <= SAMPLE_MAX_TILES * SAMPLE_TILE) {
+        c->s_ntile = cdiv(k.vocab, SAMPLE_TILE);
+        ALLOC(c->slogits, (size_t)T * k.vocab);
+        ALLOC(c->sstats, (size_t)T * c->s_ntile);
+        ALLOC(c->spkeys, (size_t)T * c->s_ntile);
+        ALLOC(c->srkeys, (size_t)k.max_batch * k.k_draft * c->s_ntile);
+    }
     if (k.ffn_kind == SV_FFN_MOE) {
         char* abuf = nullptr;
         ALLOC(c->logits_g, (size_t)T * E);
@@ -625,10 +703,12 @@ int spec_verify_set_debug(spec_verify_ctx* c, float* logits, float* hidden, int3
     return SV_OK;
 }
 
-int spec_verify_step(spec_verify_ctx* c, const spec_verify_weights* w, void* k_cache,
+// The forward pass and the greedy acceptance, or (smp != nullptr) the sampled
+// acceptance on the logits the LM head writes alongside its argmax keys.
+static int step_impl(spec_verify_ctx* c, const spec_verify_weights* w, void* k_cache,
                      void* v_cache, const int32_t* committed, const int32_t* drafts,
                      const int32_t* ctx_in, int32_t* ctx_out, int B, int32_t* accepted,
-                     int32_t* next_tok, void* stream)
+                     int32_t* next_tok, void* stream, const SampleIn* smp)
 {
     if (!c || !w) return fail(SV_ERR_INVALID_ARG, "null context or weights");
     if (B < 1 || B > c->c.max_batch) return fail(SV_ERR_INVALID_ARG, "batch outside [1, max_batch]");
@@ -724,6 +804,9 @@ int spec_verify_step(spec_verify_ctx* c, const spec_verify_weights* w, void* k_c
     // dense GEMM (or the dense SwiGLU / argmax variants); returns the K split used
     // allow_split: largest K split the consumer accepts (0 or 1: none)
     int last_nt = 0;   // column tiles of the last dense GEMM (argmax key columns)
+    // fp32 logits written by the LM head: the debug buffer, and for sampled
+    // verification the sampling input (the debug buffer when one is set)
+    float* lm_logits = smp ? (c->dbg_logits ? c->dbg_logits : c->slogits) : c->dbg_logits;
     auto dense_gemm = [&](int mode, const void* X, long ldx, int N, int Kd, const void* W,
                           const float* ws, void* out, long ldo, int allow_split) -> int {
         GemmArgs a = dense_args(X, ldx, T, N, Kd, W, ws);
@@ -732,7 +815,7 @@ int spec_verify_step(spec_verify_ctx* c, const spec_verify_weights* w, void* k_c
         a.split_stride = (long)T * ldo;
         a.keys = c->keys;
         a.key_ld = T;
-        a.dbg = c->dbg_logits;
+        a.dbg = lm_logits;
         a.dbg_ld = k.vocab;
         if (mode == GM_SWIGLU) a.dual_off = N;
         const int chunk = BIG_CHUNK_STEPS * step;
@@ -989,6 +1072,8 @@ int spec_verify_step(spec_verify_ctx* c, const spec_verify_weights* w, void* k_c
         ProfScope ps(c, SV_KC_LM_HEAD, s);
         dense_gemm(GM_ARGMAX, c->h, H, k.vocab, H, w->lm_head, w->lm_scale, nullptr, 0, 0);
     }
+    if (smp) return launch_sampling(c, *smp, lm_logits, drafts, ctx_in, ctx_out, B, accepted,
+                                    next_tok, c->seq_err, s);
     const int NT_lm = last_nt;   // argmax key columns written by the LM head
     AcceptArgs ac;
     ac.keys = c->keys;
@@ -1006,6 +1091,46 @@ int spec_verify_step(spec_verify_ctx* c, const spec_verify_weights* w, void* k_c
     accept_kernel<<<B, 1024, 0, s>>>(ac);
     HIP_TRY(hipGetLastError());
     return SV_OK;
+}
+
+int spec_verify_step(spec_verify_ctx* c, const spec_verify_weights* w, void* k_cache,
+                     void* v_cache, const int32_t* committed, const int32_t* drafts,
+                     const int32_t* ctx_in, int32_t* ctx_out, int B, int32_t* accepted,
+                     int32_t* next_tok, void* stream)
+{
+    return step_impl(c, w, k_cache, v_cache, committed, drafts, ctx_in, ctx_out, B, accepted,
+                     next_tok, stream, nullptr);
+}
+
+int spec_verify_step_sampled(spec_verify_ctx* c, const spec_verify_weights* w, void* k_cache,
+                             void* v_cache, const int32_t* committed, const int32_t* drafts,
+                             const float* draft_probs, const float* accept_u, float temperature,
+                             uint64_t seed, uint32_t offset, const int32_t* ctx_in,
+                             int32_t* ctx_out, int B, int32_t* accepted, int32_t* next_tok,
+                             void* stream)
+{
+    SampleIn smp;
+    int rc = sample_in(c, draft_probs, accept_u, temperature, seed, offset, &smp);
+    if (rc) return rc;
+    return step_impl(c, w, k_cache, v_cache, committed, drafts, ctx_in, ctx_out, B, accepted,
+                     next_tok, stream, &smp);
+}
+
+int spec_verify_sample_from_logits(spec_verify_ctx* c, const float* logits,
+                                   const int32_t* drafts, const float* draft_probs,
+                                   const float* accept_u, float temperature, uint64_t seed,
+                                   uint32_t offset, const int32_t* ctx_in, int32_t* ctx_out,
+                                   int B, int32_t* accepted, int32_t* next_tok, void* stream)
+{
+    SampleIn smp;
+    int rc = sample_in(c, draft_probs, accept_u, temperature, seed, offset, &smp);
+    if (rc) return rc;
+    if (B < 1 || B > c->c.max_batch) return fail(SV_ERR_INVALID_ARG, "batch outside [1, max_batch]");
+    if (!logits || !drafts || !ctx_in || !ctx_out || !accepted || !next_tok)
+        return fail(SV_ERR_INVALID_ARG, "null buffer pointer");
+    HIP_TRY(hipSetDevice(c->device));
+    return launch_sampling(c, smp, logits, drafts, ctx_in, ctx_out, B, accepted, next_tok,
+                           nullptr, (hipStream_t)stream);
 }
 
 int spec_verify_accept_from_logits(spec_verify_ctx* c, const float* logits, const int32_t* drafts,

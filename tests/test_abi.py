@@ -36,7 +36,7 @@ def test_every_declared_function_is_exported(sv):
 
 
 def test_status_strings_and_version(sv):
-    assert sv.spec_verify_abi_version() == 1
+    assert sv.spec_verify_abi_version() == 2
     assert sv.spec_verify_status_string(0) == "ok"
     assert "invalid" in sv.spec_verify_status_string(-1)
     assert sv.spec_verify_status_string(12345) == "unknown status"

@@ -1,8 +1,9 @@
-"""Seeded synthetic workloads for the greedy speculative-decoding verify step.
+"""Seeded synthetic workloads for the speculative-decoding verify step.
 
 This package holds only input generation: the model shapes of the five
 workloads, seeded weight / KV-cache / context-length / draft-randomness
-generators, and the byte accounting used to price a step.  It contains none
+generators, draft distributions for the sampled verify, and the byte
+accounting used to price a step.  It contains none
 of the verify step's arithmetic; both the HIP library's callers and the CPU
 oracle's callers draw their inputs from here.
 """
@@ -14,6 +15,7 @@ from .synth import (
     kv_cache,
     make_weights,
     committed_tokens,
+    sampled_drafts,
     tensor_seed,
 )
 
@@ -28,5 +30,6 @@ __all__ = [
     "kv_cache",
     "make_weights",
     "committed_tokens",
+    "sampled_drafts",
     "tensor_seed",
 ]

@@ -189,3 +189,25 @@ def kv_cache(cfg: VerifyConfig, device="cpu", capacity: int | None = None):
             t[b] = _normal(shape[1:], std, device, cfg.seed, f"{name}.{b}").to(dt)
         out.append(t)
     return out[0], out[1]
+
+
+def sampled_drafts(cfg: VerifyConfig, batch: int | None = None, step: int = 0,
+                   sigma: float | None = None):
+    """Inputs of a sampled (rejection-sampling) verify step, on the CPU:
+    draft distributions q [B][K][V] (fp32; each row the normalised weights
+    exp(sigma * N(0, 1)), the spread of the target's own logits by default:
+    sigma = weight_std * sqrt(hidden)), drafts [B][K] (int32, drawn from q),
+    acceptance uniforms u [B][K] (fp32 in [0, 1)), and the generator seed and
+    offset of the step's Gumbel noise."""
+    B = cfg.batch if batch is None else batch
+    K, V = cfg.k_draft, cfg.vocab
+    sig = cfg.weight_std * math.sqrt(cfg.hidden) if sigma is None else sigma
+    g = _gen("cpu", cfg.seed, f"draft_dist.{step}")
+    w = torch.exp(sig * torch.randn(B, K, V, generator=g, dtype=torch.float64))
+    q = w / w.sum(-1, keepdim=True)
+    g2 = _gen("cpu", cfg.seed, f"draft_pick.{step}")
+    drafts = torch.multinomial(q.reshape(B * K, V), 1, generator=g2).reshape(B, K).to(torch.int32)
+    g3 = _gen("cpu", cfg.seed, f"accept_u.{step}")
+    u = torch.rand(B, K, generator=g3, dtype=torch.float32)
+    seed = tensor_seed(cfg.seed, "gumbel_seed") * 0x100000001 & (2 ** 64 - 1)
+    return {"q": q.to(torch.float32), "drafts": drafts, "u": u, "seed": seed, "offset": step}
