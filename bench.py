@@ -1,6 +1,6 @@
 """Benchmark of the greedy speculative-decoding verify step on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config moe_b1]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config moe_b1] [--sampled]
 
 A step is one spec_verify_step over a whole batch (every row of the hot
 path: embedding, all decoder layers, LM head + argmax, acceptance + commit).
@@ -13,6 +13,10 @@ Workloads: single-step ones repeat the same step (same context, same drafts)
 K times; the chained long-context workload runs K consecutive steps in which
 contexts grow by accepted + 1 and the bonus token becomes the next committed
 token, all on the device.
+
+--sampled times the sampled (rejection-sampling) step instead, at temperature
+1 with drafts drawn from seeded draft distributions; its line adds the time
+of the sampling kernels.
 
 One JSON line is printed: accepted tokens/s (sum over sequences of
 accepted + 1 per step, over the timed wall clock), microseconds per step, the
@@ -68,15 +72,16 @@ def log(*a):
 
 
 # ------------------------------------------------------------ byte model
-def lm_head_bytes(cfg, T):
+def lm_head_bytes(cfg, T, logits=False):
     """Algorithmic HBM bytes of one LM-head launch: the weight matrix (and
     fp8 row scales) once, the normalised activations once, the argmax
-    partial keys written (one 8-byte key per 64-column tile and row)."""
+    partial keys written (one 8-byte key per 64-column tile and row), and
+    for sampled verification the fp32 logits written."""
     V, H = cfg.vocab, cfg.hidden
     w = V * H * WBYTES[cfg.wdtype] + (V * 4 if cfg.wdtype == "fp8" else 0)
     act = T * H * (4 if cfg.wdtype == "f32" else 2)
     keys = ((V + 63) // 64) * T * 8
-    return w + act + keys
+    return w + act + keys + (T * V * 4 if logits else 0)
 
 
 def step_bytes(cfg, ctx, distinct_experts):
@@ -160,8 +165,10 @@ def record_drafts(cfg, S):
     return drafts, first_routing
 
 
-def run_bench(cfg, steps, warmup):
+def run_bench(cfg, steps, warmup, sampled=False):
     import torch
+
+    import workloads
 
     S = setup(cfg, steps)
     sv, vc = S["sv"], S["vc"]
@@ -169,6 +176,12 @@ def run_bench(cfg, steps, warmup):
     log(f"[bench] {cfg.name}: B={B} L={cfg.n_layers} cap={S['cap']} recording drafts")
     drafts, routing = record_drafts(cfg, S)
     i32 = dict(dtype=torch.int32, device="cuda")
+    if sampled:
+        # drafts drawn from seeded draft distributions (rejection sampling at
+        # temperature 1); a fresh noise offset every step
+        sd = workloads.sampled_drafts(cfg)
+        sq, su = sd["q"].to("cuda").contiguous(), sd["u"].to("cuda").contiguous()
+        drafts = [sd["drafts"].to(**i32).contiguous()]
     ctx0 = S["ctx"].to(**i32)
     com0 = S["com"].to(**i32)
     nxt, cout = (torch.empty(B, **i32) for _ in range(2))
@@ -184,10 +197,13 @@ def run_bench(cfg, steps, warmup):
         # chained: the bonus token of step i is the committed token of step i+1
         # (two alternating buffers, no copy); contexts grow in place
         d = drafts[i % len(drafts)]
-        if chained:
-            vc.step(S["k"], S["v"], com_bufs[i % 2], d, ctx, ctx, acc_all[i], com_bufs[(i + 1) % 2])
+        com_in, ctx_out, nxt_out = ((com_bufs[i % 2], ctx, com_bufs[(i + 1) % 2]) if chained
+                                    else (com0, cout, nxt))
+        if sampled:
+            vc.step_sampled(S["k"], S["v"], com_in, d, sq, su, 1.0, sd["seed"], i, ctx, ctx_out,
+                            acc_all[i], nxt_out)
         else:
-            vc.step(S["k"], S["v"], com0, d, ctx, cout, acc_all[i], nxt)
+            vc.step(S["k"], S["v"], com_in, d, ctx, ctx_out, acc_all[i], nxt_out)
 
     # warmup (untimed); a chained run restarts from the recorded start state
     ctx = ctx0.clone()
@@ -209,6 +225,16 @@ def run_bench(cfg, steps, warmup):
     acc_sum = acc_all[:steps].to(torch.int64).sum(0)
     lm_ms, lm_n = vc.kernel_time(kc, enable=0)
     assert vc.error_word() == 0, "device error during the benchmark"
+    samp_us = None
+    if sampled:   # the sampling kernels, timed in a second pass of the same steps
+        ctx_s = ctx_start.clone()
+        com_bufs[0].copy_(com0)
+        vc.kernel_time(sv.SV_KC_SAMPLING, enable=1, query=False)
+        for i in range(steps):
+            one(i, ctx_s)
+        torch.cuda.synchronize()
+        s_ms, s_n = vc.kernel_time(sv.SV_KC_SAMPLING, enable=0)
+        samp_us = 1e3 * s_ms / max(steps, 1)
     wall = t1 - t0
     committed_tokens = int(acc_sum.sum().item()) + steps * B
     ms_step = wall * 1e3 / steps
@@ -218,7 +244,8 @@ def run_bench(cfg, steps, warmup):
         "tau": committed_tokens / (steps * B),
         "lm_ms": lm_ms / max(lm_n, 1),
         "lm_launches": lm_n,
-        "lm_bytes": lm_head_bytes(cfg, B * K1),
+        "lm_bytes": lm_head_bytes(cfg, B * K1, logits=sampled),
+        "sampling_us_per_step": samp_us,
         "step_bytes": step_bytes(cfg, (ctx_start if not chained else ctx0).tolist(),
                                  distinct or [0] * cfg.n_layers),
         "distinct_experts": distinct,
@@ -284,6 +311,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=None)
     ap.add_argument("--config", default="moe_b1")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--sampled", action="store_true",
+                    help="time the sampled (rejection-sampling) verify step instead of the greedy one")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                     help="only run a plain device copy of BYTES (counter calibration)")
     args = ap.parse_args()
@@ -298,7 +327,7 @@ def main():
     cfg = workloads.get_config(args.config)
     steps = args.steps if args.steps is not None else (cfg.steps if cfg.steps > 1 else 200)
     warmup = args.warmup if args.warmup is not None else 10
-    r = run_bench(cfg, steps, warmup)
+    r = run_bench(cfg, steps, warmup, sampled=args.sampled)
     lm_gbs = r["lm_bytes"] / (r["lm_ms"] * 1e-3) / 1e9 if r["lm_ms"] > 0 else None
     out = {
         "metric": METRIC,
@@ -318,11 +347,12 @@ def main():
                    "layers": cfg.n_layers, "hidden": cfg.hidden, "vocab": cfg.vocab,
                    "ctx": list(cfg.ctx), "chained_steps": cfg.steps > 1,
                    "weight_layout": "tiled16",
+                   "verification": "sampled (temperature 1)" if args.sampled else "greedy",
                    "tokens_per_verify": r["tau"]},
         "roofline": {"bound": "hbm", "kernel": "lm_head_argmax",
                      "achieved": lm_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": (lm_gbs / HBM_PEAK_GBS) if lm_gbs else None,
-                     "traffic": measured_traffic(cfg.name),
+                     "traffic": None if args.sampled else measured_traffic(cfg.name),
                      "mean_us": r["lm_ms"] * 1e3, "bytes_per_launch": r["lm_bytes"],
                      "launches_timed": r["lm_launches"]},
         "step_roofline": {"bytes_per_step": r["step_bytes"],
@@ -330,7 +360,9 @@ def main():
                           "frac": r["step_bytes"] / (r["ms_per_step"] * 1e-3) / 1e9 / HBM_PEAK_GBS,
                           "distinct_experts_per_layer": r["distinct_experts"]},
     }
-    if not args.no_cpu_baseline:
+    if args.sampled:
+        out["sampling_kernels_us_per_step"] = r["sampling_us_per_step"]
+    if not args.no_cpu_baseline and not args.sampled:
         log("[bench] timing the CPU oracle")
         out["cpu_baseline"] = cpu_baseline(cfg)
     print(json.dumps(out), flush=True)

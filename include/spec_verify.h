@@ -143,7 +143,9 @@ extern "C" {
 #define SV_KC_EXPERT_GATE_UP 2    /* grouped expert gate/up + SwiGLU (MoE) or dense gate/up */
 #define SV_KC_EXPERT_DOWN 3       /* grouped expert down projection (MoE) or dense down */
 #define SV_KC_QKV 4               /* QKV projection */
-#define SV_KC_COUNT 5
+#define SV_KC_SAMPLING 5          /* sampled verification: statistics, decision + draw, commit
+                                     (three launches per step) */
+#define SV_KC_COUNT 6
 
 typedef struct spec_verify_ctx spec_verify_ctx;   /* opaque; owns only its workspace */
 
@@ -260,12 +262,13 @@ int spec_verify_accept_from_logits(spec_verify_ctx* ctx, const float* logits,
  *   a < K) next_tok is drawn from max(0, p_a - q_{a+1}) normalised (from p_a
  *   if rounding leaves no positive entry); with every draft kept (a = K)
  *   next_tok is drawn from p_K.  ctx_lens_out = ctx_lens_in + a + 1.
- * Draws: Gumbel-max with Philox4x32-10 noise (Salmon et al., SC 2011): key =
- * seed (low 32 bits first), counter = (v / 4, position j, sequence b,
- * offset), output word v % 4 -> uniform ((w >> 9) + 0.5) * 2^-23 -> noise
- * -log(-log(uniform)); the draw is the entry with the largest fp32
- * log-weight + noise, the lower index on ties.  Pass a fresh (seed, offset)
- * every step.
+ * Draws: the exponential race (Gumbel-max): the entry with the largest fp32
+ * weight / E_v, the lower index on ties, where E_v = -log(uniform) and the
+ * uniform comes from Philox4x32-10 (Salmon et al., SC 2011): key = seed (low
+ * 32 bits first), counter = (v / 4, position j, sequence b, offset), output
+ * word v % 4 -> uniform ((w >> 9) + 0.5) * 2^-23.  This is the largest
+ * log-weight + Gumbel noise -log(E_v).  Pass a fresh (seed, offset) every
+ * step.
  *   draft_probs  [batch][K][V] fp32, q_i of every draft position (device)
  *   accept_u     [batch][K]    fp32 uniforms in [0, 1) (device)
  *   temperature  > 0, applied to the target's logits only

@@ -20,12 +20,14 @@ SV_OK, SV_ERR_INVALID_ARG, SV_ERR_UNSUPPORTED, SV_ERR_HIP, SV_ERR_NO_DEVICE, SV_
 SV_F32, SV_BF16, SV_FP8 = 0, 1, 2
 SV_FFN_MOE, SV_FFN_DENSE = 0, 1
 SV_DEV_BAD_TOKEN, SV_DEV_CAPACITY, SV_DEV_NAN_LOGIT = 1, 2, 4
-SV_KC_LM_HEAD, SV_KC_ATTENTION, SV_KC_EXPERT_GATE_UP, SV_KC_EXPERT_DOWN, SV_KC_QKV = range(5)
+(SV_KC_LM_HEAD, SV_KC_ATTENTION, SV_KC_EXPERT_GATE_UP, SV_KC_EXPERT_DOWN, SV_KC_QKV,
+ SV_KC_SAMPLING) = range(6)
 SV_LAYOUT_ROW_MAJOR, SV_LAYOUT_TILED16 = 0, 1
 _LAYOUTS = {"row_major": SV_LAYOUT_ROW_MAJOR, "tiled16": SV_LAYOUT_TILED16}
 # matrices that feed a matrix product (packed in the tiled16 layout)
 GEMM_MATRICES = ("w_qkv", "w_o", "w_gate_up", "w_down", "w_sh_gate_up", "w_sh_down")
-KERNEL_CLASSES = {"lm_head": 0, "attention": 1, "expert_gate_up": 2, "expert_down": 3, "qkv": 4}
+KERNEL_CLASSES = {"lm_head": 0, "attention": 1, "expert_gate_up": 2, "expert_down": 3, "qkv": 4,
+                  "sampling": 5}
 _DT = {"f32": SV_F32, "bf16": SV_BF16, "fp8": SV_FP8}
 
 # every function include/spec_verify.h declares

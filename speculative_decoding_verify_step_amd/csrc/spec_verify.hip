@@ -11,7 +11,7 @@
 //              -> dense: gate/up (SwiGLU) -> down -> residual + norm
 //   LM-head GEMM with argmax epilogue -> acceptance + commit
 //   (sampled verification: the LM head also writes fp32 logits, then tile
-//   statistics -> residual draws -> acceptance + commit, sampling.h)
+//   statistics -> acceptance decision + draw -> commit, sampling.h)
 //
 // Nothing here reads device memory back: context lengths, routing and
 // acceptance stay on the device, so a step can be captured in a HIP graph.
@@ -117,8 +117,9 @@ struct spec_verify_ctx {
     int s_ntile = 0;
     float* slogits = nullptr;
     float2* sstats = nullptr;
-    unsigned long long* spkeys = nullptr;
-    unsigned long long* srkeys = nullptr;
+    unsigned long long* sdkeys = nullptr;
+    unsigned long long* sfkeys = nullptr;
+    int* sdecision = nullptr;
     // debug outputs
     float* dbg_logits = nullptr;
     float* dbg_hidden = nullptr;
@@ -476,12 +477,12 @@ int sample_in(const spec_verify_ctx* c, const float* q, const float* u, float te
     return SV_OK;
 }
 
-// Tile statistics, residual draws, acceptance + commit (sampling.h).
+// Tile statistics, acceptance decision + draw, commit (sampling.h).
 int launch_sampling(spec_verify_ctx* c, const SampleIn& smp, const float* logits,
                     const int32_t* drafts, const int32_t* ctx_in, int32_t* ctx_out, int B,
                     int32_t* accepted, int32_t* next_tok, const int* seq_err, hipStream_t s)
 {
-    const int K1 = c->K1, K = K1 - 1, T = B * K1, nt = c->s_ntile;
+    const int K1 = c->K1, T = B * K1, nt = c->s_ntile;
     SampleArgs a;
     memset(&a, 0, sizeof(a));
     a.logits = logits;
@@ -497,17 +498,27 @@ int launch_sampling(spec_verify_ctx* c, const SampleIn& smp, const float* logits
     a.K1 = K1;
     a.ntile = nt;
     a.stats = c->sstats;
-    a.pkeys = c->spkeys;
-    a.rkeys = c->srkeys;
+    a.dkeys = c->sdkeys;
+    a.fkeys = c->sfkeys;
+    a.decision = c->sdecision;
     a.ctx_in = ctx_in;
     a.ctx_out = ctx_out;
     a.accepted = accepted;
     a.next_tok = next_tok;
     a.seq_err = seq_err;
     a.err_word = c->err_word;
-    sample_stats_kernel<<<dim3(nt, T), 256, 0, s>>>(a);
-    sample_residual_kernel<<<dim3(nt, B * K), 256, 0, s>>>(a);
-    sample_accept_kernel<<<B, 64, 0, s>>>(a);
+    {
+        ProfScope ps(c, SV_KC_SAMPLING, s);
+        launch(sample_stats_kernel, dim3(nt, T), dim3(256), 0, s, a);
+    }
+    {
+        ProfScope ps(c, SV_KC_SAMPLING, s);
+        launch(sample_draw_kernel, dim3(nt, B), dim3(256), 0, s, a);
+    }
+    {
+        ProfScope ps(c, SV_KC_SAMPLING, s);
+        launch(sample_finish_kernel, dim3(B), dim3(64), 0, s, a);
+    }
     HIP_TRY(hipGetLastError());
     return SV_OK;
 }
@@ -646,8 +657,9 @@ int spec_verify_init(const spec_verify_config* cfg, spec_verify_ctx** out)
         c->s_ntile = cdiv(k.vocab, SAMPLE_TILE);
         ALLOC(c->slogits, (size_t)T * k.vocab);
         ALLOC(c->sstats, (size_t)T * c->s_ntile);
-        ALLOC(c->spkeys, (size_t)T * c->s_ntile);
-        ALLOC(c->srkeys, (size_t)k.max_batch * k.k_draft * c->s_ntile);
+        ALLOC(c->sdkeys, (size_t)k.max_batch * c->s_ntile);
+        ALLOC(c->sfkeys, (size_t)k.max_batch * c->s_ntile);
+        ALLOC(c->sdecision, (size_t)k.max_batch);
     }
     if (k.ffn_kind == SV_FFN_MOE) {
         char* abuf = nullptr;
