@@ -75,3 +75,52 @@ def test_full_size_dense_fp8_k31(H):
 
 def test_full_size_moe_batch64_chained(H):
     _run(H, "moe_b64_long", sampled=[5, 40], steps=2)
+
+
+def test_full_size_sampled_moe_batch64(H):
+    """The sampled step at the batch-64 long-context workload's full size, in
+    the configuration the benchmark times: the outcome of every sequence
+    against the oracle's sampling on the GPU's logits, and two sequences'
+    logits against the oracle's own forward."""
+    from oracle import sampling as S
+    cfg = workloads.get_config("moe_b64_long")
+    case = H.Case(cfg)
+    B, K = cfg.batch, cfg.k_draft
+    sd = workloads.sampled_drafts(cfg)
+    H.say(f"[full sampled] B={B} L={cfg.n_layers} V={cfg.vocab} cap={case.cap}")
+    run = H.GpuRun(case)
+    dev = "cuda"
+    com = case.committed.to(dev, torch.int32).contiguous()
+    ci = case.ctx.to(dev, torch.int32).contiguous()
+    run.ctx.step_sampled(run.kc, run.vc, com, sd["drafts"].to(dev).contiguous(),
+                         sd["q"].to(dev).contiguous(), sd["u"].to(dev).contiguous(), 1.0,
+                         sd["seed"], sd["offset"], ci, run.ctx_out, run.acc, run.nxt, batch=B)
+    torch.cuda.synchronize()
+    ga, gn, gc = run.acc.cpu().numpy(), run.nxt.cpu().numpy(), run.ctx_out.cpu().numpy()
+    assert run.ctx.error_word(clear=True) == 0
+    glog = run.logits.cpu().double().numpy()
+    o = S.sampled_verify(glog, sd["drafts"].numpy(), sd["q"].numpy(), sd["u"].numpy(), 1.0,
+                         sd["seed"], sd["offset"], delta=1e-4, key_slack=1e-4)
+    sure = o["accept_certain"] & o["draw_certain"]
+    H.say(f"[full sampled] certain {int(sure.sum())}/{B}; accepted {ga[:8].tolist()}")
+    assert sure.mean() >= 0.9
+    for b in np.nonzero(sure)[0]:
+        assert ga[b] == o["accepted"][b] and gn[b] == o["next_tok"][b]
+        assert gc[b] == int(case.ctx[b]) + ga[b] + 1
+    orc = case.oracle()
+    tol = H.TOL[cfg.wdtype]
+    stats = {}
+    for b in (7, 50):
+        kc, vc = case.oracle_kv(b)
+        K1 = K + 1
+        forced = run.routing.cpu().numpy()[:, b * K1:(b + 1) * K1][None]
+        H.say(f"[full sampled] oracle forward of sequence {b} (ctx {int(case.ctx[b])})")
+        ob = orc.verify_step(kc, vc, [int(case.committed[b])], sd["drafts"][b:b + 1].numpy(),
+                             [int(case.ctx[b])], want_logits=True, force_sel=forced,
+                             want_routing=True)
+        H.check_routing(cfg, forced, ob, stats, label=f"seq {b}")
+        for j in range(K1):
+            lo = ob["logits"][0, j]
+            err = float(np.abs(glog[b, j] - lo).max())
+            assert err <= tol * float(lo.max() - lo.min()), f"seq {b} pos {j}: logits"
+    run.close()
