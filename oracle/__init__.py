@@ -23,8 +23,11 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "oracle.c")
 _LIB = os.path.join(_HERE, "liboracle.so")
 
-F32, BF16, FP8 = 0, 1, 2
-_DT = {"f32": F32, "bf16": BF16, "fp8": FP8}
+F32, BF16, FP8, MXFP4 = 0, 1, 2, 3
+_DT = {"f32": F32, "bf16": BF16, "fp8": FP8, "mxfp4": MXFP4}
+# matrices stored in the workload's `mx` format when it names one (the
+# weight-streaming ones: experts and the LM head)
+MX_MATRICES = ("w_gate_up", "w_down", "w_sh_gate_up", "w_sh_down", "lm_head")
 BAD_TOKEN, CAPACITY, NAN_LOGIT = 1, 2, 4
 
 
@@ -50,7 +53,7 @@ class _Cfg(ctypes.Structure):
 
 
 class _Mat(ctypes.Structure):
-    _fields_ = [("data", c_void_p), ("scale", c_void_p)]
+    _fields_ = [("data", c_void_p), ("scale", c_void_p), ("dtype", c_int)]
 
 
 class _Layer(ctypes.Structure):
@@ -89,6 +92,10 @@ def _load():
         lib.or_bf16_to_double.restype = c_double
         lib.or_e4m3_to_double.argtypes = [c_ubyte]
         lib.or_e4m3_to_double.restype = c_double
+        lib.or_e2m1_to_double.argtypes = [c_ubyte]
+        lib.or_e2m1_to_double.restype = c_double
+        lib.or_e8m0_to_double.argtypes = [c_ubyte]
+        lib.or_e8m0_to_double.restype = c_double
         lib.or_round_bf16.argtypes = [c_double]
         lib.or_round_bf16.restype = c_double
         lib.or_matvec.argtypes = [P, P, c_int, c_long, c_int, c_int, P, P]
@@ -193,7 +200,12 @@ class Oracle:
         m = _Mat()
         m.data = self._p(d[wkey])
         s = d.get(skey)
-        m.scale = self._p(s, np.float32) if s is not None else None
+        mx = getattr(self.cfg, "mx", "") == "mxfp4" and wkey in MX_MATRICES
+        m.dtype = MXFP4 if mx else -1
+        if s is None:
+            m.scale = None
+        else:
+            m.scale = self._p(s, np.uint8) if mx else self._p(s, np.float32)
         return m
 
     # ------------------------------------------------------------------ API
@@ -328,11 +340,15 @@ def silu(z):
 
 
 def matvec(W, x, dtype="f32", scale=None):
+    """y = W x.  mxfp4: W is the packed code matrix [N][K/2] (uint8) and
+    scale the E8M0 block scales [N][K/32] (uint8)."""
     Wn = as_np(W)
     x = _d(x)
-    N, K = Wn.shape
+    N = Wn.shape[0]
+    K = Wn.shape[1] * (2 if dtype == "mxfp4" else 1)
     y = np.zeros(N)
-    sc = None if scale is None else np.ascontiguousarray(as_np(scale), dtype=np.float32)
+    sdt = np.uint8 if dtype == "mxfp4" else np.float32
+    sc = None if scale is None else np.ascontiguousarray(as_np(scale), dtype=sdt)
     _load().or_matvec(_ptr(Wn), _ptr(sc), _DT[dtype], 0, N, K, _ptr(x), _ptr(y))
     return y
 
@@ -356,6 +372,14 @@ def bf16_to_double(bits: int) -> float:
 
 def e4m3_to_double(code: int) -> float:
     return _load().or_e4m3_to_double(code)
+
+
+def e2m1_to_double(code: int) -> float:
+    return _load().or_e2m1_to_double(code)
+
+
+def e8m0_to_double(code: int) -> float:
+    return _load().or_e8m0_to_double(code)
 
 
 def round_bf16(x: float) -> float:

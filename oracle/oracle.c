@@ -31,8 +31,9 @@
  * add.  A final RMSNorm, the LM head and an argmax give the greedy token.
  *
  * Arithmetic is fp64 throughout.  Stored weights are widened exactly from
- * their storage format (fp32, bf16 bit patterns, or OCP e4m3fn codes with one
- * fp32 scale per output row).  Two integer decisions are taken after
+ * their storage format (fp32, bf16 bit patterns, OCP e4m3fn codes with one
+ * fp32 scale per output row, or OCP MXFP4: E2M1 codes with one E8M0 scale per
+ * 32-element block of a row).  Two integer decisions are taken after
  * rounding the deciding values to fp32, the precision the GPU kernels decide
  * in: the expert selection (on the softmax probabilities) and the argmax (on
  * the logits).  New keys and values are rounded to the KV-cache storage type
@@ -53,7 +54,7 @@
 #include <stdlib.h>
 #include <string.h>
 
-enum { OR_F32 = 0, OR_BF16 = 1, OR_FP8 = 2 };
+enum { OR_F32 = 0, OR_BF16 = 1, OR_FP8 = 2, OR_MXFP4 = 3 };
 enum { OR_FFN_MOE = 0, OR_FFN_DENSE = 1 };
 
 /* per-sequence status bits */
@@ -71,11 +72,17 @@ typedef struct {
     int kvdtype;   /* storage of the KV cache (OR_F32 / OR_BF16) */
 } or_config;
 
-/* A row-major matrix [rows][cols]; `scale` is per row and used only for fp8. */
+/* A row-major matrix [rows][cols].  `dtype` is its storage type, or -1 for
+ * the config's wdtype.  fp8: `scale` holds one fp32 per row.  MXFP4: `data`
+ * holds two E2M1 codes per byte (even column in the low 4 bits), [rows][cols/2],
+ * and `scale` points to E8M0 bytes [rows][cols/32], one per 32-column block. */
 typedef struct {
     const void* data;
     const float* scale;
+    int dtype;
 } or_mat;
+
+static int mat_dt(const or_mat* m, int dflt) { return m->dtype >= 0 ? m->dtype : dflt; }
 
 typedef struct {
     const float* attn_norm;   /* [H] */
@@ -121,6 +128,23 @@ double or_e4m3_to_double(uint8_t c)
     return s ? -v : v;
 }
 
+/* OCP Microscaling (MX) formats: E2M1 is 1 sign bit, 2 exponent bits with
+ * bias 1 and 1 mantissa bit, a subnormal when the exponent field is 0 (values
+ * 0, 0.5, 1, 1.5, 2, 3, 4, 6 and their negatives; no infinities or NaN).  An
+ * MXFP4 block is 32 such elements sharing one E8M0 scale: an unsigned
+ * exponent with bias 127, 2^(s - 127), where 0xFF is NaN. */
+double or_e2m1_to_double(uint8_t c)
+{
+    int s = (c >> 3) & 1, e = (c >> 1) & 3, m = c & 1;
+    double v = e == 0 ? 0.5 * m : ldexp(1.0 + 0.5 * m, e - 1);
+    return s ? -v : v;
+}
+
+double or_e8m0_to_double(uint8_t s)
+{
+    return s == 0xFF ? NAN : ldexp(1.0, (int)s - 127);
+}
+
 /* Round to the nearest bf16 value (8 significant bits, ties to even), directly
  * from fp64 so that no intermediate rounding can move a tie. */
 double or_round_bf16(double x)
@@ -161,7 +185,8 @@ static void store_elem(int dtype, void* p, size_t i, double x)
 /* ------------------------------------------------------------- primitives */
 
 /* y[n] = sum_k W[row0 + n][k] * x[k] for n in [0, N), W row-major with K
- * columns; fp8 rows are scaled by their per-row scale after the sum. */
+ * columns; fp8 rows are scaled by their per-row scale after the sum; MXFP4
+ * elements are the E2M1 value times the block's E8M0 scale. */
 void or_matvec(const void* W, const float* scale, int dtype, long row0, int N, int K,
                const double* x, double* y)
 {
@@ -179,6 +204,14 @@ void or_matvec(const void* W, const float* scale, int dtype, long row0, int N, i
         case OR_BF16: {
             const uint16_t* w = (const uint16_t*)W + base;
             for (k = 0; k < K; k++) acc += or_bf16_to_double(w[k]) * x[k];
+        } break;
+        case OR_MXFP4: {
+            const uint8_t* w = (const uint8_t*)W + base / 2;
+            const uint8_t* sb = (const uint8_t*)scale + (size_t)(row0 + n) * (size_t)(K / 32);
+            for (k = 0; k < K; k++) {
+                uint8_t code = (k & 1) ? (uint8_t)(w[k >> 1] >> 4) : (uint8_t)(w[k >> 1] & 15);
+                acc += or_e2m1_to_double(code) * or_e8m0_to_double(sb[k >> 5]) * x[k];
+            }
         } break;
         default: {
             const uint8_t* w = (const uint8_t*)W + base;
@@ -281,10 +314,10 @@ void or_swiglu(const or_mat* gu, long gu_row0, const or_mat* dn, long dn_row0, i
     double* u = tmp + I;
     double* a = tmp + 2 * I;
     int i;
-    or_matvec(gu->data, gu->scale, dtype, gu_row0, I, H, h, g);
-    or_matvec(gu->data, gu->scale, dtype, gu_row0 + I, I, H, h, u);
+    or_matvec(gu->data, gu->scale, mat_dt(gu, dtype), gu_row0, I, H, h, g);
+    or_matvec(gu->data, gu->scale, mat_dt(gu, dtype), gu_row0 + I, I, H, h, u);
     for (i = 0; i < I; i++) a[i] = or_silu(g[i]) * u[i];
-    or_matvec(dn->data, dn->scale, dtype, dn_row0, H, I, a, y);
+    or_matvec(dn->data, dn->scale, mat_dt(dn, dtype), dn_row0, H, I, a, y);
 }
 
 /* Feed-forward half of a layer on the normalised input h[H]: routed experts
@@ -313,7 +346,7 @@ void or_ffn(const or_config* c, const or_layer* L, const double* h, double* y, c
         double* tmp = (double*)malloc(sizeof(double) * 3 * (size_t)I);
         int* idx = (int*)malloc(sizeof(int) * k);
         double gsum = 0.0;
-        or_matvec(L->w_router.data, L->w_router.scale, c->wdtype, 0, E, H, h, logit);
+        or_matvec(L->w_router.data, L->w_router.scale, mat_dt(&L->w_router, c->wdtype), 0, E, H, h, logit);
         or_softmax(logit, E, prob);
         if (force) for (r = 0; r < k; r++) idx[r] = force[r];
         else or_topk(prob, E, k, idx);
@@ -394,7 +427,8 @@ static void lm_logits(const or_config* c, const or_weights* w, const double* x, 
 {
     double* f = (double*)malloc(sizeof(double) * c->hidden);
     or_rmsnorm(x, w->final_norm, c->hidden, c->rms_eps, f);
-    or_matvec(w->lm_head.data, w->lm_head.scale, c->wdtype, 0, c->vocab, c->hidden, f, logits);
+    or_matvec(w->lm_head.data, w->lm_head.scale, mat_dt(&w->lm_head, c->wdtype), 0, c->vocab,
+              c->hidden, f, logits);
     free(f);
 }
 
@@ -428,7 +462,7 @@ static void forward_block(const or_config* c, const or_weights* w, void* kc, voi
             double* q = qkv + (size_t)j * QKV;
             long pos = ctx + j;
             or_rmsnorm(x + (size_t)j * H, L->attn_norm, H, c->rms_eps, h);
-            or_matvec(L->w_qkv.data, L->w_qkv.scale, c->wdtype, 0, QKV, H, h, q);
+            or_matvec(L->w_qkv.data, L->w_qkv.scale, mat_dt(&L->w_qkv, c->wdtype), 0, QKV, H, h, q);
             for (hh = 0; hh < nq + nkv; hh++) or_rope(q + (size_t)hh * D, D, pos, c->rope_theta);
             for (hh = 0; hh < nkv; hh++) {
                 const double* kk = q + (size_t)(nq + hh) * D;
@@ -453,7 +487,7 @@ static void forward_block(const or_config* c, const or_weights* w, void* kc, voi
                 or_attend(q + (size_t)hh * D, (const char*)kc + off * eb, (const char*)vc + off * eb,
                           c->kvdtype, D, nk, att + (size_t)hh * D, scratch + (size_t)hh * (ctx + n));
             }
-            or_matvec(L->w_o.data, L->w_o.scale, c->wdtype, 0, H, nq * D, att, o);
+            or_matvec(L->w_o.data, L->w_o.scale, mat_dt(&L->w_o, c->wdtype), 0, H, nq * D, att, o);
             for (i = 0; i < H; i++) xj[i] += o[i];
             or_rmsnorm(xj, L->ffn_norm, H, c->rms_eps, h);
             {

@@ -397,3 +397,76 @@ def test_routing_hook_forcing_own_choice_is_identity(oracle_mod):
     kc, vc = orc.kv_np(k, v)
     diff = orc.verify_step(kc, vc, *args, want_logits=True, force_sel=other)
     assert np.abs(diff["logits"] - free["logits"]).max() > 1e-6
+
+
+# ------------------------------------------------------------------ MXFP4
+# OCP Microscaling Formats (MX) v1.0, E2M1 element encoding: the 16 codes
+E2M1_TABLE = [0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0,
+              -0.0, -0.5, -1.0, -1.5, -2.0, -3.0, -4.0, -6.0]
+
+
+def test_e2m1_and_e8m0_codes(oracle_mod):
+    got = [oracle_mod.e2m1_to_double(c) for c in range(16)]
+    assert got == E2M1_TABLE
+    assert np.signbit(got[8])
+    assert oracle_mod.e8m0_to_double(127) == 1.0
+    assert oracle_mod.e8m0_to_double(0) == 2.0 ** -127
+    assert oracle_mod.e8m0_to_double(254) == 2.0 ** 127
+    assert math.isnan(oracle_mod.e8m0_to_double(255))
+
+
+def _mx_dequant_numpy(packed, scales):
+    """Reference decoding written from the format's definition: element 2i in
+    the low nibble of byte i, value = table[code] * 2^(scale - 127)."""
+    lo, hi = packed & 15, packed >> 4
+    codes = np.stack([lo, hi], axis=-1).reshape(packed.shape[0], -1)
+    vals = np.array(E2M1_TABLE)[codes]
+    return vals * np.repeat(np.ldexp(1.0, scales.astype(np.int64) - 127), 32, axis=1)
+
+
+def test_mxfp4_matvec_matches_numpy(oracle_mod):
+    rng = np.random.default_rng(4)
+    N, K = 37, 256
+    packed = rng.integers(0, 256, (N, K // 2), dtype=np.uint8)
+    scales = rng.integers(110, 140, (N, K // 32), dtype=np.uint8)
+    x = rng.normal(size=K)
+    y = oracle_mod.matvec(packed, x, dtype="mxfp4", scale=scales)
+    np.testing.assert_allclose(y, _mx_dequant_numpy(packed, scales) @ x, rtol=1e-12, atol=1e-12)
+
+
+def test_mxfp4_quantizer_rounds_to_nearest(oracle_mod):
+    """The workloads' MXFP4 quantizer: block scale 2^(floor(log2 amax) - 2),
+    every element the nearest representable value (brute force over the 16
+    codes), ties to the even code."""
+    from workloads.synth import _quant_mxfp4
+    g = torch.Generator().manual_seed(9)
+    w = torch.randn(24, 128, generator=g) * 0.02
+    w[3, 5] = 0.0
+    w[4, :32] = 0.0                        # an all-zero block
+    packed, scales = _quant_mxfp4(w)
+    deq = _mx_dequant_numpy(packed.numpy(), scales.numpy())
+    wn = w.double().numpy()
+    for r in range(24):
+        for blk in range(4):
+            seg = wn[r, 32 * blk:32 * blk + 32]
+            amax = np.abs(seg).max()
+            e = int(np.floor(np.log2(amax))) - 2 if amax > 0 else -127
+            assert int(scales[r, blk]) == e + 127
+            cand = np.array(E2M1_TABLE) * 2.0 ** e
+            for i, v in enumerate(seg):
+                best = np.abs(cand - v).min()
+                assert abs(deq[r, 32 * blk + i] - v) == best
+    # ties go to the even code: 2.5 -> 2, 5 -> 4, 0.25 -> 0 (block amax 5 -> scale 1)
+    t = torch.zeros(1, 32)
+    t[0, :4] = torch.tensor([4.0, 2.5, 5.0, 0.25])
+    p2, s2 = _quant_mxfp4(t)
+    d2 = _mx_dequant_numpy(p2.numpy(), s2.numpy())[0, :4]
+    assert d2.tolist() == [4.0, 2.0, 4.0, 0.0]
+
+
+def test_lossless_moe_mxfp4_scaled(oracle_mod):
+    cfg = workloads.scaled(workloads.get_config("moe_b1_mxfp4"), hidden=128, n_q=2, n_kv=2,
+                           head_dim=64, n_experts=8, expert_inter=64, top_k=3, n_shared=2,
+                           vocab=512, n_layers=2, batch=3, ctx=("uniform", 20, 90),
+                           draft_p=("const", 0.8))
+    _lossless_case(oracle_mod, cfg)

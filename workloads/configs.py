@@ -50,6 +50,7 @@ class VerifyConfig:
     seed: int = 0
     weight_std: float = 0.02
     norm_gain_std: float = 0.0    # 0: gains are exactly 1
+    mx: str = ""                  # "mxfp4": experts and LM head in OCP MXFP4 (others per wdtype)
     description: str = field(default="", compare=False)
 
     @property
@@ -91,6 +92,15 @@ CONFIGS = {
         wdtype="bf16", kvdtype="bf16", embdtype="bf16", ctx=("loguniform", 1000, 12000),
         draft_p=("const", 0.576), steps=100,
         description="12 MoE layers, bf16, batch 64, contexts log-U[1000,12000], K=3, 100 chained steps"),
+    # the batch-1 workload with the weight-streaming matrices (experts, LM
+    # head) in OCP MXFP4: gfx950 widens E2M1 with a block scale exactly to
+    # bf16; about a quarter of the bf16 bytes
+    "moe_b1_mxfp4": VerifyConfig(
+        name="moe_b1_mxfp4", n_layers=1, hidden=1280, n_q=10, n_kv=10, head_dim=128, ffn="moe",
+        n_experts=64, expert_inter=896, top_k=6, n_shared=2, vocab=129280, batch=1, k_draft=3,
+        wdtype="bf16", kvdtype="bf16", embdtype="bf16", ctx=("fixed", 1341),
+        draft_p=("const", 0.576), mx="mxfp4",
+        description="moe_b1 with MXFP4 experts and LM head (bf16 attention, router, embedding)"),
 }
 
 # index of each workload in the order the workload list gives them

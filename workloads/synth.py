@@ -52,10 +52,42 @@ def _quant_e4m3_rows(w: torch.Tensor):
     return q.view(torch.uint8), s.squeeze(-1).to(torch.float32)
 
 
-def _linear(cfg: VerifyConfig, shape, device, name):
-    """A linear weight of the given shape in the workload's storage format.
-    Returns (tensor, per-row scale or None)."""
+# E2M1 magnitudes by code (OCP Microscaling formats v1.0: 1 sign, 2 exponent
+# bits with bias 1, 1 mantissa bit)
+_E2M1 = (0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0)
+
+
+def _quant_mxfp4(w: torch.Tensor):
+    """MXFP4 along the last dimension (a multiple of 32): per 32-element block
+    an E8M0 scale 2^e with e = floor(log2(amax)) - 2 (the largest E2M1
+    exponent), elements w / 2^e rounded to the nearest E2M1 value (ties to the
+    even code) and saturated at +-6.  Returns (codes packed two per byte, even
+    element in the low 4 bits, uint8 [..., K/2]; scale bytes e + 127, uint8
+    [..., K/32])."""
+    shp = w.shape
+    K = shp[-1]
+    wb = w.to(torch.float64).reshape(*shp[:-1], K // 32, 32)
+    amax = wb.abs().amax(dim=-1, keepdim=True)
+    e = torch.where(amax > 0, torch.floor(torch.log2(torch.where(amax > 0, amax, 1.0))) - 2,
+                    torch.full_like(amax, -127.0)).clamp(-127, 127)
+    x = (wb / torch.exp2(e)).abs()
+    grid = torch.tensor(_E2M1, dtype=torch.float64, device=w.device)
+    d = (x.unsqueeze(-1) - grid).abs()
+    odd = torch.tensor([0, 1, 0, 1, 0, 1, 0, 1], dtype=torch.float64, device=w.device)
+    code = torch.argmin(d + odd * 1e-9 * (d.amin(-1, keepdim=True) == d), dim=-1)
+    code = code.to(torch.uint8) | ((wb < 0).to(torch.uint8) << 3)
+    code = code.reshape(*shp[:-1], K)
+    packed = code[..., 0::2] | (code[..., 1::2] << 4)
+    return packed.contiguous(), (e.squeeze(-1) + 127).to(torch.uint8).contiguous()
+
+
+def _linear(cfg: VerifyConfig, shape, device, name, mx_ok=False):
+    """A linear weight of the given shape in the workload's storage format
+    (the workload's `mx` format for the weight-streaming matrices when it
+    names one).  Returns (tensor, per-row scale, block scales or None)."""
     w = _normal(shape, cfg.weight_std, device, cfg.seed, name)
+    if mx_ok and cfg.mx == "mxfp4":
+        return _quant_mxfp4(w)
     if cfg.wdtype == "fp8":
         return _quant_e4m3_rows(w)
     return w.to(_TORCH_DT[cfg.wdtype]), None
@@ -75,7 +107,10 @@ def make_weights(cfg: VerifyConfig, device="cpu") -> dict:
     w_o [H][n_q D], ffn_norm [H] and either (MoE) w_router [E][H],
     w_gate_up [E][2I][H], w_down [E][H][I], w_sh_gate_up [S][2I][H],
     w_sh_down [S][H][I], or (dense) w_gate_up [2I][H], w_down [H][I].  Each
-    matrix `w_x` stored in fp8 has a companion `s_x` of per-row scales.
+    matrix `w_x` stored in fp8 has a companion `s_x` of per-row scales.  With
+    mx = "mxfp4" the expert matrices and the LM head are MXFP4: `w_x` holds
+    the packed codes [..][K/2] (uint8) and `s_x` (lm_scale) the E8M0 block
+    scales [..][K/32] (uint8).
     """
     H, D = cfg.hidden, cfg.head_dim
     out = {}
@@ -92,11 +127,13 @@ def make_weights(cfg: VerifyConfig, device="cpu") -> dict:
         if cfg.ffn == "moe":
             E, I, S = cfg.n_experts, cfg.expert_inter, cfg.n_shared
             L["w_router"], L["s_router"] = _linear(cfg, (E, H), device, p + "w_router")
-            L["w_gate_up"], L["s_gate_up"] = _linear(cfg, (E, 2 * I, H), device, p + "w_gate_up")
-            L["w_down"], L["s_down"] = _linear(cfg, (E, H, I), device, p + "w_down")
+            L["w_gate_up"], L["s_gate_up"] = _linear(cfg, (E, 2 * I, H), device, p + "w_gate_up",
+                                                    mx_ok=True)
+            L["w_down"], L["s_down"] = _linear(cfg, (E, H, I), device, p + "w_down", mx_ok=True)
             L["w_sh_gate_up"], L["s_sh_gate_up"] = _linear(cfg, (S, 2 * I, H), device,
-                                                          p + "w_sh_gate_up")
-            L["w_sh_down"], L["s_sh_down"] = _linear(cfg, (S, H, I), device, p + "w_sh_down")
+                                                          p + "w_sh_gate_up", mx_ok=True)
+            L["w_sh_down"], L["s_sh_down"] = _linear(cfg, (S, H, I), device, p + "w_sh_down",
+                                                    mx_ok=True)
         else:
             I = cfg.dense_inter
             L["w_gate_up"], L["s_gate_up"] = _linear(cfg, (2 * I, H), device, p + "w_gate_up")
@@ -104,7 +141,8 @@ def make_weights(cfg: VerifyConfig, device="cpu") -> dict:
         layers.append(L)
     out["layers"] = layers
     out["final_norm"] = _gain(cfg, H, device, "final_norm")
-    out["lm_head"], out["lm_scale"] = _linear(cfg, (cfg.vocab, H), device, "lm_head")
+    out["lm_head"], out["lm_scale"] = _linear(cfg, (cfg.vocab, H), device, "lm_head",
+                                              mx_ok=True)
     return out
 
 
