@@ -79,6 +79,8 @@ def lm_head_bytes(cfg, T, logits=False):
     for sampled verification the fp32 logits written."""
     V, H = cfg.vocab, cfg.hidden
     w = V * H * WBYTES[cfg.wdtype] + (V * 4 if cfg.wdtype == "fp8" else 0)
+    if cfg.mx == "mxfp4":            # half-byte codes + one scale byte per 32
+        w = V * H // 2 + V * H // 32
     act = T * H * (4 if cfg.wdtype == "f32" else 2)
     keys = ((V + 63) // 64) * T * 8
     return w + act + keys + (T * V * 4 if logits else 0)
@@ -99,10 +101,15 @@ def step_bytes(cfg, ctx, distinct_experts):
         total += per_layer
         if cfg.ffn == "moe":
             ex = 3 * H * cfg.expert_inter * wb
+            if cfg.mx == "mxfp4":
+                ex = 3 * H * cfg.expert_inter * 17 // 32     # codes + block scales
             total += cfg.n_experts * H * wb + (distinct_experts[l] + cfg.n_shared) * ex
         else:
             total += 3 * H * cfg.dense_inter * wb + (3 * cfg.dense_inter) * sc
-    total += cfg.vocab * H * wb + cfg.vocab * sc                 # LM head
+    if cfg.mx == "mxfp4":
+        total += cfg.vocab * H * 17 // 32                        # LM head codes + scales
+    else:
+        total += cfg.vocab * H * wb + cfg.vocab * sc             # LM head
     total += T * H * (4 if cfg.embdtype == "f32" else 2)        # embedding rows
     kv_read = sum(int(c) + cfg.k_draft + 1 for c in ctx) * 2 * cfg.n_kv * D * L * kvb
     kv_write = T * 2 * cfg.n_kv * D * L * kvb
@@ -341,7 +348,8 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16" if cfg.wdtype == "bf16" else cfg.wdtype,
+        "dtype": ("bf16+mxfp4" if cfg.mx == "mxfp4" else
+                  ("bf16" if cfg.wdtype == "bf16" else cfg.wdtype)),
         "data": "synthetic (seeded N(0,0.02) weights, seeded KV cache and drafts)",
         "config": {"workload": cfg.name, "batch": cfg.batch, "k_draft": cfg.k_draft,
                    "layers": cfg.n_layers, "hidden": cfg.hidden, "vocab": cfg.vocab,

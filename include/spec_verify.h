@@ -51,9 +51,21 @@
  *   SV_BF16  bfloat16 (the upper 16 bits of a binary32).
  *   SV_FP8   OCP 8-bit float E4M3FN (bias 7, max 448, no infinities), with one
  *            fp32 scale per output row of every matrix: W[n][k] = code * s[n].
+ *   SV_MXFP4 OCP Microscaling MXFP4 (OCP MX formats v1.0): E2M1 codes (1 sign,
+ *            2 exponent bits with bias 1, 1 mantissa bit: 0, 0.5, 1, 1.5, 2, 3,
+ *            4, 6), two per byte (the even column in the low 4 bits), and one
+ *            E8M0 scale byte 2^(s - 127) per 32 consecutive elements of a row.
  * Supported combinations: weights, embedding, activations and KV cache all
  * SV_F32; or weights SV_BF16 or SV_FP8 with embedding and KV cache SV_BF16
- * (activations bf16, accumulation fp32).
+ * (activations bf16, accumulation fp32).  With mx_dtype = SV_MXFP4 (bf16
+ * MoE models, max_batch * (K+1) < 64, hidden and expert_inter multiples of
+ * 128, tiled16 layout) the weight-streaming matrices -- w_gate_up, w_down,
+ * w_sh_gate_up, w_sh_down and lm_head -- are MXFP4: each is the byte matrix
+ * [rows][cols/2] of codes, packed with spec_verify_pack_tiled16 as an SV_FP8
+ * matrix of cols/2 columns, and its s_x pointer (lm_scale for the LM head)
+ * points to the row-major E8M0 bytes [rows][cols/32] (per expert stack:
+ * [E][rows][cols/32]).  The codes are widened exactly to bf16 (gfx950
+ * v_cvt_scalef32_pk_bf16_fp4) and multiplied on the bf16 matrix cores.
  *
  * Weight layouts (row-major, [out][in] per matrix, contiguous):
  *   embed        [V][H]                       embedding storage type
@@ -109,7 +121,7 @@
 extern "C" {
 #endif
 
-#define SPEC_VERIFY_ABI_VERSION 2
+#define SPEC_VERIFY_ABI_VERSION 3
 
 /* status codes */
 #define SV_OK 0
@@ -123,6 +135,7 @@ extern "C" {
 #define SV_F32 0
 #define SV_BF16 1
 #define SV_FP8 2
+#define SV_MXFP4 3                /* expert and LM-head weights only (spec_verify_config.mx_dtype) */
 
 /* feed-forward kinds */
 #define SV_FFN_MOE 0
@@ -171,6 +184,7 @@ typedef struct {
     int weight_dtype;   /* SV_F32 / SV_BF16 / SV_FP8 */
     int embed_dtype;    /* SV_F32 / SV_BF16 */
     int kv_dtype;       /* SV_F32 / SV_BF16 */
+    int mx_dtype;       /* 0, or SV_MXFP4: expert matrices and LM head in OCP MXFP4 (below) */
 } spec_verify_config;
 
 typedef struct {

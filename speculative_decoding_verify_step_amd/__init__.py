@@ -17,7 +17,7 @@ LIB_PATH = os.path.join(_HERE, "libspecverify.so")
 
 SV_OK, SV_ERR_INVALID_ARG, SV_ERR_UNSUPPORTED, SV_ERR_HIP, SV_ERR_NO_DEVICE, SV_ERR_NOT_SET = (
     0, -1, -2, -3, -4, -5)
-SV_F32, SV_BF16, SV_FP8 = 0, 1, 2
+SV_F32, SV_BF16, SV_FP8, SV_MXFP4 = 0, 1, 2, 3
 SV_FFN_MOE, SV_FFN_DENSE = 0, 1
 SV_DEV_BAD_TOKEN, SV_DEV_CAPACITY, SV_DEV_NAN_LOGIT = 1, 2, 4
 (SV_KC_LM_HEAD, SV_KC_ATTENTION, SV_KC_EXPERT_GATE_UP, SV_KC_EXPERT_DOWN, SV_KC_QKV,
@@ -45,7 +45,8 @@ class SpecVerifyConfig(ctypes.Structure):
                 ("n_shared", c_int), ("renorm_topk", c_int), ("dense_inter", c_int),
                 ("vocab", c_int), ("max_batch", c_int), ("k_draft", c_int),
                 ("kv_capacity", c_int), ("rope_theta", c_float), ("rms_eps", c_float),
-                ("weight_dtype", c_int), ("embed_dtype", c_int), ("kv_dtype", c_int)]
+                ("weight_dtype", c_int), ("embed_dtype", c_int), ("kv_dtype", c_int),
+                ("mx_dtype", c_int)]
 
 
 class SpecVerifyLayer(ctypes.Structure):
@@ -153,6 +154,7 @@ def make_config(cfg, max_batch: int, kv_capacity: int) -> SpecVerifyConfig:
     c.vocab, c.max_batch, c.k_draft, c.kv_capacity = cfg.vocab, max_batch, cfg.k_draft, kv_capacity
     c.rope_theta, c.rms_eps = cfg.rope_theta, cfg.rms_eps
     c.weight_dtype, c.embed_dtype, c.kv_dtype = _DT[cfg.wdtype], _DT[cfg.embdtype], _DT[cfg.kvdtype]
+    c.mx_dtype = SV_MXFP4 if getattr(cfg, "mx", "") == "mxfp4" else 0
     return c
 
 

@@ -71,6 +71,12 @@ template <int WT> struct WTraits;
 template <> struct WTraits<SV_F32> { static constexpr int KL = 4, SK = 16, XU = 1, ESZ = 4; };
 template <> struct WTraits<SV_BF16> { static constexpr int KL = 8, SK = 32, XU = 1, ESZ = 2; };
 template <> struct WTraits<SV_FP8> { static constexpr int KL = 16, SK = 64, XU = 2, ESZ = 1; };
+// MXFP4 (tiled16 layout only): 32 E2M1 codes per 16-byte lane slice, one E8M0
+// scale byte per slice; ESZ is not used (a code is half a byte)
+template <> struct WTraits<SV_MXFP4> { static constexpr int KL = 32, SK = 128, XU = 4, ESZ = 1; };
+
+// weight element size in half-bytes (byte offsets of packed 4-bit codes)
+template <int WT> constexpr int w_half_bytes() { return WT == SV_F32 ? 8 : (WT == SV_BF16 ? 4 : (WT == SV_FP8 ? 2 : 1)); }
 
 // activation element size: fp32 with fp32 weights, bf16 otherwise
 template <int WT> struct ATraits { static constexpr int ESZ = (WT == SV_F32) ? 4 : 2; };
@@ -78,7 +84,37 @@ template <int WT> struct ATraits { static constexpr int ESZ = (WT == SV_F32) ? 4
 // A weight slice in MFMA operand form: one 16-byte operand (fp32, bf16) or
 // two bf16 operands widened from 16 e4m3 codes (fp8) -- converted once per
 // fragment and reused for every row fragment.
-template <int WT> struct WOp { uint4 v[WT == SV_FP8 ? 2 : 1]; };
+template <int WT> struct WOp { uint4 v[WT == SV_FP8 ? 2 : (WT == SV_MXFP4 ? 4 : 1)]; };
+
+// E8M0 scale byte -> 2^(s - 127) (0 -> 2^-127, a subnormal; 0xFF -> NaN)
+SV_DEV float e8m0_to_f32(uint32_t s)
+{
+    return s == 0u ? __uint_as_float(0x00400000u)
+                   : (s == 255u ? __uint_as_float(0x7fc00000u) : __uint_as_float(s << 23));
+}
+
+// 8 E2M1 codes (one 32-bit word, element 2i in the low half of byte i) times
+// the block scale -> 8 bf16 in MFMA operand order: gfx950 converts two codes
+// per instruction, exactly (a code times a power of two is a bf16 value)
+SV_DEV uint4 e2m1x8_to_bf16(uint32_t w, float s)
+{
+    return make_uint4(__builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, s, 0)),
+                      __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, s, 1)),
+                      __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, s, 2)),
+                      __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, s, 3)));
+}
+
+// a 16-byte MXFP4 lane slice (32 codes, one block) -> four bf16 operands
+SV_DEV WOp<SV_MXFP4> wprep_mx(uint4 w, uint32_t sb)
+{
+    const float s = e8m0_to_f32(sb);
+    WOp<SV_MXFP4> o;
+    o.v[0] = e2m1x8_to_bf16(w.x, s);
+    o.v[1] = e2m1x8_to_bf16(w.y, s);
+    o.v[2] = e2m1x8_to_bf16(w.z, s);
+    o.v[3] = e2m1x8_to_bf16(w.w, s);
+    return o;
+}
 
 template <int WT>
 SV_DEV WOp<WT> wprep(uint4 w)
@@ -96,6 +132,11 @@ SV_DEV f32x4_t mma_op(const WOp<WT>& w, const uint4* x, f32x4_t c)
         return mma_f32x4(w.v[0], x[0], c);
     } else if constexpr (WT == SV_BF16) {
         return mma_bf16(w.v[0], x[0], c);
+    } else if constexpr (WT == SV_MXFP4) {
+        c = mma_bf16(w.v[0], x[0], c);
+        c = mma_bf16(w.v[1], x[1], c);
+        c = mma_bf16(w.v[2], x[2], c);
+        return mma_bf16(w.v[3], x[3], c);
     } else {
         c = mma_bf16(w.v[0], x[0], c);
         return mma_bf16(w.v[1], x[1], c);
@@ -217,12 +258,18 @@ template <int WT, int MF, int NF, int MODE, int WAVES = 4, int UU = 0, bool PACK
 __global__ __launch_bounds__(64 * WAVES) void gemm_kernel(GemmArgs a)
 {
     static_assert(!KW || MODE != GM_ARGMAX, "K-split waves: STORE and SWIGLU epilogues only");
+    constexpr bool MX = WT == SV_MXFP4;
+    static_assert(!MX || PACKED, "MXFP4 weights: tiled16 layout only");
     using Tr = WTraits<WT>;
     constexpr int KL = Tr::KL, SK = Tr::SK, XU = Tr::XU, WESZ = Tr::ESZ;
+    constexpr int EH = w_half_bytes<WT>();
     constexpr int AESZ = ATraits<WT>::ESZ;
     constexpr int NFT = (MODE == GM_SWIGLU) ? 2 * NF : NF;   // weight fragments per wave
     constexpr int BM = 16 * MF;
-    constexpr int U = UU ? UU : ((MF >= 4) ? 2 : (MF == 2 ? 4 : 8));   // reduction steps per stage
+    // reduction steps per stage (by row count unless given; an MXFP4 step
+    // carries four bf16 steps of activations, so half as many by default)
+    constexpr int U0 = (MF >= 4) ? 2 : (MF == 2 ? 4 : 8);
+    constexpr int U = UU ? UU : (MX ? U0 / 2 : U0);
 
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
@@ -268,12 +315,15 @@ __global__ __launch_bounds__(64 * WAVES) void gemm_kernel(GemmArgs a)
 
     const char* Wb;
     const float* sc;
+    const uint8_t* scb = nullptr;   // MXFP4: the group's E8M0 block scales [rows][K/32]
     if (group < a.G1) {
-        Wb = (const char*)a.W + (size_t)group * a.w_gstride * WESZ;
+        Wb = (const char*)a.W + (size_t)group * a.w_gstride * EH / 2;
         sc = a.ws ? a.ws + (size_t)group * a.s_gstride : nullptr;
+        if constexpr (MX) scb = (const uint8_t*)a.ws + (size_t)group * a.s_gstride;
     } else {
-        Wb = (const char*)a.W2 + (size_t)(group - a.G1) * a.w2_gstride * WESZ;
+        Wb = (const char*)a.W2 + (size_t)(group - a.G1) * a.w2_gstride * EH / 2;
         sc = a.ws2 ? a.ws2 + (size_t)(group - a.G1) * a.s2_gstride : nullptr;
+        if constexpr (MX) scb = (const uint8_t*)a.ws2 + (size_t)(group - a.G1) * a.s2_gstride;
     }
 
     const int ncol0 = KW ? nt * 16 * NF : (nt * WAVES + wave) * 16 * NF;   // this wave's first column
@@ -293,6 +343,7 @@ __global__ __launch_bounds__(64 * WAVES) void gemm_kernel(GemmArgs a)
 
     // weight rows of this lane, one per fragment (invalid fragments read row 0)
     const char* wrow[NFT];
+    const uint8_t* srow[MX ? NFT : 1];   // MXFP4: this lane's scale byte of step 0
     bool fvalid[NF];
 #pragma unroll
     for (int f = 0; f < NF; f++) {
@@ -303,9 +354,14 @@ __global__ __launch_bounds__(64 * WAVES) void gemm_kernel(GemmArgs a)
             // 16-row blocks stored step-major: block rb, step s at ((rb * K/SK) + s) KiB,
             // lane l's 16 bytes at l * 16; the k offset below is in elements of SK per KiB
             int rb = fvalid[f] ? n0 / 16 : 0;
-            wrow[f] = Wb + (size_t)rb * K * 16 * WESZ + (size_t)lane * 16;
+            wrow[f] = Wb + (size_t)rb * K * 8 * EH + (size_t)lane * 16;
             if constexpr (MODE == GM_SWIGLU)
-                wrow[NF + f] = Wb + (size_t)(rb + a.dual_off / 16) * K * 16 * WESZ + (size_t)lane * 16;
+                wrow[NF + f] = Wb + (size_t)(rb + a.dual_off / 16) * K * 8 * EH + (size_t)lane * 16;
+            if constexpr (MX) {
+                // the lane's 32 codes of step s are block 4 s + lg of its row
+                srow[f] = scb + (size_t)r * (K / 32) + lg;
+                if constexpr (MODE == GM_SWIGLU) srow[NF + f] = scb + (size_t)(r + a.dual_off) * (K / 32) + lg;
+            }
         } else {
             wrow[f] = Wb + ((size_t)r * K + (size_t)lg * KL) * WESZ;
             if constexpr (MODE == GM_SWIGLU)
@@ -332,8 +388,10 @@ __global__ __launch_bounds__(64 * WAVES) void gemm_kernel(GemmArgs a)
 
     uint4 wA[U][NFT], wB[U][NFT];
     uint4 xA[U][MF][XU], xB[U][MF][XU];
+    uint32_t sA[U][MX ? NFT : 1], sB[U][MX ? NFT : 1];   // MXFP4 scale bytes
 
-    auto load = [&](int k, uint4 (&w)[U][NFT], uint4 (&x)[U][MF][XU]) {
+    auto load = [&](int k, uint4 (&w)[U][NFT], uint4 (&x)[U][MF][XU],
+                    uint32_t (&sb)[U][MX ? NFT : 1]) {
 #pragma unroll
         for (int u = 0; u < U; u++) {
             int kk = k + u * SK;
@@ -342,6 +400,7 @@ __global__ __launch_bounds__(64 * WAVES) void gemm_kernel(GemmArgs a)
                 for (int f = 0; f < NFT; f++) {
                     if constexpr (PACKED) w[u][f] = ldg16_stream(wrow[f] + (size_t)(kk / SK) * 1024);
                     else w[u][f] = ldg16_stream(wrow[f] + (size_t)kk * WESZ);
+                    if constexpr (MX) sb[u][f] = srow[f][kk / 32];
                 }
 #pragma unroll
                 for (int m = 0; m < MF; m++)
@@ -351,13 +410,16 @@ __global__ __launch_bounds__(64 * WAVES) void gemm_kernel(GemmArgs a)
             }
         }
     };
-    auto compute = [&](int k, uint4 (&w)[U][NFT], uint4 (&x)[U][MF][XU]) {
+    auto compute = [&](int k, uint4 (&w)[U][NFT], uint4 (&x)[U][MF][XU],
+                       uint32_t (&sb)[U][MX ? NFT : 1]) {
 #pragma unroll
         for (int u = 0; u < U; u++) {
             if (k + u * SK < ke) {
 #pragma unroll
                 for (int f = 0; f < NFT; f++) {
-                    const WOp<WT> wo = wprep<WT>(w[u][f]);
+                    WOp<WT> wo;
+                    if constexpr (MX) wo = wprep_mx(w[u][f], sb[u][f]);
+                    else wo = wprep<WT>(w[u][f]);
 #pragma unroll
                     for (int m = 0; m < MF; m++) acc[m][f] = mma_op<WT>(wo, x[u][m], acc[m][f]);
                 }
@@ -366,12 +428,12 @@ __global__ __launch_bounds__(64 * WAVES) void gemm_kernel(GemmArgs a)
     };
 
     constexpr int STAGE = U * SK;
-    if (kb < ke) load(kb, wA, xA);
+    if (kb < ke) load(kb, wA, xA, sA);
     for (int k = kb; k < ke; k += 2 * STAGE) {
-        if (k + STAGE < ke) load(k + STAGE, wB, xB);
-        compute(k, wA, xA);
-        if (k + 2 * STAGE < ke) load(k + 2 * STAGE, wA, xA);
-        if (k + STAGE < ke) compute(k + STAGE, wB, xB);
+        if (k + STAGE < ke) load(k + STAGE, wB, xB, sB);
+        compute(k, wA, xA, sA);
+        if (k + 2 * STAGE < ke) load(k + 2 * STAGE, wA, xA, sA);
+        if (k + STAGE < ke) compute(k + STAGE, wB, xB, sB);
     }
     if constexpr (KW) {
         // partial sums of waves 1.. through shared memory, added by wave 0 in wave order

@@ -59,7 +59,7 @@ inline int cdiv(long a, long b) { return (int)((a + b - 1) / b); }
 
 int wsteps(int wt)
 {
-    return wt == SV_F32 ? 16 : (wt == SV_BF16 ? 32 : 64);
+    return wt == SV_F32 ? 16 : (wt == SV_BF16 ? 32 : (wt == SV_FP8 ? 64 : 128));
 }
 
 struct EventPair {
@@ -188,6 +188,15 @@ int validate_config(const spec_verify_config& c)
     } else {
         return bad("unknown ffn_kind");
     }
+    if (c.mx_dtype != 0) {
+        if (c.mx_dtype != SV_MXFP4) return bad("mx_dtype must be 0 or SV_MXFP4");
+        if (c.weight_dtype != SV_BF16 || c.ffn_kind != SV_FFN_MOE)
+            return bad("MXFP4 expert and LM-head weights need a bf16 MoE model");
+        if (c.hidden % 128 || c.expert_inter % 128)
+            return bad("MXFP4 weights need hidden and expert_inter multiples of 128");
+        if ((long)c.max_batch * (c.k_draft + 1) >= 64)
+            return bad("MXFP4 weights are supported for max_batch*(K+1) < 64 rows");
+    }
     return SV_OK;
 }
 
@@ -220,12 +229,59 @@ void launch_gemm_t(int MF, const GemmArgs& a, dim3 grid, hipStream_t s)
     }
 }
 
+// MXFP4 weights (a quarter of the bf16 bytes per column): wider wave tiles so
+// that a wave still streams as many bytes as a bf16 wave.  LM head: 4 column
+// fragments per wave (256-column workgroup tiles), 2 steps per stage.
+// Grouped experts: gate/up one column fragment per wave as with bf16 (at
+// batch 1 wider tiles leave too few waves: 11.7 -> 13.2 us with two), down 4
+// (its 2 waves split the reduction; 9.2 -> 8.6 us), 2 steps per stage.
+constexpr int MX_LM_NF = 4, MX_LM_U = 2, MX_GU_NF = 1, MX_DN_NF = 4;
+
+int small_col_tile(int wt, int mode) { return (wt == SV_MXFP4 && mode == GM_ARGMAX) ? 64 * MX_LM_NF : 64; }
+
+// columns of one grouped-expert workgroup tile on the small-row kernel
+int grouped_col_tile(int wt, int mode)
+{
+    if (wt != SV_MXFP4) return 16;
+    return 16 * (mode == GM_SWIGLU ? MX_GU_NF : MX_DN_NF);
+}
+
+template <int MODE>
+void launch_gemm_mx(int MF, const GemmArgs& a, dim3 grid, hipStream_t s)
+{
+    constexpr int WT = SV_MXFP4;
+    if (a.tiles || a.sel) {   // grouped experts: the bf16 variants' shapes (2 steps per stage)
+        if constexpr (MODE == GM_SWIGLU) {
+            switch (MF) {
+            case 1: launch(gemm_kernel<WT, 1, MX_GU_NF, MODE, 1, 0, true>, grid, dim3(64), 0, s, a); break;
+            case 2: launch(gemm_kernel<WT, 2, MX_GU_NF, MODE, 1, 0, true>, grid, dim3(64), 0, s, a); break;
+            default: launch(gemm_kernel<WT, 4, MX_GU_NF, MODE, 1, 0, true>, grid, dim3(64), 0, s, a); break;
+            }
+        } else if constexpr (MODE == GM_STORE) {
+            switch (MF) {
+            case 1: launch(gemm_kernel<WT, 1, MX_DN_NF, MODE, 2, 2, true, true>, grid, dim3(128), 0, s, a); break;
+            case 2: launch(gemm_kernel<WT, 2, MX_DN_NF, MODE, 2, 1, true, true>, grid, dim3(128), 0, s, a); break;
+            default: launch(gemm_kernel<WT, 4, MX_DN_NF, MODE, 2, 1, true, true>, grid, dim3(128), 0, s, a); break;
+            }
+        }
+        return;
+    }
+    if constexpr (MODE == GM_ARGMAX) {
+        switch (MF) {
+        case 1: launch(gemm_kernel<WT, 1, MX_LM_NF, MODE, 4, MX_LM_U, true>, grid, dim3(256), 0, s, a); break;
+        case 2: launch(gemm_kernel<WT, 2, MX_LM_NF, MODE, 4, 1, true>, grid, dim3(256), 0, s, a); break;
+        default: launch(gemm_kernel<WT, 4, MX_LM_NF, MODE, 4, 1, true>, grid, dim3(256), 0, s, a); break;
+        }
+    }
+}
+
 template <int MODE, bool PK>
 void launch_gemm_m(int wt, int MF, const GemmArgs& a, dim3 grid, hipStream_t s)
 {
     if (wt == SV_F32) launch_gemm_t<SV_F32, MODE, PK>(MF, a, grid, s);
     else if (wt == SV_BF16) launch_gemm_t<SV_BF16, MODE, PK>(MF, a, grid, s);
-    else launch_gemm_t<SV_FP8, MODE, PK>(MF, a, grid, s);
+    else if (wt == SV_FP8) launch_gemm_t<SV_FP8, MODE, PK>(MF, a, grid, s);
+    else if constexpr (PK) launch_gemm_mx<MODE>(MF, a, grid, s);   // tiled16 only
 }
 
 template <bool PK>
@@ -746,9 +802,20 @@ static int step_impl(spec_verify_ctx* c, const spec_verify_weights* w, void* k_c
     if (w->layout != SV_LAYOUT_ROW_MAJOR && w->layout != SV_LAYOUT_TILED16)
         return fail(SV_ERR_INVALID_ARG, "unknown weight layout");
     const bool packed = w->layout == SV_LAYOUT_TILED16;
+    const bool mx = k.mx_dtype == SV_MXFP4;
+    if (mx) {
+        if (!packed) return fail(SV_ERR_UNSUPPORTED, "MXFP4 weights need the tiled16 layout");
+        if (!w->lm_scale) return fail(SV_ERR_INVALID_ARG, "MXFP4 LM head needs lm_scale");
+        for (int l = 0; l < k.n_layers; l++) {
+            const spec_verify_layer& L = w->layers[l];
+            if (!L.s_gate_up || !L.s_down || (k.n_shared > 0 && (!L.s_sh_gate_up || !L.s_sh_down)))
+                return fail(SV_ERR_INVALID_ARG, "MXFP4 expert matrices need their block scales");
+        }
+    }
     HIP_TRY(hipSetDevice(c->device));
     hipStream_t s = (hipStream_t)stream;
     const int wt = k.weight_dtype, step = wsteps(wt);
+    const int wt_mx = mx ? SV_MXFP4 : wt;   // experts and LM head
     const int K1 = c->K1, T = B * K1, H = k.hidden, L = k.n_layers, QKV = c->QKV, QD = c->QD;
     const bool bf = c->bf;
     const size_t AES = bf ? 2 : 4;
@@ -820,7 +887,9 @@ static int step_impl(spec_verify_ctx* c, const spec_verify_weights* w, void* k_c
     // verification the sampling input (the debug buffer when one is set)
     float* lm_logits = smp ? (c->dbg_logits ? c->dbg_logits : c->slogits) : c->dbg_logits;
     auto dense_gemm = [&](int mode, const void* X, long ldx, int N, int Kd, const void* W,
-                          const float* ws, void* out, long ldo, int allow_split) -> int {
+                          const float* ws, void* out, long ldo, int allow_split,
+                          int wdt = -1) -> int {
+        const int wtd = wdt >= 0 ? wdt : wt;
         GemmArgs a = dense_args(X, ldx, T, N, Kd, W, ws);
         a.out = out;
         a.ldo = ldo;
@@ -853,10 +922,10 @@ static int step_impl(spec_verify_ctx* c, const spec_verify_weights* w, void* k_c
             return a.ksplit;
         }
         a.MT = MTd;
-        a.NT = cdiv(N, 64);
+        a.NT = cdiv(N, small_col_tile(wtd, mode));
         long waves = (long)a.NT * a.MT * 4;
         a.ksplit = allow_split > 1 ? pick_ksplit(waves, Kd, step, allow_split) : 1;
-        launch_gemm(wt, mode, MFd, packed, a, s);
+        launch_gemm(wtd, mode, MFd, packed, a, s);
         last_nt = a.NT;
         return a.ksplit;
     };
@@ -998,11 +1067,11 @@ static int step_impl(spec_verify_ctx* c, const spec_verify_weights* w, void* k_c
             g.W = Lw.w_gate_up;
             g.ws = Lw.s_gate_up;
             g.w_gstride = (long)2 * I * H;
-            g.s_gstride = 2L * I;
+            g.s_gstride = mx ? 2L * I * (H / 32) : 2L * I;   // MXFP4: block-scale bytes per expert
             g.W2 = Lw.w_sh_gate_up;
             g.ws2 = Lw.s_sh_gate_up;
             g.w2_gstride = (long)2 * I * H;
-            g.s2_gstride = 2L * I;
+            g.s2_gstride = g.s_gstride;
             g.G1 = E;
             g.dual_off = I;
             g.tiles = c->tiles;
@@ -1017,13 +1086,13 @@ static int step_impl(spec_verify_ctx* c, const spec_verify_weights* w, void* k_c
             // few rows: one-wave tiles streaming weights (finer balance)
             const bool big_e = big && H % (BIG_CHUNK_STEPS * step) == 0 &&
                                I % (BIG_CHUNK_STEPS * step) == 0;
-            g.NT = big_e ? cdiv(I, 16 * 4 * GROUPED_NF) : cdiv(I, 16);
+            g.NT = big_e ? cdiv(I, 16 * 4 * GROUPED_NF) : cdiv(I, grouped_col_tile(wt_mx, GM_SWIGLU));
             g.out = c->act;
             g.ldo = I;
             {
                 ProfScope ps(c, SV_KC_EXPERT_GATE_UP, s);
                 if (big_e) launch_grouped_big(wt, GM_SWIGLU, MFe, packed, g, s);
-                else launch_gemm(wt, GM_SWIGLU, MFe, packed, g, s);
+                else launch_gemm(wt_mx, GM_SWIGLU, MFe, packed, g, s);
             }
             GemmArgs d = g;
             d.X = c->act;
@@ -1034,20 +1103,20 @@ static int step_impl(spec_verify_ctx* c, const spec_verify_weights* w, void* k_c
             d.W = Lw.w_down;
             d.ws = Lw.s_down;
             d.w_gstride = (long)H * I;
-            d.s_gstride = H;
+            d.s_gstride = mx ? (long)H * (I / 32) : H;
             d.W2 = Lw.w_sh_down;
             d.ws2 = Lw.s_sh_down;
             d.w2_gstride = (long)H * I;
-            d.s2_gstride = H;
+            d.s2_gstride = d.s_gstride;
             d.dual_off = 0;
-            d.NT = big_e ? cdiv(H, 16 * 4 * GROUPED_NF) : cdiv(H, 16);
+            d.NT = big_e ? cdiv(H, 16 * 4 * GROUPED_NF) : cdiv(H, grouped_col_tile(wt_mx, GM_STORE));
             d.out = c->y;
             d.ldo = H;
             d.split_stride = 0;
             {
                 ProfScope ps(c, SV_KC_EXPERT_DOWN, s);
                 if (big_e) launch_grouped_big(wt, GM_STORE, MFe, packed, d, s);
-                else launch_gemm(wt, GM_STORE, MFe, packed, d, s);
+                else launch_gemm(wt_mx, GM_STORE, MFe, packed, d, s);
             }
             ra.y = c->y;
             ra.gate = c->gate;
@@ -1082,7 +1151,7 @@ static int step_impl(spec_verify_ctx* c, const spec_verify_weights* w, void* k_c
     // ---- LM head + argmax, acceptance
     {
         ProfScope ps(c, SV_KC_LM_HEAD, s);
-        dense_gemm(GM_ARGMAX, c->h, H, k.vocab, H, w->lm_head, w->lm_scale, nullptr, 0, 0);
+        dense_gemm(GM_ARGMAX, c->h, H, k.vocab, H, w->lm_head, w->lm_scale, nullptr, 0, 0, wt_mx);
     }
     if (smp) return launch_sampling(c, *smp, lm_logits, drafts, ctx_in, ctx_out, B, accepted,
                                     next_tok, c->seq_err, s);

@@ -36,7 +36,7 @@ def test_every_declared_function_is_exported(sv):
 
 
 def test_status_strings_and_version(sv):
-    assert sv.spec_verify_abi_version() == 2
+    assert sv.spec_verify_abi_version() == 3
     assert sv.spec_verify_status_string(0) == "ok"
     assert "invalid" in sv.spec_verify_status_string(-1)
     assert sv.spec_verify_status_string(12345) == "unknown status"
@@ -44,7 +44,7 @@ def test_status_strings_and_version(sv):
 
 def test_struct_sizes_match_header(sv):
     # 21 four-byte fields; layer = 16 pointers; weights = 5 pointers + int (padded)
-    assert ctypes.sizeof(sv.SpecVerifyConfig) == 21 * 4
+    assert ctypes.sizeof(sv.SpecVerifyConfig) == 22 * 4
     assert ctypes.sizeof(sv.SpecVerifyLayer) == 16 * 8
     assert ctypes.sizeof(sv.SpecVerifyWeights) == 6 * 8
 
