@@ -59,12 +59,13 @@
  * SV_F32; or weights SV_BF16 or SV_FP8 with embedding and KV cache SV_BF16
  * (activations bf16, accumulation fp32).  With mx_dtype = SV_MXFP4 (bf16
  * MoE models, max_batch * (K+1) < 64, hidden and expert_inter multiples of
- * 128, tiled16 layout) the weight-streaming matrices -- w_gate_up, w_down,
- * w_sh_gate_up, w_sh_down and lm_head -- are MXFP4: each is the byte matrix
- * [rows][cols/2] of codes, packed with spec_verify_pack_tiled16 as an SV_FP8
- * matrix of cols/2 columns, and its s_x pointer (lm_scale for the LM head)
- * points to the row-major E8M0 bytes [rows][cols/32] (per expert stack:
- * [E][rows][cols/32]).  The codes are widened exactly to bf16 (gfx950
+ * 128 and at most 2048, tiled16 layout) the weight-streaming matrices --
+ * w_gate_up, w_down, w_sh_gate_up, w_sh_down and lm_head -- are MXFP4: each
+ * is the byte matrix [rows][cols/2] of codes, packed with
+ * spec_verify_pack_tiled16 as an SV_FP8 matrix of cols/2 columns, and its s_x
+ * pointer (lm_scale for the LM head) points to its E8M0 bytes
+ * [rows][cols/32] packed with spec_verify_pack_mx_scales (an expert stack is
+ * packed as one tall matrix).  The codes are widened exactly to bf16 (gfx950
  * v_cvt_scalef32_pk_bf16_fp4) and multiplied on the bf16 matrix cores.
  *
  * Weight layouts (row-major, [out][in] per matrix, contiguous):
@@ -332,6 +333,21 @@ int spec_verify_pack_tiled16(const void* src, void* dst, long rows, int cols, in
 
 /* Bytes of a matrix in the SV_LAYOUT_TILED16 layout (rows padded to 16). */
 long spec_verify_tiled16_bytes(long rows, int cols, int dtype);
+
+/*
+ * Repack the E8M0 block scales of an MXFP4 matrix with `cols` columns
+ * (row-major bytes [rows][cols/32], device) into the form the kernels read
+ * (at `dst`, device, caller-owned, spec_verify_mx_scales_bytes bytes): per
+ * 16-row block and group of 16 reduction steps of 128 columns, 1024 bytes of
+ * 64 lanes x 16 bytes, at offset ((block * G + group) * 64 + l) * 16 with
+ * G = ceil(cols / 2048); byte j of lane l = r + 16 g is the scale of row
+ * 16 block + r, column block 4 (16 group + j) + g.  Padding bytes are 127.
+ * cols must be a positive multiple of 128.  Enqueued on `stream`.
+ */
+int spec_verify_pack_mx_scales(const void* src, void* dst, long rows, int cols, void* stream);
+
+/* Bytes of packed MXFP4 scales for a [rows][cols] matrix (-1 if invalid). */
+long spec_verify_mx_scales_bytes(long rows, int cols);
 
 /* Read (host) the sticky device error word (SV_DEV_* bits) accumulated since
  * the last clear; synchronises `stream` first.  clear != 0 resets it. */

@@ -35,7 +35,8 @@ EXPORTS = ("spec_verify_init", "spec_verify_destroy", "spec_verify_step", "spec_
            "spec_verify_accept_from_logits", "spec_verify_error_word", "spec_verify_kernel_time",
            "spec_verify_last_error", "spec_verify_status_string", "spec_verify_abi_version",
            "spec_verify_pack_tiled16", "spec_verify_tiled16_bytes", "spec_verify_step_sampled",
-           "spec_verify_sample_from_logits")
+           "spec_verify_sample_from_logits", "spec_verify_pack_mx_scales",
+           "spec_verify_mx_scales_bytes")
 
 
 class SpecVerifyConfig(ctypes.Structure):
@@ -99,10 +100,13 @@ def load_library() -> ctypes.CDLL:
         lib.spec_verify_abi_version.argtypes = []
         lib.spec_verify_pack_tiled16.argtypes = [P, P, ctypes.c_long, c_int, c_int, P]
         lib.spec_verify_tiled16_bytes.argtypes = [ctypes.c_long, c_int, c_int]
+        lib.spec_verify_pack_mx_scales.argtypes = [P, P, ctypes.c_long, c_int, P]
+        lib.spec_verify_mx_scales_bytes.argtypes = [ctypes.c_long, c_int]
         for f in EXPORTS:
             if f not in ("spec_verify_destroy", "spec_verify_status_string"):
                 getattr(lib, f).restype = c_int
         lib.spec_verify_tiled16_bytes.restype = ctypes.c_long
+        lib.spec_verify_mx_scales_bytes.restype = ctypes.c_long
         _lib = lib
     return _lib
 
@@ -179,6 +183,26 @@ def spec_verify_pack_tiled16(src, dst, rows: int, cols: int, dtype: int, stream=
                                                    _stream(stream)), "spec_verify_pack_tiled16")
 
 
+def spec_verify_mx_scales_bytes(rows: int, cols: int) -> int:
+    return load_library().spec_verify_mx_scales_bytes(rows, cols)
+
+
+def spec_verify_pack_mx_scales(src, dst, rows: int, cols: int, stream=None) -> None:
+    _check(load_library().spec_verify_pack_mx_scales(_p(src), _p(dst), rows, cols,
+                                                     _stream(stream)), "spec_verify_pack_mx_scales")
+
+
+def pack_mx_scales(t, stream=None):
+    """E8M0 scale bytes [..., cols/32] (row-major, stacked matrices flattened
+    into one tall matrix) repacked by the library; returns a new uint8 tensor."""
+    import torch
+    cols = t.shape[-1] * 32
+    rows = t.numel() // t.shape[-1]
+    dst = torch.empty(spec_verify_mx_scales_bytes(rows, cols), dtype=torch.uint8, device=t.device)
+    spec_verify_pack_mx_scales(t.contiguous(), dst, rows, cols, stream)
+    return dst
+
+
 def _dtype_code(t) -> int:
     import torch
     return {torch.float32: SV_F32, torch.bfloat16: SV_BF16, torch.uint8: SV_FP8,
@@ -199,9 +223,14 @@ def pack_matrix(t, stream=None):
     return dst
 
 
-def pack_weights(weights: dict, stream=None) -> dict:
+MX_MATRICES = ("w_gate_up", "w_down", "w_sh_gate_up", "w_sh_down")
+
+
+def pack_weights(weights: dict, stream=None, mx: str = "") -> dict:
     """A copy of a weight dict with every matrix-product weight in the
-    tiled16 layout (norm gains, scales and the embedding unchanged)."""
+    tiled16 layout (norm gains, fp8 scales and the embedding unchanged); with
+    mx = "mxfp4" the block scales of the MXFP4 matrices (experts, LM head)
+    are repacked too."""
     out = dict(weights)
     out["layers"] = []
     for L in weights["layers"]:
@@ -210,8 +239,15 @@ def pack_weights(weights: dict, stream=None) -> dict:
             if L.get(name) is not None:
                 # an empty stack (no shared experts) stays empty: nothing to pack
                 L2[name] = pack_matrix(L[name], stream) if L[name].numel() else L[name]
+        if mx == "mxfp4":
+            for name in MX_MATRICES:
+                sk = "s" + name[1:]
+                if L.get(sk) is not None and L[sk].numel():
+                    L2[sk] = pack_mx_scales(L[sk], stream)
         out["layers"].append(L2)
     out["lm_head"] = pack_matrix(weights["lm_head"], stream)
+    if mx == "mxfp4":
+        out["lm_scale"] = pack_mx_scales(weights["lm_scale"], stream)
     out["layout"] = "tiled16"
     return out
 
@@ -347,7 +383,7 @@ class VerifyContext:
         self._config = make_config(cfg, max_batch, kv_capacity)
         self.handle = spec_verify_init(self._config)
         if layout == "tiled16" and weights.get("layout", "row_major") == "row_major":
-            weights = pack_weights(weights)
+            weights = pack_weights(weights, mx=getattr(cfg, "mx", ""))
         self.weights = weights
         self._w, self._keep = make_weights(weights, cfg.n_layers)
 

@@ -72,7 +72,8 @@ template <> struct WTraits<SV_F32> { static constexpr int KL = 4, SK = 16, XU = 
 template <> struct WTraits<SV_BF16> { static constexpr int KL = 8, SK = 32, XU = 1, ESZ = 2; };
 template <> struct WTraits<SV_FP8> { static constexpr int KL = 16, SK = 64, XU = 2, ESZ = 1; };
 // MXFP4 (tiled16 layout only): 32 E2M1 codes per 16-byte lane slice, one E8M0
-// scale byte per slice; ESZ is not used (a code is half a byte)
+// scale byte per slice (tiled scales: 16 steps per 16-byte lane slice, K <=
+// 2048); ESZ is not used (a code is half a byte)
 template <> struct WTraits<SV_MXFP4> { static constexpr int KL = 32, SK = 128, XU = 4, ESZ = 1; };
 
 // weight element size in half-bytes (byte offsets of packed 4-bit codes)
@@ -102,6 +103,15 @@ SV_DEV uint4 e2m1x8_to_bf16(uint32_t w, float s)
                       __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, s, 1)),
                       __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, s, 2)),
                       __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, s, 3)));
+}
+
+// MXFP4 scale of reduction step st (< 16) from a lane's tiled 16-byte scale
+// slice (byte st: the block of the lane's 32 codes at that step)
+SV_DEV uint32_t mx_scale_byte(uint4 v, int st)
+{
+    const int q = st >> 2;
+    const uint32_t w = q == 0 ? v.x : (q == 1 ? v.y : (q == 2 ? v.z : v.w));
+    return (w >> (8 * (st & 3))) & 0xffu;
 }
 
 // a 16-byte MXFP4 lane slice (32 codes, one block) -> four bf16 operands
@@ -343,7 +353,7 @@ __global__ __launch_bounds__(64 * WAVES) void gemm_kernel(GemmArgs a)
 
     // weight rows of this lane, one per fragment (invalid fragments read row 0)
     const char* wrow[NFT];
-    const uint8_t* srow[MX ? NFT : 1];   // MXFP4: this lane's scale byte of step 0
+    uint4 sslice[MX ? NFT : 1];   // MXFP4: this lane's scale bytes of steps 0..15 (K <= 2048)
     bool fvalid[NF];
 #pragma unroll
     for (int f = 0; f < NF; f++) {
@@ -358,9 +368,10 @@ __global__ __launch_bounds__(64 * WAVES) void gemm_kernel(GemmArgs a)
             if constexpr (MODE == GM_SWIGLU)
                 wrow[NF + f] = Wb + (size_t)(rb + a.dual_off / 16) * K * 8 * EH + (size_t)lane * 16;
             if constexpr (MX) {
-                // the lane's 32 codes of step s are block 4 s + lg of its row
-                srow[f] = scb + (size_t)r * (K / 32) + lg;
-                if constexpr (MODE == GM_SWIGLU) srow[NF + f] = scb + (size_t)(r + a.dual_off) * (K / 32) + lg;
+                // tiled scales: one 16-byte slice per lane and row block (16 steps)
+                sslice[f] = ldg16(scb + ((size_t)rb * 64 + lane) * 16);
+                if constexpr (MODE == GM_SWIGLU)
+                    sslice[NF + f] = ldg16(scb + ((size_t)(rb + a.dual_off / 16) * 64 + lane) * 16);
             }
         } else {
             wrow[f] = Wb + ((size_t)r * K + (size_t)lg * KL) * WESZ;
@@ -400,7 +411,7 @@ __global__ __launch_bounds__(64 * WAVES) void gemm_kernel(GemmArgs a)
                 for (int f = 0; f < NFT; f++) {
                     if constexpr (PACKED) w[u][f] = ldg16_stream(wrow[f] + (size_t)(kk / SK) * 1024);
                     else w[u][f] = ldg16_stream(wrow[f] + (size_t)kk * WESZ);
-                    if constexpr (MX) sb[u][f] = srow[f][kk / 32];
+                    if constexpr (MX) sb[u][f] = mx_scale_byte(sslice[f], kk / SK);
                 }
 #pragma unroll
                 for (int m = 0; m < MF; m++)
@@ -462,6 +473,88 @@ __global__ __launch_bounds__(64 * WAVES) void gemm_kernel(GemmArgs a)
         gemm_epilogue<WT, MF, NF, MODE, WAVES>(a, acc, row0, nrows, ncol0, nt, sc, fvalid, red);
     } else {
         gemm_epilogue<WT, MF, NF, MODE, WAVES>(a, acc, row0, nrows, ncol0, nt, sc, fvalid, nullptr);
+    }
+}
+
+// ---------------------------------------------------------------------------
+// MXFP4 weights, up to 16 rows, K <= 128 MAXS (the LM head at few rows).  A
+// quarter of the bf16 bytes per reduction step leaves the small-row kernel
+// above latency-bound (a wave's weights arrive in several dependent stages,
+// four activation registers per weight load).  Here each wave issues every
+// weight load of its NF column fragments at once (the whole reduction in
+// registers), while the workgroup copies the activations straight into LDS
+// (global_load_lds: no registers) in MFMA operand order; after one wait the
+// steps run from registers and LDS.  Grid and tiles as gemm_kernel (dense,
+// 16-row tiles, 4 waves of NF fragments side by side).
+template <int NF, int MAXS, int MODE>
+__global__ __launch_bounds__(256) void gemm_mx_lds_kernel(GemmArgs a)
+{
+    constexpr int WAVES = 4, MF = 1, BM = 16;
+    __shared__ uint4 xs[MAXS][4][64];   // [step][8-element unit][lane]
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int l16 = lane & 15, lg = lane >> 4;
+    const int id = blockIdx.x, xcd = id & 7, q = id >> 3;
+    const int mt = q % a.MT;
+    const int nt = (q / a.MT) * 8 + xcd;
+    if (nt >= a.NT) return;
+    const int row0 = mt * BM, nrows = min(BM, a.M - row0);
+    if (nrows <= 0) return;
+    const int K = a.K, nsteps = K / 128;
+    const int ncol0 = (nt * WAVES + wave) * 16 * NF;
+
+    const char* wrow[NF];
+    uint4 sslice[NF];
+    bool fvalid[NF];
+#pragma unroll
+    for (int f = 0; f < NF; f++) {
+        const int n0 = ncol0 + 16 * f;
+        fvalid[f] = n0 < a.N;
+        const int rb = fvalid[f] ? n0 / 16 : 0;
+        wrow[f] = (const char*)a.W + (size_t)rb * K * 8 + (size_t)lane * 16;
+        sslice[f] = ldg16((const uint8_t*)a.ws + ((size_t)rb * 64 + lane) * 16);   // K <= 2048
+    }
+    uint4 w[MAXS][NF];
+#pragma unroll
+    for (int s = 0; s < MAXS; s++)
+        if (s < nsteps)
+#pragma unroll
+            for (int f = 0; f < NF; f++) w[s][f] = ldg16_stream(wrow[f] + (size_t)s * 1024);
+    // activations: wave v stages steps v, v + 4, ...; lane (l16, lg) of unit u
+    // of step s holds row l16, columns 128 s + 32 lg + 8 u .. + 7
+    {
+        const int xr = row0 + min(l16, nrows - 1);
+        const char* xsrc = (const char*)a.X + ((size_t)xr * a.ldx + (size_t)lg * 32) * 2;
+        for (int s = wave; s < nsteps; s += WAVES)
+#pragma unroll
+            for (int u = 0; u < 4; u++)
+                __builtin_amdgcn_global_load_lds((const void*)(xsrc + ((size_t)s * 128 + 8 * u) * 2),
+                                                 (__attribute__((address_space(3))) void*)&xs[s][u][0],
+                                                 16, 0, 0);
+    }
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+
+    f32x4_t acc[MF][NF];
+#pragma unroll
+    for (int f = 0; f < NF; f++) acc[0][f] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s = 0; s < MAXS; s++) {
+        if (s < nsteps) {
+            uint4 xf[4];
+#pragma unroll
+            for (int u = 0; u < 4; u++) xf[u] = xs[s][u][lane];
+#pragma unroll
+            for (int f = 0; f < NF; f++) {
+                const WOp<SV_MXFP4> wo = wprep_mx(w[s][f], mx_scale_byte(sslice[f], s));
+                acc[0][f] = mma_op<SV_MXFP4>(wo, xf, acc[0][f]);
+            }
+        }
+    }
+    if constexpr (MODE == GM_ARGMAX) {
+        __shared__ unsigned long long red[WAVES * BM];
+        gemm_epilogue<SV_MXFP4, MF, NF, MODE, WAVES>(a, acc, row0, nrows, ncol0, nt, nullptr, fvalid, red);
+    } else {
+        gemm_epilogue<SV_MXFP4, MF, NF, MODE, WAVES>(a, acc, row0, nrows, ncol0, nt, nullptr, fvalid, nullptr);
     }
 }
 

@@ -838,3 +838,39 @@ __global__ __launch_bounds__(256) void pack_tiled16_kernel(const char* __restric
         *reinterpret_cast<uint4*>(dst + i * 16) = v;
     }
 }
+
+// MXFP4 block scales, row-major [rows][cols/32] bytes -> the tiled form the
+// GEMM kernels read: per 16-row block and group of 16 reduction steps (128
+// columns each), 64 lanes x 16 bytes, lane l = r + 16 g holding the scales of
+// row r, column blocks 4 s + g for the group's steps s (one 16-byte load per
+// lane covers 16 steps).  Bytes past the row's blocks and rows past `rows`
+// are written as 127 (scale 1).  One thread per 16-byte lane slice.
+__global__ __launch_bounds__(256) void pack_mx_scales_kernel(const uint8_t* __restrict__ src,
+                                                             uint8_t* __restrict__ dst, long rows,
+                                                             int cols)
+{
+    const int nb = cols / 32, steps = cols / 128, nchunk = (steps + 15) / 16;
+    const long nblk = (rows + 15) / 16;
+    const long total = nblk * nchunk * 64;
+    for (long i = (long)blockIdx.x * 256 + threadIdx.x; i < total; i += (long)gridDim.x * 256) {
+        const int l = (int)(i & 63);
+        const long bc = i >> 6;             // block * nchunk + chunk
+        const long rb = bc / nchunk;
+        const int c = (int)(bc % nchunk);
+        const long row = rb * 16 + (l & 15);
+        const int g = l >> 4;
+        uint32_t w[4];
+#pragma unroll
+        for (int q = 0; q < 4; q++) {
+            uint32_t v = 0;
+#pragma unroll
+            for (int b = 0; b < 4; b++) {
+                const int st = 16 * c + 4 * q + b, blk = 4 * st + g;
+                const uint32_t byte = (row < rows && st < steps) ? src[row * nb + blk] : 127u;
+                v |= byte << (8 * b);
+            }
+            w[q] = v;
+        }
+        *reinterpret_cast<uint4*>(dst + i * 16) = make_uint4(w[0], w[1], w[2], w[3]);
+    }
+}

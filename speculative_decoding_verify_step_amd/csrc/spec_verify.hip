@@ -192,8 +192,8 @@ int validate_config(const spec_verify_config& c)
         if (c.mx_dtype != SV_MXFP4) return bad("mx_dtype must be 0 or SV_MXFP4");
         if (c.weight_dtype != SV_BF16 || c.ffn_kind != SV_FFN_MOE)
             return bad("MXFP4 expert and LM-head weights need a bf16 MoE model");
-        if (c.hidden % 128 || c.expert_inter % 128)
-            return bad("MXFP4 weights need hidden and expert_inter multiples of 128");
+        if (c.hidden % 128 || c.expert_inter % 128 || c.hidden > 2048 || c.expert_inter > 2048)
+            return bad("MXFP4 weights need hidden and expert_inter multiples of 128, at most 2048");
         if ((long)c.max_batch * (c.k_draft + 1) >= 64)
             return bad("MXFP4 weights are supported for max_batch*(K+1) < 64 rows");
     }
@@ -230,12 +230,14 @@ void launch_gemm_t(int MF, const GemmArgs& a, dim3 grid, hipStream_t s)
 }
 
 // MXFP4 weights (a quarter of the bf16 bytes per column): wider wave tiles so
-// that a wave still streams as many bytes as a bf16 wave.  LM head: 4 column
-// fragments per wave (256-column workgroup tiles), 2 steps per stage.
+// that a wave still streams enough bytes.  LM head: 2 column fragments per
+// wave (128-column workgroup tiles; same-box step 81.4 us with 4, 79.8 with
+// 2, 88.0 with 8), 2 steps per stage on the general kernel.
 // Grouped experts: gate/up one column fragment per wave as with bf16 (at
 // batch 1 wider tiles leave too few waves: 11.7 -> 13.2 us with two), down 4
 // (its 2 waves split the reduction; 9.2 -> 8.6 us), 2 steps per stage.
-constexpr int MX_LM_NF = 4, MX_LM_U = 2, MX_GU_NF = 1, MX_DN_NF = 4;
+constexpr int MX_LM_NF = 2, MX_LM_U = 2, MX_GU_NF = 1, MX_DN_NF = 4;
+constexpr int MX_LDS_MAXS = 10;   // reduction steps (128 columns each) the LDS kernel holds
 
 int small_col_tile(int wt, int mode) { return (wt == SV_MXFP4 && mode == GM_ARGMAX) ? 64 * MX_LM_NF : 64; }
 
@@ -267,6 +269,11 @@ void launch_gemm_mx(int MF, const GemmArgs& a, dim3 grid, hipStream_t s)
         return;
     }
     if constexpr (MODE == GM_ARGMAX) {
+        // up to 16 rows and K <= 1280: whole reduction in flight, activations in LDS
+        if (MF == 1 && a.K <= 128 * MX_LDS_MAXS) {
+            launch(gemm_mx_lds_kernel<MX_LM_NF, MX_LDS_MAXS, MODE>, grid, dim3(256), 0, s, a);
+            return;
+        }
         switch (MF) {
         case 1: launch(gemm_kernel<WT, 1, MX_LM_NF, MODE, 4, MX_LM_U, true>, grid, dim3(256), 0, s, a); break;
         case 2: launch(gemm_kernel<WT, 2, MX_LM_NF, MODE, 4, 1, true>, grid, dim3(256), 0, s, a); break;
@@ -1067,7 +1074,7 @@ static int step_impl(spec_verify_ctx* c, const spec_verify_weights* w, void* k_c
             g.W = Lw.w_gate_up;
             g.ws = Lw.s_gate_up;
             g.w_gstride = (long)2 * I * H;
-            g.s_gstride = mx ? 2L * I * (H / 32) : 2L * I;   // MXFP4: block-scale bytes per expert
+            g.s_gstride = mx ? spec_verify_mx_scales_bytes(2L * I, H) : 2L * I;   // MXFP4: bytes per expert
             g.W2 = Lw.w_sh_gate_up;
             g.ws2 = Lw.s_sh_gate_up;
             g.w2_gstride = (long)2 * I * H;
@@ -1103,7 +1110,7 @@ static int step_impl(spec_verify_ctx* c, const spec_verify_weights* w, void* k_c
             d.W = Lw.w_down;
             d.ws = Lw.s_down;
             d.w_gstride = (long)H * I;
-            d.s_gstride = mx ? (long)H * (I / 32) : H;
+            d.s_gstride = mx ? spec_verify_mx_scales_bytes(H, I) : H;
             d.W2 = Lw.w_sh_down;
             d.ws2 = Lw.s_sh_down;
             d.w2_gstride = (long)H * I;
@@ -1242,6 +1249,25 @@ int spec_verify_accept_from_logits(spec_verify_ctx* c, const float* logits, cons
     ac.seq_err = nullptr;
     ac.err_word = c->err_word;
     accept_kernel<<<B, 1024, 0, s>>>(ac);
+    HIP_TRY(hipGetLastError());
+    return SV_OK;
+}
+
+long spec_verify_mx_scales_bytes(long rows, int cols)
+{
+    if (rows < 1 || cols < 128 || cols % 128) return -1;
+    return (rows + 15) / 16 * (long)((cols / 128 + 15) / 16) * 1024;
+}
+
+int spec_verify_pack_mx_scales(const void* src, void* dst, long rows, int cols, void* stream)
+{
+    if (!src || !dst) return fail(SV_ERR_INVALID_ARG, "null scale pointer");
+    if (rows < 1 || cols < 128 || cols % 128)
+        return fail(SV_ERR_INVALID_ARG, "MXFP4 scales: cols must be a positive multiple of 128");
+    hipStream_t s = (hipStream_t)stream;
+    long slices = spec_verify_mx_scales_bytes(rows, cols) / 16;
+    long blocks = std::min<long>((slices + 255) / 256, 65536);
+    pack_mx_scales_kernel<<<(unsigned)blocks, 256, 0, s>>>((const uint8_t*)src, (uint8_t*)dst, rows, cols);
     HIP_TRY(hipGetLastError());
     return SV_OK;
 }

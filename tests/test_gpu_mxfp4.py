@@ -43,3 +43,28 @@ def test_mxfp4_rejects_large_batches(H):
     cfg = workloads.scaled(workloads.get_config("moe_b1_mxfp4"), batch=16)
     with pytest.raises(sv.SpecVerifyError):
         sv.spec_verify_init(sv.make_config(cfg, 16, 1408))
+
+
+@pytest.mark.parametrize("rows,cols", [(40, 1280), (16, 896), (3, 128)])
+def test_pack_mx_scales_layout(H, rows, cols):
+    """The tiled scale layout against its definition, element by element."""
+    import numpy as np
+    import speculative_decoding_verify_step_amd as sv
+    g = torch.Generator().manual_seed(rows + cols)
+    src = torch.randint(0, 255, (rows, cols // 32), generator=g, dtype=torch.int32).to(torch.uint8)
+    got = sv.pack_mx_scales(src.to("cuda")).cpu().numpy()
+    steps = cols // 128
+    nchunk = (steps + 15) // 16
+    nblk = (rows + 15) // 16
+    want = np.full((nblk, nchunk, 64, 16), 127, np.uint8)
+    s = src.numpy()
+    for rb in range(nblk):
+        for c in range(nchunk):
+            for l in range(64):
+                r, gq = 16 * rb + (l & 15), l >> 4
+                for j in range(16):
+                    st = 16 * c + j
+                    if r < rows and st < steps:
+                        want[rb, c, l, j] = s[r, 4 * st + gq]
+    assert got.shape[0] == want.size
+    np.testing.assert_array_equal(got, want.reshape(-1))
