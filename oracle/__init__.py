@@ -110,6 +110,10 @@ def _load():
         lib.or_argmax.argtypes = [P, c_long]
         lib.or_argmax.restype = c_int
         lib.or_accept.argtypes = [c_int, P, P, P, P]
+        lib.or_forward_rows.argtypes = [P, P, P, P, c_long, c_long, c_int, P, P, P, P]
+        lib.or_forward_rows.restype = None
+        lib.or_mtp_draft.argtypes = [P, P, P, P, P, P, P, c_long, c_long, c_int, P, c_int, P, P, P]
+        lib.or_mtp_draft.restype = None
         lib.or_num_threads.argtypes = []
         lib.or_num_threads.restype = c_int
         for f in ("or_matvec", "or_rmsnorm", "or_rope", "or_attend", "or_softmax", "or_topk",
@@ -277,6 +281,40 @@ class Oracle:
                                _ptr(v_cache), b, ctx, int(committed), _ptr(co), _ptr(rt),
                                _ptr(out))
         return out
+
+    def forward_rows(self, k_cache, v_cache, b: int, ctx: int, x_in, want_logits=False):
+        """The decoder on given residual rows x_in [n][H] at positions ctx ..
+        ctx+n-1 of sequence b (caches updated); returns (final-normed rows
+        [n][H], logits [n][V] or None, greedy tokens [n])."""
+        x = np.ascontiguousarray(x_in, dtype=np.float64)
+        n = x.shape[0]
+        f = np.zeros((n, self.cfg.hidden))
+        lg = np.zeros((n, self.cfg.vocab)) if want_logits else None
+        am = np.zeros(n, np.int32)
+        _load().or_forward_rows(ctypes.byref(self._c), ctypes.byref(self._w), _ptr(k_cache),
+                                _ptr(v_cache), b, ctx, n, _ptr(x), _ptr(f), _ptr(lg), _ptr(am))
+        return f, lg, am
+
+    def mtp_draft(self, mtp: dict, k_cache, v_cache, b: int, ctx: int, accepted: int, drafts,
+                  next_tok: int, bstate):
+        """FastMTP drafting after a verify step (Jina-OCR-v1 paper, section
+        3.1), with this oracle's model as the shared draft block: `mtp` holds
+        enorm [H], hnorm [H] (fp32 gains) and eh_proj [H][2H] (+ s_eh_proj for
+        fp8); bstate [accepted+1][H] are the target's post-norm rows of
+        positions ctx .. ctx+accepted.  Returns (drafts [K], gaps [K])."""
+        K = self.cfg.k_draft
+        a = int(accepted)
+        m = self._m(mtp, "eh_proj", "s_eh_proj")
+        ge = np.ascontiguousarray(as_np(mtp["enorm"]), dtype=np.float32)
+        gh = np.ascontiguousarray(as_np(mtp["hnorm"]), dtype=np.float32)
+        dr = np.ascontiguousarray(as_np(drafts), dtype=np.int32).reshape(K)
+        bs = np.ascontiguousarray(bstate, dtype=np.float64).reshape(a + 1, self.cfg.hidden)
+        out = np.zeros(K, np.int32)
+        gaps = np.zeros(K)
+        _load().or_mtp_draft(ctypes.byref(self._c), ctypes.byref(self._w), _ptr(ge), _ptr(gh),
+                             ctypes.byref(m), _ptr(k_cache), _ptr(v_cache), b, ctx, a, _ptr(dr),
+                             int(next_tok), _ptr(bs), _ptr(out), _ptr(gaps))
+        return out, gaps
 
     def _check_kv(self, k, v, B):
         cfg = self.cfg

@@ -441,8 +441,8 @@ static void lm_logits(const or_config* c, const or_weights* w, const double* x, 
  * (optional, [L][n][H]) receives it after each layer.
  */
 static void forward_block(const or_config* c, const or_weights* w, void* kc, void* vc, long b,
-                          long ctx, int n, const int* tok, double* x, double* layer_hidden,
-                          const or_route_io* rio)
+                          long ctx, int n, const int* tok, const double* x_in, double* x,
+                          double* layer_hidden, const or_route_io* rio)
 {
     int H = c->hidden, D = c->head_dim, nq = c->n_q, nkv = c->n_kv;
     int QKV = (nq + 2 * nkv) * D;
@@ -453,7 +453,8 @@ static void forward_block(const or_config* c, const or_weights* w, void* kc, voi
     double* scratch = (double*)malloc(sizeof(double) * (size_t)(ctx + n) * nq);
     int l, j, i, hh;
 
-    for (j = 0; j < n; j++) embed_row(c, w, tok[j], x + (size_t)j * H);
+    if (x_in) memcpy(x, x_in, sizeof(double) * (size_t)n * H);   /* given residual input */
+    else for (j = 0; j < n; j++) embed_row(c, w, tok[j], x + (size_t)j * H);
 
     for (l = 0; l < c->n_layers; l++) {
         const or_layer* L = &w->layers[l];
@@ -543,7 +544,7 @@ void or_verify_step(const or_config* c, const or_weights* w, void* kc, void* vc,
                 if (route->rlogits_out)
                     rio.rlogits_out = route->rlogits_out + (size_t)b * per_b * c->n_experts;
             }
-            forward_block(c, w, kc, vc, b, ctx_in[b], n, tok, x,
+            forward_block(c, w, kc, vc, b, ctx_in[b], n, tok, NULL, x,
                           layer_hidden ? layer_hidden + (size_t)b * c->n_layers * n * H : NULL,
                           &rio);
             for (j = 0; j < n; j++) {
@@ -579,7 +580,7 @@ int or_decode_one(const or_config* c, const or_weights* w, void* kc, void* vc, l
     double* x = (double*)malloc(sizeof(double) * c->hidden);
     double* lg = (double*)malloc(sizeof(double) * c->vocab);
     int g;
-    forward_block(c, w, kc, vc, b, pos, 1, &tok, x, NULL, NULL);
+    forward_block(c, w, kc, vc, b, pos, 1, &tok, NULL, x, NULL, NULL);
     lm_logits(c, w, x, lg);
     g = or_argmax(lg, c->vocab);
     if (logits) memcpy(logits, lg, sizeof(double) * c->vocab);
@@ -604,6 +605,100 @@ void or_make_drafts(const or_config* c, const or_weights* w, void* kc, void* vc,
         drafts[i] = coin[i] ? g : rand_tok[i];
         prev = drafts[i];
     }
+}
+
+/*
+ * The decoder on given residual inputs: rows x_in[n][H] at cache positions
+ * ctx .. ctx+n-1 of sequence b, through all layers (keys and values written
+ * to the cache), then the final norm: f_out[n][H] (the LM head's input),
+ * logits[n][V] (optional) and the greedy token of every row (argmax_out[n],
+ * -1 on a NaN logit).
+ */
+void or_forward_rows(const or_config* c, const or_weights* w, void* kc, void* vc, long b, long ctx,
+                     int n, const double* x_in, double* f_out, double* logits, int* argmax_out)
+{
+    int H = c->hidden, j;
+    long V = c->vocab;
+    double* x = (double*)malloc(sizeof(double) * (size_t)n * H);
+    double* lg = (double*)malloc(sizeof(double) * V);
+    forward_block(c, w, kc, vc, b, ctx, n, NULL, x_in, x, NULL, NULL);
+    for (j = 0; j < n; j++) {
+        double* f = f_out + (size_t)j * H;
+        or_rmsnorm(x + (size_t)j * H, w->final_norm, H, c->rms_eps, f);
+        or_matvec(w->lm_head.data, w->lm_head.scale, mat_dt(&w->lm_head, c->wdtype), 0, V, H, f, lg);
+        argmax_out[j] = or_argmax(lg, V);
+        if (logits) memcpy(logits + (size_t)j * V, lg, sizeof(double) * V);
+    }
+    free(x); free(lg);
+}
+
+/*
+ * FastMTP drafting (Jina-OCR-v1 paper, section 3.1): one shared dense block
+ * B applied recursively for K depths.  With e = embedding, N_e / N_h RMSNorms
+ * with gains g_e / g_h, P the [H][2H] projection, N_o and the LM head shared
+ * with the target:
+ *   a(1) = the target's post-norm state at a position, a(k) = u(k-1) of the
+ *   previous depth; z(k) = P [N_e(e(next token)); N_h(a(k))];
+ *   u(k) = N_o(B(z(k); pos)); the draft is argmax of W_lm u(k).
+ * After a verify step that kept `a` drafts of sequence b (positions ctx ..
+ * ctx+a committed, `next_tok` the target's token at ctx+a+1): depth 1 runs
+ * the block over rows j = 0..a (state bstate[j], the target's post-norm row
+ * of position ctx+j; next token d_{j+1} for j < a, next_tok for j = a) at
+ * positions ctx+j, writing the block's cache there, and the draft d'_1 comes
+ * from row a; depth k > 1 runs one row at position ctx+a+k-1 with state
+ * u(k-1) and token d'_{k-1}.  The block is `w`'s single layer (the LM head,
+ * final norm and embedding are the target's, as the paper ties them).
+ * Outputs drafts_out[K] and gap_out[K] (each depth's top-2 logit gap over
+ * its logit range, in fp32, for choosing a check set).
+ */
+void or_mtp_draft(const or_config* c, const or_weights* w, const float* g_e, const float* g_h,
+                  const or_mat* P, void* kc, void* vc, long b, long ctx, int a, const int* drafts,
+                  int next_tok, const double* bstate, int* drafts_out, double* gap_out)
+{
+    int H = c->hidden, K = c->k_draft, k, j;
+    long V = c->vocab;
+    int n = a + 1;
+    double* cat = (double*)malloc(sizeof(double) * 2 * H);
+    double* e = (double*)malloc(sizeof(double) * H);
+    double* z = (double*)malloc(sizeof(double) * (size_t)n * H);
+    double* f = (double*)malloc(sizeof(double) * (size_t)n * H);
+    double* lg = (double*)malloc(sizeof(double) * (size_t)n * V);
+    int* am = (int*)malloc(sizeof(int) * n);
+    double* u = (double*)malloc(sizeof(double) * H);
+    int prev = -1;
+    for (k = 1; k <= K; k++) drafts_out[k - 1] = -1;
+    for (k = 1; k <= K; k++) {
+        if (k > 1 && prev < 0) break;   /* a NaN logit ended the recursion */
+        int rows = k == 1 ? n : 1;
+        long pos0 = k == 1 ? ctx : ctx + a + k - 1;
+        for (j = 0; j < rows; j++) {
+            int tok = k == 1 ? (j < a ? drafts[j] : next_tok) : prev;
+            const double* st = k == 1 ? bstate + (size_t)j * H : u;
+            embed_row(c, w, tok, e);
+            or_rmsnorm(e, g_e, H, c->rms_eps, cat);
+            or_rmsnorm(st, g_h, H, c->rms_eps, cat + H);
+            or_matvec(P->data, P->scale, mat_dt(P, c->wdtype), 0, H, 2 * H, cat, z + (size_t)j * H);
+        }
+        or_forward_rows(c, w, kc, vc, b, pos0, rows, z, f, lg, am);
+        {
+            int r = k == 1 ? a : 0;
+            const double* l = lg + (size_t)r * V;
+            float t1 = -INFINITY, t2 = -INFINITY;
+            double lo = l[0], hi = l[0];
+            long v;
+            for (v = 0; v < V; v++) {
+                float fv = (float)l[v];
+                if (fv > t1) { t2 = t1; t1 = fv; } else if (fv > t2) t2 = fv;
+                if (l[v] < lo) lo = l[v];
+                if (l[v] > hi) hi = l[v];
+            }
+            prev = am[r];
+            drafts_out[k - 1] = prev;
+            gap_out[k - 1] = hi > lo ? ((double)t1 - (double)t2) / (hi - lo) : 0.0;
+            memcpy(u, f + (size_t)r * H, sizeof(double) * H);
+        }
+    }
+    free(cat); free(e); free(z); free(f); free(lg); free(am); free(u);
 }
 
 /* Threads the parallel loops use (for reporting). */

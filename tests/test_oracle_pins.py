@@ -470,3 +470,85 @@ def test_lossless_moe_mxfp4_scaled(oracle_mod):
                            vocab=512, n_layers=2, batch=3, ctx=("uniform", 20, 90),
                            draft_p=("const", 0.8))
     _lossless_case(oracle_mod, cfg)
+
+
+# ------------------------------------------------------------------ FastMTP
+def _torch_dense_block(cfg, L, x, kcache, vcache, ctx):
+    """One dense pre-norm decoder layer on residual rows x [n][H] at positions
+    ctx .. ctx+n-1 composed from torch operators (float64; the caches
+    [n_kv][cap][D] are written in place, rounded to fp32)."""
+    H, D, nq, nkv = cfg.hidden, cfg.head_dim, cfg.n_q, cfg.n_kv
+    n = x.shape[0]
+    pos = ctx + torch.arange(n, dtype=torch.float64)
+    inv = cfg.rope_theta ** (-torch.arange(0, D // 2, dtype=torch.float64) * 2 / D)
+    rot = torch.polar(torch.ones(n, D // 2, dtype=torch.float64), pos[:, None] * inv[None])
+
+    def rope(t):
+        z = torch.complex(t[..., : D // 2], t[..., D // 2:]) * rot[:, None, :]
+        return torch.cat([z.real, z.imag], -1)
+
+    h = F.rms_norm(x, (H,), L["attn_norm"].double(), eps=cfg.rms_eps)
+    qkv = F.linear(h, L["w_qkv"].double())
+    q = rope(qkv[:, : nq * D].reshape(n, nq, D))
+    k = rope(qkv[:, nq * D:(nq + nkv) * D].reshape(n, nkv, D))
+    v = qkv[:, (nq + nkv) * D:].reshape(n, nkv, D)
+    kcache[:, ctx:ctx + n] = k.float().double().transpose(0, 1)
+    vcache[:, ctx:ctx + n] = v.float().double().transpose(0, 1)
+    keys = kcache[:, : ctx + n].repeat_interleave(nq // nkv, 0)
+    vals = vcache[:, : ctx + n].repeat_interleave(nq // nkv, 0)
+    mask = torch.arange(ctx + n)[None, :] <= (ctx + torch.arange(n))[:, None]
+    o = F.scaled_dot_product_attention(q.transpose(0, 1), keys, vals, attn_mask=mask)
+    x = x + F.linear(o.transpose(0, 1).reshape(n, nq * D), L["w_o"].double())
+    h = F.rms_norm(x, (H,), L["ffn_norm"].double(), eps=cfg.rms_eps)
+    I = cfg.dense_inter
+    gu = L["w_gate_up"].double()
+    return x + F.linear(F.silu(F.linear(h, gu[:I])) * F.linear(h, gu[I:]), L["w_down"].double())
+
+
+@pytest.mark.parametrize("accepted", [0, 2, 3])
+def test_mtp_draft_matches_torch_composition(oracle_mod, accepted):
+    """FastMTP drafting (Jina-OCR-v1 paper, section 3.1) against the same
+    recursion composed from torch operators: z = P [N_e(e); N_h(a)], u =
+    N_o(B(z)), draft = argmax W_lm u, depth 1 over the committed rows, deeper
+    depths on the previous depth's u and draft."""
+    base = workloads.scaled(workloads.get_config("tiny_fp32"), n_q=4, n_kv=2, norm_gain_std=0.1)
+    mc = workloads.mtp_config(base)
+    tw = workloads.make_weights(base)
+    mw = workloads.mtp_weights(base)
+    cap = workloads.capacity_for(base) + 16
+    k, v = workloads.kv_cache(mc, capacity=cap)
+    orc = oracle_mod.Oracle(mc, workloads.mtp_model_weights(tw, mw), cap)
+    kc, vc = orc.kv_np(k, v)
+    kt, vt = torch.tensor(kc[0, 0]).double(), torch.tensor(vc[0, 0]).double()
+    K, H, ctx = base.k_draft, base.hidden, 200
+    g = torch.Generator().manual_seed(accepted)
+    drafts = torch.randint(0, base.vocab, (K,), generator=g).tolist()
+    nxt = 77
+    bstate = torch.randn(accepted + 1, H, generator=g, dtype=torch.float64)
+    got, gaps = orc.mtp_draft(mw, kc, vc, 0, ctx, accepted, drafts, nxt, bstate.numpy())
+
+    def zrows(toks, states):
+        e = F.rms_norm(tw["embed"].double()[torch.tensor(toks)], (H,), mw["enorm"].double(),
+                       eps=base.rms_eps)
+        s = F.rms_norm(states, (H,), mw["hnorm"].double(), eps=base.rms_eps)
+        return F.linear(torch.cat([e, s], -1), mw["eh_proj"].double())
+
+    def head(xo):
+        f = F.rms_norm(xo, (H,), tw["final_norm"].double(), eps=base.rms_eps)
+        return f, F.linear(f, tw["lm_head"].double())
+
+    toks = [drafts[j] if j < accepted else nxt for j in range(accepted + 1)]
+    xo = _torch_dense_block(mc, mw["block"], zrows(toks, bstate), kt, vt, ctx)
+    f, lg = head(xo)
+    want = [int(torch.argmax(lg[accepted].float()))]
+    u = f[accepted:accepted + 1]
+    for k_ in range(2, K + 1):
+        xo = _torch_dense_block(mc, mw["block"], zrows([want[-1]], u), kt, vt, ctx + accepted + k_ - 1)
+        f, lg = head(xo)
+        want.append(int(torch.argmax(lg[0].float())))
+        u = f
+    assert got.tolist() == want
+    assert np.all(gaps > 0)
+    # the block's cache now holds the committed rows and the deeper depths' rows
+    np.testing.assert_allclose(kc[0, 0, :, : ctx + accepted + K], kt[:, : ctx + accepted + K].numpy(),
+                               rtol=1e-6, atol=1e-9)

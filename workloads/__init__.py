@@ -2,8 +2,8 @@
 
 This package holds only input generation: the model shapes of the five
 workloads, seeded weight / KV-cache / context-length / draft-randomness
-generators, draft distributions for the sampled verify, and the byte
-accounting used to price a step.  It contains none
+generators, draft distributions for the sampled verify, the FastMTP draft
+head's weights, and the byte accounting used to price a step.  It contains none
 of the verify step's arithmetic; both the HIP library's callers and the CPU
 oracle's callers draw their inputs from here.
 """
@@ -15,6 +15,9 @@ from .synth import (
     kv_cache,
     make_weights,
     committed_tokens,
+    mtp_config,
+    mtp_model_weights,
+    mtp_weights,
     sampled_drafts,
     tensor_seed,
 )
@@ -30,6 +33,9 @@ __all__ = [
     "kv_cache",
     "make_weights",
     "committed_tokens",
+    "mtp_config",
+    "mtp_model_weights",
+    "mtp_weights",
     "sampled_drafts",
     "tensor_seed",
 ]

@@ -249,3 +249,43 @@ def sampled_drafts(cfg: VerifyConfig, batch: int | None = None, step: int = 0,
     u = torch.rand(B, K, generator=g3, dtype=torch.float32)
     seed = tensor_seed(cfg.seed, "gumbel_seed") * 0x100000001 & (2 ** 64 - 1)
     return {"q": q.to(torch.float32), "drafts": drafts, "u": u, "seed": seed, "offset": step}
+
+
+def mtp_weights(cfg: VerifyConfig, device="cpu") -> dict:
+    """The FastMTP draft head of a target workload (Jina-OCR-v1 paper,
+    section 3.1; the released checkpoint names enorm, hnorm, eh_proj and
+    mtp_block): RMSNorm gains enorm and hnorm [H] (1, or 1 + N(0,
+    norm_gain_std^2)), the projection eh_proj [H][2H] (+ s_eh_proj for fp8)
+    and one dense decoder layer `block` (attn_norm, w_qkv, w_o, ffn_norm,
+    w_gate_up [2 I_d][H], w_down [H][I_d]) with I_d = cfg.dense_inter if set,
+    else 4 H.  The embedding, final norm and LM head are the target's.  Same
+    seeded N(0, 0.02^2) recipe and storage formats as the target's weights."""
+    H, D = cfg.hidden, cfg.head_dim
+    mc = mtp_config(cfg)
+    I = mc.dense_inter
+    out = {"enorm": _gain(cfg, H, device, "mtp.enorm"), "hnorm": _gain(cfg, H, device, "mtp.hnorm")}
+    out["eh_proj"], out["s_eh_proj"] = _linear(cfg, (H, 2 * H), device, "mtp.eh_proj")
+    L = {"attn_norm": _gain(cfg, H, device, "mtp.attn_norm"),
+         "ffn_norm": _gain(cfg, H, device, "mtp.ffn_norm")}
+    L["w_qkv"], L["s_qkv"] = _linear(cfg, (cfg.qkv_dim, H), device, "mtp.w_qkv")
+    L["w_o"], L["s_o"] = _linear(cfg, (H, cfg.n_q * D), device, "mtp.w_o")
+    L["w_gate_up"], L["s_gate_up"] = _linear(cfg, (2 * I, H), device, "mtp.w_gate_up")
+    L["w_down"], L["s_down"] = _linear(cfg, (H, I), device, "mtp.w_down")
+    out["block"] = L
+    return out
+
+
+def mtp_config(cfg: VerifyConfig) -> VerifyConfig:
+    """Shape of the FastMTP draft block as a one-layer dense model sharing the
+    target's attention shape, vocabulary, K and storage types."""
+    import dataclasses
+    I = cfg.dense_inter if cfg.ffn == "dense" and cfg.dense_inter else 4 * cfg.hidden
+    return dataclasses.replace(cfg, name=cfg.name + "_mtp", n_layers=1, ffn="dense", dense_inter=I,
+                               n_experts=0, expert_inter=0, top_k=0, n_shared=0, mx="")
+
+
+def mtp_model_weights(target: dict, mtp: dict) -> dict:
+    """The draft block as a weight dict of a one-layer model: the block layer
+    with the target's embedding, final norm and LM head (tied)."""
+    return {"embed": target["embed"], "layers": [mtp["block"]], "final_norm": target["final_norm"],
+            "lm_head": target["lm_head"], "lm_scale": target.get("lm_scale")}
