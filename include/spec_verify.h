@@ -122,7 +122,7 @@
 extern "C" {
 #endif
 
-#define SPEC_VERIFY_ABI_VERSION 3
+#define SPEC_VERIFY_ABI_VERSION 4
 
 /* status codes */
 #define SV_OK 0
@@ -313,6 +313,60 @@ int spec_verify_sample_from_logits(spec_verify_ctx* ctx, const float* logits,
                                    uint32_t offset, const int32_t* ctx_lens_in,
                                    int32_t* ctx_lens_out, int batch, int32_t* accepted_len,
                                    int32_t* next_tok, void* stream);
+
+/*
+ * FastMTP drafting (Jina-OCR-v1 paper, section 3.1; the jina-ocr-v1 tweet
+ * digest: one shared dense draft block run recursively K times).  After a
+ * verify step on `verify_ctx`, proposes the next step's K drafts of every
+ * sequence:
+ *   a(1) = the target's post-norm state (LM-head input) of a committed
+ *   position, a(k) = u(k-1); z(k) = P [N_e(e(next token)); N_h(a(k))];
+ *   u(k) = N_o(B(z(k); pos)); draft k = argmax_v (W_lm u(k))[v] (lowest
+ *   index on ties), where N_e / N_h are RMSNorms with gains enorm / hnorm,
+ *   P = eh_proj [H][2H] (column block 0 multiplies N_e(e)), B the draft
+ *   block, and the embedding, N_o (the final norm) and W_lm the target's.
+ * Depth 1 runs the block over the committed positions ctx .. ctx+a of the
+ * verify step (a = accepted_len; next token d_{j+1} for j < a and next_tok
+ * at j = a), writing the block's cache there; depth k > 1 runs at position
+ * ctx+a+k-1 on the previous depth's u and draft.
+ *   draft_ctx     a context made for the draft block: n_layers = 1,
+ *                 SV_FFN_DENSE (dense_inter = the block's FFN width), the
+ *                 target's hidden, heads, vocab, K, dtypes; kv_capacity >=
+ *                 the largest ctx + 3 (K+1) (deeper depths also fill K
+ *                 slots past their position, which the next depth-1 pass
+ *                 rewrites)
+ *   w             the draft block as a one-layer model: layers[0] = the
+ *                 block (attn_norm, w_qkv, w_o, ffn_norm, w_gate_up, w_down),
+ *                 embed / final_norm / lm_head (+ lm_scale) the target's;
+ *                 layout as for spec_verify_step
+ *   mtp           enorm, hnorm [H] fp32; eh_proj [H][2H] in the weight
+ *                 storage type and layout (+ s_eh_proj for SV_FP8)
+ *   k_cache, v_cache  the block's own KV cache (layout as for the target's,
+ *                 one layer)
+ *   verify_ctx    the context of the verify step just run: its final-normed
+ *                 rows are the states a(1) (call before its next step)
+ *   ctx_in, accepted_len, next_tok, draft_toks  that verify step's inputs
+ *                 and outputs ([batch] / [batch][K], device)
+ *   drafts_out    [batch][K] int32 <- the next step's drafts; all -1 for a
+ *                 sequence whose verify step failed (accepted_len < 0; no new
+ *                 error bit) or whose tokens are out of range, and -1 from the
+ *                 first depth whose K+1 rows would pass the capacity or that
+ *                 meets a NaN logit (those set SV_DEV_* bits in draft_ctx's
+ *                 error word); a skipped pass does not write the block cache
+ * Every pass is enqueued on `stream` with no host synchronisation.
+ */
+typedef struct {
+    const float* enorm;       /* N_e gain [H] */
+    const float* hnorm;       /* N_h gain [H] */
+    const void* eh_proj;      /* P [H][2H] */
+    const float* s_eh_proj;   /* fp8 row scales of P [H] (SV_FP8 only) */
+} spec_mtp_weights;
+
+int spec_draft_step(spec_verify_ctx* draft_ctx, const spec_verify_weights* w,
+                    const spec_mtp_weights* mtp, void* k_cache, void* v_cache,
+                    const spec_verify_ctx* verify_ctx, const int32_t* ctx_in,
+                    const int32_t* accepted_len, const int32_t* next_tok,
+                    const int32_t* draft_toks, int batch, int32_t* drafts_out, void* stream);
 
 /*
  * Repack one row-major matrix W[rows][cols] (device, storage `dtype`) into

@@ -36,7 +36,7 @@ EXPORTS = ("spec_verify_init", "spec_verify_destroy", "spec_verify_step", "spec_
            "spec_verify_last_error", "spec_verify_status_string", "spec_verify_abi_version",
            "spec_verify_pack_tiled16", "spec_verify_tiled16_bytes", "spec_verify_step_sampled",
            "spec_verify_sample_from_logits", "spec_verify_pack_mx_scales",
-           "spec_verify_mx_scales_bytes")
+           "spec_verify_mx_scales_bytes", "spec_draft_step")
 
 
 class SpecVerifyConfig(ctypes.Structure):
@@ -61,6 +61,11 @@ class SpecVerifyWeights(ctypes.Structure):
     _fields_ = [("embed", c_void_p), ("layers", POINTER(SpecVerifyLayer)),
                 ("final_norm", c_void_p), ("lm_head", c_void_p), ("lm_scale", c_void_p),
                 ("layout", c_int)]
+
+
+class SpecMtpWeights(ctypes.Structure):
+    _fields_ = [("enorm", c_void_p), ("hnorm", c_void_p), ("eh_proj", c_void_p),
+                ("s_eh_proj", c_void_p)]
 
 
 class SpecVerifyError(RuntimeError):
@@ -101,6 +106,7 @@ def load_library() -> ctypes.CDLL:
         lib.spec_verify_pack_tiled16.argtypes = [P, P, ctypes.c_long, c_int, c_int, P]
         lib.spec_verify_tiled16_bytes.argtypes = [ctypes.c_long, c_int, c_int]
         lib.spec_verify_pack_mx_scales.argtypes = [P, P, ctypes.c_long, c_int, P]
+        lib.spec_draft_step.argtypes = [P, P, P, P, P, P, P, P, P, P, c_int, P, P]
         lib.spec_verify_mx_scales_bytes.argtypes = [ctypes.c_long, c_int]
         for f in EXPORTS:
             if f not in ("spec_verify_destroy", "spec_verify_status_string"):
@@ -323,6 +329,15 @@ def spec_verify_sample_from_logits(ctx: int, logits, draft_toks, draft_probs, ac
         "spec_verify_sample_from_logits")
 
 
+def spec_draft_step(ctx: int, weights: SpecVerifyWeights, mtp: SpecMtpWeights, k_cache, v_cache,
+                    verify_ctx: int, ctx_in, accepted_len, next_tok, draft_toks, batch: int,
+                    drafts_out, stream=None) -> None:
+    _check(load_library().spec_draft_step(
+        ctx, ctypes.byref(weights), ctypes.byref(mtp), _p(k_cache), _p(v_cache), verify_ctx,
+        _p(ctx_in), _p(accepted_len), _p(next_tok), _p(draft_toks), int(batch), _p(drafts_out),
+        _stream(stream)), "spec_draft_step")
+
+
 def spec_verify_error_word(ctx: int, clear: bool = False, stream=None) -> int:
     v = c_uint32()
     _check(load_library().spec_verify_error_word(ctx, ctypes.byref(v), int(clear),
@@ -421,6 +436,63 @@ class VerifyContext:
 
     def kernel_time(self, kclass, enable=-1, query=True):
         return spec_verify_kernel_time(self.handle, kclass, enable, query)
+
+    def close(self):
+        if self.handle:
+            spec_verify_destroy(self.handle)
+            self.handle = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+class DraftContext:
+    """Owns a library context for the FastMTP draft block; wraps
+    spec_draft_step.  `cfg` is the block's one-layer dense shape, `target`
+    the target's weight dict (its embedding, final norm and LM head are
+    used; already tiled16-packed ones are taken as they are), `mtp` the draft
+    head's weights (enorm, hnorm, eh_proj (+ s_eh_proj), block)."""
+
+    def __init__(self, cfg, max_batch: int, kv_capacity: int, target: dict, mtp: dict,
+                 layout: str = "tiled16"):
+        self.cfg = cfg
+        self.handle = spec_verify_init(make_config(cfg, max_batch, kv_capacity))
+        block = dict(mtp["block"])
+        P = mtp["eh_proj"]
+        tl = target.get("layout", "row_major")
+        if layout == "tiled16":
+            for name in GEMM_MATRICES:
+                if block.get(name) is not None:
+                    block[name] = pack_matrix(block[name])
+            P = pack_matrix(P)
+            if tl == "row_major":
+                target = pack_weights(target)
+        elif tl != "row_major":
+            raise ValueError("row-major draft weights need a row-major target")
+        self.weights = {"embed": target["embed"], "layers": [block],
+                        "final_norm": target["final_norm"], "lm_head": target["lm_head"],
+                        "lm_scale": target.get("lm_scale"), "layout": layout}
+        self._w, self._keep = make_weights(self.weights, 1)
+        self._mtp = SpecMtpWeights()
+        self._mtp.enorm = mtp["enorm"].data_ptr()
+        self._mtp.hnorm = mtp["hnorm"].data_ptr()
+        self._mtp.eh_proj = P.data_ptr()
+        s = mtp.get("s_eh_proj")
+        self._mtp.s_eh_proj = s.data_ptr() if s is not None else None
+        self._keep += [mtp, P]
+
+    def draft(self, k_cache, v_cache, verify_ctx, ctx_in, accepted, next_tok, drafts_in,
+              drafts_out, batch=None, stream=None):
+        B = accepted.shape[0] if batch is None else batch
+        vh = verify_ctx.handle if hasattr(verify_ctx, "handle") else verify_ctx
+        spec_draft_step(self.handle, self._w, self._mtp, k_cache, v_cache, vh, ctx_in, accepted,
+                        next_tok, drafts_in, B, drafts_out, stream)
+
+    def error_word(self, clear=False, stream=None) -> int:
+        return spec_verify_error_word(self.handle, clear, stream)
 
     def close(self):
         if self.handle:

@@ -32,6 +32,7 @@
 #include "small_kernels.h"
 #include "qkv_rope.h"
 #include "sampling.h"
+#include "draft.h"
 
 namespace {
 
@@ -120,6 +121,12 @@ struct spec_verify_ctx {
     unsigned long long* sdkeys = nullptr;
     unsigned long long* sfkeys = nullptr;
     int* sdecision = nullptr;
+    // FastMTP drafting (draft.h): concatenated input rows, a zero residual,
+    // row-0 positions of a pass, the state carried between depths
+    void* dcat = nullptr;
+    float* dzero = nullptr;
+    int* dpos = nullptr;
+    void* dstate = nullptr;
     // debug outputs
     float* dbg_logits = nullptr;
     float* dbg_hidden = nullptr;
@@ -514,6 +521,13 @@ struct ProfScope {
     ~ProfScope() { g_ev_start = g_ev_stop = nullptr; }
 };
 
+// One depth of FastMTP drafting run through the step (draft.h).
+struct DraftPass {
+    DraftArgs args;           // pass-invariant fields; k, keys, h, NT, T set per pass
+    const void* P;            // eh_proj [H][2H]
+    const float* sP;          // its fp8 row scales
+};
+
 struct SampleIn {
     const float* q;
     const float* u;
@@ -716,6 +730,16 @@ int spec_verify_init(const spec_verify_config* cfg, spec_verify_ctx** out)
     ALLOC(c->keys, c->keys_elems);
     ALLOC(c->seq_err, (size_t)k.max_batch);
     ALLOC(c->err_word, 1);
+    {
+        char* dc = nullptr;
+        char* ds = nullptr;
+        ALLOC(dc, (size_t)T * 2 * H * AES);
+        c->dcat = dc;
+        ALLOC(c->dzero, (size_t)T * H);
+        ALLOC(c->dpos, (size_t)k.max_batch);
+        ALLOC(ds, (size_t)k.max_batch * H * AES);
+        c->dstate = ds;
+    }
     if (k.vocab <= SAMPLE_MAX_TILES * SAMPLE_TILE) {
         c->s_ntile = cdiv(k.vocab, SAMPLE_TILE);
         ALLOC(c->slogits, (size_t)T * k.vocab);
@@ -759,9 +783,10 @@ int spec_verify_init(const spec_verify_config* cfg, spec_verify_ctx** out)
         }
     }
     hipError_t e = hipMemset(c->err_word, 0, sizeof(unsigned));
+    if (e == hipSuccess) e = hipMemset(c->dzero, 0, (size_t)T * H * sizeof(float));
     if (e != hipSuccess) {
         spec_verify_destroy(c);
-        return fail(SV_ERR_HIP, std::string("error word reset: ") + hipGetErrorString(e));
+        return fail(SV_ERR_HIP, std::string("workspace reset: ") + hipGetErrorString(e));
     }
     *out = c;
     return SV_OK;
@@ -783,12 +808,13 @@ int spec_verify_set_debug(spec_verify_ctx* c, float* logits, float* hidden, int3
 static int step_impl(spec_verify_ctx* c, const spec_verify_weights* w, void* k_cache,
                      void* v_cache, const int32_t* committed, const int32_t* drafts,
                      const int32_t* ctx_in, int32_t* ctx_out, int B, int32_t* accepted,
-                     int32_t* next_tok, void* stream, const SampleIn* smp)
+                     int32_t* next_tok, void* stream, const SampleIn* smp,
+                     DraftPass* dp = nullptr)
 {
     if (!c || !w) return fail(SV_ERR_INVALID_ARG, "null context or weights");
     if (B < 1 || B > c->c.max_batch) return fail(SV_ERR_INVALID_ARG, "batch outside [1, max_batch]");
-    if (!k_cache || !v_cache || !committed || !drafts || !ctx_in || !ctx_out || !accepted ||
-        !next_tok)
+    if (!k_cache || !v_cache || !ctx_in ||
+        (!dp && (!committed || !drafts || !ctx_out || !accepted || !next_tok)))
         return fail(SV_ERR_INVALID_ARG, "null buffer pointer");
     const spec_verify_config& k = c->c;
     if (!w->embed || !w->layers || !w->final_norm || !w->lm_head)
@@ -855,7 +881,7 @@ static int step_impl(spec_verify_ctx* c, const spec_verify_weights* w, void* k_c
     // fewer rows: the attention input (embedding + norm for the first layer,
     // QKV, rotary, cache append) is one kernel
     const bool big = T >= 64 && wt != SV_F32;
-    if (big) {
+    if (big && !dp) {
         if (bf) embed_norm_kernel<true><<<T, 1024, 0, s>>>(ra);
         else embed_norm_kernel<false><<<T, 1024, 0, s>>>(ra);
     }
@@ -957,6 +983,28 @@ static int step_impl(spec_verify_ctx* c, const spec_verify_weights* w, void* k_c
     at.opart = c->opart;
     at.mlpart = c->mlpart;
 
+    if (dp) {
+        // drafting: the block's input rows z = P [N_e(e); N_h(state)] instead
+        // of an embedding, then the block's first norm
+        DraftArgs& da = dp->args;
+        da.T = T;
+        da.cat = c->dcat;
+        da.pos = c->dpos;
+        da.seq_err = c->seq_err;
+        da.ustate = c->dstate;
+        if (bf) mtp_input_kernel<true><<<T, 256, 0, s>>>(da);
+        else mtp_input_kernel<false><<<T, 256, 0, s>>>(da);
+        const int ks = dense_gemm(GM_STORE, c->dcat, 2L * H, H, 2 * H, dp->P, dp->sP, c->parts, H,
+                                  KS_MAX);
+        ra.x = c->dzero;
+        ra.x_out = c->x;
+        ra.parts = c->parts;
+        ra.nsplit = ks;
+        ra.gain = w->layers[0].attn_norm;
+        ra.dbg_hidden = nullptr;
+        if (bf) residual_norm_kernel<true, false><<<T, 1024, 0, s>>>(ra);
+        else residual_norm_kernel<false, false><<<T, 1024, 0, s>>>(ra);
+    }
     for (int l = 0; l < L; l++) {
         const spec_verify_layer& Lw = w->layers[l];
         // ---- attention half
@@ -966,7 +1014,7 @@ static int step_impl(spec_verify_ctx* c, const spec_verify_weights* w, void* k_c
             qa.ws = Lw.s_qkv;
             qa.layer = l;
             ProfScope ps(c, SV_KC_QKV, s);
-            launch_qkv_rope(wt, MFd, packed, l == 0, qa, s);
+            launch_qkv_rope(wt, MFd, packed, l == 0 && !dp, qa, s);
         } else {
             {
                 ProfScope ps(c, SV_KC_QKV, s);
@@ -1160,6 +1208,16 @@ static int step_impl(spec_verify_ctx* c, const spec_verify_weights* w, void* k_c
         ProfScope ps(c, SV_KC_LM_HEAD, s);
         dense_gemm(GM_ARGMAX, c->h, H, k.vocab, H, w->lm_head, w->lm_scale, nullptr, 0, 0, wt_mx);
     }
+    if (dp) {
+        DraftArgs& da = dp->args;
+        da.keys = c->keys;
+        da.NT = last_nt;
+        da.h = c->h;
+        if (bf) draft_pick_kernel<true><<<B, 64, 0, s>>>(da);
+        else draft_pick_kernel<false><<<B, 64, 0, s>>>(da);
+        HIP_TRY(hipGetLastError());
+        return SV_OK;
+    }
     if (smp) return launch_sampling(c, *smp, lm_logits, drafts, ctx_in, ctx_out, B, accepted,
                                     next_tok, c->seq_err, s);
     const int NT_lm = last_nt;   // argmax key columns written by the LM head
@@ -1202,6 +1260,52 @@ int spec_verify_step_sampled(spec_verify_ctx* c, const spec_verify_weights* w, v
     if (rc) return rc;
     return step_impl(c, w, k_cache, v_cache, committed, drafts, ctx_in, ctx_out, B, accepted,
                      next_tok, stream, &smp);
+}
+
+int spec_draft_step(spec_verify_ctx* c, const spec_verify_weights* w, const spec_mtp_weights* m,
+                    void* k_cache, void* v_cache, const spec_verify_ctx* vc, const int32_t* ctx_in,
+                    const int32_t* accepted, const int32_t* next_tok, const int32_t* drafts_in,
+                    int B, int32_t* drafts_out, void* stream)
+{
+    if (!c || !w || !m || !vc) return fail(SV_ERR_INVALID_ARG, "null context or weights");
+    const spec_verify_config& k = c->c;
+    if (k.n_layers != 1 || k.ffn_kind != SV_FFN_DENSE || k.mx_dtype != 0)
+        return fail(SV_ERR_UNSUPPORTED, "the draft context must be a one-layer dense model");
+    if (vc->c.hidden != k.hidden || vc->c.k_draft != k.k_draft || vc->c.vocab != k.vocab ||
+        vc->bf != c->bf || B > vc->c.max_batch)
+        return fail(SV_ERR_INVALID_ARG, "draft and verify contexts differ in hidden, K, vocab, "
+                                        "activation type or batch");
+    if (!ctx_in || !accepted || !next_tok || !drafts_in || !drafts_out)
+        return fail(SV_ERR_INVALID_ARG, "null buffer pointer");
+    if (!m->enorm || !m->hnorm || !m->eh_proj || (k.weight_dtype == SV_FP8 && !m->s_eh_proj))
+        return fail(SV_ERR_INVALID_ARG, "null draft-head weight");
+    DraftPass dp;
+    memset(&dp, 0, sizeof(dp));
+    DraftArgs& da = dp.args;
+    da.H = k.hidden;
+    da.K1 = c->K1;
+    da.V = k.vocab;
+    da.cap = k.kv_capacity;
+    da.eps = k.rms_eps;
+    da.embed = w->embed;
+    da.vstate = vc->h;
+    da.g_e = m->enorm;
+    da.g_h = m->hnorm;
+    da.accepted = accepted;
+    da.next_tok = next_tok;
+    da.drafts_in = drafts_in;
+    da.drafts_out = drafts_out;
+    da.ctx_in = ctx_in;
+    da.err_word = c->err_word;
+    dp.P = m->eh_proj;
+    dp.sP = m->s_eh_proj;
+    for (int d = 1; d <= k.k_draft; d++) {
+        da.k = d;
+        int rc = step_impl(c, w, k_cache, v_cache, nullptr, nullptr, c->dpos, nullptr, B, nullptr,
+                           nullptr, stream, nullptr, &dp);
+        if (rc) return rc;
+    }
+    return SV_OK;
 }
 
 int spec_verify_sample_from_logits(spec_verify_ctx* c, const float* logits,

@@ -13,7 +13,7 @@ HEADER = os.path.join(ROOT, "include", "spec_verify.h")
 def _declared():
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(spec_verify_[a-z0-9_]+)\s*\(", text)))
+    return sorted(set(re.findall(r"\b(spec_(?:verify|draft)_[a-z0-9_]+)\s*\(", text)))
 
 
 @pytest.fixture(scope="module")
@@ -36,7 +36,7 @@ def test_every_declared_function_is_exported(sv):
 
 
 def test_status_strings_and_version(sv):
-    assert sv.spec_verify_abi_version() == 3
+    assert sv.spec_verify_abi_version() == 4
     assert sv.spec_verify_status_string(0) == "ok"
     assert "invalid" in sv.spec_verify_status_string(-1)
     assert sv.spec_verify_status_string(12345) == "unknown status"
