@@ -1,6 +1,6 @@
 """Benchmark of the greedy speculative-decoding verify step on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config moe_b1] [--sampled]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config moe_b1] [--sampled | --draft-loop]
 
 A step is one spec_verify_step over a whole batch (every row of the hot
 path: embedding, all decoder layers, LM head + argmax, acceptance + commit).
@@ -16,7 +16,9 @@ token, all on the device.
 
 --sampled times the sampled (rejection-sampling) step instead, at temperature
 1 with drafts drawn from seeded draft distributions; its line adds the time
-of the sampling kernels.
+of the sampling kernels.  --draft-loop times the device-resident FastMTP
+draft -> verify loop (spec_draft_step after every spec_verify_step) and
+reports the draft step's share.
 
 One JSON line is printed: accepted tokens/s (sum over sequences of
 accepted + 1 per step, over the timed wall clock), microseconds per step, the
@@ -262,6 +264,76 @@ def run_bench(cfg, steps, warmup, sampled=False):
     return res
 
 
+def run_draft_loop(cfg, steps, warmup):
+    """The device-resident draft -> verify loop: every iteration verifies the
+    current drafts (spec_verify_step) and lets the FastMTP draft head propose
+    the next ones (spec_draft_step) from the verify step's outcome; contexts
+    grow by accepted + 1 and the bonus token becomes the next committed token,
+    all on the device.  Seeded random weights for the target and the draft
+    head, so drafts are rarely accepted: the line measures cost, not the
+    pages' acceptance."""
+    import torch
+
+    import speculative_decoding_verify_step_amd as sv
+    import workloads
+
+    K1 = cfg.k_draft + 1
+    n_it = warmup + 2 * steps
+    c_loop = workloads.scaled(cfg, steps=n_it)
+    cap = workloads.capacity_for(c_loop) + 64
+    w = workloads.make_weights(cfg, "cuda")
+    k, v = workloads.kv_cache(cfg, "cuda", capacity=cap)
+    k, v = sv.kv_to_library(k, v)
+    vc = sv.VerifyContext(cfg, cfg.batch, cap, w)
+    mc = workloads.mtp_config(cfg)
+    mw = workloads.mtp_weights(cfg, "cuda")
+    mk, mv = workloads.kv_cache(mc, "cuda", capacity=cap)
+    mk, mv = sv.kv_to_library(mk, mv)
+    dc = sv.DraftContext(mc, cfg.batch, cap, vc.weights, mw)
+    B = cfg.batch
+    i32 = dict(dtype=torch.int32, device="cuda")
+    ctx0 = workloads.context_lengths(cfg).to(**i32)
+    com0 = workloads.committed_tokens(cfg).to(**i32)
+    _, rtok = workloads.draft_randomness(cfg, steps=1)
+    d0 = rtok[0].to(**i32).contiguous()
+    ctxs = [ctx0.clone(), ctx0.clone()]
+    coms = [com0.clone(), com0.clone()]
+    drs = [d0.clone(), d0.clone()]
+    acc_all = torch.empty(n_it, B, **i32)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(n_it)]
+
+    def one(i, timed):
+        a, b_ = i % 2, (i + 1) % 2
+        vc.step(k, v, coms[a], drs[a], ctxs[a], ctxs[b_], acc_all[i], coms[b_])
+        if timed:
+            ev[i][0].record()
+        dc.draft(mk, mv, vc, ctxs[a], acc_all[i], coms[b_], drs[a], drs[b_])
+        if timed:
+            ev[i][1].record()
+
+    for i in range(warmup):
+        one(i, False)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(warmup, warmup + steps):
+        one(i, False)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    for i in range(warmup + steps, n_it):   # a second pass with events around the drafts
+        one(i, True)
+    torch.cuda.synchronize()
+    draft_ms = sum(ev[i][0].elapsed_time(ev[i][1]) for i in range(warmup + steps, n_it)) / steps
+    assert vc.error_word() == 0 and dc.error_word() == 0, "device error during the loop"
+    acc = acc_all[warmup:warmup + steps].to(torch.int64)
+    tok = int(acc.sum().item()) + steps * B
+    res = {"ms_per_step": wall * 1e3 / steps, "tok_s": tok / wall, "tau": tok / (steps * B),
+           "draft_ms": draft_ms}
+    dc.close()
+    vc.close()
+    return res
+
+
 # ----------------------------------------------------------- CPU baseline
 def cpu_baseline(cfg, budget_s=15.0):
     """The oracle, as it is, on this host: whole verify steps of sequence 0
@@ -320,6 +392,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--sampled", action="store_true",
                     help="time the sampled (rejection-sampling) verify step instead of the greedy one")
+    ap.add_argument("--draft-loop", action="store_true",
+                    help="time the device-resident FastMTP draft -> verify loop")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                     help="only run a plain device copy of BYTES (counter calibration)")
     args = ap.parse_args()
@@ -334,6 +408,18 @@ def main():
     cfg = workloads.get_config(args.config)
     steps = args.steps if args.steps is not None else (cfg.steps if cfg.steps > 1 else 200)
     warmup = args.warmup if args.warmup is not None else 10
+    if args.draft_loop:
+        r = run_draft_loop(cfg, steps, warmup)
+        print(json.dumps({
+            "metric": METRIC, "value": r["tok_s"], "unit": "tokens/s", "n_gpus": 1,
+            "steps": steps, "warmup": warmup, "ms_per_step": r["ms_per_step"],
+            "us_per_step": r["ms_per_step"] * 1e3, "higher_is_better": True, "scaling": "weak",
+            "vs_baseline": None, "dtype": "bf16" if cfg.wdtype == "bf16" else cfg.wdtype,
+            "data": "synthetic (seeded random target and draft-head weights)",
+            "config": {"workload": cfg.name, "batch": cfg.batch, "k_draft": cfg.k_draft,
+                       "mode": "FastMTP draft -> verify loop", "tokens_per_verify": r["tau"]},
+            "draft_us_per_step": r["draft_ms"] * 1e3}), flush=True)
+        return
     r = run_bench(cfg, steps, warmup, sampled=args.sampled)
     lm_gbs = r["lm_bytes"] / (r["lm_ms"] * 1e-3) / 1e9 if r["lm_ms"] > 0 else None
     out = {

@@ -118,22 +118,35 @@ __global__ __launch_bounds__(256) void mtp_input_kernel(DraftArgs a)
     }
 }
 
-// One wave per sequence: the draft of depth k (the greedy token of row a of
-// depth 1, row 0 of deeper depths) and that row's final-normed state.
+// One 256-thread workgroup per sequence: the draft of depth k (the greedy
+// token of row a of depth 1, row 0 of deeper depths) and that row's
+// final-normed state.  Every thread issues its key loads (8 at a time,
+// clamped indices) before reducing them.
 template <bool BF>
-__global__ __launch_bounds__(64) void draft_pick_kernel(DraftArgs a)
+__global__ __launch_bounds__(256) void draft_pick_kernel(DraftArgs a)
 {
     using A = Act<BF>;
-    const int b = blockIdx.x, lane = threadIdx.x, K = a.K1 - 1;
+    constexpr int KB = 8;
+    __shared__ unsigned long long red[4];
+    const int b = blockIdx.x, tid = threadIdx.x, lane = tid & 63, K = a.K1 - 1;
     const int r = a.k == 1 ? min(max(a.accepted[b], 0), K) : 0;
     const int t = b * a.K1 + r;
     unsigned long long best = 0ull;
-    for (int n = lane; n < a.NT; n += 64) best = umax64(best, a.keys[(size_t)n * a.T + t]);
+    for (int n0 = tid; n0 < a.NT; n0 += 256 * KB) {
+        unsigned long long v[KB];
+#pragma unroll
+        for (int u = 0; u < KB; u++) v[u] = a.keys[(size_t)min(n0 + 256 * u, a.NT - 1) * a.T + t];
+#pragma unroll
+        for (int u = 0; u < KB; u++) best = umax64(best, v[u]);
+    }
     best = wave_max_u64(best);
+    if (lane == 0) red[tid >> 6] = best;
+    __syncthreads();
+    best = umax64(umax64(red[0], red[1]), umax64(red[2], red[3]));
     const bool nan = best == ~0ull;
     const bool bad = a.seq_err[b] != 0 || nan;
     const int tok = (int)(0xffffffffu - (uint32_t)(best & 0xffffffffull));
-    if (lane == 0) {
+    if (tid == 0) {
         a.drafts_out[(size_t)b * K + a.k - 1] = bad ? -1 : tok;
         const unsigned e = ((unsigned)a.seq_err[b] & 0xffu) | (nan ? SV_DEV_NAN_LOGIT : 0u);
         if (e) atomicOr(a.err_word, e);
@@ -143,5 +156,5 @@ __global__ __launch_bounds__(64) void draft_pick_kernel(DraftArgs a)
     }
     const typename A::T* src = (const typename A::T*)a.h + (size_t)t * a.H;
     typename A::T* dst = (typename A::T*)a.ustate + (size_t)b * a.H;
-    for (int i = lane; i < a.H; i += 64) dst[i] = src[i];
+    for (int i = tid; i < a.H; i += 256) dst[i] = src[i];
 }

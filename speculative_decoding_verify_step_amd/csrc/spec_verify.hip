@@ -1213,8 +1213,8 @@ static int step_impl(spec_verify_ctx* c, const spec_verify_weights* w, void* k_c
         da.keys = c->keys;
         da.NT = last_nt;
         da.h = c->h;
-        if (bf) draft_pick_kernel<true><<<B, 64, 0, s>>>(da);
-        else draft_pick_kernel<false><<<B, 64, 0, s>>>(da);
+        if (bf) draft_pick_kernel<true><<<B, 256, 0, s>>>(da);
+        else draft_pick_kernel<false><<<B, 256, 0, s>>>(da);
         HIP_TRY(hipGetLastError());
         return SV_OK;
     }
