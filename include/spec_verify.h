@@ -58,8 +58,8 @@
  * Supported combinations: weights, embedding, activations and KV cache all
  * SV_F32; or weights SV_BF16 or SV_FP8 with embedding and KV cache SV_BF16
  * (activations bf16, accumulation fp32).  With mx_dtype = SV_MXFP4 (bf16
- * MoE models, max_batch * (K+1) < 64, hidden and expert_inter multiples of
- * 128 and at most 2048, tiled16 layout) the weight-streaming matrices --
+ * MoE models, hidden and expert_inter multiples of 128 and at most 2048,
+ * tiled16 layout) the weight-streaming matrices --
  * w_gate_up, w_down, w_sh_gate_up, w_sh_down and lm_head -- are MXFP4: each
  * is the byte matrix [rows][cols/2] of codes, packed with
  * spec_verify_pack_tiled16 as an SV_FP8 matrix of cols/2 columns, and its s_x

@@ -571,12 +571,15 @@ __global__ __launch_bounds__(256) void gemm_mx_lds_kernel(GemmArgs a)
 template <int WT, int MF, int NF, int MODE, bool PACKED>
 __global__ __launch_bounds__(256) void gemm_bigm_kernel(GemmArgs a)
 {
+    constexpr bool MX = WT == SV_MXFP4;
+    static_assert(!MX || PACKED, "MXFP4 weights: tiled16 layout only");
     using Tr = WTraits<WT>;
     constexpr int KL = Tr::KL, SK = Tr::SK, XU = Tr::XU, WESZ = Tr::ESZ;
+    constexpr int EH = w_half_bytes<WT>();
     constexpr int AESZ = ATraits<WT>::ESZ;
     constexpr int NFT = (MODE == GM_SWIGLU) ? 2 * NF : NF;
     constexpr int BM = 16 * MF;
-    constexpr int CS = 2;                        // reduction steps per chunk
+    constexpr int CS = MX ? 1 : 2;               // reduction steps per chunk (an MXFP4 step is 128 long)
     constexpr int KC = CS * SK;                  // chunk length
     constexpr int PIECES = MF * CS * XU;         // 1 KiB activation pieces per chunk
     constexpr int PPW = (PIECES + 3) / 4;        // pieces each wave stages (the last may idle)
@@ -601,12 +604,15 @@ __global__ __launch_bounds__(256) void gemm_bigm_kernel(GemmArgs a)
     if (nrows <= 0) return;
     const char* Wb;
     const float* sc;
+    const uint8_t* scb = nullptr;   // MXFP4: the group's tiled E8M0 scales
     if (group < a.G1) {
-        Wb = (const char*)a.W + (size_t)group * a.w_gstride * WESZ;
+        Wb = (const char*)a.W + (size_t)group * a.w_gstride * EH / 2;
         sc = a.ws ? a.ws + (size_t)group * a.s_gstride : nullptr;
+        if constexpr (MX) scb = (const uint8_t*)a.ws + (size_t)group * a.s_gstride;
     } else {
-        Wb = (const char*)a.W2 + (size_t)(group - a.G1) * a.w2_gstride * WESZ;
+        Wb = (const char*)a.W2 + (size_t)(group - a.G1) * a.w2_gstride * EH / 2;
         sc = a.ws2 ? a.ws2 + (size_t)(group - a.G1) * a.s2_gstride : nullptr;
+        if constexpr (MX) scb = (const uint8_t*)a.ws2 + (size_t)(group - a.G1) * a.s2_gstride;
     }
     const int ncol0 = (nt * 4 + wave) * 16 * NF;
     const int K = a.K;
@@ -615,6 +621,7 @@ __global__ __launch_bounds__(256) void gemm_bigm_kernel(GemmArgs a)
     const int nchunk = kspan / KC;
 
     const char* wrow[NFT];
+    uint4 sslice[MX ? NFT : 1];   // MXFP4: the lane's scale bytes of steps 0..15 (K <= 2048)
     bool fvalid[NF];
 #pragma unroll
     for (int f = 0; f < NF; f++) {
@@ -623,9 +630,14 @@ __global__ __launch_bounds__(256) void gemm_bigm_kernel(GemmArgs a)
         int r = fvalid[f] ? min(n0 + l16, a.N - 1) : 0;
         if constexpr (PACKED) {
             int rb = fvalid[f] ? n0 / 16 : 0;
-            wrow[f] = Wb + (size_t)rb * K * 16 * WESZ + (size_t)lane * 16;
+            wrow[f] = Wb + (size_t)rb * K * 8 * EH + (size_t)lane * 16;
             if constexpr (MODE == GM_SWIGLU)
-                wrow[NF + f] = Wb + (size_t)(rb + a.dual_off / 16) * K * 16 * WESZ + (size_t)lane * 16;
+                wrow[NF + f] = Wb + (size_t)(rb + a.dual_off / 16) * K * 8 * EH + (size_t)lane * 16;
+            if constexpr (MX) {
+                sslice[f] = ldg16(scb + ((size_t)rb * 64 + lane) * 16);
+                if constexpr (MODE == GM_SWIGLU)
+                    sslice[NF + f] = ldg16(scb + ((size_t)(rb + a.dual_off / 16) * 64 + lane) * 16);
+            }
         } else {
             wrow[f] = Wb + ((size_t)r * K + (size_t)lg * KL) * WESZ;
             if constexpr (MODE == GM_SWIGLU)
@@ -688,7 +700,10 @@ __global__ __launch_bounds__(256) void gemm_bigm_kernel(GemmArgs a)
         for (int s = 0; s < CS; s++) {
             WOp<WT> wo[NFT];
 #pragma unroll
-            for (int f = 0; f < NFT; f++) wo[f] = wprep<WT>(wcur[s][f]);
+            for (int f = 0; f < NFT; f++) {
+                if constexpr (MX) wo[f] = wprep_mx(wcur[s][f], mx_scale_byte(sslice[f], (kb + c * KC) / SK + s));
+                else wo[f] = wprep<WT>(wcur[s][f]);
+            }
 #pragma unroll
             for (int m = 0; m < MF; m++) {
                 uint4 xf[XU];

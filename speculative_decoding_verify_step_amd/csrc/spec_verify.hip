@@ -201,8 +201,6 @@ int validate_config(const spec_verify_config& c)
             return bad("MXFP4 expert and LM-head weights need a bf16 MoE model");
         if (c.hidden % 128 || c.expert_inter % 128 || c.hidden > 2048 || c.expert_inter > 2048)
             return bad("MXFP4 weights need hidden and expert_inter multiples of 128, at most 2048");
-        if ((long)c.max_batch * (c.k_draft + 1) >= 64)
-            return bad("MXFP4 weights are supported for max_batch*(K+1) < 64 rows");
     }
     return SV_OK;
 }
@@ -321,7 +319,8 @@ void launch_big_m(int wt, const GemmArgs& a, dim3 grid, hipStream_t s)
 {
     if (wt == SV_F32) launch(gemm_bigm_kernel<SV_F32, BIG_MF, BIG_NF, MODE, PK>, grid, dim3(256), 0, s, a);
     else if (wt == SV_BF16) launch(gemm_bigm_kernel<SV_BF16, BIG_MF, BIG_NF, MODE, PK>, grid, dim3(256), 0, s, a);
-    else launch(gemm_bigm_kernel<SV_FP8, BIG_MF, BIG_NF, MODE, PK>, grid, dim3(256), 0, s, a);
+    else if (wt == SV_FP8) launch(gemm_bigm_kernel<SV_FP8, BIG_MF, BIG_NF, MODE, PK>, grid, dim3(256), 0, s, a);
+    else if constexpr (PK) launch(gemm_bigm_kernel<SV_MXFP4, BIG_MF, BIG_NF, MODE, PK>, grid, dim3(256), 0, s, a);
 }
 
 // Grouped (expert) GEMMs on the large-row kernel: MF row fragments per tile,
@@ -333,7 +332,8 @@ template <int MODE, bool PK, int MF>
 void launch_grouped_mf(int wt, const GemmArgs& a, dim3 grid, hipStream_t s)
 {
     if (wt == SV_BF16) launch(gemm_bigm_kernel<SV_BF16, MF, GROUPED_NF, MODE, PK>, grid, dim3(256), 0, s, a);
-    else launch(gemm_bigm_kernel<SV_FP8, MF, GROUPED_NF, MODE, PK>, grid, dim3(256), 0, s, a);
+    else if (wt == SV_FP8) launch(gemm_bigm_kernel<SV_FP8, MF, GROUPED_NF, MODE, PK>, grid, dim3(256), 0, s, a);
+    else if constexpr (PK) launch(gemm_bigm_kernel<SV_MXFP4, MF, GROUPED_NF, MODE, PK>, grid, dim3(256), 0, s, a);
 }
 
 template <int MODE, bool PK>
@@ -932,10 +932,12 @@ static int step_impl(spec_verify_ctx* c, const spec_verify_weights* w, void* k_c
         a.dbg = lm_logits;
         a.dbg_ld = k.vocab;
         if (mode == GM_SWIGLU) a.dual_off = N;
-        const int chunk = BIG_CHUNK_STEPS * step;
+        // MXFP4 (LM head): one 128-long step per chunk, and the 128-row tiles
+        const int chunk = wtd == SV_MXFP4 ? wsteps(wtd) : BIG_CHUNK_STEPS * step;
         // bf16 at up to 128 rows: one 128-row tile reads each weight once, which
         // the HBM-bound shapes prefer (LM head at 128 rows: 6% faster)
-        const bool wide = big && packed && Kd % chunk == 0 && (wt == SV_FP8 || T > 128);
+        const bool wide = big && packed && Kd % chunk == 0 && wtd != SV_MXFP4 &&
+                          (wt == SV_FP8 || T > 128);
         if (big && Kd % chunk == 0) {
             a.MT = wide ? cdiv(T, 32 * WIDE_MW) : MTb;
             a.NT = wide ? cdiv(N, wide_col_tile(mode)) : cdiv(N, 16 * 4 * BIG_NF);
@@ -950,7 +952,7 @@ static int step_impl(spec_verify_ctx* c, const spec_verify_weights* w, void* k_c
                 }
             }
             if (wide) launch_gemm_wide(wt, mode, a, s);
-            else launch_gemm_big(wt, mode, packed, a, s);
+            else launch_gemm_big(wtd, mode, packed, a, s);
             last_nt = a.NT;
             return a.ksplit;
         }
@@ -1146,7 +1148,7 @@ static int step_impl(spec_verify_ctx* c, const spec_verify_weights* w, void* k_c
             g.ldo = I;
             {
                 ProfScope ps(c, SV_KC_EXPERT_GATE_UP, s);
-                if (big_e) launch_grouped_big(wt, GM_SWIGLU, MFe, packed, g, s);
+                if (big_e) launch_grouped_big(wt_mx, GM_SWIGLU, MFe, packed, g, s);
                 else launch_gemm(wt_mx, GM_SWIGLU, MFe, packed, g, s);
             }
             GemmArgs d = g;
@@ -1170,7 +1172,7 @@ static int step_impl(spec_verify_ctx* c, const spec_verify_weights* w, void* k_c
             d.split_stride = 0;
             {
                 ProfScope ps(c, SV_KC_EXPERT_DOWN, s);
-                if (big_e) launch_grouped_big(wt, GM_STORE, MFe, packed, d, s);
+                if (big_e) launch_grouped_big(wt_mx, GM_STORE, MFe, packed, d, s);
                 else launch_gemm(wt_mx, GM_STORE, MFe, packed, d, s);
             }
             ra.y = c->y;

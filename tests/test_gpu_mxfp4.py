@@ -38,11 +38,14 @@ def test_mxfp4_batched_scaled(H, batch, n_experts, top_k, n_shared):
     assert stats["argmax_agree"] >= 0.9 * stats["positions"]
 
 
-def test_mxfp4_rejects_large_batches(H):
-    import speculative_decoding_verify_step_amd as sv
-    cfg = workloads.scaled(workloads.get_config("moe_b1_mxfp4"), batch=16)
-    with pytest.raises(sv.SpecVerifyError):
-        sv.spec_verify_init(sv.make_config(cfg, 16, 1408))
+@pytest.mark.parametrize("batch", [16, 40])
+def test_mxfp4_many_rows(H, batch):
+    """64 and 160 verified rows: the large-row kernel (activation chunks in
+    LDS) for the grouped experts and the LM head, with MXFP4 weights."""
+    cfg = workloads.scaled(workloads.get_config("moe_b1_mxfp4"), n_layers=2, batch=batch,
+                           vocab=4112, ctx=("uniform", 5, 300), norm_gain_std=0.2)
+    stats, _ = _run(H, cfg, f"mxfp4_many_rows_b{batch}")
+    assert stats["argmax_agree"] >= 0.9 * stats["positions"]
 
 
 @pytest.mark.parametrize("rows,cols", [(40, 1280), (16, 896), (3, 128)])

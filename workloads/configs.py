@@ -101,6 +101,12 @@ CONFIGS = {
         wdtype="bf16", kvdtype="bf16", embdtype="bf16", ctx=("fixed", 1341),
         draft_p=("const", 0.576), mx="mxfp4",
         description="moe_b1 with MXFP4 experts and LM head (bf16 attention, router, embedding)"),
+    "moe_b32_mxfp4": VerifyConfig(
+        name="moe_b32_mxfp4", n_layers=12, hidden=1280, n_q=10, n_kv=10, head_dim=128, ffn="moe",
+        n_experts=64, expert_inter=896, top_k=6, n_shared=2, vocab=129280, batch=32, k_draft=3,
+        wdtype="bf16", kvdtype="bf16", embdtype="bf16", ctx=("uniform", 300, 2500),
+        draft_p=("per_seq_uniform", 0.4, 0.8), mx="mxfp4",
+        description="moe_b32 with MXFP4 experts and LM head"),
 }
 
 # index of each workload in the order the workload list gives them
