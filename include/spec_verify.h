@@ -58,9 +58,9 @@
  * Supported combinations: weights, embedding, activations and KV cache all
  * SV_F32; or weights SV_BF16 or SV_FP8 with embedding and KV cache SV_BF16
  * (activations bf16, accumulation fp32).  With mx_dtype = SV_MXFP4 (bf16
- * MoE models, hidden and expert_inter multiples of 128 and at most 2048,
- * tiled16 layout) the weight-streaming matrices --
- * w_gate_up, w_down, w_sh_gate_up, w_sh_down and lm_head -- are MXFP4: each
+ * models, hidden and expert_inter multiples of 128 and at most 2048, tiled16
+ * layout) the weight-streaming matrices -- MoE: w_gate_up, w_down,
+ * w_sh_gate_up, w_sh_down; every model: lm_head -- are MXFP4: each
  * is the byte matrix [rows][cols/2] of codes, packed with
  * spec_verify_pack_tiled16 as an SV_FP8 matrix of cols/2 columns, and its s_x
  * pointer (lm_scale for the LM head) points to its E8M0 bytes
@@ -331,7 +331,8 @@ int spec_verify_sample_from_logits(spec_verify_ctx* ctx, const float* logits,
  * ctx+a+k-1 on the previous depth's u and draft.
  *   draft_ctx     a context made for the draft block: n_layers = 1,
  *                 SV_FFN_DENSE (dense_inter = the block's FFN width), the
- *                 target's hidden, heads, vocab, K, dtypes; kv_capacity >=
+ *                 target's hidden, heads, vocab, K, dtypes and mx_dtype (the
+ *                 tied LM head keeps its storage); kv_capacity >=
  *                 the largest ctx + 3 (K+1) (deeper depths also fill K
  *                 slots past their position, which the next depth-1 pass
  *                 rewrites)

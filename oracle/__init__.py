@@ -26,7 +26,7 @@ _LIB = os.path.join(_HERE, "liboracle.so")
 F32, BF16, FP8, MXFP4 = 0, 1, 2, 3
 _DT = {"f32": F32, "bf16": BF16, "fp8": FP8, "mxfp4": MXFP4}
 # matrices stored in the workload's `mx` format when it names one (the
-# weight-streaming ones: experts and the LM head)
+# weight-streaming ones: the LM head, and a MoE model's experts)
 MX_MATRICES = ("w_gate_up", "w_down", "w_sh_gate_up", "w_sh_down", "lm_head")
 BAD_TOKEN, CAPACITY, NAN_LOGIT = 1, 2, 4
 
@@ -204,7 +204,8 @@ class Oracle:
         m = _Mat()
         m.data = self._p(d[wkey])
         s = d.get(skey)
-        mx = getattr(self.cfg, "mx", "") == "mxfp4" and wkey in MX_MATRICES
+        mx = getattr(self.cfg, "mx", "") == "mxfp4" and (
+            wkey == "lm_head" or (self.cfg.ffn == "moe" and wkey in MX_MATRICES))
         m.dtype = MXFP4 if mx else -1
         if s is None:
             m.scale = None

@@ -197,9 +197,10 @@ int validate_config(const spec_verify_config& c)
     }
     if (c.mx_dtype != 0) {
         if (c.mx_dtype != SV_MXFP4) return bad("mx_dtype must be 0 or SV_MXFP4");
-        if (c.weight_dtype != SV_BF16 || c.ffn_kind != SV_FFN_MOE)
-            return bad("MXFP4 expert and LM-head weights need a bf16 MoE model");
-        if (c.hidden % 128 || c.expert_inter % 128 || c.hidden > 2048 || c.expert_inter > 2048)
+        if (c.weight_dtype != SV_BF16)
+            return bad("MXFP4 expert and LM-head weights need a bf16 model");
+        const bool moe = c.ffn_kind == SV_FFN_MOE;
+        if (c.hidden % 128 || c.hidden > 2048 || (moe && (c.expert_inter % 128 || c.expert_inter > 2048)))
             return bad("MXFP4 weights need hidden and expert_inter multiples of 128, at most 2048");
     }
     return SV_OK;
@@ -839,7 +840,7 @@ static int step_impl(spec_verify_ctx* c, const spec_verify_weights* w, void* k_c
     if (mx) {
         if (!packed) return fail(SV_ERR_UNSUPPORTED, "MXFP4 weights need the tiled16 layout");
         if (!w->lm_scale) return fail(SV_ERR_INVALID_ARG, "MXFP4 LM head needs lm_scale");
-        for (int l = 0; l < k.n_layers; l++) {
+        for (int l = 0; l < k.n_layers && k.ffn_kind == SV_FFN_MOE; l++) {
             const spec_verify_layer& L = w->layers[l];
             if (!L.s_gate_up || !L.s_down || (k.n_shared > 0 && (!L.s_sh_gate_up || !L.s_sh_down)))
                 return fail(SV_ERR_INVALID_ARG, "MXFP4 expert matrices need their block scales");
@@ -1271,8 +1272,9 @@ int spec_draft_step(spec_verify_ctx* c, const spec_verify_weights* w, const spec
 {
     if (!c || !w || !m || !vc) return fail(SV_ERR_INVALID_ARG, "null context or weights");
     const spec_verify_config& k = c->c;
-    if (k.n_layers != 1 || k.ffn_kind != SV_FFN_DENSE || k.mx_dtype != 0)
-        return fail(SV_ERR_UNSUPPORTED, "the draft context must be a one-layer dense model");
+    if (k.n_layers != 1 || k.ffn_kind != SV_FFN_DENSE || k.mx_dtype != vc->c.mx_dtype)
+        return fail(SV_ERR_UNSUPPORTED, "the draft context must be a one-layer dense model "
+                                         "with the target's LM-head storage");
     if (vc->c.hidden != k.hidden || vc->c.k_draft != k.k_draft || vc->c.vocab != k.vocab ||
         vc->bf != c->bf || B > vc->c.max_batch)
         return fail(SV_ERR_INVALID_ARG, "draft and verify contexts differ in hidden, K, vocab, "

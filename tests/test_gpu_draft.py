@@ -121,6 +121,11 @@ def test_draft_dense_fp8_scaled(H):
     _draft_case(H, cfg, "draft fp8 scaled", min_checked=0.0)
 
 
+def test_draft_mxfp4_target(H):
+    """The tied LM head in MXFP4 (a target with MXFP4 experts and LM head)."""
+    _draft_case(H, workloads.get_config("moe_b1_mxfp4"), "draft moe_b1_mxfp4", min_checked=0.0)
+
+
 def test_draft_failed_sequences_get_no_drafts(H):
     """A sequence whose verify step failed (accepted -1) or whose positions
     exceed the block cache gets drafts -1 and raises the error bits; the

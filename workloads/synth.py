@@ -277,11 +277,12 @@ def mtp_weights(cfg: VerifyConfig, device="cpu") -> dict:
 
 def mtp_config(cfg: VerifyConfig) -> VerifyConfig:
     """Shape of the FastMTP draft block as a one-layer dense model sharing the
-    target's attention shape, vocabulary, K and storage types."""
+    target's attention shape, vocabulary, K and storage types (an MXFP4 LM
+    head stays MXFP4: it is the target's)."""
     import dataclasses
     I = cfg.dense_inter if cfg.ffn == "dense" and cfg.dense_inter else 4 * cfg.hidden
     return dataclasses.replace(cfg, name=cfg.name + "_mtp", n_layers=1, ffn="dense", dense_inter=I,
-                               n_experts=0, expert_inter=0, top_k=0, n_shared=0, mx="")
+                               n_experts=0, expert_inter=0, top_k=0, n_shared=0)
 
 
 def mtp_model_weights(target: dict, mtp: dict) -> dict:
