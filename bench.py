@@ -119,22 +119,36 @@ def step_bytes(cfg, ctx, distinct_experts):
 
 
 # ------------------------------------------------------------- workload
-def setup(cfg, steps):
+def setup(cfg, steps, kv_page=0):
+    """Weights, caches and a context.  kv_page > 0: the caches live in page
+    pools of that many positions, in a seeded random physical order (every
+    sequence's pages scattered over the pool)."""
+    import numpy as np
     import torch
 
     import speculative_decoding_verify_step_amd as sv
     import workloads
 
     cap = workloads.capacity_for(workloads.scaled(cfg, steps=max(cfg.steps, steps)))
+    if kv_page:
+        cap = (cap + kv_page - 1) // kv_page * kv_page
     w = workloads.make_weights(cfg, "cuda")
     k, v = workloads.kv_cache(cfg, "cuda", capacity=cap)
     k, v = sv.kv_to_library(k, v)
+    table = None
+    if kv_page:
+        n_pages = cfg.batch * cap // kv_page
+        order = np.random.default_rng(cfg.seed).permutation(n_pages)
+        k, v, table = sv.kv_paged_from_library(k, v, kv_page, order)
     torch.cuda.synchronize()
     ctx = workloads.context_lengths(cfg)
     com = workloads.committed_tokens(cfg)
     n_rec = steps if cfg.steps > 1 else 1
     coins, rtok = workloads.draft_randomness(cfg, steps=n_rec)
-    vc = sv.VerifyContext(cfg, cfg.batch, cap, w)
+    vc = sv.VerifyContext(cfg, cfg.batch, cap, w, kv_page_size=kv_page,
+                          kv_pool_pages=k.shape[0] if kv_page else 0)
+    if kv_page:
+        vc.set_kv_pages(table)
     return dict(sv=sv, w=w, k=k, v=v, cap=cap, ctx=ctx, com=com, coins=coins, rtok=rtok, vc=vc,
                 n_rec=n_rec)
 
@@ -174,12 +188,14 @@ def record_drafts(cfg, S):
     return drafts, first_routing
 
 
-def run_bench(cfg, steps, warmup, sampled=False):
+def run_bench(cfg, steps, warmup, sampled=False, kv_page=0, graph=False):
+    """graph: the K timed steps are captured once into one HIP graph and the
+    timed region is a single replay of it (no host work between steps)."""
     import torch
 
     import workloads
 
-    S = setup(cfg, steps)
+    S = setup(cfg, steps, kv_page)
     sv, vc = S["sv"], S["vc"]
     B, K1 = cfg.batch, cfg.k_draft + 1
     log(f"[bench] {cfg.name}: B={B} L={cfg.n_layers} cap={S['cap']} recording drafts")
@@ -219,20 +235,45 @@ def run_bench(cfg, steps, warmup, sampled=False):
     for i in range(warmup):
         one(i, ctx)
     torch.cuda.synchronize()
-    ctx = ctx0.clone()
+    ctx.copy_(ctx0)
     com_bufs[0].copy_(com0)
     ctx_start = ctx.clone()
-    # timed region
     kc = sv.SV_KC_LM_HEAD
-    vc.kernel_time(kc, enable=1, query=False)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(steps):
-        one(i, ctx)
-    torch.cuda.synchronize()
-    t1 = time.perf_counter()
-    acc_sum = acc_all[:steps].to(torch.int64).sum(0)
-    lm_ms, lm_n = vc.kernel_time(kc, enable=0)
+    if graph:
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for i in range(steps):
+                one(i, ctx)
+        ctx.copy_(ctx0)
+        com_bufs[0].copy_(com0)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        g.replay()
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
+        acc_sum = acc_all[:steps].to(torch.int64).sum(0)
+        ctx_graph = ctx.clone()
+        # the LM-head kernel's time from an eager pass of the same steps
+        ctx.copy_(ctx0)
+        com_bufs[0].copy_(com0)
+        vc.kernel_time(kc, enable=1, query=False)
+        for i in range(steps):
+            one(i, ctx)
+        torch.cuda.synchronize()
+        lm_ms, lm_n = vc.kernel_time(kc, enable=0)
+        assert torch.equal(ctx, ctx_graph), "graph replay and eager steps disagree"
+        del g
+    else:
+        # timed region
+        vc.kernel_time(kc, enable=1, query=False)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(steps):
+            one(i, ctx)
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
+        acc_sum = acc_all[:steps].to(torch.int64).sum(0)
+        lm_ms, lm_n = vc.kernel_time(kc, enable=0)
     assert vc.error_word() == 0, "device error during the benchmark"
     samp_us = None
     if sampled:   # the sampling kernels, timed in a second pass of the same steps
@@ -394,6 +435,10 @@ def main():
                     help="time the sampled (rejection-sampling) verify step instead of the greedy one")
     ap.add_argument("--draft-loop", action="store_true",
                     help="time the device-resident FastMTP draft -> verify loop")
+    ap.add_argument("--kv-page", type=int, default=0, metavar="P",
+                    help="paged KV caches: pages of P positions in a shuffled pool")
+    ap.add_argument("--graph", action="store_true",
+                    help="capture the timed steps into one HIP graph and time its replay")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                     help="only run a plain device copy of BYTES (counter calibration)")
     args = ap.parse_args()
@@ -420,7 +465,7 @@ def main():
                        "mode": "FastMTP draft -> verify loop", "tokens_per_verify": r["tau"]},
             "draft_us_per_step": r["draft_ms"] * 1e3}), flush=True)
         return
-    r = run_bench(cfg, steps, warmup, sampled=args.sampled)
+    r = run_bench(cfg, steps, warmup, sampled=args.sampled, kv_page=args.kv_page, graph=args.graph)
     lm_gbs = r["lm_bytes"] / (r["lm_ms"] * 1e-3) / 1e9 if r["lm_ms"] > 0 else None
     out = {
         "metric": METRIC,
@@ -441,6 +486,8 @@ def main():
                    "layers": cfg.n_layers, "hidden": cfg.hidden, "vocab": cfg.vocab,
                    "ctx": list(cfg.ctx), "chained_steps": cfg.steps > 1,
                    "weight_layout": "tiled16",
+                   "kv": f"paged ({args.kv_page} positions per page)" if args.kv_page else "contiguous",
+                   "launch": "one HIP graph of all timed steps" if args.graph else "eager",
                    "verification": "sampled (temperature 1)" if args.sampled else "greedy",
                    "tokens_per_verify": r["tau"]},
         "roofline": {"bound": "hbm", "kernel": "lm_head_argmax",

@@ -122,7 +122,7 @@
 extern "C" {
 #endif
 
-#define SPEC_VERIFY_ABI_VERSION 4
+#define SPEC_VERIFY_ABI_VERSION 5
 
 /* status codes */
 #define SV_OK 0
@@ -186,6 +186,9 @@ typedef struct {
     int embed_dtype;    /* SV_F32 / SV_BF16 */
     int kv_dtype;       /* SV_F32 / SV_BF16 */
     int mx_dtype;       /* 0, or SV_MXFP4: expert matrices and LM head in OCP MXFP4 (below) */
+    int kv_page_size;   /* 0: contiguous KV regions; else positions per page (multiple of 64,
+                           dividing kv_capacity): paged caches, see spec_verify_set_kv_pages */
+    int kv_pool_pages;  /* paged caches: physical pages in the K (and the V) pool */
 } spec_verify_config;
 
 typedef struct {
@@ -239,6 +242,24 @@ int spec_verify_step(spec_verify_ctx* ctx, const spec_verify_weights* w, void* k
                      void* v_cache, const int32_t* committed_tok, const int32_t* draft_toks,
                      const int32_t* ctx_lens_in, int32_t* ctx_lens_out, int batch,
                      int32_t* accepted_len, int32_t* next_tok, void* stream);
+
+/*
+ * Paged KV caches (kv_page_size = P > 0).  The k_cache / v_cache arguments of
+ * the steps are then pools of kv_pool_pages physical pages: page g holds, for
+ * every layer l and KV head h, P positions at element offset
+ * ((g * L + l) * n_kv + h) * P * D, tiled exactly like a contiguous region of
+ * P positions (the KV-cache layout above with capacity P).  `table`
+ * [max_batch][kv_capacity / P] int32 (device, caller-owned, read by every
+ * following step until replaced) maps logical page i of sequence b -- its
+ * positions i P .. i P + P - 1 -- to a physical page.  Sequences may share
+ * physical pages for a common prefix (the pages are only read); the pages
+ * that receive a step's new positions ctx .. ctx+K must be the sequence's
+ * own.  An entry outside [0, kv_pool_pages) that a step touches is clamped
+ * into the pool and raises SV_DEV_CAPACITY in the error word (that
+ * sequence's results are then meaningless).  SV_ERR_UNSUPPORTED for a
+ * context without paged caches.
+ */
+int spec_verify_set_kv_pages(spec_verify_ctx* ctx, const int32_t* table);
 
 /*
  * Debug outputs for the following steps (any pointer may be NULL; all NULL

@@ -36,7 +36,7 @@ EXPORTS = ("spec_verify_init", "spec_verify_destroy", "spec_verify_step", "spec_
            "spec_verify_last_error", "spec_verify_status_string", "spec_verify_abi_version",
            "spec_verify_pack_tiled16", "spec_verify_tiled16_bytes", "spec_verify_step_sampled",
            "spec_verify_sample_from_logits", "spec_verify_pack_mx_scales",
-           "spec_verify_mx_scales_bytes", "spec_draft_step")
+           "spec_verify_mx_scales_bytes", "spec_draft_step", "spec_verify_set_kv_pages")
 
 
 class SpecVerifyConfig(ctypes.Structure):
@@ -47,7 +47,7 @@ class SpecVerifyConfig(ctypes.Structure):
                 ("vocab", c_int), ("max_batch", c_int), ("k_draft", c_int),
                 ("kv_capacity", c_int), ("rope_theta", c_float), ("rms_eps", c_float),
                 ("weight_dtype", c_int), ("embed_dtype", c_int), ("kv_dtype", c_int),
-                ("mx_dtype", c_int)]
+                ("mx_dtype", c_int), ("kv_page_size", c_int), ("kv_pool_pages", c_int)]
 
 
 class SpecVerifyLayer(ctypes.Structure):
@@ -107,6 +107,7 @@ def load_library() -> ctypes.CDLL:
         lib.spec_verify_tiled16_bytes.argtypes = [ctypes.c_long, c_int, c_int]
         lib.spec_verify_pack_mx_scales.argtypes = [P, P, ctypes.c_long, c_int, P]
         lib.spec_draft_step.argtypes = [P, P, P, P, P, P, P, P, P, P, c_int, P, P]
+        lib.spec_verify_set_kv_pages.argtypes = [P, P]
         lib.spec_verify_mx_scales_bytes.argtypes = [ctypes.c_long, c_int]
         for f in EXPORTS:
             if f not in ("spec_verify_destroy", "spec_verify_status_string"):
@@ -153,8 +154,10 @@ def spec_verify_last_error() -> str:
     return buf.value.decode(errors="replace")
 
 
-def make_config(cfg, max_batch: int, kv_capacity: int) -> SpecVerifyConfig:
-    """Config struct from any object with the workload fields."""
+def make_config(cfg, max_batch: int, kv_capacity: int, kv_page_size: int = 0,
+                kv_pool_pages: int = 0) -> SpecVerifyConfig:
+    """Config struct from any object with the workload fields (paged KV caches
+    when kv_page_size > 0)."""
     c = SpecVerifyConfig()
     c.n_layers, c.hidden, c.n_q_heads, c.n_kv_heads = cfg.n_layers, cfg.hidden, cfg.n_q, cfg.n_kv
     c.head_dim = cfg.head_dim
@@ -165,6 +168,7 @@ def make_config(cfg, max_batch: int, kv_capacity: int) -> SpecVerifyConfig:
     c.rope_theta, c.rms_eps = cfg.rope_theta, cfg.rms_eps
     c.weight_dtype, c.embed_dtype, c.kv_dtype = _DT[cfg.wdtype], _DT[cfg.embdtype], _DT[cfg.kvdtype]
     c.mx_dtype = SV_MXFP4 if getattr(cfg, "mx", "") == "mxfp4" else 0
+    c.kv_page_size, c.kv_pool_pages = kv_page_size, kv_pool_pages
     return c
 
 
@@ -298,6 +302,33 @@ def spec_verify_set_debug(ctx: int, logits=None, hidden=None, target_tok=None,
                                                 _p(routing)), "spec_verify_set_debug")
 
 
+def spec_verify_set_kv_pages(ctx: int, table) -> None:
+    _check(load_library().spec_verify_set_kv_pages(ctx, _p(table)), "spec_verify_set_kv_pages")
+
+
+def kv_paged_from_library(k_cache, v_cache, page: int, order=None):
+    """Contiguous tiled caches [B][L][n_kv][cap][D] (the library layout) ->
+    page pools [B*cap/page][L][n_kv][page][D] and a page table [B][cap/page]
+    (int32): logical page i of sequence b is stored in physical page
+    order[b*cap/page + i] (default: the identity).  A pure data movement."""
+    import torch
+    B, L, H, cap, D = k_cache.shape
+    npg = cap // page
+
+    def pool(t):
+        p = t.reshape(B, L, H, npg, page, D).permute(0, 3, 1, 2, 4, 5).reshape(B * npg, L, H, page, D)
+        if order is None:
+            return p.contiguous()
+        # a fresh contiguous pool (empty_like would keep a permuted view's strides)
+        out = torch.empty(p.shape, dtype=p.dtype, device=p.device)
+        out[torch.as_tensor(order, device=t.device)] = p
+        return out
+
+    ident = torch.arange(B * npg, dtype=torch.int32, device=k_cache.device)
+    table = ident if order is None else torch.as_tensor(order, dtype=torch.int32, device=k_cache.device)
+    return pool(k_cache), pool(v_cache), table.reshape(B, npg).contiguous()
+
+
 def spec_verify_accept_from_logits(ctx: int, logits, draft_toks, ctx_lens_in, ctx_lens_out,
                                    batch: int, accepted_len, next_tok, target_tok=None,
                                    stream=None) -> None:
@@ -388,14 +419,14 @@ class VerifyContext:
     """Owns one library context; wraps spec_verify_step for torch tensors."""
 
     def __init__(self, cfg, max_batch: int, kv_capacity: int, weights: dict,
-                 layout: str = "tiled16"):
+                 layout: str = "tiled16", kv_page_size: int = 0, kv_pool_pages: int = 0):
         """`weights`: row-major device tensors (the workload dict).  With
         layout "tiled16" the matrix-product weights are repacked once by the
         library into a copy owned by this object."""
         self.cfg = cfg
         self.max_batch = max_batch
         self.kv_capacity = kv_capacity
-        self._config = make_config(cfg, max_batch, kv_capacity)
+        self._config = make_config(cfg, max_batch, kv_capacity, kv_page_size, kv_pool_pages)
         self.handle = spec_verify_init(self._config)
         if layout == "tiled16" and weights.get("layout", "row_major") == "row_major":
             weights = pack_weights(weights, mx=getattr(cfg, "mx", ""))
@@ -407,6 +438,10 @@ class VerifyContext:
         B = committed.shape[0] if batch is None else batch
         spec_verify_step(self.handle, self._w, k_cache, v_cache, committed, drafts, ctx_in,
                          ctx_out, B, accepted, next_tok, stream)
+
+    def set_kv_pages(self, table):
+        self._kv_table = table
+        spec_verify_set_kv_pages(self.handle, table)
 
     def set_debug(self, logits=None, hidden=None, target_tok=None, routing=None):
         self._dbg = (logits, hidden, target_tok, routing)

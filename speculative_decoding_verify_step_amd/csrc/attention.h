@@ -26,8 +26,10 @@
 
 struct AttnArgs {
     const void* q;            // [T][n_q][D] activations (rotary applied)
-    const void* kc;           // K cache, tiled (see the C ABI)
+    const void* kc;           // K cache, tiled (see the C ABI; a page pool when kvp.table is set)
     const void* vc;           // V cache, tiled
+    KvPages kvp;
+    unsigned* err_word;
     const int* ctx_in;        // [B]
     const int* seq_err;       // [B]
     int layer, L, n_q, n_kv, D, K1, cap, CH, maxch, QG;
@@ -72,6 +74,19 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(1, STREAM ? 
     const char* kbase = (const char*)a.kc + head * (size_t)a.cap * DH * ESZ + lane * 16;
     const char* vbase = (const char*)a.vc + head * (size_t)a.cap * DH * ESZ + lane * 16;
     constexpr size_t TILE = (size_t)KT * DH * ESZ;     // bytes per key tile
+    // paged caches: lane i holds the physical page of this chunk's i-th page
+    // (loaded once; each tile takes its page with a cross-lane read)
+    const bool paged = a.kvp.table != nullptr;
+    const int pg0 = paged ? c0 / a.kvp.page : 0;
+    int my_page = 0;
+    if (paged) {
+        const int pi = min(pg0 + lane, a.kvp.max_pages - 1);
+        my_page = a.kvp.table[(size_t)b * a.kvp.max_pages + pi];
+        const bool bad = pg0 + lane <= (c1 - 1) / a.kvp.page && (my_page < 0 || my_page >= a.kvp.n_pages);
+        if (__any(bad) && lane == 0) atomicOr(a.err_word, SV_DEV_CAPACITY);
+        my_page = min(max(my_page, 0), a.kvp.n_pages - 1);
+    }
+    const size_t page_bytes = paged ? (size_t)a.kvp.page * DH * ESZ : 0;
 
     // query fragments (B operand): lane supplies row l16, slice lg of each step
     uint4 qf[QPW][DS];
@@ -105,17 +120,29 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(1, STREAM ? 
         else return ldg16(p);
     };
     for (int kt = c0; kt < c1; kt += KT) {
-        const size_t toff = (size_t)(kt / KT) * TILE;
+        const char* kt_k;
+        const char* kt_v;
+        if (paged) {
+            const int pg = __shfl(my_page, kt / a.kvp.page - pg0, 64);
+            const size_t off = (((size_t)pg * a.L + a.layer) * a.n_kv + hkv) * page_bytes +
+                               (size_t)((kt % a.kvp.page) / KT) * TILE + lane * 16;
+            kt_k = (const char*)a.kc + off;
+            kt_v = (const char*)a.vc + off;
+        } else {
+            const size_t toff = (size_t)(kt / KT) * TILE;
+            kt_k = kbase + toff;
+            kt_v = vbase + toff;
+        }
         // key tile (A operand of the score product): lane (slot l16, slice lg)
         uint4 kf[NB][DS];
 #pragma unroll
         for (int blk = 0; blk < NB; blk++)
 #pragma unroll
-            for (int s = 0; s < DS; s++) kf[blk][s] = kvload(kbase + toff + (size_t)(blk * DS + s) * 1024);
+            for (int s = 0; s < DS; s++) kf[blk][s] = kvload(kt_k + (size_t)(blk * DS + s) * 1024);
         // value tile (A operand of the output product): lane (channel 16 df + l16, keys KL lg ..)
         uint4 vf[DF];
 #pragma unroll
-        for (int d = 0; d < DF; d++) vf[d] = kvload(vbase + toff + (size_t)d * 1024);
+        for (int d = 0; d < DF; d++) vf[d] = kvload(kt_v + (size_t)d * 1024);
 #pragma unroll
         for (int f = 0; f < QPW; f++) {
             float s[KL];

@@ -252,3 +252,35 @@ SV_DEV int implied_slot(int sv, int A, int j)
 }
 
 SV_DEV float silu_f32(float z) { return z / (1.0f + __expf(-z)); }
+
+// ---------------------------------------------------------------- paged KV
+// With a page table the cache of (sequence b, layer l, KV head h) is split in
+// pages of `page` positions: table [B][max_pages] holds physical page indices
+// into a pool [n_pages][L][n_kv][page][D], every (page, layer, head) block
+// tiled like a contiguous region of `page` positions.  Without a table the
+// region of (b, l, h) holds `cap` positions.  An index outside the pool is
+// clamped (no access leaves the pool) and reported through `bad`.
+struct KvPages {
+    const int* table;     // [B][max_pages], or nullptr: contiguous regions
+    int page, max_pages, n_pages;
+};
+
+// Element offset of the (page or region, layer l, head 0) block that holds
+// position pos of sequence b, and the position inside it (`pin`); the head's
+// block is at + h * span * D with span = page (paged) or cap.
+SV_DEV size_t kv_block(const KvPages& p, int b, int L, int l, int n_kv, int cap, int D, int pos,
+                       int& pin, int& span, bool& bad)
+{
+    if (!p.table) {
+        pin = pos;
+        span = cap;
+        return ((size_t)b * L + l) * n_kv * (size_t)cap * D;
+    }
+    const int pi = min(max(pos / p.page, 0), p.max_pages - 1);
+    int pg = p.table[(size_t)b * p.max_pages + pi];
+    bad = bad || pg < 0 || pg >= p.n_pages;
+    pg = min(max(pg, 0), p.n_pages - 1);
+    pin = pos - pi * p.page;
+    span = p.page;
+    return ((size_t)pg * L + l) * n_kv * (size_t)p.page * D;
+}

@@ -30,8 +30,9 @@ struct QkvArgs {
     const float* ws;            // fp8 per-row scales
     const float2* rope;         // [cap][D/2] (cos, sin)
     void* q;                    // [T][n_q][D]
-    void* kc;                   // K cache (tiled)
+    void* kc;                   // K cache (tiled; a page pool when kvp.table is set)
     void* vc;                   // V cache (tiled)
+    KvPages kvp;
     int V, cap, K1, T, H, n_q, n_kv, D, L, layer, MT, NT;
     float eps;
 };
@@ -109,7 +110,9 @@ __global__ __launch_bounds__(64 * W) void qkv_rope_kernel(QkvArgs a)
     const char* xrow[MF];
     const int i0 = 16 * a16 + 4 * lg;
     const bool rot = hh < a.n_q + a.n_kv;
-    int pos[MF];
+    int pos[MF], pin[MF], span[MF];
+    size_t kvb[MF];             // cache block of the row's position (paged or contiguous)
+    bool kv_bad = false;
     float4 csa[MF], csb[MF];
 #pragma unroll
     for (int m = 0; m < MF; m++) {
@@ -117,10 +120,12 @@ __global__ __launch_bounds__(64 * W) void qkv_rope_kernel(QkvArgs a)
         if constexpr (EMBED) xrow[m] = (const char*)a.embed + ((size_t)row_token(t) * H + (size_t)lg * KL) * AESZ;
         else xrow[m] = (const char*)a.X + ((size_t)t * H + (size_t)lg * KL) * AESZ;
         pos[m] = min(max(a.ctx_in[b], 0), a.cap - K1) + j;
+        kvb[m] = kv_block(a.kvp, b, a.L, a.layer, a.n_kv, a.cap, a.D, pos[m], pin[m], span[m], kv_bad);
         const float4* cp = reinterpret_cast<const float4*>(a.rope + (size_t)pos[m] * half + (rot ? i0 : 0));
         csa[m] = cp[0];
         csb[m] = cp[1];
     }
+    if (kv_bad) atomicOr(a.err_word, SV_DEV_CAPACITY);   // a page index outside the pool
     float rsd[MF];   // 1 / rms of the lane's rows (first layer; set after the prologue)
 #pragma unroll
     for (int m = 0; m < MF; m++) rsd[m] = 1.f;
@@ -314,20 +319,20 @@ __global__ __launch_bounds__(64 * W) void qkv_rope_kernel(QkvArgs a)
                 }
             } else if (write_cache) {
                 const int kh = hh - a.n_q;
-                AT* kp = (AT*)a.kc + (((size_t)b * a.L + a.layer) * a.n_kv + kh) * (size_t)a.cap * D;
+                AT* kp = (AT*)a.kc + kvb[m] + (size_t)kh * span[m] * D;
 #pragma unroll
                 for (int e = 0; e < 4; e++) {
-                    Act<BF>::st(kp, k_cache_index<BF>(pos[m], i0 + e, D), r0[e]);
-                    Act<BF>::st(kp, k_cache_index<BF>(pos[m], i0 + half + e, D), r1[e]);
+                    Act<BF>::st(kp, k_cache_index<BF>(pin[m], i0 + e, D), r0[e]);
+                    Act<BF>::st(kp, k_cache_index<BF>(pin[m], i0 + half + e, D), r1[e]);
                 }
             }
         } else if (write_cache) {
             const int vh = hh - a.n_q - a.n_kv;
-            AT* vp = (AT*)a.vc + (((size_t)b * a.L + a.layer) * a.n_kv + vh) * (size_t)a.cap * D;
+            AT* vp = (AT*)a.vc + kvb[m] + (size_t)vh * span[m] * D;
 #pragma unroll
             for (int e = 0; e < 4; e++) {
-                Act<BF>::st(vp, v_cache_index<BF>(pos[m], i0 + e, D), x0[e]);
-                Act<BF>::st(vp, v_cache_index<BF>(pos[m], i0 + half + e, D), x1[e]);
+                Act<BF>::st(vp, v_cache_index<BF>(pin[m], i0 + e, D), x0[e]);
+                Act<BF>::st(vp, v_cache_index<BF>(pin[m], i0 + half + e, D), x1[e]);
             }
         }
     }

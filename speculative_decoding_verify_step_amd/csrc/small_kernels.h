@@ -640,8 +640,10 @@ struct RopeArgs {
     const int* seq_err;
     const float2* rope;         // [cap][D/2] (cos, sin)
     void* q;                    // [T][n_q][D] act
-    void* kc;                   // K cache
+    void* kc;                   // K cache (a page pool when kvp.table is set)
     void* vc;                   // V cache
+    KvPages kvp;
+    unsigned* err_word;
 };
 
 // Element offsets of (pos, d) inside one (sequence, layer, KV head) region of
@@ -692,6 +694,10 @@ __global__ __launch_bounds__(64) void rope_append_kernel(RopeArgs a)
     const int ctx = a.ctx_in[b];
     const bool write_cache = a.seq_err[b] == 0;
     const int pos = min(max(ctx, 0), a.cap - K1) + j;
+    int pin, span;
+    bool kv_bad = false;
+    const size_t kvb = kv_block(a.kvp, b, a.L, a.layer, a.n_kv, a.cap, D, pos, pin, span, kv_bad);
+    if (kv_bad && lane == 0 && write_cache) atomicOr(a.err_word, SV_DEV_CAPACITY);
     const float x0 = sum_in_order(p0), x1 = sum_in_order(p1);
     if (rot) {
         if (!ok0) return;
@@ -704,15 +710,15 @@ __global__ __launch_bounds__(64) void rope_append_kernel(RopeArgs a)
             Act<BF>::st(qo, lane + half, r1);
         } else if (write_cache) {
             const int kh = hh - a.n_q;
-            AT* kp = (AT*)a.kc + (((size_t)b * a.L + a.layer) * a.n_kv + kh) * (size_t)a.cap * D;
-            Act<BF>::st(kp, k_cache_index<BF>(pos, lane, D), r0);
-            Act<BF>::st(kp, k_cache_index<BF>(pos, lane + half, D), r1);
+            AT* kp = (AT*)a.kc + kvb + (size_t)kh * span * D;
+            Act<BF>::st(kp, k_cache_index<BF>(pin, lane, D), r0);
+            Act<BF>::st(kp, k_cache_index<BF>(pin, lane + half, D), r1);
         }
     } else if (write_cache) {
         const int vh = hh - a.n_q - a.n_kv;
-        AT* vp = (AT*)a.vc + (((size_t)b * a.L + a.layer) * a.n_kv + vh) * (size_t)a.cap * D;
-        if (ok0) Act<BF>::st(vp, v_cache_index<BF>(pos, i0, D), x0);
-        if (ok1) Act<BF>::st(vp, v_cache_index<BF>(pos, i1, D), x1);
+        AT* vp = (AT*)a.vc + kvb + (size_t)vh * span * D;
+        if (ok0) Act<BF>::st(vp, v_cache_index<BF>(pin, i0, D), x0);
+        if (ok1) Act<BF>::st(vp, v_cache_index<BF>(pin, i1, D), x1);
     }
 }
 

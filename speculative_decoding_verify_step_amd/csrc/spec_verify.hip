@@ -127,6 +127,8 @@ struct spec_verify_ctx {
     float* dzero = nullptr;
     int* dpos = nullptr;
     void* dstate = nullptr;
+    // paged KV caches: page table [max_batch][kv_capacity / kv_page_size] (device)
+    const int* kv_table = nullptr;
     // debug outputs
     float* dbg_logits = nullptr;
     float* dbg_hidden = nullptr;
@@ -194,6 +196,11 @@ int validate_config(const spec_verify_config& c)
             return bad("dense_inter must be a multiple of 64");
     } else {
         return bad("unknown ffn_kind");
+    }
+    if (c.kv_page_size != 0) {
+        if (c.kv_page_size < 64 || c.kv_page_size % 64 || c.kv_capacity % c.kv_page_size)
+            return bad("kv_page_size must be a multiple of 64 that divides kv_capacity");
+        if (c.kv_pool_pages < 1) return bad("kv_pool_pages must be >= 1");
     }
     if (c.mx_dtype != 0) {
         if (c.mx_dtype != SV_MXFP4) return bad("mx_dtype must be 0 or SV_MXFP4");
@@ -793,6 +800,15 @@ int spec_verify_init(const spec_verify_config* cfg, spec_verify_ctx** out)
     return SV_OK;
 }
 
+int spec_verify_set_kv_pages(spec_verify_ctx* c, const int32_t* table)
+{
+    if (!c) return fail(SV_ERR_INVALID_ARG, "null context");
+    if (!c->c.kv_page_size) return fail(SV_ERR_UNSUPPORTED, "the context's caches are not paged");
+    if (!table) return fail(SV_ERR_INVALID_ARG, "null page table");
+    c->kv_table = table;
+    return SV_OK;
+}
+
 int spec_verify_set_debug(spec_verify_ctx* c, float* logits, float* hidden, int32_t* target,
                           int32_t* routing)
 {
@@ -836,6 +852,8 @@ static int step_impl(spec_verify_ctx* c, const spec_verify_weights* w, void* k_c
     if (w->layout != SV_LAYOUT_ROW_MAJOR && w->layout != SV_LAYOUT_TILED16)
         return fail(SV_ERR_INVALID_ARG, "unknown weight layout");
     const bool packed = w->layout == SV_LAYOUT_TILED16;
+    if (k.kv_page_size && !c->kv_table)
+        return fail(SV_ERR_NOT_SET, "paged KV caches need a page table (spec_verify_set_kv_pages)");
     const bool mx = k.mx_dtype == SV_MXFP4;
     if (mx) {
         if (!packed) return fail(SV_ERR_UNSUPPORTED, "MXFP4 weights need the tiled16 layout");
@@ -899,8 +917,14 @@ static int step_impl(spec_verify_ctx* c, const spec_verify_weights* w, void* k_c
     qa.x_out = c->x;
     qa.rope = c->rope;
     qa.q = c->q;
+    KvPages kvp;
+    kvp.table = k.kv_page_size ? c->kv_table : nullptr;
+    kvp.page = k.kv_page_size;
+    kvp.max_pages = k.kv_page_size ? k.kv_capacity / k.kv_page_size : 0;
+    kvp.n_pages = k.kv_pool_pages;
     qa.kc = k_cache;
     qa.vc = v_cache;
+    qa.kvp = kvp;
     qa.V = k.vocab;
     qa.cap = k.kv_capacity;
     qa.K1 = K1;
@@ -971,6 +995,8 @@ static int step_impl(spec_verify_ctx* c, const spec_verify_weights* w, void* k_c
     at.q = c->q;
     at.kc = k_cache;
     at.vc = v_cache;
+    at.kvp = kvp;
+    at.err_word = c->err_word;
     at.ctx_in = ctx_in;
     at.seq_err = c->seq_err;
     at.L = L;
@@ -1040,6 +1066,8 @@ static int step_impl(spec_verify_ctx* c, const spec_verify_weights* w, void* k_c
             rp.q = c->q;
             rp.kc = k_cache;
             rp.vc = v_cache;
+            rp.kvp = kvp;
+            rp.err_word = c->err_word;
             dim3 grid(T, k.n_q_heads + 2 * k.n_kv_heads);
             if (bf) rope_append_kernel<true><<<grid, 64, 0, s>>>(rp);
             else rope_append_kernel<false><<<grid, 64, 0, s>>>(rp);

@@ -36,7 +36,7 @@ def test_every_declared_function_is_exported(sv):
 
 
 def test_status_strings_and_version(sv):
-    assert sv.spec_verify_abi_version() == 4
+    assert sv.spec_verify_abi_version() == 5
     assert sv.spec_verify_status_string(0) == "ok"
     assert "invalid" in sv.spec_verify_status_string(-1)
     assert sv.spec_verify_status_string(12345) == "unknown status"
@@ -44,7 +44,7 @@ def test_status_strings_and_version(sv):
 
 def test_struct_sizes_match_header(sv):
     # 21 four-byte fields; layer = 16 pointers; weights = 5 pointers + int (padded)
-    assert ctypes.sizeof(sv.SpecVerifyConfig) == 22 * 4
+    assert ctypes.sizeof(sv.SpecVerifyConfig) == 24 * 4
     assert ctypes.sizeof(sv.SpecVerifyLayer) == 16 * 8
     assert ctypes.sizeof(sv.SpecVerifyWeights) == 6 * 8
 
@@ -124,3 +124,30 @@ def test_kv_layout_permutation_matches_documented_formulas(sv, dtype, D):
     y = torch.randn(2, 3, 2, cap, D).to(tdt)
     k2, v2 = sv.kv_from_library(*sv.kv_to_library(x, y))
     assert torch.equal(k2, x) and torch.equal(v2, y)
+
+
+@pytest.mark.parametrize("B,L,H,order_seed", [(1, 3, 2, 0), (2, 1, 4, 1), (3, 2, 1, None)])
+def test_paged_pool_layout(sv, B, L, H, order_seed):
+    """kv_paged_from_library: the pool is contiguous and page-major; physical
+    page table[b][i] holds logical page i of sequence b, for every (layer,
+    head), element for element."""
+    import numpy as np
+    import torch
+    cap, D, page = 256, 64, 64
+    npg = cap // page
+    k = torch.randn(B, L, H, cap, D)
+    v = torch.randn(B, L, H, cap, D)
+    order = None if order_seed is None else np.random.default_rng(order_seed).permutation(B * npg)
+    kp, vp, table = sv.kv_paged_from_library(k, v, page, order)
+    assert kp.is_contiguous() and kp.shape == (B * npg, L, H, page, D)
+    flat_k, flat_v = kp.reshape(-1), vp.reshape(-1)
+    for b in range(B):
+        for i in range(npg):
+            pg = int(table[b, i])
+            for l in range(L):
+                for h in range(H):
+                    off = ((pg * L + l) * H + h) * page * D
+                    want_k = k[b, l, h, i * page:(i + 1) * page].reshape(-1)
+                    want_v = v[b, l, h, i * page:(i + 1) * page].reshape(-1)
+                    assert torch.equal(flat_k[off:off + page * D], want_k)
+                    assert torch.equal(flat_v[off:off + page * D], want_v)
