@@ -45,7 +45,7 @@ HBM_PEAK_GBS = 8000.0
 # sources it was measured on (SHA-256 prefix of common.h + gemm.h +
 # spec_verify.hip).
 MEASURED_TRAFFIC = {
-    "moe_b1": {"source_sha": "5c82d2e3058b80d1", "fetch_kib": 161690.3, "fetch_scale": 2.000,
+    "moe_b1": {"source_sha": "df667f9e92c5d912", "fetch_kib": 161690.5, "fetch_scale": 2.000,
                "write_kib": 63.1, "write_scale": 1.000},
 }
 
