@@ -64,9 +64,16 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(1, STREAM ? 
     const int hkv = blockIdx.y / a.QG, qgi = blockIdx.y % a.QG;
     const int b = blockIdx.z;
     const int K1 = a.K1, G = a.n_q / a.n_kv, R = K1 * G;
+    const int c0 = chunk * a.CH;
+    // paged caches: lane i holds the physical page of this chunk's i-th page,
+    // loaded once (its index needs only the chunk, so the load overlaps the
+    // context-length load); each tile takes its page with a cross-lane read
+    const bool paged = a.kvp.table != nullptr;
+    const int pg0 = paged ? c0 / a.kvp.page : 0;
+    int my_page = 0;
+    if (paged) my_page = a.kvp.table[(size_t)b * a.kvp.max_pages + min(pg0 + lane, a.kvp.max_pages - 1)];
     const int ctx = min(max(a.ctx_in[b], 0), a.cap - K1);
     const int total = ctx + K1;
-    const int c0 = chunk * a.CH;
     if (c0 >= total) return;
     const int c1 = min(c0 + a.CH, total);
 
@@ -74,14 +81,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(1, STREAM ? 
     const char* kbase = (const char*)a.kc + head * (size_t)a.cap * DH * ESZ + lane * 16;
     const char* vbase = (const char*)a.vc + head * (size_t)a.cap * DH * ESZ + lane * 16;
     constexpr size_t TILE = (size_t)KT * DH * ESZ;     // bytes per key tile
-    // paged caches: lane i holds the physical page of this chunk's i-th page
-    // (loaded once; each tile takes its page with a cross-lane read)
-    const bool paged = a.kvp.table != nullptr;
-    const int pg0 = paged ? c0 / a.kvp.page : 0;
-    int my_page = 0;
     if (paged) {
-        const int pi = min(pg0 + lane, a.kvp.max_pages - 1);
-        my_page = a.kvp.table[(size_t)b * a.kvp.max_pages + pi];
         const bool bad = pg0 + lane <= (c1 - 1) / a.kvp.page && (my_page < 0 || my_page >= a.kvp.n_pages);
         if (__any(bad) && lane == 0) atomicOr(a.err_word, SV_DEV_CAPACITY);
         my_page = min(max(my_page, 0), a.kvp.n_pages - 1);
