@@ -244,7 +244,11 @@ int spec_verify_step(spec_verify_ctx* ctx, const spec_verify_weights* w, void* k
                      int32_t* accepted_len, int32_t* next_tok, void* stream);
 
 /*
- * Paged KV caches (kv_page_size = P > 0).  The k_cache / v_cache arguments of
+ * Paged KV caches (kv_page_size = P > 0).  Defined by: OCRia-1 technical-
+ * report digest, third item of its list of things worth copying (the
+ * inference stack reuses a shared prompt prefix); "Architecture and
+ * acceleration of an end-to-end OCR expert model", section 9 (long contexts
+ * need KV-cache management).  The k_cache / v_cache arguments of
  * the steps are then pools of kv_pool_pages physical pages: page g holds, for
  * every layer l and KV head h, P positions at element offset
  * ((g * L + l) * n_kv + h) * P * D, tiled exactly like a contiguous region of
