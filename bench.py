@@ -305,14 +305,17 @@ def run_bench(cfg, steps, warmup, sampled=False, kv_page=0, graph=False):
     return res
 
 
-def run_draft_loop(cfg, steps, warmup):
+def run_draft_loop(cfg, steps, warmup, graph=False):
     """The device-resident draft -> verify loop: every iteration verifies the
     current drafts (spec_verify_step) and lets the FastMTP draft head propose
     the next ones (spec_draft_step) from the verify step's outcome; contexts
     grow by accepted + 1 and the bonus token becomes the next committed token,
     all on the device.  Seeded random weights for the target and the draft
     head, so drafts are rarely accepted: the line measures cost, not the
-    pages' acceptance."""
+    pages' acceptance.  graph: the timed iterations are captured once into
+    one HIP graph and replayed; an eager re-run of the same iterations from
+    the same state (events around the drafting) must give the same accepted
+    lengths and contexts."""
     import torch
 
     import speculative_decoding_verify_step_amd as sv
@@ -356,15 +359,40 @@ def run_draft_loop(cfg, steps, warmup):
     for i in range(warmup):
         one(i, False)
     torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(warmup, warmup + steps):
-        one(i, False)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    for i in range(warmup + steps, n_it):   # a second pass with events around the drafts
-        one(i, True)
-    torch.cuda.synchronize()
-    draft_ms = sum(ev[i][0].elapsed_time(ev[i][1]) for i in range(warmup + steps, n_it)) / steps
+    timed_its = range(warmup, warmup + steps)
+    if graph:
+        state = [t.clone() for t in ctxs + coms + drs + [k, v, mk, mv]]
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for i in timed_its:
+                one(i, False)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        g.replay()
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        acc_graph = acc_all[warmup:warmup + steps].clone()
+        end_graph = [t.clone() for t in ctxs + coms + drs]
+        for t, s0 in zip(ctxs + coms + drs + [k, v, mk, mv], state):
+            t.copy_(s0)
+        del state, g
+        for i in timed_its:   # the same iterations, eager, with events around the drafts
+            one(i, True)
+        torch.cuda.synchronize()
+        assert torch.equal(acc_all[warmup:warmup + steps], acc_graph), "graph replay differs"
+        assert all(torch.equal(a_, b2) for a_, b2 in zip(ctxs + coms + drs, end_graph)), \
+            "graph replay differs"
+        draft_ms = sum(ev[i][0].elapsed_time(ev[i][1]) for i in timed_its) / steps
+    else:
+        t0 = time.perf_counter()
+        for i in timed_its:
+            one(i, False)
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        for i in range(warmup + steps, n_it):   # a second pass with events around the drafts
+            one(i, True)
+        torch.cuda.synchronize()
+        draft_ms = sum(ev[i][0].elapsed_time(ev[i][1]) for i in range(warmup + steps, n_it)) / steps
     assert vc.error_word() == 0 and dc.error_word() == 0, "device error during the loop"
     acc = acc_all[warmup:warmup + steps].to(torch.int64)
     tok = int(acc.sum().item()) + steps * B
@@ -456,8 +484,13 @@ def main():
     cfg = workloads.get_config(args.config)
     steps = args.steps if args.steps is not None else (cfg.steps if cfg.steps > 1 else 200)
     warmup = args.warmup if args.warmup is not None else 10
+    # short independent steps measured faster replayed from one graph (batch
+    # 1, same box, alternating: 118.0 -> 113.4 us; the batch-1 draft loop
+    # 434.6 -> 434.0 us); long chained steps measured faster with eager
+    # launches (graph nodes add about 1 us per kernel there)
+    graph = args.graph or (cfg.steps == 1 and not args.eager)
     if args.draft_loop:
-        r = run_draft_loop(cfg, steps, warmup)
+        r = run_draft_loop(cfg, steps, warmup, graph=graph)
         print(json.dumps({
             "metric": METRIC, "value": r["tok_s"], "unit": "tokens/s", "n_gpus": 1,
             "steps": steps, "warmup": warmup, "ms_per_step": r["ms_per_step"],
@@ -465,13 +498,10 @@ def main():
             "vs_baseline": None, "dtype": "bf16" if cfg.wdtype == "bf16" else cfg.wdtype,
             "data": "synthetic (seeded random target and draft-head weights)",
             "config": {"workload": cfg.name, "batch": cfg.batch, "k_draft": cfg.k_draft,
-                       "mode": "FastMTP draft -> verify loop", "tokens_per_verify": r["tau"]},
+                       "mode": "FastMTP draft -> verify loop", "tokens_per_verify": r["tau"],
+                       "launch": "one HIP graph of all timed iterations" if graph else "eager"},
             "draft_us_per_step": r["draft_ms"] * 1e3}), flush=True)
         return
-    # short independent steps measured faster replayed from one graph (batch
-    # 1: 118.6 -> 113.9 us on one box); long chained steps measured faster
-    # with eager launches (graph nodes add about 1 us per kernel there)
-    graph = args.graph or (cfg.steps == 1 and not args.eager)
     r = run_bench(cfg, steps, warmup, sampled=args.sampled, kv_page=args.kv_page, graph=graph)
     lm_gbs = r["lm_bytes"] / (r["lm_ms"] * 1e-3) / 1e9 if r["lm_ms"] > 0 else None
     out = {

@@ -156,3 +156,72 @@ def test_draft_failed_sequences_get_no_drafts(H):
     assert dctx.error_word(clear=True) == sv.SV_DEV_CAPACITY
     dctx.close()
     run.close()
+
+
+def test_draft_verify_loop_replays_from_one_graph(H):
+    """Three iterations of the device-resident loop (verify the drafts, then
+    draft the next ones from the outcome; contexts and committed tokens carried
+    on the device) captured into one HIP graph: each replay from the restored
+    start state gives the eager loop's accepted lengths, tokens, contexts and
+    drafts."""
+    import speculative_decoding_verify_step_amd as sv
+    cfg = workloads.scaled(workloads.get_config("moe_b32"), n_layers=2, vocab=8192, batch=4,
+                           steps=4, ctx=("uniform", 100, 300))
+    case = H.Case(cfg)
+    B, S = cfg.batch, 3
+    vc = sv.VerifyContext(cfg, B, case.cap, case.w_gpu)
+    kc0, vc0 = sv.kv_to_library(case.k_nat[:B], case.v_nat[:B])
+    mc = workloads.mtp_config(cfg)
+    mw = workloads.mtp_weights(cfg, "cuda")
+    mk0, mv0 = workloads.kv_cache(workloads.scaled(mc, batch=B), "cuda", capacity=case.cap)
+    mk0, mv0 = sv.kv_to_library(mk0, mv0)
+    dctx = sv.DraftContext(mc, B, case.cap, vc.weights, mw)
+    kc, vcc, mk, mv = kc0.clone(), vc0.clone(), mk0.clone(), mv0.clone()
+    i32 = dict(dtype=torch.int32, device="cuda")
+    com0 = case.committed[:B].to(**i32)
+    ctx0 = case.ctx[:B].to(**i32)
+    d0 = case.rtok[0][:B].to(**i32).contiguous()
+    coms = [torch.empty(B, **i32) for _ in range(S + 1)]
+    ctxs = [torch.empty(B, **i32) for _ in range(S + 1)]
+    drs = [torch.empty(B, cfg.k_draft, **i32) for _ in range(S + 1)]
+    accs = [torch.empty(B, **i32) for _ in range(S)]
+
+    def loop():
+        for s_ in range(S):
+            vc.step(kc, vcc, coms[s_], drs[s_], ctxs[s_], ctxs[s_ + 1], accs[s_], coms[s_ + 1])
+            dctx.draft(mk, mv, vc, ctxs[s_], accs[s_], coms[s_ + 1], drs[s_], drs[s_ + 1])
+
+    def restore():
+        for t, t0 in ((kc, kc0), (vcc, vc0), (mk, mk0), (mv, mv0), (coms[0], com0),
+                      (ctxs[0], ctx0), (drs[0], d0)):
+            t.copy_(t0)
+
+    outs = accs + coms + ctxs + drs
+    restore()
+    loop()
+    torch.cuda.synchronize()
+    eager = [t.clone() for t in outs]
+    assert vc.error_word() == 0 and dctx.error_word() == 0
+    assert all(int(a.min()) >= 0 for a in accs)
+    st = torch.cuda.Stream()
+    st.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(st):
+        restore()
+        loop()
+    torch.cuda.current_stream().wait_stream(st)
+    torch.cuda.synchronize()
+    gr = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(gr):
+        loop()
+    for rep in range(3):
+        restore()
+        for t in accs + coms[1:] + ctxs[1:] + drs[1:]:
+            t.fill_(-5)
+        torch.cuda.synchronize()
+        gr.replay()
+        torch.cuda.synchronize()
+        for got, want in zip(outs, eager):
+            assert torch.equal(got, want), f"replay {rep}"
+    assert vc.error_word() == 0 and dctx.error_word() == 0
+    dctx.close()
+    vc.close()
