@@ -87,6 +87,51 @@ def test_paged_equals_contiguous(H, name, overrides, page):
     run.close()
 
 
+@pytest.mark.parametrize("name,overrides", [
+    ("moe_b32", {"n_layers": 2, "vocab": 8192, "batch": 5, "ctx": ("uniform", 30, 700)}),
+    ("moe_b1_mxfp4", {"n_layers": 1, "batch": 3, "ctx": ("uniform", 100, 900)}),
+])
+def test_paged_sampled_and_mxfp4_equal_contiguous(H, name, overrides):
+    """The sampled step (rejection sampling, temperature 0.8) and MXFP4
+    weights on paged caches in a shuffled pool: accepted lengths, tokens,
+    contexts and the written pages equal the contiguous run's bit for bit."""
+    import speculative_decoding_verify_step_amd as sv
+    page = 64
+    cfg = workloads.scaled(workloads.get_config(name), **overrides)
+    case = _case(H, cfg, page)
+    B = cfg.batch
+    sd = workloads.sampled_drafts(cfg)
+    dev = "cuda"
+    i32 = dict(dtype=torch.int32, device=dev)
+    com = case.committed[:B].to(**i32)
+    dr = sd["drafts"].to(dev).contiguous()
+    q, u = sd["q"].to(dev).contiguous(), sd["u"].to(dev).contiguous()
+    ci = case.ctx[:B].to(**i32)
+    npg = case.cap // page
+    H.say(f"[paged sampled {cfg.name}] B={B} cap={case.cap} pool={B * npg}")
+    outs = []
+    for paged in (False, True):
+        kc, vc = sv.kv_to_library(case.k_nat[:B], case.v_nat[:B])
+        table = None
+        if paged:
+            kc, vc, table = sv.kv_paged_from_library(
+                kc, vc, page, np.random.default_rng(7).permutation(B * npg))
+        ctx_obj = sv.VerifyContext(cfg, B, case.cap, case.w_gpu, kv_page_size=page if paged else 0,
+                                   kv_pool_pages=kc.shape[0] if paged else 0)
+        if paged:
+            ctx_obj.set_kv_pages(table)
+        acc, nxt, co = (torch.full((B,), -9, **i32) for _ in range(3))
+        ctx_obj.step_sampled(kc, vc, com, dr, q, u, 0.8, sd["seed"], sd["offset"], ci, co, acc, nxt)
+        torch.cuda.synchronize()
+        assert ctx_obj.error_word() == 0
+        if paged:
+            kc, vc = _unpage(kc, table, B, case.cap, page), _unpage(vc, table, B, case.cap, page)
+        outs.append([acc.cpu(), nxt.cpu(), co.cpu(), kc, vc])
+        ctx_obj.close()
+    for got, want in zip(outs[1], outs[0]):
+        assert torch.equal(got, want)
+
+
 def test_paged_prefix_sharing(H):
     """Sequences 1..3 read sequence 0's pages for a common prefix of 4 pages;
     the results equal a contiguous run in which they hold copies of it."""
