@@ -118,6 +118,33 @@ def step_bytes(cfg, ctx, distinct_experts):
     return total + kv_read + kv_write
 
 
+def attention_bytes(cfg, ctx_sum_mean):
+    """Algorithmic bytes of one split-KV attention launch (one layer): every
+    cached and new K/V row of every sequence read once, the queries read once.
+    ctx_sum_mean: the sum over sequences of (context + K + 1), averaged over
+    the timed steps."""
+    kvb = 4 if cfg.kvdtype == "f32" else 2
+    T = cfg.batch * (cfg.k_draft + 1)
+    return int(ctx_sum_mean * 2 * cfg.n_kv * cfg.head_dim * kvb + T * cfg.n_q * cfg.head_dim * 2)
+
+
+def gate_up_bytes(cfg, distinct_mean):
+    """Algorithmic bytes of one grouped expert gate/up launch (one layer): the
+    gate and up rows of every routed expert used and of the shared experts
+    once, the normalised rows once, the SwiGLU outputs written once."""
+    H, I = cfg.hidden, cfg.expert_inter
+    T = cfg.batch * (cfg.k_draft + 1)
+    w = (distinct_mean + cfg.n_shared) * 2 * I * H * WBYTES[cfg.wdtype]
+    return int(w + T * H * 2 + (T * cfg.top_k + cfg.n_shared * T) * I * 2)
+
+
+# The kernel class with the largest share of a step (kernel traces): the LM
+# head at batch 1; at batch 32 the grouped expert gate/up (742 us of 2,450);
+# at batch 64 with long contexts the attention (3,050 of 5,331); dense fp8
+# with K = 31 the attention (401 of 2,014).
+DOMINANT = {"moe_b32": "expert_gate_up", "moe_b64_long": "attention", "dense_fp8_b8": "attention"}
+
+
 # ------------------------------------------------------------- workload
 def setup(cfg, steps, kv_page=0):
     """Weights, caches and a context.  kv_page > 0: the caches live in page
@@ -238,7 +265,9 @@ def run_bench(cfg, steps, warmup, sampled=False, kv_page=0, graph=False):
     ctx.copy_(ctx0)
     com_bufs[0].copy_(com0)
     ctx_start = ctx.clone()
-    kc = sv.SV_KC_LM_HEAD
+    dom = "lm_head" if sampled else DOMINANT.get(cfg.name, "lm_head")
+    kc = {"lm_head": sv.SV_KC_LM_HEAD, "attention": sv.SV_KC_ATTENTION,
+          "expert_gate_up": sv.SV_KC_EXPERT_GATE_UP}[dom]
     if graph:
         g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g):
@@ -253,7 +282,7 @@ def run_bench(cfg, steps, warmup, sampled=False, kv_page=0, graph=False):
         t1 = time.perf_counter()
         acc_sum = acc_all[:steps].to(torch.int64).sum(0)
         ctx_graph = ctx.clone()
-        # the LM-head kernel's time from an eager pass of the same steps
+        # the dominant kernel's time from an eager pass of the same steps
         ctx.copy_(ctx0)
         com_bufs[0].copy_(com0)
         vc.kernel_time(kc, enable=1, query=False)
@@ -288,13 +317,28 @@ def run_bench(cfg, steps, warmup, sampled=False, kv_page=0, graph=False):
     wall = t1 - t0
     committed_tokens = int(acc_sum.sum().item()) + steps * B
     ms_step = wall * 1e3 / steps
+    if dom == "lm_head":
+        kbytes = lm_head_bytes(cfg, B * K1, logits=sampled)
+    elif dom == "attention":
+        # contexts of every timed step: the start plus the commits before it
+        acc_t = acc_all[:steps].to(torch.int64).cpu()
+        c0 = (ctx_start if not chained else ctx0).to(torch.int64).cpu()
+        if chained:
+            grown = torch.cumsum(acc_t + 1, 0) - (acc_t + 1)      # commits before step s
+            ctx_sum_mean = float((c0.unsqueeze(0) + grown + K1).sum(1).double().mean())
+        else:
+            ctx_sum_mean = float((c0 + K1).sum())
+        kbytes = attention_bytes(cfg, ctx_sum_mean)
+    else:
+        kbytes = gate_up_bytes(cfg, sum(distinct) / len(distinct))
     res = {
         "ms_per_step": ms_step,
         "tok_s": committed_tokens / wall,
         "tau": committed_tokens / (steps * B),
+        "kernel": dom,
         "lm_ms": lm_ms / max(lm_n, 1),
         "lm_launches": lm_n,
-        "lm_bytes": lm_head_bytes(cfg, B * K1, logits=sampled),
+        "lm_bytes": kbytes,
         "sampling_us_per_step": samp_us,
         "step_bytes": step_bytes(cfg, (ctx_start if not chained else ctx0).tolist(),
                                  distinct or [0] * cfg.n_layers),
@@ -527,10 +571,13 @@ def main():
                    "launch": "one HIP graph of all timed steps" if graph else "eager",
                    "verification": "sampled (temperature 1)" if args.sampled else "greedy",
                    "tokens_per_verify": r["tau"]},
-        "roofline": {"bound": "hbm", "kernel": "lm_head_argmax",
+        "roofline": {"bound": "hbm",
+                     "kernel": {"lm_head": "lm_head_argmax", "attention": "attn_split",
+                                "expert_gate_up": "expert_gate_up_swiglu"}[r["kernel"]],
                      "achieved": lm_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": (lm_gbs / HBM_PEAK_GBS) if lm_gbs else None,
-                     "traffic": None if args.sampled else measured_traffic(cfg.name),
+                     "traffic": (measured_traffic(cfg.name)
+                                 if r["kernel"] == "lm_head" and not args.sampled else None),
                      "mean_us": r["lm_ms"] * 1e3, "bytes_per_launch": r["lm_bytes"],
                      "launches_timed": r["lm_launches"]},
         "step_roofline": {"bytes_per_step": r["step_bytes"],

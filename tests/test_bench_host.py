@@ -68,3 +68,18 @@ def test_traffic_only_for_the_measured_sources(monkeypatch):
     monkeypatch.setattr(bench, "kernel_source_sha", lambda: "0" * 16)
     assert bench.measured_traffic("moe_b1") is None
     assert bench.measured_traffic("moe_b32") is None
+
+
+def test_attention_and_gate_up_bytes_by_hand():
+    b64 = workloads.get_config("moe_b64_long")
+    # one layer: K and V rows of every (context + K + 1) position, bf16, per KV head; queries once
+    ctx_sum = 64 * (4756 + 4)
+    want = ctx_sum * 2 * 10 * 128 * 2 + 256 * 10 * 128 * 2
+    assert bench.attention_bytes(b64, ctx_sum) == want
+    b32 = workloads.get_config("moe_b32")
+    H, I, T = 1280, 896, 128
+    # 64 routed experts used + 2 shared: gate and up rows once, rows in, SwiGLU out
+    want = (64 + 2) * 2 * I * H * 2 + T * H * 2 + (T * 6 + 2 * T) * I * 2
+    assert bench.gate_up_bytes(b32, 64) == want
+    for name in bench.DOMINANT:
+        assert workloads.get_config(name).name == name
