@@ -33,6 +33,7 @@ struct AttnArgs {
     const int* ctx_in;        // [B]
     const int* seq_err;       // [B]
     int layer, L, n_q, n_kv, D, K1, cap, CH, maxch, QG;
+    int B;                    // sequences in the step
     float scale_log2;         // log2(e) / sqrt(D)
     float* opart;             // [B][n_q][K1][maxch][D]
     float* mlpart;            // [B][n_q][K1][maxch][2]  (max in log2 units, sum)
@@ -60,9 +61,28 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(1, STREAM ? 
     constexpr int NB = KL / 4;              // 16-key score blocks per tile
 
     const int lane = threadIdx.x, l16 = lane & 15, lg = lane >> 4;
-    const int chunk = blockIdx.x;
-    const int hkv = blockIdx.y / a.QG, qgi = blockIdx.y % a.QG;
-    const int b = blockIdx.z;
+    // grid: with one query group per KV head (chunk, KV head, sequence).  With
+    // QG > 1 groups a 1-D grid: the work items u = (sequence, KV head, chunk)
+    // in blocks of 8, x = (u / 8, query group, u % 8), so that the groups
+    // reading one K/V tile are 8 workgroups apart -- on the same XCD
+    // (workgroups go to the 8 XCDs round-robin), where the later readers find
+    // the tile in that XCD's L2 instead of fetching it from HBM again -- and
+    // every XCD gets the same share of the work items
+    int chunk, qgi, hkv, b;
+    if (a.QG > 1) {
+        const int x = blockIdx.x;
+        const int u = (x / (8 * a.QG)) * 8 + (x & 7);
+        if (u >= a.B * a.n_kv * a.maxch) return;   // padding of the last block of 8
+        qgi = (x >> 3) % a.QG;
+        chunk = u % a.maxch;
+        hkv = (u / a.maxch) % a.n_kv;
+        b = u / (a.maxch * a.n_kv);
+    } else {
+        chunk = blockIdx.x;
+        qgi = 0;
+        hkv = blockIdx.y;
+        b = blockIdx.z;
+    }
     const int K1 = a.K1, G = a.n_q / a.n_kv, R = K1 * G;
     const int c0 = chunk * a.CH;
     // paged caches: lane i holds the physical page of this chunk's i-th page,

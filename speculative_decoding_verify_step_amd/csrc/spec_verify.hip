@@ -1076,7 +1076,10 @@ static int step_impl(spec_verify_ctx* c, const spec_verify_weights* w, void* k_c
         at.layer = l;
         {
             ProfScope ps(c, SV_KC_ATTENTION, s);
-            dim3 grid(c->att_maxch, k.n_kv_heads * c->att_QG, B);
+            at.B = B;
+            const dim3 grid = c->att_QG > 1
+                ? dim3((unsigned)(cdiv(B * k.n_kv_heads * c->att_maxch, 8) * 8 * c->att_QG), 1, 1)
+                : dim3(c->att_maxch, k.n_kv_heads, B);
             launch_attention(bf, k.head_dim, c->att_QPW, c->att_stream, grid, at, s);
         }
         launch_merge(bf, c->att_maxch, at, c->o, B * k.n_q_heads * K1, s);
