@@ -39,14 +39,20 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
 
-# HBM traffic of the dominant kernel from rocprofv3 counter runs (see
-# profiles/lm_head_argmax_moe_b1.md): KiB per dispatch, scaled by what the same
-# counter reads for a plain copy of known size.  Valid only for the kernel
-# sources it was measured on (SHA-256 prefix of common.h + gemm.h +
-# spec_verify.hip).
-MEASURED_TRAFFIC = {
-    "moe_b1": {"source_sha": "df667f9e92c5d912", "fetch_kib": 161690.5, "fetch_scale": 2.000,
+# HBM traffic of each workload's dominant kernel from rocprofv3 counter runs
+# (see profiles/hbm_traffic_dominant_kernels.md): KiB per dispatch, scaled by
+# what the same counter reads for a plain copy of known size.  Valid only for
+# the kernel sources it was measured on (SHA-256 prefix of every .h / .hip file
+# of the library's csrc/, in name order).
+MEASURED_TRAFFIC = {   # the dominant kernel of each workload (see DOMINANT)
+    "moe_b1": {"source_sha": "fce1f40b83e17eea", "fetch_kib": 161690.9, "fetch_scale": 2.000,
                "write_kib": 63.1, "write_scale": 1.000},
+    "moe_b32": {"source_sha": "fce1f40b83e17eea", "fetch_kib": 161796.5, "fetch_scale": 2.000,
+                "write_kib": 1792.0, "write_scale": 1.000},
+    "moe_b64_long": {"source_sha": "fce1f40b83e17eea", "fetch_kib": 766094.8, "fetch_scale": 2.000,
+                     "write_kib": 7143.3, "write_scale": 1.000},
+    "dense_fp8_b8": {"source_sha": "fce1f40b83e17eea", "fetch_kib": 60667.9, "fetch_scale": 2.000,
+                     "write_kib": 30494.3, "write_scale": 1.000},
 }
 
 
@@ -54,7 +60,9 @@ def kernel_source_sha() -> str:
     import hashlib
     h = hashlib.sha256()
     d = os.path.join(ROOT, "speculative_decoding_verify_step_amd", "csrc")
-    for f in ("common.h", "gemm.h", "spec_verify.hip"):
+    for f in sorted(os.listdir(d)):
+        if not f.endswith((".h", ".hip")):
+            continue
         with open(os.path.join(d, f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
@@ -576,8 +584,8 @@ def main():
                                 "expert_gate_up": "expert_gate_up_swiglu"}[r["kernel"]],
                      "achieved": lm_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": (lm_gbs / HBM_PEAK_GBS) if lm_gbs else None,
-                     "traffic": (measured_traffic(cfg.name)
-                                 if r["kernel"] == "lm_head" and not args.sampled else None),
+                     "traffic": (None if args.sampled or args.kv_page
+                                 else measured_traffic(cfg.name)),
                      "mean_us": r["lm_ms"] * 1e3, "bytes_per_launch": r["lm_bytes"],
                      "launches_timed": r["lm_launches"]},
         "step_roofline": {"bytes_per_step": r["step_bytes"],

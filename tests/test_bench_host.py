@@ -68,6 +68,7 @@ def test_traffic_only_for_the_measured_sources(monkeypatch):
     monkeypatch.setattr(bench, "kernel_source_sha", lambda: "0" * 16)
     assert bench.measured_traffic("moe_b1") is None
     assert bench.measured_traffic("moe_b32") is None
+    assert bench.measured_traffic("tiny_fp32") is None
 
 
 def test_attention_and_gate_up_bytes_by_hand():
