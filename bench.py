@@ -290,6 +290,7 @@ def run_bench(cfg, steps, warmup, sampled=False, kv_page=0, graph=False):
         t1 = time.perf_counter()
         acc_sum = acc_all[:steps].to(torch.int64).sum(0)
         ctx_graph = ctx.clone()
+        acc_graph = acc_all[:steps].clone()
         # the dominant kernel's time from an eager pass of the same steps
         ctx.copy_(ctx0)
         com_bufs[0].copy_(com0)
@@ -298,7 +299,8 @@ def run_bench(cfg, steps, warmup, sampled=False, kv_page=0, graph=False):
             one(i, ctx)
         torch.cuda.synchronize()
         lm_ms, lm_n = vc.kernel_time(kc, enable=0)
-        assert torch.equal(ctx, ctx_graph), "graph replay and eager steps disagree"
+        assert torch.equal(ctx, ctx_graph) and torch.equal(acc_all[:steps], acc_graph), \
+            "graph replay and eager steps disagree"
         del g
     else:
         # timed region

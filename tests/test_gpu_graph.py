@@ -22,14 +22,16 @@ def H():
 
 
 @pytest.mark.parametrize("name,overrides", [
+    ("moe_b1", {}),       # the full-size batch-1 workload, as bench.py replays it
     ("moe_b1", dict(n_layers=1, vocab=8192)),
     ("moe_b32", dict(n_layers=2, vocab=4096, batch=20, ctx=("uniform", 50, 400))),
 ])
 def test_graph_replays_match_eager(H, name, overrides):
-    cfg = workloads.scaled(workloads.get_config(name), **overrides)
+    cfg = workloads.scaled(workloads.get_config(name), **overrides) if overrides else \
+        workloads.get_config(name)
     case = H.Case(cfg)
     run = H.GpuRun(case, debug=False)
-    H.say(f"[graph {name}] B={run.B} L={cfg.n_layers}")
+    H.say(f"[graph {name}] B={run.B} L={cfg.n_layers} V={cfg.vocab}")
     dev = "cuda"
     com = case.committed[: run.B].to(dev, torch.int32).contiguous()
     dr = case.rtok[0][: run.B].to(dev, torch.int32).contiguous()
@@ -67,6 +69,7 @@ def test_graph_replays_match_eager(H, name, overrides):
 
 
 @pytest.mark.parametrize("name,overrides", [
+    ("moe_b1", {}),       # the full-size batch-1 workload, as bench.py replays it
     ("moe_b1", dict(n_layers=1, vocab=8192)),
     ("dense_fp8_b8", dict(n_layers=1, vocab=8192, batch=3, k_draft=7, ctx=("uniform", 100, 300))),
 ])
