@@ -531,7 +531,7 @@ def main():
         copy_calibration(args.copy_calibration, args.steps or 5)
         return
     if args.gpus != 1:
-        print(json.dumps({"error": "this build runs on one GPU; --gpus must be 1",
+        print(json.dumps({"error": "this library runs on one GPU; --gpus must be 1",
                           "n_gpus": args.gpus}))
         sys.exit(2)
     import workloads
