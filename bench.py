@@ -1,6 +1,6 @@
 """Benchmark of the greedy speculative-decoding verify step on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config moe_b1] [--sampled | --draft-loop]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config NAME] [--sampled | --draft-loop]
 
 A step is one spec_verify_step over a whole batch (every row of the hot
 path: embedding, all decoder layers, LM head + argmax, acceptance + commit).
@@ -9,9 +9,12 @@ Drafts follow the workload's rule (copy the target's greedy token with the
 match probability, else a uniform token) and are recorded in untimed passes,
 then replayed, so the timed steps accept exactly what was recorded.
 
-Workloads: single-step ones repeat the same step (same context, same drafts)
-K times; the chained long-context workload runs K consecutive steps in which
-contexts grow by accepted + 1 and the bonus token becomes the next committed
+Without --config the run covers the metric's three batch points in one
+invocation: batch 1 (moe_b1, the line's headline value), batch 32 (moe_b32,
+12 layers) and batch 64 (moe_b64_long, 12 layers, its chain of 100 steps).
+Single-step workloads cycle through 16 recorded draft sets over K timed
+steps (same contexts); the chained workload runs its steps in order, contexts
+growing by accepted + 1 and the bonus token becoming the next committed
 token, all on the device.
 
 --sampled times the sampled (rejection-sampling) step instead, at temperature
@@ -21,10 +24,13 @@ draft -> verify loop (spec_draft_step after every spec_verify_step) and
 reports the draft step's share.
 
 One JSON line is printed: accepted tokens/s (sum over sequences of
-accepted + 1 per step, over the timed wall clock), microseconds per step, the
-roofline of the dominant kernel (algorithmic bytes / its mean duration from
-HIP events recorded around its launches on the launch stream during the timed
-steps) and the CPU oracle's throughput on the host as a reported baseline.
+accepted + 1 per step, over the timed wall clock), microseconds per step
+(mean over the timed region; p50 / p90 from an eager re-run with events
+between steps), the roofline of the dominant kernel (algorithmic bytes / its
+mean duration from HIP events recorded around its launches on the launch
+stream), every kernel class's time per step, the whole step against the HBM
+roofline, and the CPU oracle's throughput on the host as a reported
+baseline; the default run adds a block per batch point under "batches".
 """
 from __future__ import annotations
 
@@ -151,6 +157,31 @@ def gate_up_bytes(cfg, distinct_mean):
 # at batch 64 with long contexts the attention (3,050 of 5,331); dense fp8
 # with K = 31 the attention (401 of 2,014).
 DOMINANT = {"moe_b32": "expert_gate_up", "moe_b64_long": "attention", "dense_fp8_b8": "attention"}
+# kernel classes timed per step in every workload block
+CLASSES = ("lm_head", "attention", "expert_gate_up", "expert_down", "qkv")
+MFMA_PEAK_TFLOPS = 2500.0     # dense bf16 (fp8 weights are widened to bf16 before the product)
+HEADLINE = "moe_b1"           # the batch-1 workload the headline value is quoted on
+MULTI = ("moe_b1", "moe_b32", "moe_b64_long")   # the metric's batch 1 / 32 / 64 points
+STEP_TARGET_FRAC = 0.60       # the batch-1 step's target fraction of the HBM roofline
+N_DRAFT_SETS = 16             # recorded draft sets cycled by single-step workloads
+
+
+def class_flops(cfg, kclass):
+    """Algorithmic flops of one launch of a matrix-product kernel class (2
+    per multiply-add; routed experts counted per routed row), or None."""
+    T = cfg.batch * (cfg.k_draft + 1)
+    H = cfg.hidden
+    if kclass == "lm_head":
+        return 2 * T * cfg.vocab * H
+    if kclass == "qkv":
+        return 2 * T * cfg.qkv_dim * H
+    if kclass in ("expert_gate_up", "expert_down"):
+        if cfg.ffn == "moe":
+            rows, inter = T * cfg.top_k + cfg.n_shared * T, cfg.expert_inter
+        else:
+            rows, inter = T, cfg.dense_inter
+        return 2 * rows * inter * H * (2 if kclass == "expert_gate_up" else 1)
+    return None
 
 
 # ------------------------------------------------------------- workload
@@ -178,22 +209,24 @@ def setup(cfg, steps, kv_page=0):
     torch.cuda.synchronize()
     ctx = workloads.context_lengths(cfg)
     com = workloads.committed_tokens(cfg)
-    n_rec = steps if cfg.steps > 1 else 1
+    n_rec = steps if cfg.steps > 1 else N_DRAFT_SETS
     coins, rtok = workloads.draft_randomness(cfg, steps=n_rec)
     vc = sv.VerifyContext(cfg, cfg.batch, cap, w, kv_page_size=kv_page,
                           kv_pool_pages=k.shape[0] if kv_page else 0)
     if kv_page:
         vc.set_kv_pages(table)
     return dict(sv=sv, w=w, k=k, v=v, cap=cap, ctx=ctx, com=com, coins=coins, rtok=rtok, vc=vc,
-                n_rec=n_rec)
+                n_rec=n_rec, chained=cfg.steps > 1)
 
 
 def record_drafts(cfg, S):
-    """Drafts of every step by the workload's rule, the target's tokens taken
-    from untimed passes of the library itself; returns per-step device
-    tensors plus the routing of the first step (for the byte model)."""
+    """Drafts of every recorded set (single-step workloads: N_DRAFT_SETS
+    independent draw sets on the same start state; chained: one per step of
+    the chain) by the workload's rule, the target's tokens taken from untimed
+    passes of the library itself; returns per-set device tensors and the
+    number of distinct routed experts per layer under each set's routing."""
     import torch
-    sv, vc = S["sv"], S["vc"]
+    vc = S["vc"]
     B, K = cfg.batch, cfg.k_draft
     K1 = K + 1
     dev = "cuda"
@@ -204,7 +237,7 @@ def record_drafts(cfg, S):
     ctx = S["ctx"].to(**i32)
     com = S["com"].to(**i32)
     tmp_ctx, acc, nxt = (torch.empty(B, **i32) for _ in range(3))
-    drafts, first_routing = [], None
+    drafts, distinct = [], []
     for s in range(S["n_rec"]):
         d = S["rtok"][s].to(**i32).clone()
         coin = S["coins"][s].to(dev).bool()
@@ -212,20 +245,33 @@ def record_drafts(cfg, S):
             vc.step(S["k"], S["v"], com, d, ctx, tmp_ctx, acc, nxt)
             d[:, i] = torch.where(coin[:, i], target[:, i], d[:, i])
         drafts.append(d)
-        if s == 0 and routing is not None:
-            vc.step(S["k"], S["v"], com, d, ctx, tmp_ctx, acc, nxt)
-            first_routing = routing.clone()
-        if S["n_rec"] > 1:     # advance the chain
-            vc.step(S["k"], S["v"], com, d, ctx, ctx, acc, nxt)
+        # the set's own pass (routing for the byte model); a chain advances
+        vc.step(S["k"], S["v"], com, d, ctx, ctx if S["chained"] else tmp_ctx, acc, nxt)
+        if routing is not None:
+            distinct.append([int(torch.unique(routing[l]).numel()) for l in range(cfg.n_layers)])
+        if S["chained"]:
             com = nxt.clone()
     vc.set_debug(None, None, None, None)
     torch.cuda.synchronize()
-    return drafts, first_routing
+    return drafts, distinct
 
 
-def run_bench(cfg, steps, warmup, sampled=False, kv_page=0, graph=False):
-    """graph: the K timed steps are captured once into one HIP graph and the
-    timed region is a single replay of it (no host work between steps)."""
+def _pct(xs, q):
+    import numpy as np
+    return float(np.percentile(np.asarray(xs), q))
+
+
+def run_bench(cfg, steps, warmup, sampled=False, kv_page=0, graph=False, classes=True):
+    """Times `steps` verify steps of `cfg` (one pass of the whole hot path over
+    the batch each) and returns the workload's measurements.  graph: the
+    timed steps are captured once into one HIP graph and the timed region is a
+    single replay of it (no host work between steps); otherwise eager
+    launches.  Single-step workloads cycle through the recorded draft sets;
+    a chained workload runs its steps in order, contexts growing by accepted +
+    1 on the device.  After the timed region, eager passes of the same steps
+    from the same start state give the per-step distribution (HIP events
+    between steps) and the time of each kernel class (HIP events riding on
+    the class's launches)."""
     import torch
 
     import workloads
@@ -233,8 +279,9 @@ def run_bench(cfg, steps, warmup, sampled=False, kv_page=0, graph=False):
     S = setup(cfg, steps, kv_page)
     sv, vc = S["sv"], S["vc"]
     B, K1 = cfg.batch, cfg.k_draft + 1
-    log(f"[bench] {cfg.name}: B={B} L={cfg.n_layers} cap={S['cap']} recording drafts")
-    drafts, routing = record_drafts(cfg, S)
+    log(f"[bench] {cfg.name}: B={B} L={cfg.n_layers} cap={S['cap']} recording "
+        f"{S['n_rec']} draft set(s)")
+    drafts, distinct_sets = record_drafts(cfg, S)
     i32 = dict(dtype=torch.int32, device="cuda")
     if sampled:
         # drafts drawn from seeded draft distributions (rejection sampling at
@@ -245,11 +292,7 @@ def run_bench(cfg, steps, warmup, sampled=False, kv_page=0, graph=False):
     ctx0 = S["ctx"].to(**i32)
     com0 = S["com"].to(**i32)
     nxt, cout = (torch.empty(B, **i32) for _ in range(2))
-    chained = S["n_rec"] > 1
-    distinct = []
-    if routing is not None:
-        for l in range(cfg.n_layers):
-            distinct.append(int(torch.unique(routing[l]).numel()))
+    chained = S["chained"]
     acc_all = torch.empty(max(steps, warmup, 1), B, **i32)
     com_bufs = [com0.clone(), com0.clone()]
 
@@ -265,98 +308,172 @@ def run_bench(cfg, steps, warmup, sampled=False, kv_page=0, graph=False):
         else:
             vc.step(S["k"], S["v"], com_in, d, ctx, ctx_out, acc_all[i], nxt_out)
 
-    # warmup (untimed); a chained run restarts from the recorded start state
     ctx = ctx0.clone()
+
+    def restore():
+        ctx.copy_(ctx0)
+        com_bufs[0].copy_(com0)
+
+    # warmup (untimed); a chained run restarts from the recorded start state
     for i in range(warmup):
         one(i, ctx)
     torch.cuda.synchronize()
-    ctx.copy_(ctx0)
-    com_bufs[0].copy_(com0)
-    ctx_start = ctx.clone()
+    restore()
     dom = "lm_head" if sampled else DOMINANT.get(cfg.name, "lm_head")
-    kc = {"lm_head": sv.SV_KC_LM_HEAD, "attention": sv.SV_KC_ATTENTION,
-          "expert_gate_up": sv.SV_KC_EXPERT_GATE_UP}[dom]
+    kc_of = {"lm_head": sv.SV_KC_LM_HEAD, "attention": sv.SV_KC_ATTENTION,
+             "expert_gate_up": sv.SV_KC_EXPERT_GATE_UP, "expert_down": sv.SV_KC_EXPERT_DOWN,
+             "qkv": sv.SV_KC_QKV}
+    ktime = {}
     if graph:
         g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g):
             for i in range(steps):
                 one(i, ctx)
-        ctx.copy_(ctx0)
-        com_bufs[0].copy_(com0)
+        restore()
         torch.cuda.synchronize()
         t0 = time.perf_counter()
         g.replay()
         torch.cuda.synchronize()
         t1 = time.perf_counter()
-        acc_sum = acc_all[:steps].to(torch.int64).sum(0)
-        ctx_graph = ctx.clone()
-        acc_graph = acc_all[:steps].clone()
-        # the dominant kernel's time from an eager pass of the same steps
-        ctx.copy_(ctx0)
-        com_bufs[0].copy_(com0)
-        vc.kernel_time(kc, enable=1, query=False)
-        for i in range(steps):
-            one(i, ctx)
-        torch.cuda.synchronize()
-        lm_ms, lm_n = vc.kernel_time(kc, enable=0)
-        assert torch.equal(ctx, ctx_graph) and torch.equal(acc_all[:steps], acc_graph), \
-            "graph replay and eager steps disagree"
+        ref = (ctx.clone(), acc_all[:steps].clone())
         del g
     else:
-        # timed region
-        vc.kernel_time(kc, enable=1, query=False)
+        vc.kernel_time(kc_of[dom], enable=1, query=False)
         torch.cuda.synchronize()
         t0 = time.perf_counter()
         for i in range(steps):
             one(i, ctx)
         torch.cuda.synchronize()
         t1 = time.perf_counter()
-        acc_sum = acc_all[:steps].to(torch.int64).sum(0)
-        lm_ms, lm_n = vc.kernel_time(kc, enable=0)
+        ktime[dom] = vc.kernel_time(kc_of[dom], enable=0)
+        ref = (ctx.clone(), acc_all[:steps].clone())
+    acc_t = acc_all[:steps].to(torch.int64).cpu()
+    assert vc.error_word() == 0, "device error during the benchmark"
+    # per-step times: an eager pass with events between steps; it must
+    # reproduce the timed steps' outcome
+    restore()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    torch.cuda.synchronize()
+    ev[0].record()
+    for i in range(steps):
+        one(i, ctx)
+        ev[i + 1].record()
+    torch.cuda.synchronize()
+    per_step_us = [1e3 * ev[i].elapsed_time(ev[i + 1]) for i in range(steps)]
+    assert torch.equal(ctx, ref[0]) and torch.equal(acc_all[:steps], ref[1]), \
+        "timed and re-run steps disagree"
+    # each kernel class in its own eager pass of the same steps
+    for name in (CLASSES if classes else (dom,)):
+        if name in ktime:
+            continue
+        restore()
+        vc.kernel_time(kc_of[name], enable=1, query=False)
+        for i in range(steps):
+            one(i, ctx)
+        torch.cuda.synchronize()
+        ktime[name] = vc.kernel_time(kc_of[name], enable=0)
     assert vc.error_word() == 0, "device error during the benchmark"
     samp_us = None
-    if sampled:   # the sampling kernels, timed in a second pass of the same steps
-        ctx_s = ctx_start.clone()
-        com_bufs[0].copy_(com0)
+    if sampled:   # the sampling kernels, timed in a further pass of the same steps
+        restore()
         vc.kernel_time(sv.SV_KC_SAMPLING, enable=1, query=False)
         for i in range(steps):
-            one(i, ctx_s)
+            one(i, ctx)
         torch.cuda.synchronize()
         s_ms, s_n = vc.kernel_time(sv.SV_KC_SAMPLING, enable=0)
         samp_us = 1e3 * s_ms / max(steps, 1)
     wall = t1 - t0
-    committed_tokens = int(acc_sum.sum().item()) + steps * B
+    committed_tokens = int(acc_t.sum().item()) + steps * B
     ms_step = wall * 1e3 / steps
+    # contexts of every timed step: the start plus the commits before it
+    c0 = ctx0.to(torch.int64).cpu()
+    if chained:
+        grown = torch.cumsum(acc_t + 1, 0) - (acc_t + 1)
+        ctx_steps = c0.unsqueeze(0) + grown               # [steps][B]
+    else:
+        ctx_steps = c0.unsqueeze(0).expand(steps, B)
+    ctx_sum_mean = float((ctx_steps + K1).sum(1).double().mean())
+    nsets = len(drafts)
+    sb = []
+    for i in range(steps):
+        dist = distinct_sets[i % nsets] if distinct_sets else [0] * cfg.n_layers
+        sb.append(step_bytes(cfg, ctx_steps[i].tolist(), dist))
+    step_b = sum(sb) / len(sb)
+    if distinct_sets:
+        dmean = [sum(distinct_sets[i % nsets][l] for i in range(steps)) / steps
+                 for l in range(cfg.n_layers)]
+    else:
+        dmean = []
     if dom == "lm_head":
         kbytes = lm_head_bytes(cfg, B * K1, logits=sampled)
     elif dom == "attention":
-        # contexts of every timed step: the start plus the commits before it
-        acc_t = acc_all[:steps].to(torch.int64).cpu()
-        c0 = (ctx_start if not chained else ctx0).to(torch.int64).cpu()
-        if chained:
-            grown = torch.cumsum(acc_t + 1, 0) - (acc_t + 1)      # commits before step s
-            ctx_sum_mean = float((c0.unsqueeze(0) + grown + K1).sum(1).double().mean())
-        else:
-            ctx_sum_mean = float((c0 + K1).sum())
         kbytes = attention_bytes(cfg, ctx_sum_mean)
     else:
-        kbytes = gate_up_bytes(cfg, sum(distinct) / len(distinct))
+        kbytes = gate_up_bytes(cfg, sum(dmean) / len(dmean))
+    kernels = {}
+    for name, (ms, n) in ktime.items():
+        if n == 0:
+            continue
+        ent = {"mean_us": 1e3 * ms / n, "launches_per_step": n / steps,
+               "us_per_step": 1e3 * ms / steps}
+        fl = class_flops(cfg, name)
+        if fl is not None:
+            tf = fl / (ms / n * 1e-3) / 1e12
+            ent["tflops"] = tf
+            ent["mfma_frac"] = tf / MFMA_PEAK_TFLOPS
+        if name == "attention":
+            ent["GBs"] = attention_bytes(cfg, ctx_sum_mean) / (ms / n * 1e-3) / 1e9
+        if name == "lm_head":
+            ent["GBs"] = lm_head_bytes(cfg, B * K1, logits=sampled) / (ms / n * 1e-3) / 1e9
+        kernels[name] = ent
+    dom_ms, dom_n = ktime[dom]
     res = {
         "ms_per_step": ms_step,
+        "p50_us": _pct(per_step_us, 50),
+        "p90_us": _pct(per_step_us, 90),
         "tok_s": committed_tokens / wall,
         "tau": committed_tokens / (steps * B),
+        "draft_sets": nsets,
         "kernel": dom,
-        "lm_ms": lm_ms / max(lm_n, 1),
-        "lm_launches": lm_n,
+        "lm_ms": dom_ms / max(dom_n, 1),
+        "lm_launches": dom_n,
         "lm_bytes": kbytes,
         "sampling_us_per_step": samp_us,
-        "step_bytes": step_bytes(cfg, (ctx_start if not chained else ctx0).tolist(),
-                                 distinct or [0] * cfg.n_layers),
-        "distinct_experts": distinct,
+        "step_bytes": step_b,
+        "distinct_experts": [round(x, 2) for x in dmean],
+        "kernels": kernels,
         "ctx_end": ctx.tolist() if chained else None,
+        "weights": S["w"],
+        "cap": S["cap"],
     }
     vc.close()
     return res
+
+
+def block(cfg, r, steps, graph, sampled=False, kv_page=0):
+    """The JSON object of one workload's measurements."""
+    lm_gbs = r["lm_bytes"] / (r["lm_ms"] * 1e-3) / 1e9 if r["lm_ms"] > 0 else None
+    step_gbs = r["step_bytes"] / (r["ms_per_step"] * 1e-3) / 1e9
+    return {
+        "workload": cfg.name, "batch": cfg.batch, "k_draft": cfg.k_draft, "layers": cfg.n_layers,
+        "steps": steps, "chained_steps": cfg.steps > 1,
+        "launch": "one HIP graph of all timed steps" if graph else "eager",
+        "us_per_step": r["ms_per_step"] * 1e3, "p50_us": r["p50_us"], "p90_us": r["p90_us"],
+        "accepted_tok_s": r["tok_s"], "tokens_per_verify": r["tau"],
+        "draft_sets": r["draft_sets"],
+        "roofline": {"bound": "hbm",
+                     "kernel": {"lm_head": "lm_head_argmax", "attention": "attn_split",
+                                "expert_gate_up": "expert_gate_up_swiglu"}[r["kernel"]],
+                     "achieved": lm_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": (lm_gbs / HBM_PEAK_GBS) if lm_gbs else None,
+                     "traffic": (None if sampled or kv_page else measured_traffic(cfg.name)),
+                     "mean_us": r["lm_ms"] * 1e3, "bytes_per_launch": r["lm_bytes"],
+                     "launches_timed": r["lm_launches"]},
+        "step_roofline": {"bytes_per_step": r["step_bytes"], "achieved_GBs": step_gbs,
+                          "frac": step_gbs / HBM_PEAK_GBS,
+                          "distinct_experts_per_layer": r["distinct_experts"]},
+        "kernels": r["kernels"],
+    }
 
 
 def run_draft_loop(cfg, steps, warmup, graph=False):
@@ -458,21 +575,42 @@ def run_draft_loop(cfg, steps, warmup, graph=False):
 
 
 # ----------------------------------------------------------- CPU baseline
-def cpu_baseline(cfg, budget_s=15.0):
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def _host_tree(w):
+    import torch
+    if isinstance(w, dict):
+        return {k: _host_tree(v) for k, v in w.items()}
+    if isinstance(w, list):
+        return [_host_tree(v) for v in w]
+    return w.cpu() if isinstance(w, torch.Tensor) else w
+
+
+def cpu_baseline(cfg, budget_s=15.0, weights=None, min_steps=3):
     """The oracle, as it is, on this host: whole verify steps of sequence 0
     of the workload (the same shapes and seeds; drafts by the workload's rule
-    through the oracle), repeated until about `budget_s` seconds of work."""
-    import numpy as np
-
+    through the oracle), repeated until about `budget_s` seconds of work (at
+    least `min_steps`).  `weights`: the workload's weight dict (any device;
+    copied to the host), else generated on the host."""
     import oracle
     import workloads
 
     c1 = workloads.scaled(cfg, batch=1)
     cap = workloads.capacity_for(cfg)
-    w = workloads.make_weights(c1, "cpu")
+    w = _host_tree(weights) if weights is not None else workloads.make_weights(c1, "cpu")
     k, v = workloads.kv_cache(c1, "cpu", capacity=cap)
     orc = oracle.Oracle(c1, w, cap)
     kc, vc = orc.kv_np(k, v)
+    del k, v
     ctx = int(workloads.context_lengths(cfg)[0])
     com = int(workloads.committed_tokens(cfg)[0])
     coins, rtok = workloads.draft_randomness(cfg, steps=1)
@@ -483,10 +621,10 @@ def cpu_baseline(cfg, budget_s=15.0):
         tok += int(out["accepted"][0]) + 1
         n += 1
         el = time.perf_counter() - t0
-        if el >= budget_s or n >= 200:
+        if (el >= budget_s and n >= min_steps) or n >= 200:
             break
     return {"value": tok / el, "unit": "tokens/s", "cores": oracle.num_threads(),
-            "kind": "oracle",
+            "cpu_model": cpu_model(), "kind": "oracle",
             "sample": f"{n} whole verify steps of one sequence of {cfg.name} "
                       f"(ctx {ctx}, K={cfg.k_draft}, {cfg.n_layers} layer(s)), "
                       f"{el:.1f} s; per-step {1e3 * el / n:.1f} ms"}
@@ -506,58 +644,8 @@ def copy_calibration(nbytes: int, reps: int):
     print(json.dumps({"copy_calibration_bytes": nbytes, "reps": reps}), flush=True)
 
 
-def main():
-    ap = argparse.ArgumentParser()
-    ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=None)
-    ap.add_argument("--warmup", type=int, default=None)
-    ap.add_argument("--config", default="moe_b1")
-    ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--sampled", action="store_true",
-                    help="time the sampled (rejection-sampling) verify step instead of the greedy one")
-    ap.add_argument("--draft-loop", action="store_true",
-                    help="time the device-resident FastMTP draft -> verify loop")
-    ap.add_argument("--kv-page", type=int, default=0, metavar="P",
-                    help="paged KV caches: pages of P positions in a shuffled pool")
-    ap.add_argument("--graph", action="store_true",
-                    help="capture the timed steps into one HIP graph and time its replay "
-                         "(the default for single-step workloads)")
-    ap.add_argument("--eager", action="store_true",
-                    help="launch every step from the host (the default for chained workloads)")
-    ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
-                    help="only run a plain device copy of BYTES (counter calibration)")
-    args = ap.parse_args()
-    if args.copy_calibration:
-        copy_calibration(args.copy_calibration, args.steps or 5)
-        return
-    if args.gpus != 1:
-        print(json.dumps({"error": "this library runs on one GPU; --gpus must be 1",
-                          "n_gpus": args.gpus}))
-        sys.exit(2)
-    import workloads
-    cfg = workloads.get_config(args.config)
-    steps = args.steps if args.steps is not None else (cfg.steps if cfg.steps > 1 else 200)
-    warmup = args.warmup if args.warmup is not None else 10
-    # short independent steps measured faster replayed from one graph (batch
-    # 1, same box, alternating: 118.0 -> 113.4 us; the batch-1 draft loop
-    # 434.6 -> 434.0 us); long chained steps measured faster with eager
-    # launches (graph nodes add about 1 us per kernel there)
-    graph = args.graph or (cfg.steps == 1 and not args.eager)
-    if args.draft_loop:
-        r = run_draft_loop(cfg, steps, warmup, graph=graph)
-        print(json.dumps({
-            "metric": METRIC, "value": r["tok_s"], "unit": "tokens/s", "n_gpus": 1,
-            "steps": steps, "warmup": warmup, "ms_per_step": r["ms_per_step"],
-            "us_per_step": r["ms_per_step"] * 1e3, "higher_is_better": True, "scaling": "weak",
-            "vs_baseline": None, "dtype": "bf16" if cfg.wdtype == "bf16" else cfg.wdtype,
-            "data": "synthetic (seeded random target and draft-head weights)",
-            "config": {"workload": cfg.name, "batch": cfg.batch, "k_draft": cfg.k_draft,
-                       "mode": "FastMTP draft -> verify loop", "tokens_per_verify": r["tau"],
-                       "launch": "one HIP graph of all timed iterations" if graph else "eager"},
-            "draft_us_per_step": r["draft_ms"] * 1e3}), flush=True)
-        return
-    r = run_bench(cfg, steps, warmup, sampled=args.sampled, kv_page=args.kv_page, graph=graph)
-    lm_gbs = r["lm_bytes"] / (r["lm_ms"] * 1e-3) / 1e9 if r["lm_ms"] > 0 else None
+def _line(cfg, r, steps, warmup, graph, args, blk):
+    """The top-level JSON object for one workload."""
     out = {
         "metric": METRIC,
         "value": r["tok_s"],
@@ -577,30 +665,113 @@ def main():
                    "layers": cfg.n_layers, "hidden": cfg.hidden, "vocab": cfg.vocab,
                    "ctx": list(cfg.ctx), "chained_steps": cfg.steps > 1,
                    "weight_layout": "tiled16",
-                   "kv": f"paged ({args.kv_page} positions per page)" if args.kv_page else "contiguous",
-                   "launch": "one HIP graph of all timed steps" if graph else "eager",
+                   "kv": (f"paged ({args.kv_page} positions per page)" if args.kv_page
+                          else "contiguous"),
+                   "launch": blk["launch"],
                    "verification": "sampled (temperature 1)" if args.sampled else "greedy",
-                   "tokens_per_verify": r["tau"]},
-        "roofline": {"bound": "hbm",
-                     "kernel": {"lm_head": "lm_head_argmax", "attention": "attn_split",
-                                "expert_gate_up": "expert_gate_up_swiglu"}[r["kernel"]],
-                     "achieved": lm_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": (lm_gbs / HBM_PEAK_GBS) if lm_gbs else None,
-                     "traffic": (None if args.sampled or args.kv_page
-                                 else measured_traffic(cfg.name)),
-                     "mean_us": r["lm_ms"] * 1e3, "bytes_per_launch": r["lm_bytes"],
-                     "launches_timed": r["lm_launches"]},
-        "step_roofline": {"bytes_per_step": r["step_bytes"],
-                          "achieved_GBs": r["step_bytes"] / (r["ms_per_step"] * 1e-3) / 1e9,
-                          "frac": r["step_bytes"] / (r["ms_per_step"] * 1e-3) / 1e9 / HBM_PEAK_GBS,
-                          "distinct_experts_per_layer": r["distinct_experts"]},
+                   "tokens_per_verify": r["tau"], "draft_sets": r["draft_sets"]},
+        "roofline": blk["roofline"],
+        "step_roofline": dict(blk["step_roofline"]),
+        "p50_us": blk["p50_us"],
+        "p90_us": blk["p90_us"],
+        "kernels": blk["kernels"],
     }
-    if args.sampled:
-        out["sampling_kernels_us_per_step"] = r["sampling_us_per_step"]
-    if not args.no_cpu_baseline and not args.sampled:
-        log("[bench] timing the CPU oracle")
-        out["cpu_baseline"] = cpu_baseline(cfg)
-    print(json.dumps(out), flush=True)
+    if cfg.name == HEADLINE and not args.sampled and not args.kv_page:
+        # the batch-1 target applies to the whole step, not to one kernel
+        out["step_roofline"]["target_frac"] = STEP_TARGET_FRAC
+        out["step_roofline"]["meets_target"] = out["step_roofline"]["frac"] >= STEP_TARGET_FRAC
+    return out
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=None,
+                    help="timed steps of single-step workloads (a chained workload runs its "
+                         "own number of steps)")
+    ap.add_argument("--warmup", type=int, default=None)
+    ap.add_argument("--config", default=None,
+                    help="one workload; default: batch 1, 32 and 64 (moe_b1, moe_b32, "
+                         "moe_b64_long) in one line, quoted on batch 1")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--sampled", action="store_true",
+                    help="time the sampled (rejection-sampling) verify step instead of the greedy one")
+    ap.add_argument("--draft-loop", action="store_true",
+                    help="time the device-resident FastMTP draft -> verify loop")
+    ap.add_argument("--kv-page", type=int, default=0, metavar="P",
+                    help="paged KV caches: pages of P positions in a shuffled pool")
+    ap.add_argument("--graph", action="store_true",
+                    help="capture the timed steps into one HIP graph and time its replay "
+                         "(the default for single-step workloads)")
+    ap.add_argument("--eager", action="store_true",
+                    help="launch every step from the host (the default for chained workloads)")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
+                    help="only run a plain device copy of BYTES (counter calibration)")
+    args = ap.parse_args()
+    if args.copy_calibration:
+        copy_calibration(args.copy_calibration, args.steps or 5)
+        return
+    if args.gpus != 1:
+        print(json.dumps({"error": "libspecverify runs the verify step on one GPU; "
+                                   "--gpus must be 1", "n_gpus": args.gpus}))
+        sys.exit(2)
+    import torch
+
+    import workloads
+    warmup = args.warmup if args.warmup is not None else 10
+
+    def steps_of(cfg):
+        if cfg.steps > 1:
+            return cfg.steps
+        return args.steps if args.steps is not None else 200
+
+    def graph_of(cfg):
+        # short independent steps measured faster replayed from one graph
+        # (batch 1, same box, alternating: 118.0 -> 113.4 us; the batch-1
+        # draft loop 434.6 -> 434.0 us); long chained steps measured faster
+        # with eager launches (graph nodes add about 1 us per kernel there)
+        return args.graph or (cfg.steps == 1 and not args.eager)
+
+    if args.draft_loop:
+        cfg = workloads.get_config(args.config or HEADLINE)
+        steps = args.steps if args.steps is not None else (cfg.steps if cfg.steps > 1 else 200)
+        graph = graph_of(cfg)
+        r = run_draft_loop(cfg, steps, warmup, graph=graph)
+        print(json.dumps({
+            "metric": METRIC, "value": r["tok_s"], "unit": "tokens/s", "n_gpus": 1,
+            "steps": steps, "warmup": warmup, "ms_per_step": r["ms_per_step"],
+            "us_per_step": r["ms_per_step"] * 1e3, "higher_is_better": True, "scaling": "weak",
+            "vs_baseline": None, "dtype": "bf16" if cfg.wdtype == "bf16" else cfg.wdtype,
+            "data": "synthetic (seeded random target and draft-head weights)",
+            "config": {"workload": cfg.name, "batch": cfg.batch, "k_draft": cfg.k_draft,
+                       "mode": "FastMTP draft -> verify loop", "tokens_per_verify": r["tau"],
+                       "launch": "one HIP graph of all timed iterations" if graph else "eager"},
+            "draft_us_per_step": r["draft_ms"] * 1e3}), flush=True)
+        return
+
+    names = [args.config] if args.config else list(MULTI)
+    blocks, head = {}, None
+    for name in names:
+        cfg = workloads.get_config(name)
+        steps, graph = steps_of(cfg), graph_of(cfg)
+        r = run_bench(cfg, steps, warmup, sampled=args.sampled, kv_page=args.kv_page, graph=graph)
+        blk = block(cfg, r, steps, graph, args.sampled, args.kv_page)
+        log(f"[bench] {name}: {blk['us_per_step']:.1f} us/step, "
+            f"{blk['accepted_tok_s']:.0f} tok/s, tau {blk['tokens_per_verify']:.3f}")
+        if not args.no_cpu_baseline and not args.sampled:
+            log(f"[bench] timing the CPU oracle on {name}")
+            blk["cpu_baseline"] = cpu_baseline(cfg, 15.0 if name == names[0] else 8.0,
+                                               weights=r["weights"])
+        if head is None:
+            head = _line(cfg, r, steps, warmup, graph, args, blk)
+            if "cpu_baseline" in blk:
+                head["cpu_baseline"] = blk["cpu_baseline"]
+        blocks[str(cfg.batch) if not args.config else cfg.name] = blk
+        del r
+        torch.cuda.empty_cache()
+    if not args.config:
+        head["batches"] = blocks
+    print(json.dumps(head), flush=True)
 
 
 if __name__ == "__main__":

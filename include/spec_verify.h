@@ -278,6 +278,15 @@ int spec_verify_set_debug(spec_verify_ctx* ctx, float* logits, float* hidden,
                           int32_t* target_tok, int32_t* routing);
 
 /*
+ * Router debug output for the following steps (MoE models; NULL turns it
+ * off): router_logits [L][batch (K+1)][E] fp32, the router's logits W_r h of
+ * every position and layer (fp8 row scale applied) -- the values the top-k
+ * selection of the jina-ocr-v1 tweet digest's "64 routed experts, top-6"
+ * router is taken on.  SV_ERR_UNSUPPORTED for a dense model.
+ */
+int spec_verify_set_debug_router(spec_verify_ctx* ctx, float* router_logits);
+
+/*
  * Acceptance and commit alone, from given fp32 logits [batch][K+1][V]
  * (device): argmax per position (lowest index on ties, NaN -> error) and the
  * same acceptance / commit as spec_verify_step.  target_tok may be NULL.

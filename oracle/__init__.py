@@ -21,7 +21,11 @@ import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "oracle.c")
-_LIB = os.path.join(_HERE, "liboracle.so")
+# ORACLE_SANITIZE=1 loads a build instrumented with AddressSanitizer and
+# UndefinedBehaviorSanitizer (host code only; run Python with the ASan runtime
+# preloaded, see build())
+_SANITIZE = os.environ.get("ORACLE_SANITIZE", "") == "1"
+_LIB = os.path.join(_HERE, "liboracle_san.so" if _SANITIZE else "liboracle.so")
 
 F32, BF16, FP8, MXFP4 = 0, 1, 2, 3
 _DT = {"f32": F32, "bf16": BF16, "fp8": FP8, "mxfp4": MXFP4}
@@ -33,9 +37,15 @@ BAD_TOKEN, CAPACITY, NAN_LOGIT = 1, 2, 4
 
 def build(force: bool = True) -> str:
     """Compile oracle.c into liboracle.so next to it (gcc, OpenMP, no
-    fast-math, no floating-point contraction)."""
+    fast-math, no floating-point contraction).  With ORACLE_SANITIZE=1 the
+    library is liboracle_san.so, built with -fsanitize=address,undefined
+    (aborting on the first report); load it with the ASan runtime preloaded:
+      ORACLE_SANITIZE=1 ASAN_OPTIONS=detect_leaks=0 \
+      LD_PRELOAD=$(gcc -print-file-name=libasan.so) python -m pytest tests/test_oracle_pins.py"""
     if force or not os.path.exists(_LIB):
-        cmd = ["gcc", "-O2", "-ffp-contract=off", "-fno-fast-math", "-fopenmp", "-shared",
+        san = ["-fsanitize=address,undefined", "-fno-sanitize-recover=all",
+               "-fno-omit-frame-pointer", "-g"] if _SANITIZE else []
+        cmd = ["gcc", "-O2", "-ffp-contract=off", "-fno-fast-math", "-fopenmp", *san, "-shared",
                "-fPIC", _SRC, "-o", _LIB + ".tmp", "-lm"]
         subprocess.run(cmd, check=True)
         os.replace(_LIB + ".tmp", _LIB)

@@ -36,7 +36,8 @@ EXPORTS = ("spec_verify_init", "spec_verify_destroy", "spec_verify_step", "spec_
            "spec_verify_last_error", "spec_verify_status_string", "spec_verify_abi_version",
            "spec_verify_pack_tiled16", "spec_verify_tiled16_bytes", "spec_verify_step_sampled",
            "spec_verify_sample_from_logits", "spec_verify_pack_mx_scales",
-           "spec_verify_mx_scales_bytes", "spec_draft_step", "spec_verify_set_kv_pages")
+           "spec_verify_mx_scales_bytes", "spec_draft_step", "spec_verify_set_kv_pages",
+           "spec_verify_set_debug_router")
 
 
 class SpecVerifyConfig(ctypes.Structure):
@@ -91,6 +92,7 @@ def load_library() -> ctypes.CDLL:
         lib.spec_verify_destroy.restype = None
         lib.spec_verify_step.argtypes = [P, P, P, P, P, P, P, P, c_int, P, P, P]
         lib.spec_verify_set_debug.argtypes = [P, P, P, P, P]
+        lib.spec_verify_set_debug_router.argtypes = [P, P]
         lib.spec_verify_accept_from_logits.argtypes = [P, P, P, P, P, c_int, P, P, P, P]
         U64, U32 = ctypes.c_uint64, ctypes.c_uint32
         lib.spec_verify_step_sampled.argtypes = [P, P, P, P, P, P, P, P, c_float, U64, U32, P, P,
@@ -302,6 +304,11 @@ def spec_verify_set_debug(ctx: int, logits=None, hidden=None, target_tok=None,
                                                 _p(routing)), "spec_verify_set_debug")
 
 
+def spec_verify_set_debug_router(ctx: int, router_logits=None) -> None:
+    _check(load_library().spec_verify_set_debug_router(ctx, _p(router_logits)),
+           "spec_verify_set_debug_router")
+
+
 def spec_verify_set_kv_pages(ctx: int, table) -> None:
     _check(load_library().spec_verify_set_kv_pages(ctx, _p(table)), "spec_verify_set_kv_pages")
 
@@ -446,6 +453,10 @@ class VerifyContext:
     def set_debug(self, logits=None, hidden=None, target_tok=None, routing=None):
         self._dbg = (logits, hidden, target_tok, routing)
         spec_verify_set_debug(self.handle, logits, hidden, target_tok, routing)
+
+    def set_debug_router(self, router_logits=None):
+        self._dbg_router = router_logits
+        spec_verify_set_debug_router(self.handle, router_logits)
 
     def accept_from_logits(self, logits, drafts, ctx_in, ctx_out, accepted, next_tok,
                            target_tok=None, stream=None):

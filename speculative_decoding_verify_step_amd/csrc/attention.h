@@ -163,6 +163,27 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(1, STREAM ? 
         uint4 vf[DF];
 #pragma unroll
         for (int d = 0; d < DF; d++) vf[d] = kvload(kt_v + (size_t)d * 1024);
+        if (kt + KT > total) {
+            // the last tile reaches past the newest written position: those
+            // slots were never written (or hold an older step's data) and may
+            // be any bit pattern.  Their probabilities are 0, but 0 * NaN or
+            // 0 * Inf in the product would still poison the row, so their
+            // values are cleared (lane group lg holds keys kt + KL lg + e)
+            const int nv = total - (kt + KL * lg);
+            uint32_t m[4];
+#pragma unroll
+            for (int w = 0; w < 4; w++) {
+                if constexpr (BF) m[w] = (2 * w < nv ? 0xffffu : 0u) | (2 * w + 1 < nv ? 0xffff0000u : 0u);
+                else m[w] = w < nv ? 0xffffffffu : 0u;
+            }
+#pragma unroll
+            for (int d = 0; d < DF; d++) {
+                vf[d].x &= m[0];
+                vf[d].y &= m[1];
+                vf[d].z &= m[2];
+                vf[d].w &= m[3];
+            }
+        }
 #pragma unroll
         for (int f = 0; f < QPW; f++) {
             float s[KL];

@@ -62,6 +62,7 @@ struct RowArgs {
     int* sel;                   // [T][topk] out
     float* gate_out;            // [T][topk] out
     int* dbg_sel;               // optional copy of sel
+    float* dbg_rlogits;         // optional [T][E] copy of the router logits (ROUTE)
     // the router's experts shared out over S workgroups per row
     int S;
     float* logits_g;            // [T][E] router logits (S > 1)
@@ -515,6 +516,8 @@ __global__ __launch_bounds__(1024) void residual_norm_kernel(RowArgs a)
         __syncthreads();
         router_logits<UPW>(a, xs, wv, ebeg, eend, logit);
         __syncthreads();
+        if (a.dbg_rlogits && tid >= 64 && tid - 64 < eend - ebeg)
+            a.dbg_rlogits[(size_t)t * a.E + ebeg + tid - 64] = logit[ebeg + tid - 64];
         if (tid < 64) {
             const int lane = tid, E = a.E;
             if (a.S > 1) {

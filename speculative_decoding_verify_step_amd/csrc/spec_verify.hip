@@ -24,6 +24,7 @@
 #include <cstring>
 #include <mutex>
 #include <string>
+#include <type_traits>
 #include <vector>
 
 #include "attention.h"
@@ -134,6 +135,7 @@ struct spec_verify_ctx {
     float* dbg_hidden = nullptr;
     int* dbg_target = nullptr;
     int* dbg_routing = nullptr;
+    float* dbg_rlogits = nullptr;
     // kernel timing
     int prof_class = -1;
     std::vector<EventPair> prof_events;
@@ -608,6 +610,140 @@ int launch_sampling(spec_verify_ctx* c, const SampleIn& smp, const float* logits
     return SV_OK;
 }
 
+// The current device, which must be a gfx950.
+int check_device(int* dev)
+{
+    int ndev = 0;
+    if (hipGetDeviceCount(&ndev) != hipSuccess || ndev < 1)
+        return fail(SV_ERR_NO_DEVICE, "no HIP device visible");
+    HIP_TRY(hipGetDevice(dev));
+    hipDeviceProp_t prop;
+    HIP_TRY(hipGetDeviceProperties(&prop, *dev));
+    if (strncmp(prop.gcnArchName, "gfx950", 6) != 0)
+        return fail(SV_ERR_NO_DEVICE, std::string("device is ") + prop.gcnArchName + ", not gfx950");
+    return SV_OK;
+}
+
+// Shapes and the attention plan of a context for `cfg` (no memory).
+int plan_context(spec_verify_ctx* c, const spec_verify_config& cfg, int dev)
+{
+    c->c = cfg;
+    c->device = dev;
+    const spec_verify_config& k = c->c;
+    c->K1 = k.k_draft + 1;
+    c->T_max = k.max_batch * c->K1;
+    c->QD = k.n_q_heads * k.head_dim;
+    c->QKV = (k.n_q_heads + 2 * k.n_kv_heads) * k.head_dim;
+    c->bf = k.weight_dtype != SV_F32;
+    // attention plan: rows per KV head and chunking
+    int G = k.n_q_heads / k.n_kv_heads;
+    int R = c->K1 * G;
+    int QF = cdiv(R, 16);
+    // more query fragments per wave reuse each loaded K/V tile more often:
+    // dense GQA verify (128 rows per KV head) 78 -> 62 us per layer with four
+    c->att_QPW = QF >= 4 ? 4 : (QF >= 2 ? 2 : 1);
+    c->att_QG = cdiv(QF, c->att_QPW);
+    {
+        long work = (long)k.max_batch * k.n_kv_heads * c->att_QG * k.kv_capacity;
+        int ch = 64;
+        const long waves_target = c->att_QPW >= 4 ? 2048 : 2 * 2048;   // busier waves: fewer of them
+        while (ch < 1024 && work / ch > waves_target) ch *= 2;
+        c->att_CH = ch;
+        c->att_maxch = cdiv(k.kv_capacity, ch);
+        // streaming K/V loads only when every tile has one reader (one query
+        // group per KV head) and the caches are far larger than the 256 MB
+        // Infinity Cache; a smaller cache stays resident from step to step
+        const double kv_bytes = 2.0 * k.max_batch * k.n_layers * k.n_kv_heads * (double)k.kv_capacity *
+                                k.head_dim * (k.kv_dtype == SV_F32 ? 4 : 2);
+        c->att_stream = c->att_QG == 1 && kv_bytes > 1024.0 * 1024 * 1024;
+        if (c->att_maxch > ATT_MAXCH_CAP)
+            return fail(SV_ERR_UNSUPPORTED, "kv_capacity too large for the attention plan");
+    }
+
+    return SV_OK;
+}
+
+// The workspace of a context for up to B sequences, taken piece by piece
+// from `take(bytes)` (nullptr: out of memory).  `extras`: also the buffers of
+// sampled verification and of FastMTP drafting.
+template <class Take>
+int carve_workspace(spec_verify_ctx* c, int B, bool extras, Take take)
+{
+    const spec_verify_config& k = c->c;
+    const int T = B * c->K1, H = k.hidden;
+    const size_t AES = c->bf ? 2 : 4;
+    int E = k.n_experts, tk = k.top_k, S = k.n_shared;
+    long moe_rows = (long)T * tk + (long)S * T;
+    int NT_lm = cdiv(k.vocab, 64);
+    int NT_lg = cdiv(k.vocab, 1024);
+    size_t part_cols = std::max<size_t>({(size_t)c->QKV, (size_t)H, (size_t)(E > 0 ? E : 1)});
+    c->parts_elems = (size_t)KS_MAX * T * part_cols;
+    c->keys_elems = (size_t)std::max(NT_lm, NT_lg) * T;
+    bool ok = true;
+    auto get = [&](auto*& p, size_t elems) {
+        using E_ = std::remove_reference_t<decltype(*p)>;
+        void* v = ok ? take(std::max<size_t>(elems * sizeof(E_), 1)) : nullptr;
+        ok = ok && v;
+        p = (E_*)v;
+    };
+    char* hbuf = nullptr;
+    char* qbuf = nullptr;
+    char* obuf = nullptr;
+    get(c->x, (size_t)T * H);
+    get(c->x2, (size_t)T * H);
+    get(hbuf, (size_t)T * H * AES);
+    c->h = hbuf;
+    get(c->parts, c->parts_elems);
+    get(qbuf, (size_t)T * c->QD * AES);
+    c->q = qbuf;
+    get(obuf, (size_t)T * c->QD * AES);
+    c->o = obuf;
+    size_t prow = (size_t)B * k.n_q_heads * c->K1 * c->att_maxch;
+    get(c->opart, prow * k.head_dim);
+    get(c->mlpart, prow * 2);
+    get(c->rope, (size_t)k.kv_capacity * (k.head_dim / 2));
+    get(c->keys, c->keys_elems);
+    get(c->seq_err, (size_t)B);
+    get(c->err_word, 1);
+    if (extras) {
+        char* dc = nullptr;
+        char* ds = nullptr;
+        get(dc, (size_t)T * 2 * H * AES);
+        c->dcat = dc;
+        get(c->dzero, (size_t)T * H);
+        get(c->dpos, (size_t)B);
+        get(ds, (size_t)B * H * AES);
+        c->dstate = ds;
+        if (k.vocab <= SAMPLE_MAX_TILES * SAMPLE_TILE) {
+            c->s_ntile = cdiv(k.vocab, SAMPLE_TILE);
+            get(c->slogits, (size_t)T * k.vocab);
+            get(c->sstats, (size_t)T * c->s_ntile);
+            get(c->sdkeys, (size_t)B * c->s_ntile);
+            get(c->sfkeys, (size_t)B * c->s_ntile);
+            get(c->sdecision, (size_t)B);
+        }
+    }
+    if (k.ffn_kind == SV_FFN_MOE) {
+        char* abuf = nullptr;
+        get(c->logits_g, (size_t)T * E);
+        get(c->sel, (size_t)T * tk);
+        get(c->gate, (size_t)T * tk);
+        get(c->slot, (size_t)T * tk);
+        get(c->perm_tok, (size_t)moe_rows);
+        get(c->tiles, (size_t)3 * (E + moe_rows + 8));
+        get(c->n_tiles, 1);
+        get(abuf, (size_t)moe_rows * k.expert_inter * AES);
+        c->act = abuf;
+        get(c->y, (size_t)moe_rows * H);
+    } else {
+        char* abuf = nullptr;
+        get(abuf, (size_t)T * k.dense_inter * AES);
+        c->act = abuf;
+    }
+    if (!ok) return fail(SV_ERR_HIP, "workspace allocation failed");
+    return SV_OK;
+}
+
 }  // namespace
 
 // ====================================================================== ABI
@@ -657,123 +793,27 @@ int spec_verify_init(const spec_verify_config* cfg, spec_verify_ctx** out)
     *out = nullptr;
     int rc = validate_config(*cfg);
     if (rc) return rc;
-    int ndev = 0;
-    if (hipGetDeviceCount(&ndev) != hipSuccess || ndev < 1)
-        return fail(SV_ERR_NO_DEVICE, "no HIP device visible");
     int dev = 0;
-    HIP_TRY(hipGetDevice(&dev));
-    hipDeviceProp_t prop;
-    HIP_TRY(hipGetDeviceProperties(&prop, dev));
-    if (strncmp(prop.gcnArchName, "gfx950", 6) != 0)
-        return fail(SV_ERR_NO_DEVICE, std::string("device is ") + prop.gcnArchName + ", not gfx950");
+    rc = check_device(&dev);
+    if (rc) return rc;
 
     spec_verify_ctx* c = new spec_verify_ctx();
-    c->c = *cfg;
-    c->device = dev;
+    rc = plan_context(c, *cfg, dev);
+    if (rc) {
+        delete c;
+        return rc;
+    }
+    rc = carve_workspace(c, cfg->max_batch, true, [c](size_t bytes) -> void* {
+        void* v = nullptr;
+        if (hipMalloc(&v, std::max<size_t>(bytes, 256)) != hipSuccess) return nullptr;
+        c->allocs.push_back(v);
+        return v;
+    });
+    if (rc) {
+        spec_verify_destroy(c);
+        return rc;
+    }
     const spec_verify_config& k = c->c;
-    c->K1 = k.k_draft + 1;
-    c->T_max = k.max_batch * c->K1;
-    c->QD = k.n_q_heads * k.head_dim;
-    c->QKV = (k.n_q_heads + 2 * k.n_kv_heads) * k.head_dim;
-    c->bf = k.weight_dtype != SV_F32;
-    const int T = c->T_max, H = k.hidden;
-    const size_t AES = c->bf ? 2 : 4;
-
-    // attention plan: rows per KV head and chunking
-    int G = k.n_q_heads / k.n_kv_heads;
-    int R = c->K1 * G;
-    int QF = cdiv(R, 16);
-    // more query fragments per wave reuse each loaded K/V tile more often:
-    // dense GQA verify (128 rows per KV head) 78 -> 62 us per layer with four
-    c->att_QPW = QF >= 4 ? 4 : (QF >= 2 ? 2 : 1);
-    c->att_QG = cdiv(QF, c->att_QPW);
-    {
-        long work = (long)k.max_batch * k.n_kv_heads * c->att_QG * k.kv_capacity;
-        int ch = 64;
-        const long waves_target = c->att_QPW >= 4 ? 2048 : 2 * 2048;   // busier waves: fewer of them
-        while (ch < 1024 && work / ch > waves_target) ch *= 2;
-        c->att_CH = ch;
-        c->att_maxch = cdiv(k.kv_capacity, ch);
-        // streaming K/V loads only when every tile has one reader (one query
-        // group per KV head) and the caches are far larger than the 256 MB
-        // Infinity Cache; a smaller cache stays resident from step to step
-        const double kv_bytes = 2.0 * k.max_batch * k.n_layers * k.n_kv_heads * (double)k.kv_capacity *
-                                k.head_dim * (k.kv_dtype == SV_F32 ? 4 : 2);
-        c->att_stream = c->att_QG == 1 && kv_bytes > 1024.0 * 1024 * 1024;
-        if (c->att_maxch > ATT_MAXCH_CAP) {
-            delete c;
-            return fail(SV_ERR_UNSUPPORTED, "kv_capacity too large for the attention plan");
-        }
-    }
-
-    int E = k.n_experts, tk = k.top_k, S = k.n_shared;
-    long moe_rows = (long)T * tk + (long)S * T;
-    int NT_lm = cdiv(k.vocab, 64);
-    int NT_lg = cdiv(k.vocab, 1024);
-    size_t part_cols = std::max<size_t>({(size_t)c->QKV, (size_t)H, (size_t)(E > 0 ? E : 1)});
-    c->parts_elems = (size_t)KS_MAX * T * part_cols;
-    c->keys_elems = (size_t)std::max(NT_lm, NT_lg) * T;
-
-#define ALLOC(p, n)                                           \
-    do {                                                      \
-        int r_ = dalloc(c, &(p), (n));                        \
-        if (r_) { spec_verify_destroy(c); return r_; }        \
-    } while (0)
-    char* hbuf = nullptr;
-    char* qbuf = nullptr;
-    char* obuf = nullptr;
-    ALLOC(c->x, (size_t)T * H);
-    ALLOC(c->x2, (size_t)T * H);
-    ALLOC(hbuf, (size_t)T * H * AES);
-    c->h = hbuf;
-    ALLOC(c->parts, c->parts_elems);
-    ALLOC(qbuf, (size_t)T * c->QD * AES);
-    c->q = qbuf;
-    ALLOC(obuf, (size_t)T * c->QD * AES);
-    c->o = obuf;
-    size_t prow = (size_t)k.max_batch * k.n_q_heads * c->K1 * c->att_maxch;
-    ALLOC(c->opart, prow * k.head_dim);
-    ALLOC(c->mlpart, prow * 2);
-    ALLOC(c->rope, (size_t)k.kv_capacity * (k.head_dim / 2));
-    ALLOC(c->keys, c->keys_elems);
-    ALLOC(c->seq_err, (size_t)k.max_batch);
-    ALLOC(c->err_word, 1);
-    {
-        char* dc = nullptr;
-        char* ds = nullptr;
-        ALLOC(dc, (size_t)T * 2 * H * AES);
-        c->dcat = dc;
-        ALLOC(c->dzero, (size_t)T * H);
-        ALLOC(c->dpos, (size_t)k.max_batch);
-        ALLOC(ds, (size_t)k.max_batch * H * AES);
-        c->dstate = ds;
-    }
-    if (k.vocab <= SAMPLE_MAX_TILES * SAMPLE_TILE) {
-        c->s_ntile = cdiv(k.vocab, SAMPLE_TILE);
-        ALLOC(c->slogits, (size_t)T * k.vocab);
-        ALLOC(c->sstats, (size_t)T * c->s_ntile);
-        ALLOC(c->sdkeys, (size_t)k.max_batch * c->s_ntile);
-        ALLOC(c->sfkeys, (size_t)k.max_batch * c->s_ntile);
-        ALLOC(c->sdecision, (size_t)k.max_batch);
-    }
-    if (k.ffn_kind == SV_FFN_MOE) {
-        char* abuf = nullptr;
-        ALLOC(c->logits_g, (size_t)T * E);
-        ALLOC(c->sel, (size_t)T * tk);
-        ALLOC(c->gate, (size_t)T * tk);
-        ALLOC(c->slot, (size_t)T * tk);
-        ALLOC(c->perm_tok, (size_t)moe_rows);
-        ALLOC(c->tiles, (size_t)3 * (E + moe_rows + 8));
-        ALLOC(c->n_tiles, 1);
-        ALLOC(abuf, (size_t)moe_rows * k.expert_inter * AES);
-        c->act = abuf;
-        ALLOC(c->y, (size_t)moe_rows * H);
-    } else {
-        char* abuf = nullptr;
-        ALLOC(abuf, (size_t)T * k.dense_inter * AES);
-        c->act = abuf;
-    }
-#undef ALLOC
     // rotary table: angle pos * theta^(-2i/D) in double, stored as fp32 (cos, sin)
     {
         int half = k.head_dim / 2;
@@ -791,7 +831,7 @@ int spec_verify_init(const spec_verify_config* cfg, spec_verify_ctx** out)
         }
     }
     hipError_t e = hipMemset(c->err_word, 0, sizeof(unsigned));
-    if (e == hipSuccess) e = hipMemset(c->dzero, 0, (size_t)T * H * sizeof(float));
+    if (e == hipSuccess) e = hipMemset(c->dzero, 0, (size_t)c->T_max * k.hidden * sizeof(float));
     if (e != hipSuccess) {
         spec_verify_destroy(c);
         return fail(SV_ERR_HIP, std::string("workspace reset: ") + hipGetErrorString(e));
@@ -817,6 +857,15 @@ int spec_verify_set_debug(spec_verify_ctx* c, float* logits, float* hidden, int3
     c->dbg_hidden = hidden;
     c->dbg_target = target;
     c->dbg_routing = routing;
+    return SV_OK;
+}
+
+int spec_verify_set_debug_router(spec_verify_ctx* c, float* router_logits)
+{
+    if (!c) return fail(SV_ERR_INVALID_ARG, "null context");
+    if (router_logits && c->c.ffn_kind != SV_FFN_MOE)
+        return fail(SV_ERR_UNSUPPORTED, "router logits exist for MoE models only");
+    c->dbg_rlogits = router_logits;
     return SV_OK;
 }
 
@@ -1110,6 +1159,7 @@ static int step_impl(spec_verify_ctx* c, const spec_verify_weights* w, void* k_c
             ra.sel = c->sel;
             ra.gate_out = c->gate;
             ra.dbg_sel = c->dbg_routing ? c->dbg_routing + (size_t)l * T * k.top_k : nullptr;
+            ra.dbg_rlogits = c->dbg_rlogits ? c->dbg_rlogits + (size_t)l * T * E : nullptr;
             ra.S = S;
             ra.logits_g = c->logits_g;
             ra.BM = BMe;

@@ -9,17 +9,25 @@ weights, 1e-4 for the fp32 workload):
   * residual stream after every layer: the same rule against the oracle
     vector's own range;
   * greedy token: bit-exact at every position whose oracle top-2 margin (in
-    fp32) exceeds tol * range;
+    fp32) exceeds tol * range (the stated-tolerance rule), and also at every
+    position whose margin exceeds twice the largest logit error measured at
+    that position (the measured-error rule: with every GPU logit within e of
+    the oracle's, a margin above 2e cannot flip the argmax, since the GPU's
+    argmax is taken on exactly the logits it reports);
   * accepted length, bonus token, new context length: bit-exact for every
-    sequence whose deciding positions 0 .. min(a, K) all pass the margin test;
+    sequence whose deciding positions 0 .. min(a, K) all qualify, under each
+    rule;
   * new cache entries: within tol of the oracle's range at every written slot;
-  * expert routing (MoE): the oracle is run with the GPU's routing forced, so
-    both sides follow one trajectory; the GPU's choice must equal the oracle's
-    own top-k wherever the k-th / (k+1)-th router-logit gap exceeds
-    tol * (range of the router logits), and elsewhere every expert it chose
-    must lie within that band of the oracle's k-th logit.  A near-tie in the
-    router is a decision on which both choices are correct to the precision
-    of the arithmetic (bf16 activations), so only the band is checked there.
+  * expert routing (MoE): the GPU reports its router logits; (1) they must lie
+    within ROUTER_TOL * (range of the oracle's router logits) of the oracle's,
+    element by element; (2) the GPU's experts must be the top-k of its own
+    logits; (3) the oracle is then run with the GPU's routing forced, so both
+    sides follow one trajectory, and wherever the GPU's choice differs from
+    the oracle's own top-k, the oracle-logit gap between the oracle's k-th
+    expert and the GPU's weakest one must be at most twice the router-logit
+    error measured on that row -- the only way two experts' order can swap
+    when every logit is off by at most that error.  The number of such forced
+    decisions is counted and capped per test.
 """
 from __future__ import annotations
 
@@ -33,6 +41,10 @@ import speculative_decoding_verify_step_amd as sv
 import workloads
 
 TOL = {"f32": 1e-4, "bf16": 2e-2, "fp8": 5e-2}
+# element-wise bound on the router logits, relative to the row's oracle range
+ROUTER_TOL = dict(TOL)
+# forced routing decisions allowed per test: a fraction of all decisions + 2
+FORCED_CAP = 0.10
 
 
 def say(*a):
@@ -108,7 +120,11 @@ class GpuRun:
         self.target = torch.full((self.B, K1), -7, dtype=torch.int32, device=dev)
         self.routing = (torch.full((cfg.n_layers, T, cfg.top_k), -1, dtype=torch.int32, device=dev)
                         if cfg.ffn == "moe" else None)
+        self.rlogits = (torch.full((cfg.n_layers, T, cfg.n_experts), float("nan"), device=dev)
+                        if cfg.ffn == "moe" else None)
         self.ctx.set_debug(self.logits, self.hidden, self.target, self.routing)
+        if self.rlogits is not None:
+            self.ctx.set_debug_router(self.rlogits)
         self.acc = torch.full((self.B,), -9, dtype=torch.int32, device=dev)
         self.nxt = torch.full((self.B,), -9, dtype=torch.int32, device=dev)
         self.ctx_out = torch.full((self.B,), -9, dtype=torch.int32, device=dev)
@@ -125,7 +141,8 @@ class GpuRun:
                 "ctx_out": co.cpu().numpy(), "target": self.target.cpu().numpy(),
                 "logits": None if self.logits is None else self.logits.cpu().numpy(),
                 "hidden": None if self.hidden is None else self.hidden.cpu().numpy(),
-                "routing": None if self.routing is None else self.routing.cpu().numpy()}
+                "routing": None if self.routing is None else self.routing.cpu().numpy(),
+                "rlogits": None if self.rlogits is None else self.rlogits.cpu().numpy()}
 
     def routing_of(self, g: dict, b: int):
         """The GPU's expert choice for sequence b as [1][L][K+1][top_k] (MoE)."""
@@ -133,6 +150,13 @@ class GpuRun:
             return None
         K1 = self.case.cfg.k_draft + 1
         return g["routing"][:, b * K1:(b + 1) * K1][None]
+
+    def rlogits_of(self, g: dict, b: int):
+        """The GPU's router logits for sequence b as [L][K+1][E] (MoE)."""
+        if g.get("rlogits") is None:
+            return None
+        K1 = self.case.cfg.k_draft + 1
+        return g["rlogits"][:, b * K1:(b + 1) * K1]
 
     def close(self):
         self.ctx.close()
@@ -145,12 +169,22 @@ def margin_ok(lo: np.ndarray, tol: float) -> bool:
     return float(top[1] - top[0]) > tol * rng
 
 
+def margin_measured_ok(lo: np.ndarray, err: float) -> bool:
+    """True when the oracle's top-2 gap exceeds twice the measured logit error
+    (on fp64 values, and still positive after rounding to fp32, where the
+    oracle takes its argmax)."""
+    top = np.partition(lo, -2)[-2:]
+    lf = lo.astype(np.float32)
+    top32 = np.partition(lf, -2)[-2:]
+    return float(top[1] - top[0]) > 2.0 * err * (1.0 + 1e-6) and float(top32[1] - top32[0]) > 0.0
+
+
 def compare_sequence(cfg, g: dict, b: int, o: dict, i: int, stats: dict, check_hidden=True):
     """Compare GPU sequence b with oracle output row i under the rules above."""
     tol = TOL[cfg.wdtype]
     K = cfg.k_draft
     K1 = K + 1
-    qual = []
+    qual, qual_m = [], []
     for j in range(K1):
         lo = o["logits"][i, j]
         lg = g["logits"][b, j].astype(np.float64)
@@ -159,13 +193,17 @@ def compare_sequence(cfg, g: dict, b: int, o: dict, i: int, stats: dict, check_h
         stats["max_rel_logit_err"] = max(stats.get("max_rel_logit_err", 0.0), err / rng)
         assert err <= tol * rng, f"seq {b} pos {j}: logit err {err:.3e} > {tol} * range {rng:.3e}"
         q = margin_ok(lo, tol)
+        qm = margin_measured_ok(lo, err)
         qual.append(q)
+        qual_m.append(qm)
         stats["positions"] = stats.get("positions", 0) + 1
         stats["qualified"] = stats.get("qualified", 0) + int(q)
+        stats["qualified_measured"] = stats.get("qualified_measured", 0) + int(qm)
         same = int(g["target"][b, j]) == int(o["target"][i, j])
         stats["argmax_agree"] = stats.get("argmax_agree", 0) + int(same)
-        if q:
-            assert same, f"seq {b} pos {j}: argmax {g['target'][b, j]} vs {o['target'][i, j]}"
+        if q or qm:
+            assert same, (f"seq {b} pos {j}: argmax {g['target'][b, j]} vs {o['target'][i, j]} "
+                          f"(stated rule {q}, measured rule {qm}, err {err:.3e})")
     if check_hidden and "layer_hidden" in o:
         for l in range(cfg.n_layers):
             for j in range(K1):
@@ -180,8 +218,13 @@ def compare_sequence(cfg, g: dict, b: int, o: dict, i: int, stats: dict, check_h
     stats["sequences"] = stats.get("sequences", 0) + 1
     same_acc = int(g["accepted"][b]) == a_or and int(g["next_tok"][b]) == int(o["next_tok"][i])
     stats["accept_agree"] = stats.get("accept_agree", 0) + int(same_acc)
-    if all(qual[j] for j in deciding):
+    stated = all(qual[j] for j in deciding)
+    measured = all(qual_m[j] for j in deciding)
+    if stated:
         stats["accept_checked"] = stats.get("accept_checked", 0) + 1
+    if measured:
+        stats["accept_checked_measured"] = stats.get("accept_checked_measured", 0) + 1
+    if stated or measured:
         assert int(g["accepted"][b]) == a_or, f"seq {b}: accepted {g['accepted'][b]} vs {a_or}"
         assert int(g["next_tok"][b]) == int(o["next_tok"][i])
         assert int(g["ctx_out"][b]) == int(o["ctx_out"][i])
@@ -206,28 +249,54 @@ def compare_new_kv(cfg, run: GpuRun, b: int, kc_or, vc_or, ctx_b: int, stats: di
         assert err <= tol * rng, f"seq {b}: new {name} cache err {err:.3e} > {tol} * {rng:.3e}"
 
 
-def check_routing(cfg, forced: np.ndarray, o: dict, stats: dict, label=""):
-    """forced [1][L][K+1][k]: the GPU's routing; o: the oracle run with that
-    routing forced (want_routing=True)."""
+def check_routing(cfg, forced: np.ndarray, o: dict, stats: dict, label="", rl_gpu=None):
+    """forced [1][L][K+1][k]: the GPU's routing; rl_gpu [L][K+1][E]: the
+    GPU's router logits; o: the oracle run with that routing forced
+    (want_routing=True)."""
     if forced is None:
         return
-    tol = TOL[cfg.wdtype]
+    assert rl_gpu is not None, "MoE parity needs the GPU's router logits"
+    rtol = ROUTER_TOL[cfg.wdtype]
     rl = o["router_logits"][0]
     L, K1, k = forced.shape[1:]
     for l in range(L):
         for j in range(K1):
             r = rl[l, j]
+            rg = rl_gpu[l, j].astype(np.float64)
             gsel = [int(e) for e in forced[0, l, j]]
             assert len(set(gsel)) == k and min(gsel) >= 0 and max(gsel) < cfg.n_experts, (
                 f"{label} layer {l} pos {j}: invalid routing {gsel}")
-            own = [int(e) for e in oracle.topk(oracle.softmax(r), k)]
+            # (1) router logits element by element
+            rng = float(r.max() - r.min())
+            err = float(np.abs(rg - r).max())
+            stats["max_rel_router_err"] = max(stats.get("max_rel_router_err", 0.0), err / rng)
+            assert err <= rtol * rng, (f"{label} layer {l} pos {j}: router logit err {err:.3e} > "
+                                       f"{rtol} * range {rng:.3e}")
+            # (2) the GPU's experts are the top-k of its own logits, in rank
+            # order (fp32 probabilities may tie logits closer than 1e-5)
+            rest = [e for e in range(cfg.n_experts) if e not in gsel]
+            assert min(rg[gsel]) >= max(rg[rest]) - 1e-5, (
+                f"{label} layer {l} pos {j}: GPU experts {gsel} are not the top-{k} of its logits")
+            assert all(rg[gsel[q]] >= rg[gsel[q + 1]] - 1e-5 for q in range(k - 1)), (
+                f"{label} layer {l} pos {j}: GPU rank order {gsel}")
             stats["routings"] = stats.get("routings", 0) + 1
+            # (3) a choice that differs from the oracle's own is a near-tie
+            # within twice the measured error of this row
+            own = [int(e) for e in oracle.topk(oracle.softmax(r), k)]
             if set(own) == set(gsel):
                 continue
-            band = tol * float(r.max() - r.min())
             kth = min(r[e] for e in own)
             worst = min(r[e] for e in gsel)
-            stats["routing_near_ties"] = stats.get("routing_near_ties", 0) + 1
-            assert worst >= kth - band, (
+            band = 2.0 * err * (1.0 + 1e-6) + 1e-12
+            stats["routing_forced"] = stats.get("routing_forced", 0) + 1
+            assert kth - worst <= band, (
                 f"{label} layer {l} pos {j}: GPU experts {sorted(gsel)} vs oracle {sorted(own)}, "
-                f"logit gap {kth - worst:.4f} > band {band:.4f}")
+                f"oracle-logit gap {kth - worst:.3e} > twice the measured router error {err:.3e}")
+
+
+def assert_forced_cap(stats: dict, label=""):
+    """Forced routing decisions (near-ties) within the cap; printed."""
+    n, f = stats.get("routings", 0), stats.get("routing_forced", 0)
+    say(f"[{label}] routing decisions {n}, forced {f}, "
+        f"max router err {stats.get('max_rel_router_err', 0.0):.2e} of range")
+    assert f <= FORCED_CAP * n + 2, f"{label}: {f} forced routing decisions of {n}"

@@ -1,9 +1,10 @@
 """Paged KV caches (spec_verify_set_kv_pages): the same step on caches split
 into pages of a shuffled pool must give the contiguous step's results bit for
-bit (the kernels only read and write different addresses, in the same order);
-sequences sharing the pages of a common prefix must match unshared copies; a
-page index outside the pool is reported, not followed; and a chain of steps
-captured into one HIP graph replays like the eager chain."""
+bit (the kernels only read and write different addresses, in the same order)
+and must match the oracle on its natural caches under the parity rules;
+sequences sharing the pages of a common prefix must match unshared copies and
+the oracle; a page index outside the pool is reported, not followed; and a
+chain of steps captured into one HIP graph replays like the eager chain."""
 import numpy as np
 import pytest
 import torch
@@ -39,13 +40,47 @@ def _paged_run(H, case, B, page, order, committed, drafts, ctx, n_pool=None):
     ctx_obj.set_kv_pages(table)
     dev = "cuda"
     i32 = dict(dtype=torch.int32, device=dev)
-    logits = torch.full((B, cfg.k_draft + 1, cfg.vocab), float("nan"), device=dev)
-    ctx_obj.set_debug(logits)
+    K1, T = cfg.k_draft + 1, B * (cfg.k_draft + 1)
+    logits = torch.full((B, K1, cfg.vocab), float("nan"), device=dev)
+    target = torch.full((B, K1), -7, **i32)
+    moe = cfg.ffn == "moe"
+    routing = torch.full((cfg.n_layers, T, cfg.top_k), -1, **i32) if moe else None
+    rlogits = torch.full((cfg.n_layers, T, cfg.n_experts), float("nan"), device=dev) if moe else None
+    ctx_obj.set_debug(logits, None, target, routing)
+    if moe:
+        ctx_obj.set_debug_router(rlogits)
     acc, nxt, co = (torch.full((B,), -9, **i32) for _ in range(3))
     ctx_obj.step(kp, vp, committed.to(**i32), drafts.to(**i32).contiguous(), ctx.to(**i32), co,
                  acc, nxt)
     torch.cuda.synchronize()
-    return ctx_obj, kp, vp, table, acc.cpu(), nxt.cpu(), co.cpu(), logits.cpu()
+    gd = {"accepted": acc.cpu().numpy(), "next_tok": nxt.cpu().numpy(), "ctx_out": co.cpu().numpy(),
+          "target": target.cpu().numpy(), "logits": logits.cpu().numpy(), "hidden": None,
+          "routing": routing.cpu().numpy() if moe else None,
+          "rlogits": rlogits.cpu().numpy() if moe else None}
+    return ctx_obj, kp, vp, table, acc.cpu(), nxt.cpu(), co.cpu(), logits.cpu(), gd
+
+
+def _oracle_check(H, case, gd, seqs, committed, drafts, ctx, label):
+    """The paged run's sequences `seqs` against the oracle on the natural
+    caches (the parity rules of gpu_harness; the oracle follows the GPU's
+    routing where it is a measured near-tie)."""
+    cfg = case.cfg
+    K1 = cfg.k_draft + 1
+    orc = case.oracle()
+    stats = {}
+    for b in seqs:
+        kc, vc = case.oracle_kv(b)
+        forced = gd["routing"][:, b * K1:(b + 1) * K1][None] if gd["routing"] is not None else None
+        o = orc.verify_step(kc, vc, [int(committed[b])], drafts[b:b + 1].numpy(), [int(ctx[b])],
+                            want_logits=True, force_sel=forced, want_routing=forced is not None)
+        if forced is not None:
+            H.check_routing(cfg, forced, o, stats, label=f"{label} seq {b}",
+                            rl_gpu=gd["rlogits"][:, b * K1:(b + 1) * K1])
+        H.compare_sequence(cfg, gd, b, o, 0, stats, check_hidden=False)
+    H.say(f"[{label}] oracle stats {stats}")
+    if cfg.ffn == "moe":
+        H.assert_forced_cap(stats, label)
+    return stats
 
 
 def _case(H, cfg, page):
@@ -67,16 +102,19 @@ def test_paged_equals_contiguous(H, name, overrides, page):
         workloads.get_config(name)
     case = _case(H, cfg, page)
     B = cfg.batch
-    drafts = case.rtok[0][:B]
+    checked = sorted({0, B - 1})
+    drafts = case.drafts(checked)[:B]       # oracle drafts for the checked sequences
     run = H.GpuRun(case, batch=B)
     g = run.step(case.committed[:B], drafts, case.ctx[:B])
     npg = case.cap // page
     rng = np.random.default_rng(page + B)
     order = rng.permutation(B * npg)
     H.say(f"[paged {cfg.name}] B={B} cap={case.cap} page={page} pool={B * npg}")
-    ctx_obj, kp, vp, table, acc, nxt, co, logits = _paged_run(
+    ctx_obj, kp, vp, table, acc, nxt, co, logits, gd = _paged_run(
         H, case, B, page, order, case.committed[:B], drafts, case.ctx[:B])
     assert ctx_obj.error_word() == 0
+    _oracle_check(H, case, gd, checked, case.committed[:B], drafts, case.ctx[:B],
+                  f"paged {cfg.name} vs oracle")
     assert np.array_equal(acc.numpy(), g["accepted"]) and np.array_equal(nxt.numpy(), g["next_tok"])
     assert np.array_equal(co.numpy(), g["ctx_out"])
     assert torch.equal(logits, torch.from_numpy(g["logits"]))
@@ -144,7 +182,7 @@ def test_paged_prefix_sharing(H):
     for b in range(1, B):   # give every sequence sequence 0's first `pre` positions
         case.k_nat[b, :, :, :pre] = case.k_nat[0, :, :, :pre]
         case.v_nat[b, :, :, :pre] = case.v_nat[0, :, :, :pre]
-    drafts = case.rtok[0][:B]
+    drafts = case.drafts(range(B))[:B]
     run = H.GpuRun(case, batch=B)
     g = run.step(case.committed[:B], drafts, case.ctx[:B])
     npg = case.cap // page
@@ -156,6 +194,13 @@ def test_paged_prefix_sharing(H):
                                kv_pool_pages=B * npg)
     ctx_obj.set_kv_pages(table)
     i32 = dict(dtype=torch.int32, device="cuda")
+    K1, T = cfg.k_draft + 1, B * (cfg.k_draft + 1)
+    logits = torch.full((B, K1, cfg.vocab), float("nan"), device="cuda")
+    target = torch.full((B, K1), -7, **i32)
+    routing = torch.full((cfg.n_layers, T, cfg.top_k), -1, **i32)
+    rlogits = torch.full((cfg.n_layers, T, cfg.n_experts), float("nan"), device="cuda")
+    ctx_obj.set_debug(logits, None, target, routing)
+    ctx_obj.set_debug_router(rlogits)
     acc, nxt, co = (torch.full((B,), -9, **i32) for _ in range(3))
     ctx_obj.step(kp, vp, case.committed[:B].to(**i32), drafts.to(**i32).contiguous(),
                  case.ctx[:B].to(**i32), co, acc, nxt)
@@ -163,6 +208,13 @@ def test_paged_prefix_sharing(H):
     assert ctx_obj.error_word() == 0
     assert np.array_equal(acc.cpu().numpy(), g["accepted"])
     assert np.array_equal(nxt.cpu().numpy(), g["next_tok"])
+    assert torch.equal(logits.cpu(), torch.from_numpy(g["logits"]))
+    gd = {"accepted": acc.cpu().numpy(), "next_tok": nxt.cpu().numpy(), "ctx_out": co.cpu().numpy(),
+          "target": target.cpu().numpy(), "logits": logits.cpu().numpy(), "hidden": None,
+          "routing": routing.cpu().numpy(), "rlogits": rlogits.cpu().numpy()}
+    # every sequence against the oracle on natural caches holding the shared prefix
+    _oracle_check(H, case, gd, range(B), case.committed[:B], drafts, case.ctx[:B],
+                  "paged prefix vs oracle")
     ctx_obj.close()
     run.close()
 

@@ -23,9 +23,28 @@ def H():
     return gpu_harness
 
 
-def _verify_case(H, cfg, sampled=None, batch=None, check_kv=True, label=""):
+def _poison_dead_slots(case, B):
+    """Positions at or past ctx + K + 1 (never written by the step, never read
+    by any query) filled with NaN, +Inf and -Inf in turn."""
+    K1 = case.cfg.k_draft + 1
+    pat = torch.tensor([float("nan"), float("inf"), float("-inf")])
+    for b in range(B):
+        c = int(case.ctx[b]) + K1
+        n = case.cap - c
+        fill = pat.repeat(n // 3 + 1)[:n].to(case.k_nat.dtype).to(case.k_nat.device)
+        case.k_nat[b, :, :, c:] = fill[:, None]
+        case.v_nat[b, :, :, c:] = fill.flip(0)[:, None]
+
+
+def _bits(t):
+    return t.view(torch.int16) if t.element_size() == 2 else t.view(torch.int32)
+
+
+def _verify_case(H, cfg, sampled=None, batch=None, check_kv=True, label="", poison=False):
     case = H.Case(cfg)
     B = cfg.batch if batch is None else batch
+    if poison:
+        _poison_dead_slots(case, B)
     sampled = list(range(B)) if sampled is None else sampled
     H.say(f"[{label}] {cfg.name}: B={B} L={cfg.n_layers} H={cfg.hidden} V={cfg.vocab} "
           f"K={cfg.k_draft} cap={case.cap} ctx={case.ctx[:B].tolist()[:8]} sampled={sampled}")
@@ -41,7 +60,7 @@ def _verify_case(H, cfg, sampled=None, batch=None, check_kv=True, label=""):
         o = orc.verify_step(kc, vc, [int(case.committed[b])], drafts[b:b + 1].numpy(),
                             [int(case.ctx[b])], want_logits=True, want_layer_hidden=True,
                             force_sel=forced, want_routing=forced is not None)
-        H.check_routing(cfg, forced, o, stats, label=f"seq {b}")
+        H.check_routing(cfg, forced, o, stats, label=f"seq {b}", rl_gpu=run.rlogits_of(g, b))
         H.compare_sequence(cfg, g, b, o, 0, stats)
         if check_kv:
             H.compare_new_kv(cfg, run, b, kc, vc, int(case.ctx[b]), stats)
@@ -55,8 +74,11 @@ def _verify_case(H, cfg, sampled=None, batch=None, check_kv=True, label=""):
                                     (case.v_nat[b].clone(), v_after[b].clone(), "V")):
             before[:, :, c:c + K1] = 0
             after[:, :, c:c + K1] = 0
-            assert torch.equal(before, after), f"seq {b}: {name} cache changed outside the new slots"
+            assert torch.equal(_bits(before), _bits(after)), \
+                f"seq {b}: {name} cache changed outside the new slots"
     H.say(f"[{label}] stats {stats}")
+    if cfg.ffn == "moe":
+        H.assert_forced_cap(stats, label)
     run.close()
     return stats, g
 
@@ -123,6 +145,23 @@ def test_dense_fp8_gqa_full_width_sampled(H):
     _verify_case(H, cfg, sampled=[5], label="dense_fp8_wide")
 
 
+@pytest.mark.parametrize("name,overrides", [
+    ("tiny_fp32", {"batch": 3, "ctx": ("uniform", 20, 400)}),
+    ("moe_b32", {"n_layers": 2, "vocab": 4096, "batch": 5, "ctx": ("uniform", 30, 500)}),
+    ("dense_fp8_b8", {"n_layers": 1, "hidden": 512, "n_q": 8, "n_kv": 2, "dense_inter": 1024,
+                      "vocab": 4096, "batch": 2, "k_draft": 7, "ctx": ("uniform", 50, 300)}),
+])
+def test_dead_cache_slots_may_hold_nan_and_inf(H, name, overrides):
+    """Cache slots past the newest position of a sequence are dead (never
+    written by the step, masked for every query) and may hold any bit
+    pattern: filled with NaN / +-Inf, the step still matches the oracle and
+    raises no error."""
+    cfg = workloads.scaled(workloads.get_config(name), **overrides)
+    stats, g = _verify_case(H, cfg, label=f"dead_slots_{name}", poison=True)
+    assert np.all(g["accepted"] >= 0)
+    assert np.all(np.isfinite(g["logits"]))
+
+
 def test_deterministic_reruns(H):
     cfg = workloads.scaled(workloads.get_config("moe_b32"), n_layers=2, vocab=4096, batch=6,
                            ctx=("uniform", 50, 400))
@@ -163,13 +202,15 @@ def test_chained_steps_scaled(H):
             o = orc.verify_step(kc, vc, [int(com[b])], drafts[b:b + 1].numpy(),
                                 [int(ctx_cpu[b])], want_logits=True, force_sel=forced,
                                 want_routing=True)
-            H.check_routing(cfg, forced, o, stats, label=f"step {s} seq {b}")
+            H.check_routing(cfg, forced, o, stats, label=f"step {s} seq {b}",
+                            rl_gpu=run.rlogits_of(g, b))
             H.compare_sequence(cfg, g, b, o, 0, stats, check_hidden=False)
             # continue both chains from the oracle's decision
             com[b] = int(o["next_tok"][0])
             ctx_cpu[b] = int(o["ctx_out"][0])
         ctx_dev.copy_(ctx_cpu.to("cuda", torch.int32))
     H.say(f"[chained] stats {stats}")
+    H.assert_forced_cap(stats, "chained")
     assert stats["accept_agree"] >= 0.9 * stats["sequences"]
     assert int(ctx_cpu.min()) > int(case.ctx.min())
     run.close()

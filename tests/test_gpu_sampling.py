@@ -251,14 +251,15 @@ def test_sampled_step_matches_oracle(H, S, name, overrides):
     o_logits = np.zeros((B, cfg.k_draft + 1, cfg.vocab))
     for b in range(B):
         kc, vc = case.oracle_kv(b)
-        forced = None
+        forced = rlg = None
         if cfg.ffn == "moe":
             K1 = cfg.k_draft + 1
             forced = run.routing.cpu().numpy()[:, b * K1:(b + 1) * K1][None]
+            rlg = run.rlogits.cpu().numpy()[:, b * K1:(b + 1) * K1]
         o = orc.verify_step(kc, vc, [int(case.committed[b])], sd["drafts"][b:b + 1].numpy(),
                             [int(case.ctx[b])], want_logits=True, force_sel=forced,
                             want_routing=forced is not None)
-        H.check_routing(cfg, forced, o, stats, label=f"seq {b}")
+        H.check_routing(cfg, forced, o, stats, label=f"seq {b}", rl_gpu=rlg)
         o_logits[b] = o["logits"][0]
         for j in range(cfg.k_draft + 1):
             lo, lg = o["logits"][0, j], glog[b, j].double().numpy()
@@ -272,6 +273,8 @@ def test_sampled_step_matches_oracle(H, S, name, overrides):
     sure = o["accept_certain"] & o["draw_certain"]
     for b in np.nonzero(sure)[0]:
         assert ga[b] == o["accepted"][b] and gn[b] == o["next_tok"][b]
+    if cfg.ffn == "moe":
+        H.assert_forced_cap(stats, f"sampled step {cfg.name}")
     H.say(f"[sampled step {cfg.name}] oracle-forward check: max logit err {err:.2e}, "
           f"certain {int(sure.sum())}/{B}, agree {int(((ga == o['accepted']) & (gn == o['next_tok'])).sum())}/{B}")
     run.close()
