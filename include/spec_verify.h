@@ -244,6 +244,32 @@ int spec_verify_step(spec_verify_ctx* ctx, const spec_verify_weights* w, void* k
                      int32_t* accepted_len, int32_t* next_tok, void* stream);
 
 /*
+ * The greedy verify step for callers that cannot allocate device memory:
+ * code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc.  It needs no context: it plans the step from `cfg` and takes
+ * its workspace from a static device array of the library (64 MiB, one per
+ * GPU, held until the process ends); it calls no hipMalloc, hipFree or
+ * allocating library routine.
+ *   cfg           the model (as for spec_verify_init; kv_page_size must be 0);
+ *                 max_batch picks the attention plan, as it does for a context,
+ *                 so a context with the same cfg gives the same results
+ *   error_word    device uint32 that receives the SV_DEV_* bits of the call
+ *                 (OR-ed in; the caller clears it), or NULL
+ * Other arguments, outputs and per-sequence errors as in spec_verify_step.
+ * SV_ERR_UNSUPPORTED (nothing launched) when the step's workspace for this
+ * batch exceeds the array, e.g. 12 layers at batch 64 with long contexts.
+ * Every call on a GPU shares that GPU's array: calls that overlap in time on
+ * one GPU race.  Each call rewrites the rotary table and clears its error
+ * word in the array with kernels (no memset), so it may be captured into a
+ * HIP graph; a replay uses the array as the captured launches left it.
+ */
+int spec_verify_step_noalloc(const spec_verify_config* cfg, const spec_verify_weights* w,
+                             void* k_cache, void* v_cache, const int32_t* committed_tok,
+                             const int32_t* draft_toks, const int32_t* ctx_lens_in,
+                             int32_t* ctx_lens_out, int batch, int32_t* accepted_len,
+                             int32_t* next_tok, uint32_t* error_word, void* stream);
+
+/*
  * Paged KV caches (kv_page_size = P > 0).  Defined by: OCRia-1 technical-
  * report digest, third item of its list of things worth copying (the
  * inference stack reuses a shared prompt prefix); "Architecture and

@@ -37,7 +37,7 @@ EXPORTS = ("spec_verify_init", "spec_verify_destroy", "spec_verify_step", "spec_
            "spec_verify_pack_tiled16", "spec_verify_tiled16_bytes", "spec_verify_step_sampled",
            "spec_verify_sample_from_logits", "spec_verify_pack_mx_scales",
            "spec_verify_mx_scales_bytes", "spec_draft_step", "spec_verify_set_kv_pages",
-           "spec_verify_set_debug_router")
+           "spec_verify_set_debug_router", "spec_verify_step_noalloc")
 
 
 class SpecVerifyConfig(ctypes.Structure):
@@ -93,6 +93,7 @@ def load_library() -> ctypes.CDLL:
         lib.spec_verify_step.argtypes = [P, P, P, P, P, P, P, P, c_int, P, P, P]
         lib.spec_verify_set_debug.argtypes = [P, P, P, P, P]
         lib.spec_verify_set_debug_router.argtypes = [P, P]
+        lib.spec_verify_step_noalloc.argtypes = [P, P, P, P, P, P, P, P, c_int, P, P, P, P]
         lib.spec_verify_accept_from_logits.argtypes = [P, P, P, P, P, c_int, P, P, P, P]
         U64, U32 = ctypes.c_uint64, ctypes.c_uint32
         lib.spec_verify_step_sampled.argtypes = [P, P, P, P, P, P, P, P, c_float, U64, U32, P, P,
@@ -296,6 +297,15 @@ def spec_verify_step(ctx: int, weights: SpecVerifyWeights, k_cache, v_cache, com
         ctx, ctypes.byref(weights), _p(k_cache), _p(v_cache), _p(committed_tok), _p(draft_toks),
         _p(ctx_lens_in), _p(ctx_lens_out), int(batch), _p(accepted_len), _p(next_tok),
         _stream(stream)), "spec_verify_step")
+
+
+def spec_verify_step_noalloc(config: SpecVerifyConfig, weights: SpecVerifyWeights, k_cache, v_cache,
+                             committed_tok, draft_toks, ctx_lens_in, ctx_lens_out, batch: int,
+                             accepted_len, next_tok, error_word=None, stream=None) -> None:
+    _check(load_library().spec_verify_step_noalloc(
+        ctypes.byref(config), ctypes.byref(weights), _p(k_cache), _p(v_cache), _p(committed_tok),
+        _p(draft_toks), _p(ctx_lens_in), _p(ctx_lens_out), int(batch), _p(accepted_len),
+        _p(next_tok), _p(error_word), _stream(stream)), "spec_verify_step_noalloc")
 
 
 def spec_verify_set_debug(ctx: int, logits=None, hidden=None, target_tok=None,

@@ -1533,3 +1533,5 @@ int spec_verify_kernel_time(spec_verify_ctx* c, int kclass, int enable, double* 
 }
 
 }  // extern "C"
+
+#include "noalloc.h"
