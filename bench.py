@@ -351,17 +351,19 @@ def run_bench(cfg, steps, warmup, sampled=False, kv_page=0, graph=False, classes
     assert vc.error_word() == 0, "device error during the benchmark"
     # per-step times: an eager pass with events between steps; it must
     # reproduce the timed steps' outcome
-    restore()
-    ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
-    torch.cuda.synchronize()
-    ev[0].record()
-    for i in range(steps):
-        one(i, ctx)
-        ev[i + 1].record()
-    torch.cuda.synchronize()
-    per_step_us = [1e3 * ev[i].elapsed_time(ev[i + 1]) for i in range(steps)]
-    assert torch.equal(ctx, ref[0]) and torch.equal(acc_all[:steps], ref[1]), \
-        "timed and re-run steps disagree"
+    per_step_us = [1e6 * (t1 - t0) / steps] * steps     # without the re-run: the mean
+    if classes:
+        restore()
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+        torch.cuda.synchronize()
+        ev[0].record()
+        for i in range(steps):
+            one(i, ctx)
+            ev[i + 1].record()
+        torch.cuda.synchronize()
+        per_step_us = [1e3 * ev[i].elapsed_time(ev[i + 1]) for i in range(steps)]
+        assert torch.equal(ctx, ref[0]) and torch.equal(acc_all[:steps], ref[1]), \
+            "timed and re-run steps disagree"
     # each kernel class in its own eager pass of the same steps
     for name in (CLASSES if classes else (dom,)):
         if name in ktime:
@@ -705,6 +707,11 @@ def main():
                          "(the default for single-step workloads)")
     ap.add_argument("--eager", action="store_true",
                     help="launch every step from the host (the default for chained workloads)")
+    ap.add_argument("--no-breakdown", action="store_true",
+                    help="skip the untimed re-runs that give p50/p90 and the per-class kernel "
+                         "times (profiler runs)")
+    ap.add_argument("--chain-steps", type=int, default=None, metavar="N",
+                    help="steps of a chained workload (default: the workload's own, 100)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                     help="only run a plain device copy of BYTES (counter calibration)")
     args = ap.parse_args()
@@ -722,7 +729,7 @@ def main():
 
     def steps_of(cfg):
         if cfg.steps > 1:
-            return cfg.steps
+            return args.chain_steps or cfg.steps
         return args.steps if args.steps is not None else 200
 
     def graph_of(cfg):
@@ -754,7 +761,8 @@ def main():
     for name in names:
         cfg = workloads.get_config(name)
         steps, graph = steps_of(cfg), graph_of(cfg)
-        r = run_bench(cfg, steps, warmup, sampled=args.sampled, kv_page=args.kv_page, graph=graph)
+        r = run_bench(cfg, steps, warmup, sampled=args.sampled, kv_page=args.kv_page, graph=graph,
+                      classes=not args.no_breakdown)
         blk = block(cfg, r, steps, graph, args.sampled, args.kv_page)
         log(f"[bench] {name}: {blk['us_per_step']:.1f} us/step, "
             f"{blk['accepted_tok_s']:.0f} tok/s, tau {blk['tokens_per_verify']:.3f}")

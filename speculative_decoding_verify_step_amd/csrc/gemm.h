@@ -66,6 +66,22 @@ struct GemmArgs {
     long dbg_ld;
 };
 
+// Work item (column tile nt, row tile mt) of workgroup `id` among NT x MT
+// items, row tiles fastest.  Workgroup ids are dealt to the 8 XCDs round
+// robin; each XCD takes one contiguous range of equal length of the items, so
+// every XCD streams the same share of the weights (with column tiles dealt
+// out by id modulo 8, NT = 14 gave six XCDs two slabs and two XCDs one), and
+// the row tiles of one column slab stay together on one XCD's L2.  False for
+// a workgroup past the items (the grid is sized for an upper bound).
+SV_DEV bool xcd_item(int id, int NT, int MT, int& nt, int& mt)
+{
+    const int x = id & 7, q = id >> 3, total = NT * MT, per = (total + 7) >> 3, u = x * per + q;
+    if (q >= per || u >= total) return false;
+    nt = u / MT;
+    mt = u % MT;
+    return true;
+}
+
 // per weight storage type: elements per 16-byte lane slice, reduction step
 template <int WT> struct WTraits;
 template <> struct WTraits<SV_F32> { static constexpr int KL = 4, SK = 16, XU = 1, ESZ = 4; };
@@ -286,13 +302,18 @@ __global__ __launch_bounds__(64 * WAVES) void gemm_kernel(GemmArgs a)
     const int l16 = lane & 15;
     const int lg = lane >> 4;
 
-    // XCD-aware tile mapping
+    // XCD-aware tile mapping (tiles implied by the selections: the column
+    // tile by id modulo 8, its row tiles 8 ids apart; otherwise balanced, the
+    // device-built tile count in grouped mode)
     const int id = blockIdx.x;
-    const int xcd = id & 7;
-    const int q = id >> 3;
-    const int mt = q % a.MT;
-    const int nt = (q / a.MT) * 8 + xcd;
-    if (nt >= a.NT) return;
+    int mt, nt;
+    if (a.sel) {
+        mt = (id >> 3) % a.MT;
+        nt = ((id >> 3) / a.MT) * 8 + (id & 7);
+        if (nt >= a.NT) return;
+    } else if (!xcd_item(id, a.NT, a.tiles ? *a.n_tiles : a.MT, nt, mt)) {
+        return;
+    }
 
     int group = 0, row0, nrows;
     int xtok = -1;   // implied tiles: activation row of this lane's row l16 (MF == 1)
@@ -313,7 +334,6 @@ __global__ __launch_bounds__(64 * WAVES) void gemm_kernel(GemmArgs a)
             xtok = l16;   // shared expert: row i is token i
         }
     } else if (a.tiles) {
-        if (mt >= *a.n_tiles) return;
         group = a.tiles[3 * mt];
         row0 = a.tiles[3 * mt + 1];
         nrows = a.tiles[3 * mt + 2];
@@ -587,13 +607,10 @@ __global__ __launch_bounds__(256) void gemm_bigm_kernel(GemmArgs a)
 
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int l16 = lane & 15, lg = lane >> 4;
-    const int id = blockIdx.x, xcd = id & 7, q = id >> 3;
-    const int mt = q % a.MT;
-    const int nt = (q / a.MT) * 8 + xcd;
-    if (nt >= a.NT) return;
+    int mt, nt;
+    if (!xcd_item(blockIdx.x, a.NT, a.tiles ? *a.n_tiles : a.MT, nt, mt)) return;
     int group = 0, row0, nrows;
     if (a.tiles) {
-        if (mt >= *a.n_tiles) return;
         group = a.tiles[3 * mt];
         row0 = a.tiles[3 * mt + 1];
         nrows = a.tiles[3 * mt + 2];
@@ -779,10 +796,8 @@ __global__ __launch_bounds__(64 * WAVES) void gemm_wide_kernel(GemmArgs a)
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int l32 = lane & 31, lh = lane >> 5;
-    const int id = blockIdx.x, xcd = id & 7, q = id >> 3;
-    const int mt = q % a.MT;
-    const int nt = (q / a.MT) * 8 + xcd;
-    if (nt >= a.NT) return;
+    int mt, nt;
+    if (!xcd_item(blockIdx.x, a.NT, a.MT, nt, mt)) return;
     const int row0 = mt * BM;
     const int nrows = min(BM, a.M - row0);
     if (nrows <= 0) return;
