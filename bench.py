@@ -45,20 +45,18 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
 
-# HBM traffic of each workload's dominant kernel from rocprofv3 counter runs
-# (see profiles/hbm_traffic_dominant_kernels.md): KiB per dispatch, scaled by
-# what the same counter reads for a plain copy of known size.  Valid only for
-# the kernel sources it was measured on (SHA-256 prefix of every .h / .hip file
-# of the library's csrc/, in name order).
+# HBM traffic of each workload's dominant kernel, measured with rocprofv3
+# (profiles/hbm_traffic_dominant_kernels.md): bytes read per dispatch =
+# 128 TCC_EA0_RDREQ_128B + 64 TCC_EA0_RDREQ_64B + 32 TCC_EA0_RDREQ_32B, bytes
+# written = 64 TCC_EA0_WRREQ_64B + 32 (TCC_EA0_WRREQ - TCC_EA0_WRREQ_64B); a
+# plain 1 GiB device copy reads and writes exactly 1 GiB by these formulas.
+# Median over the dispatches of the same command.  Valid only for the kernel
+# sources it was measured on (SHA-256 prefix of every .h / .hip file of the
+# library's csrc/, in name order).
 MEASURED_TRAFFIC = {   # the dominant kernel of each workload (see DOMINANT)
-    "moe_b1": {"source_sha": "fce1f40b83e17eea", "fetch_kib": 161690.9, "fetch_scale": 2.000,
-               "write_kib": 63.1, "write_scale": 1.000},
-    "moe_b32": {"source_sha": "fce1f40b83e17eea", "fetch_kib": 161796.5, "fetch_scale": 2.000,
-                "write_kib": 1792.0, "write_scale": 1.000},
-    "moe_b64_long": {"source_sha": "fce1f40b83e17eea", "fetch_kib": 766094.8, "fetch_scale": 2.000,
-                     "write_kib": 7143.3, "write_scale": 1.000},
-    "dense_fp8_b8": {"source_sha": "fce1f40b83e17eea", "fetch_kib": 60667.9, "fetch_scale": 2.000,
-                     "write_kib": 30494.3, "write_scale": 1.000},
+    "moe_b1": {"source_sha": "2bfa038396a68d00", "read_bytes": 331_090_000, "write_bytes": 65_000},
+    "moe_b32": {"source_sha": "2bfa038396a68d00", "read_bytes": 327_214_000, "write_bytes": 1_835_000},
+    "dense_fp8_b8": {"source_sha": "2bfa038396a68d00", "read_bytes": 124_129_000, "write_bytes": 31_221_000},
 }
 
 
@@ -78,7 +76,7 @@ def measured_traffic(workload: str):
     m = MEASURED_TRAFFIC.get(workload)
     if m is None or m["source_sha"] != kernel_source_sha():
         return None
-    return (m["fetch_kib"] * m["fetch_scale"] + m["write_kib"] * m["write_scale"]) * 1024
+    return m["read_bytes"] + m["write_bytes"]
 METRIC = "accepted tokens/s + verify-step µs at batch 1/32/64, K=3, MoE decoder"
 WBYTES = {"f32": 4, "bf16": 2, "fp8": 1}
 

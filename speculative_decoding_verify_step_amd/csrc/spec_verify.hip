@@ -30,6 +30,7 @@
 #include "attention.h"
 #include "common.h"
 #include "gemm.h"
+#include "gemm_lds.h"
 #include "small_kernels.h"
 #include "qkv_rope.h"
 #include "sampling.h"
@@ -413,6 +414,14 @@ void launch_gemm_wide(int wt, int mode, GemmArgs& a, hipStream_t s)
     else launch_wide_t<SV_FP8>(mode, cs, a, grid, s);
 }
 
+// bf16 LM head at 129 .. 256 rows: both operands staged in LDS, 256-row
+// tiles of 8 waves, 4 stages (gemm_lds.h)
+void launch_lm_head_lds(const GemmArgs& a, hipStream_t s)
+{
+    dim3 grid((unsigned)(cdiv(a.NT * a.MT, 8) * 8), 1, 1), blk(512);
+    launch(gemm_lds_kernel<SV_BF16, GM_ARGMAX, 2, 4, 4>, grid, blk, 0, s, a);
+}
+
 // merge: CB partials per load batch, NI = ceil(maxch / 32) chunk weights per lane
 template <bool BF>
 void launch_merge_t(int maxch, const AttnArgs& at, void* out, int rows, hipStream_t s)
@@ -644,18 +653,21 @@ int plan_context(spec_verify_ctx* c, const spec_verify_config& cfg, int dev)
     c->att_QPW = QF >= 4 ? 4 : (QF >= 2 ? 2 : 1);
     c->att_QG = cdiv(QF, c->att_QPW);
     {
-        long work = (long)k.max_batch * k.n_kv_heads * c->att_QG * k.kv_capacity;
-        int ch = 64;
-        const long waves_target = c->att_QPW >= 4 ? 2048 : 2 * 2048;   // busier waves: fewer of them
-        while (ch < 1024 && work / ch > waves_target) ch *= 2;
-        c->att_CH = ch;
-        c->att_maxch = cdiv(k.kv_capacity, ch);
         // streaming K/V loads only when every tile has one reader (one query
         // group per KV head) and the caches are far larger than the 256 MB
         // Infinity Cache; a smaller cache stays resident from step to step
         const double kv_bytes = 2.0 * k.max_batch * k.n_layers * k.n_kv_heads * (double)k.kv_capacity *
                                 k.head_dim * (k.kv_dtype == SV_F32 ? 4 : 2);
         c->att_stream = c->att_QG == 1 && kv_bytes > 1024.0 * 1024 * 1024;
+        long work = (long)k.max_batch * k.n_kv_heads * c->att_QG * k.kv_capacity;
+        int ch = 64;
+        const long waves_target = c->att_QPW >= 4 ? 2048 : 2 * 2048;   // busier waves: fewer of them
+        // streamed chunks at most 512 keys: batch 64 with long contexts,
+        // 271 -> 258 us per layer against 1,024-key chunks (same box)
+        const int ch_max = c->att_stream ? 512 : 1024;
+        while (ch < ch_max && work / ch > waves_target) ch *= 2;
+        c->att_CH = ch;
+        c->att_maxch = cdiv(k.kv_capacity, ch);
         if (c->att_maxch > ATT_MAXCH_CAP)
             return fail(SV_ERR_UNSUPPORTED, "kv_capacity too large for the attention plan");
     }
@@ -1012,6 +1024,15 @@ static int step_impl(spec_verify_ctx* c, const spec_verify_weights* w, void* k_c
         // the HBM-bound shapes prefer (LM head at 128 rows: 6% faster)
         const bool wide = big && packed && Kd % chunk == 0 && wtd != SV_MXFP4 &&
                           (wt == SV_FP8 || T > 128);
+        if (big && packed && mode == GM_ARGMAX && wtd == SV_BF16 && T > 128 && T <= 256 &&
+            Kd % wsteps(SV_BF16) == 0) {
+            a.MT = 1;
+            a.NT = cdiv(N, 256);
+            a.ksplit = 1;
+            launch_lm_head_lds(a, s);
+            last_nt = a.NT;
+            return 1;
+        }
         if (big && Kd % chunk == 0) {
             a.MT = wide ? cdiv(T, 32 * WIDE_MW) : MTb;
             a.NT = wide ? cdiv(N, wide_col_tile(mode)) : cdiv(N, 16 * 4 * BIG_NF);
