@@ -47,6 +47,109 @@ struct AttnArgs {
 // i.e. weights under 2^-126 of the row maximum).
 SV_DEV float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// The last tile of a sequence reaches past its newest written position:
+// those slots were never written (or hold an older step's data) and may be
+// any bit pattern.  Their probabilities are 0, but 0 * NaN or 0 * Inf in the
+// output product would still poison the row, so their values are cleared
+// (lane group lg holds keys kt + KL lg + e of every value fragment).
+template <bool BF, int DF>
+SV_DEV void attn_clear_dead(uint4 (&vf)[DF], int kt, int lg, int total)
+{
+    constexpr int KL = BF ? 8 : 4;
+    const int nv = total - (kt + KL * lg);
+    uint32_t m[4];
+#pragma unroll
+    for (int w = 0; w < 4; w++) {
+        if constexpr (BF) m[w] = (2 * w < nv ? 0xffffu : 0u) | (2 * w + 1 < nv ? 0xffff0000u : 0u);
+        else m[w] = w < nv ? 0xffffffffu : 0u;
+    }
+#pragma unroll
+    for (int d = 0; d < DF; d++) {
+        vf[d].x &= m[0];
+        vf[d].y &= m[1];
+        vf[d].z &= m[2];
+        vf[d].w &= m[3];
+    }
+}
+
+// One key tile (4 KL keys) for one 16-row query fragment: the scores, the
+// running (max, sum) of each row and the output product.  Row l16's keys past
+// `limit` (causal end; -1 for a padding row) are masked.
+template <bool BF, int DH>
+SV_DEV void attn_tile(const uint4 (&kf)[(BF ? 8 : 4) / 4][DH / (4 * (BF ? 8 : 4))],
+                      const uint4 (&vf)[DH / 16], const uint4 (&qf)[DH / (4 * (BF ? 8 : 4))], int kt,
+                      int lg, int limit, float scale_log2, float& m_run, float& l_run,
+                      f32x4_t (&o)[DH / 16])
+{
+    constexpr int KL = BF ? 8 : 4, DS = DH / (4 * KL), DF = DH / 16, NB = KL / 4;
+    float s[KL];
+#pragma unroll
+    for (int blk = 0; blk < NB; blk++) {
+        f32x4_t acc = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int st = 0; st < DS; st++) {
+            if constexpr (BF) acc = mma_bf16(kf[blk][st], qf[st], acc);
+            else acc = mma_f32x4(kf[blk][st], qf[st], acc);
+        }
+#pragma unroll
+        for (int r = 0; r < 4; r++) s[4 * blk + r] = acc[r];
+    }
+    // lane (lg, l16) holds keys kt + KL*lg + e for row l16 of the fragment
+    float mt = -INFINITY;
+#pragma unroll
+    for (int e = 0; e < KL; e++) {
+        int key = kt + KL * lg + e;
+        s[e] = (key <= limit) ? s[e] * scale_log2 : -INFINITY;
+        mt = fmaxf(mt, s[e]);
+    }
+    mt = fmaxf(mt, __shfl_xor(mt, 16, 64));
+    mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
+    float mnew = fmaxf(m_run, mt);
+    float muse = (mnew == -INFINITY) ? 0.f : mnew;
+    float alpha = exp2_fast(m_run - muse);
+    m_run = mnew;
+    float p[KL], ps = 0.f;
+#pragma unroll
+    for (int e = 0; e < KL; e++) { p[e] = exp2_fast(s[e] - muse); ps += p[e]; }
+    l_run = l_run * alpha + ps;
+    uint4 pb;
+    if constexpr (BF) {
+        pb = make_uint4(pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]),
+                        pack_bf16x2(p[4], p[5]), pack_bf16x2(p[6], p[7]));
+    } else {
+        pb = make_uint4(__float_as_uint(p[0]), __float_as_uint(p[1]), __float_as_uint(p[2]),
+                        __float_as_uint(p[3]));
+    }
+#pragma unroll
+    for (int d = 0; d < DF; d++) {
+        o[d] = o[d] * alpha;
+        if constexpr (BF) o[d] = mma_bf16(vf[d], pb, o[d]);
+        else o[d] = mma_f32x4(vf[d], pb, o[d]);
+    }
+}
+
+// Partial of one chunk for one 16-row query fragment (row r = 16 f + l16 of
+// the KV head's R rows): O^T[d = 16 df + 4 lg + i][row l16] and (max, sum).
+template <int DH>
+SV_DEV void attn_write_partial(const AttnArgs& a, int b, int hkv, int chunk, int f, int l16, int lg,
+                               float m_run, float l_run, const f32x4_t (&o)[DH / 16])
+{
+    constexpr int DF = DH / 16;
+    const int K1 = a.K1, G = a.n_q / a.n_kv, R = K1 * G;
+    float l = l_run;
+    l += __shfl_xor(l, 16, 64);
+    l += __shfl_xor(l, 32, 64);
+    const int r = f * 16 + l16;
+    if (r >= R) return;
+    const int j = r / G, hq = hkv * G + r % G;
+    const size_t slot = (((size_t)b * a.n_q + hq) * K1 + j) * a.maxch + chunk;
+    float* op = a.opart + slot * DH;
+#pragma unroll
+    for (int d = 0; d < DF; d++)
+        *reinterpret_cast<float4*>(op + 16 * d + 4 * lg) = make_float4(o[d][0], o[d][1], o[d][2], o[d][3]);
+    if (lg == 0) *reinterpret_cast<float2*>(a.mlpart + slot * 2) = make_float2(m_run, l);
+}
+
 // With streaming loads (one reader per tile, caches far beyond the Infinity
 // Cache) at most two waves per SIMD: more concurrent streams measured slower
 // (batch 64: 254 us per layer at two, 283 us at three).
@@ -163,93 +266,15 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(1, STREAM ? 
         uint4 vf[DF];
 #pragma unroll
         for (int d = 0; d < DF; d++) vf[d] = kvload(kt_v + (size_t)d * 1024);
-        if (kt + KT > total) {
-            // the last tile reaches past the newest written position: those
-            // slots were never written (or hold an older step's data) and may
-            // be any bit pattern.  Their probabilities are 0, but 0 * NaN or
-            // 0 * Inf in the product would still poison the row, so their
-            // values are cleared (lane group lg holds keys kt + KL lg + e)
-            const int nv = total - (kt + KL * lg);
-            uint32_t m[4];
+        if (kt + KT > total) attn_clear_dead<BF, DF>(vf, kt, lg, total);
 #pragma unroll
-            for (int w = 0; w < 4; w++) {
-                if constexpr (BF) m[w] = (2 * w < nv ? 0xffffu : 0u) | (2 * w + 1 < nv ? 0xffff0000u : 0u);
-                else m[w] = w < nv ? 0xffffffffu : 0u;
-            }
-#pragma unroll
-            for (int d = 0; d < DF; d++) {
-                vf[d].x &= m[0];
-                vf[d].y &= m[1];
-                vf[d].z &= m[2];
-                vf[d].w &= m[3];
-            }
-        }
-#pragma unroll
-        for (int f = 0; f < QPW; f++) {
-            float s[KL];
-#pragma unroll
-            for (int blk = 0; blk < NB; blk++) {
-                f32x4_t acc = f32x4_t{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                for (int st = 0; st < DS; st++) {
-                    if constexpr (BF) acc = mma_bf16(kf[blk][st], qf[f][st], acc);
-                    else acc = mma_f32x4(kf[blk][st], qf[f][st], acc);
-                }
-#pragma unroll
-                for (int r = 0; r < 4; r++) s[4 * blk + r] = acc[r];
-            }
-            // lane (lg, l16) holds keys kt + KL*lg + e for row l16 of fragment f
-            float mt = -INFINITY;
-#pragma unroll
-            for (int e = 0; e < KL; e++) {
-                int key = kt + KL * lg + e;
-                s[e] = (key <= limit[f]) ? s[e] * a.scale_log2 : -INFINITY;
-                mt = fmaxf(mt, s[e]);
-            }
-            mt = fmaxf(mt, __shfl_xor(mt, 16, 64));
-            mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
-            float mnew = fmaxf(m_run[f], mt);
-            float muse = (mnew == -INFINITY) ? 0.f : mnew;
-            float alpha = exp2_fast(m_run[f] - muse);
-            m_run[f] = mnew;
-            float p[KL], ps = 0.f;
-#pragma unroll
-            for (int e = 0; e < KL; e++) { p[e] = exp2_fast(s[e] - muse); ps += p[e]; }
-            l_run[f] = l_run[f] * alpha + ps;
-            uint4 pb;
-            if constexpr (BF) {
-                pb = make_uint4(pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]),
-                                pack_bf16x2(p[4], p[5]), pack_bf16x2(p[6], p[7]));
-            } else {
-                pb = make_uint4(__float_as_uint(p[0]), __float_as_uint(p[1]), __float_as_uint(p[2]),
-                                __float_as_uint(p[3]));
-            }
-#pragma unroll
-            for (int d = 0; d < DF; d++) {
-                o[f][d] = o[f][d] * alpha;
-                if constexpr (BF) o[f][d] = mma_bf16(vf[d], pb, o[f][d]);
-                else o[f][d] = mma_f32x4(vf[d], pb, o[f][d]);
-            }
-        }
+        for (int f = 0; f < QPW; f++)
+            attn_tile<BF, DH>(kf, vf, qf[f], kt, lg, limit[f], a.scale_log2, m_run[f], l_run[f], o[f]);
     }
 
-    // partial of this chunk: O^T[d = 16 df + 4 lg + r][row l16]
 #pragma unroll
-    for (int f = 0; f < QPW; f++) {
-        float l = l_run[f];
-        l += __shfl_xor(l, 16, 64);
-        l += __shfl_xor(l, 32, 64);
-        int r = (qgi * QPW + f) * 16 + l16;
-        if (r >= R) continue;
-        int j = r / G, hq = hkv * G + r % G;
-        size_t slot = (((size_t)b * a.n_q + hq) * K1 + j) * a.maxch + chunk;
-        float* op = a.opart + slot * DH;
-#pragma unroll
-        for (int d = 0; d < DF; d++)
-            *reinterpret_cast<float4*>(op + 16 * d + 4 * lg) =
-                make_float4(o[f][d][0], o[f][d][1], o[f][d][2], o[f][d][3]);
-        if (lg == 0) *reinterpret_cast<float2*>(a.mlpart + slot * 2) = make_float2(m_run[f], l);
-    }
+    for (int f = 0; f < QPW; f++)
+        attn_write_partial<DH>(a, b, hkv, chunk, qgi * QPW + f, l16, lg, m_run[f], l_run[f], o[f]);
 }
 
 // Merge the chunk partials of one (sequence, query head, position) row in

@@ -25,27 +25,7 @@
 // measured slower here than on gemm_wide_kernel and stay there.
 #pragma once
 #include "gemm.h"
-
-// The global -> LDS copies are issued from inline assembly: the compiler
-// then does not treat them as pending writes to every LDS location (it would
-// wait for all of them, the stages still in flight included, before any LDS
-// read).  They have no register results; the waits for them are explicit:
-// s_waitcnt vmcnt <= N, and a workgroup barrier, both also compiler barriers
-// for memory accesses.
-template <int N>
-SV_DEV void wait_vmcnt()
-{
-    static_assert(N >= 0 && N < 64, "vmcnt range");
-    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
-}
-SV_DEV void lds_barrier() { asm volatile("s_barrier" ::: "memory"); }
-// 16 bytes per lane from global memory to LDS at lds_off + 16 * lane
-SV_DEV void copy_to_lds(const void* g, uint32_t lds_off)
-{
-    asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g),
-                 "s"(__builtin_amdgcn_readfirstlane(lds_off))
-                 : "memory", "m0");
-}
+#include "lds_dma.h"
 
 template <int WT, int MODE, int RG, int MR, int S>
 __global__ __launch_bounds__(256 * RG) void gemm_lds_kernel(GemmArgs a)

@@ -31,6 +31,7 @@
 #include "common.h"
 #include "gemm.h"
 #include "gemm_lds.h"
+#include "attention_lds.h"
 #include "small_kernels.h"
 #include "qkv_rope.h"
 #include "sampling.h"
@@ -91,6 +92,7 @@ struct spec_verify_ctx {
     bool bf = true;
     int att_CH = 256, att_maxch = 1, att_QPW = 1, att_QG = 1;
     bool att_stream = false;
+    int att_lds_nw = 0;   // > 0: attn_lds_kernel with this many waves per workgroup
     // workspace
     std::vector<void*> allocs;
     float* x = nullptr;
@@ -443,6 +445,20 @@ void launch_merge(bool bf, int maxch, const AttnArgs& at, void* out, int rows, h
 
 int rows_mf(int rows) { return rows <= 16 ? 1 : (rows <= 32 ? 2 : 4); }
 
+void launch_attention_lds(int D, int NW, dim3 grid, const AttnArgs& at, hipStream_t s)
+{
+    constexpr int FPW = 2, S = 4;
+#define ATT_LDS(DH)                                                                                   \
+    switch (NW) {                                                                                     \
+    case 1: launch(attn_lds_kernel<DH, FPW, 1, S>, grid, dim3(64), 0, s, at); break;                  \
+    case 2: launch(attn_lds_kernel<DH, FPW, 2, S>, grid, dim3(128), 0, s, at); break;                 \
+    case 4: launch(attn_lds_kernel<DH, FPW, 4, S>, grid, dim3(256), 0, s, at); break;                 \
+    default: launch(attn_lds_kernel<DH, FPW, 8, S>, grid, dim3(512), 0, s, at); break;                \
+    }
+    if (D == 128) { ATT_LDS(128) } else { ATT_LDS(64) }
+#undef ATT_LDS
+}
+
 template <bool BF, int DH, bool ST>
 void launch_attention_t(int QPW, dim3 grid, const AttnArgs& at, hipStream_t s)
 {
@@ -652,7 +668,26 @@ int plan_context(spec_verify_ctx* c, const spec_verify_config& cfg, int dev)
     // dense GQA verify (128 rows per KV head) 78 -> 62 us per layer with four
     c->att_QPW = QF >= 4 ? 4 : (QF >= 2 ? 2 : 1);
     c->att_QG = cdiv(QF, c->att_QPW);
-    {
+    // bf16 caches with 17 .. 256 rows per KV head: one workgroup per (sequence,
+    // KV head, chunk) for all rows, K/V tiles staged in LDS (two fragments per
+    // wave, 1 .. 8 waves)
+    c->att_lds_nw = 0;
+    if (c->bf && QF >= 2 && QF <= 16 && (k.head_dim == 64 || k.head_dim == 128)) {
+        int nw = 1;
+        while (nw * 2 < QF) nw *= 2;
+        c->att_lds_nw = nw;
+    }
+    if (c->att_lds_nw > 0) {
+        // about two workgroups per CU over the largest batch, chunks of at
+        // most 512 keys (the chunk partials of all R rows are written per chunk)
+        const long work = (long)k.max_batch * k.n_kv_heads * k.kv_capacity;
+        int ch = 64;
+        while (ch < 512 && work / ch > 512) ch *= 2;
+        c->att_CH = ch;
+        c->att_maxch = cdiv(k.kv_capacity, ch);
+        if (c->att_maxch > ATT_MAXCH_CAP)
+            return fail(SV_ERR_UNSUPPORTED, "kv_capacity too large for the attention plan");
+    } else {
         // streaming K/V loads only when every tile has one reader (one query
         // group per KV head) and the caches are far larger than the 256 MB
         // Infinity Cache; a smaller cache stays resident from step to step
@@ -1147,10 +1182,14 @@ static int step_impl(spec_verify_ctx* c, const spec_verify_weights* w, void* k_c
         {
             ProfScope ps(c, SV_KC_ATTENTION, s);
             at.B = B;
-            const dim3 grid = c->att_QG > 1
-                ? dim3((unsigned)(cdiv(B * k.n_kv_heads * c->att_maxch, 8) * 8 * c->att_QG), 1, 1)
-                : dim3(c->att_maxch, k.n_kv_heads, B);
-            launch_attention(bf, k.head_dim, c->att_QPW, c->att_stream, grid, at, s);
+            if (c->att_lds_nw > 0) {
+                launch_attention_lds(k.head_dim, c->att_lds_nw, dim3(c->att_maxch, k.n_kv_heads, B), at, s);
+            } else {
+                const dim3 grid = c->att_QG > 1
+                    ? dim3((unsigned)(cdiv(B * k.n_kv_heads * c->att_maxch, 8) * 8 * c->att_QG), 1, 1)
+                    : dim3(c->att_maxch, k.n_kv_heads, B);
+                launch_attention(bf, k.head_dim, c->att_QPW, c->att_stream, grid, at, s);
+            }
         }
         launch_merge(bf, c->att_maxch, at, c->o, B * k.n_q_heads * K1, s);
         // the MoE consumer (residual + norm + router) takes at most 4 splits
