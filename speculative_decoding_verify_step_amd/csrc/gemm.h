@@ -66,6 +66,17 @@ struct GemmArgs {
     long dbg_ld;
 };
 
+// Whether the group (expert) of tile mt of a device-built tile list has other
+// row tiles (its tiles are consecutive in the list): those tiles read the
+// same weights, so the loads keep them in L2 for the others instead of
+// streaming them past it.
+SV_DEV bool group_has_siblings(const int* tiles, int mt, int ntiles, int group)
+{
+    const int prev = tiles[3 * max(mt - 1, 0)];
+    const int next = tiles[3 * min(mt + 1, ntiles - 1)];
+    return (mt > 0 && prev == group) || (mt + 1 < ntiles && next == group);
+}
+
 // Work item (column tile nt, row tile mt) of workgroup `id` among NT x MT
 // items, row tiles fastest.  Workgroup ids are dealt to the 8 XCDs round
 // robin; each XCD takes one contiguous range of equal length of the items, so
@@ -316,6 +327,7 @@ __global__ __launch_bounds__(64 * WAVES) void gemm_kernel(GemmArgs a)
     }
 
     int group = 0, row0, nrows;
+    bool keep = false;   // weights also read by sibling row tiles: normal (cached) loads
     int xtok = -1;   // implied tiles: activation row of this lane's row l16 (MF == 1)
     if (a.sel) {
         const int A = a.sel_T * a.sel_k;
@@ -337,6 +349,7 @@ __global__ __launch_bounds__(64 * WAVES) void gemm_kernel(GemmArgs a)
         group = a.tiles[3 * mt];
         row0 = a.tiles[3 * mt + 1];
         nrows = a.tiles[3 * mt + 2];
+        keep = group_has_siblings(a.tiles, mt, *a.n_tiles, group);
     } else {
         row0 = mt * BM;
         nrows = min(BM, a.M - row0);
@@ -427,12 +440,16 @@ __global__ __launch_bounds__(64 * WAVES) void gemm_kernel(GemmArgs a)
         for (int u = 0; u < U; u++) {
             int kk = k + u * SK;
             if (kk < ke) {
+                auto wl = [&](auto ld) {
 #pragma unroll
-                for (int f = 0; f < NFT; f++) {
-                    if constexpr (PACKED) w[u][f] = ldg16_stream(wrow[f] + (size_t)(kk / SK) * 1024);
-                    else w[u][f] = ldg16_stream(wrow[f] + (size_t)kk * WESZ);
-                    if constexpr (MX) sb[u][f] = mx_scale_byte(sslice[f], kk / SK);
-                }
+                    for (int f = 0; f < NFT; f++) {
+                        if constexpr (PACKED) w[u][f] = ld(wrow[f] + (size_t)(kk / SK) * 1024);
+                        else w[u][f] = ld(wrow[f] + (size_t)kk * WESZ);
+                        if constexpr (MX) sb[u][f] = mx_scale_byte(sslice[f], kk / SK);
+                    }
+                };
+                if (keep) wl([](const void* p) { return ldg16(p); });
+                else wl([](const void* p) { return ldg16_stream(p); });
 #pragma unroll
                 for (int m = 0; m < MF; m++)
 #pragma unroll
@@ -608,12 +625,15 @@ __global__ __launch_bounds__(256) void gemm_bigm_kernel(GemmArgs a)
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int l16 = lane & 15, lg = lane >> 4;
     int mt, nt;
-    if (!xcd_item(blockIdx.x, a.NT, a.tiles ? *a.n_tiles : a.MT, nt, mt)) return;
+    const int ntiles = a.tiles ? *a.n_tiles : a.MT;
+    if (!xcd_item(blockIdx.x, a.NT, ntiles, nt, mt)) return;
     int group = 0, row0, nrows;
+    bool keep = false;
     if (a.tiles) {
         group = a.tiles[3 * mt];
         row0 = a.tiles[3 * mt + 1];
         nrows = a.tiles[3 * mt + 2];
+        keep = group_has_siblings(a.tiles, mt, ntiles, group);
     } else {
         row0 = mt * BM;
         nrows = min(BM, a.M - row0);
@@ -674,14 +694,18 @@ __global__ __launch_bounds__(256) void gemm_bigm_kernel(GemmArgs a)
     }
     auto staged = [&](int i) { return wave * PPW + i < PIECES; };
     auto wload = [&](int k, uint4 (&w)[CS][NFT]) {
+        auto one = [&](auto ld) {
 #pragma unroll
-        for (int s = 0; s < CS; s++)
+            for (int s = 0; s < CS; s++)
 #pragma unroll
-            for (int f = 0; f < NFT; f++) {
-                int kk = k + s * SK;
-                if constexpr (PACKED) w[s][f] = ldg16_stream(wrow[f] + (size_t)(kk / SK) * 1024);
-                else w[s][f] = ldg16_stream(wrow[f] + (size_t)kk * WESZ);
-            }
+                for (int f = 0; f < NFT; f++) {
+                    int kk = k + s * SK;
+                    if constexpr (PACKED) w[s][f] = ld(wrow[f] + (size_t)(kk / SK) * 1024);
+                    else w[s][f] = ld(wrow[f] + (size_t)kk * WESZ);
+                }
+        };
+        if (keep) one([](const void* p) { return ldg16(p); });
+        else one([](const void* p) { return ldg16_stream(p); });
     };
     auto xload = [&](int k, uint4 (&st)[PPW]) {
 #pragma unroll
