@@ -453,6 +453,14 @@ def run_bench(cfg, steps, warmup, sampled=False, kv_page=0, graph=False, classes
     return res
 
 
+def attention_kernel(cfg):
+    """The library's attention kernel for cfg: the LDS-ring kernel when a KV
+    head has 17 .. 256 query rows (block positions x grouped query heads) and
+    the cache is bf16, else the split-KV kernel."""
+    rows = (cfg.k_draft + 1) * (cfg.n_q // cfg.n_kv)
+    return "attn_lds" if cfg.kvdtype == "bf16" and 17 <= rows <= 256 else "attn_split"
+
+
 def block(cfg, r, steps, graph, sampled=False, kv_page=0):
     """The JSON object of one workload's measurements."""
     lm_gbs = r["lm_bytes"] / (r["lm_ms"] * 1e-3) / 1e9 if r["lm_ms"] > 0 else None
@@ -465,7 +473,7 @@ def block(cfg, r, steps, graph, sampled=False, kv_page=0):
         "accepted_tok_s": r["tok_s"], "tokens_per_verify": r["tau"],
         "draft_sets": r["draft_sets"],
         "roofline": {"bound": "hbm",
-                     "kernel": {"lm_head": "lm_head_argmax", "attention": "attn_split",
+                     "kernel": {"lm_head": "lm_head_argmax", "attention": attention_kernel(cfg),
                                 "expert_gate_up": "expert_gate_up_swiglu"}[r["kernel"]],
                      "achieved": lm_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": (lm_gbs / HBM_PEAK_GBS) if lm_gbs else None,

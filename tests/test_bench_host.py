@@ -87,3 +87,15 @@ def test_attention_and_gate_up_bytes_by_hand():
     assert bench.gate_up_bytes(b32, 64) == want
     for name in bench.DOMINANT:
         assert workloads.get_config(name).name == name
+
+
+def test_attention_kernel_label_follows_the_library_rule():
+    """The roofline names the LDS-ring attention kernel where the library
+    uses it: bf16 caches with 17 .. 256 query rows per KV head."""
+    assert bench.attention_kernel(workloads.get_config("dense_fp8_b8")) == "attn_lds"   # 32 x 4 rows
+    for name in ("moe_b1", "moe_b32", "moe_b64_long", "tiny_fp32"):
+        assert bench.attention_kernel(workloads.get_config(name)) == "attn_split"
+    wide = workloads.scaled(workloads.get_config("dense_fp8_b8"), k_draft=63)   # 64 x 4 = 256 rows
+    assert bench.attention_kernel(wide) == "attn_lds"
+    wider = workloads.scaled(workloads.get_config("dense_fp8_b8"), k_draft=64)  # 260 rows
+    assert bench.attention_kernel(wider) == "attn_split"
