@@ -253,6 +253,181 @@ SV_DEV int implied_slot(int sv, int A, int j)
 
 SV_DEV float silu_f32(float z) { return z / (1.0f + __expf(-z)); }
 
+// Selection order of the routing: larger probability first, then the lower
+// expert index (a NaN probability above every number).  The probability part
+// is an order-preserving 32-bit key (0 for an empty slot); ties are broken by
+// the lowest index with a wave vote.
+SV_DEV uint32_t route_hi(float v)
+{
+    if (v != v) return 0xffffffffu;
+    const uint32_t u = __float_as_uint(v);
+    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+// The probability a key was made from (exact; NaN for NaN).
+SV_DEV float route_hi_value(uint32_t hi)
+{
+    if (hi == 0xffffffffu) return __uint_as_float(0x7fc00000u);
+    return __uint_as_float((hi & 0x80000000u) ? (hi & 0x7fffffffu) : ~hi);
+}
+
+template <int CTRL, int RM>
+SV_DEV uint32_t dpp_max_u32(uint32_t v)
+{
+    const uint32_t o = dpp_u32<CTRL, RM>(0u, v);
+    return o > v ? o : v;
+}
+
+SV_DEV uint32_t wave_max_u32(uint32_t v)
+{
+    v = dpp_max_u32<DPP_SHR1, 0xf>(v);
+    v = dpp_max_u32<DPP_SHR2, 0xf>(v);
+    v = dpp_max_u32<DPP_SHR4, 0xf>(v);
+    v = dpp_max_u32<DPP_SHR8, 0xf>(v);
+    v = dpp_max_u32<DPP_BCAST15, 0xa>(v);
+    v = dpp_max_u32<DPP_BCAST31, 0xc>(v);
+    return (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
+}
+
+// Softmax over the E logits of row t (lane l holds experts l + 64 q) in fp32,
+// top-k by probability with the lower expert index first on ties, gates = the
+// selected probabilities (optionally renormalised, summed in rank order).  One
+// wave, k <= 8.  The r-th choice is the largest remaining probability key
+// (a DPP maximum over the wave), the lowest expert holding it (a wave vote),
+// which then drops out: k rounds.  Outputs sel and gate_out [T][k] (dbg_sel,
+// sel_lds if given).
+SV_DEV void router_select_to(int E, int k, bool renorm, int t, float (&p)[4], int* sel, float* gate_out,
+                             int* dbg_sel, unsigned short* sel_lds)
+{
+    const int lane = threadIdx.x & 63;
+    float m = -INFINITY;
+#pragma unroll
+    for (int q = 0; q < 4; q++) m = fmaxf(m, p[q]);
+    m = wave_max(m);
+    float sum = 0.f;
+#pragma unroll
+    for (int q = 0; q < 4; q++) {
+        p[q] = (lane + 64 * q < E) ? __expf(p[q] - m) : 0.f;
+        sum += p[q];
+    }
+    sum = wave_sum(sum);
+    const float inv = 1.f / sum;
+    uint32_t hi[4];
+#pragma unroll
+    for (int q = 0; q < 4; q++) {
+        p[q] *= inv;
+        hi[q] = lane + 64 * q < E ? route_hi(p[q]) : 0u;
+    }
+    float pr[8];
+#pragma unroll
+    for (int r = 0; r < 8; r++) {
+        pr[r] = 0.f;
+        if (r < k) {
+            uint32_t mx = hi[0] > hi[1] ? hi[0] : hi[1];
+            const uint32_t m23 = hi[2] > hi[3] ? hi[2] : hi[3];
+            mx = wave_max_u32(mx > m23 ? mx : m23);
+            // the lowest expert e = lane + 64 q holding the maximum
+            int e = 0x7fffffff;
+#pragma unroll
+            for (int q = 3; q >= 0; q--) {
+                const unsigned long long b = __ballot(hi[q] == mx);
+                if (b) e = 64 * q + __builtin_ctzll(b);
+            }
+            pr[r] = route_hi_value(mx);
+#pragma unroll
+            for (int q = 0; q < 4; q++) hi[q] = lane + 64 * q == e ? 0u : hi[q];
+            if (lane == 0) {
+                sel[t * k + r] = e;
+                if (sel_lds) sel_lds[t * k + r] = (unsigned short)e;
+                if (dbg_sel) dbg_sel[t * k + r] = e;
+            }
+        }
+    }
+    if (lane < k) {
+        float gsum = 0.f;
+#pragma unroll
+        for (int rr = 0; rr < 8; rr++) gsum += rr < k ? pr[rr] : 0.f;   // in rank order
+        float pe = pr[0];
+#pragma unroll
+        for (int rr = 1; rr < 8; rr++) pe = lane == rr ? pr[rr] : pe;
+        gate_out[t * k + lane] = renorm ? pe / gsum : pe;
+    }
+}
+
+// The selections of up to four rows at once when E <= 64 (lane e holds
+// expert e of every row): router_select_to's arithmetic for each row, the
+// four rows' dependent reductions interleaved (independent DPP chains).
+SV_DEV void router_select_rows4(int E, int k, bool renorm, int T, const float (&lv)[4], int* sel,
+                                float* gate_out)
+{
+    const int lane = threadIdx.x & 63;
+    float m[4], e[4];
+#pragma unroll
+    for (int t = 0; t < 4; t++) m[t] = fmaxf(-INFINITY, lane < E ? lv[t] : -INFINITY);   // as router_select_to
+#define SV_ROWS4_MAX(CTRL, RM)                                                              \
+    _Pragma("unroll") for (int t = 0; t < 4; t++) m[t] = fmaxf(m[t], dpp_f32<CTRL, RM>(-INFINITY, m[t]));
+    SV_ROWS4_MAX(DPP_SHR1, 0xf) SV_ROWS4_MAX(DPP_SHR2, 0xf) SV_ROWS4_MAX(DPP_SHR4, 0xf)
+    SV_ROWS4_MAX(DPP_SHR8, 0xf) SV_ROWS4_MAX(DPP_BCAST15, 0xa) SV_ROWS4_MAX(DPP_BCAST31, 0xc)
+#undef SV_ROWS4_MAX
+#pragma unroll
+    for (int t = 0; t < 4; t++) {
+        m[t] = lane63(m[t]);
+        e[t] = lane < E ? __expf(lv[t] - m[t]) : 0.f;
+    }
+    float sum[4];
+#pragma unroll
+    for (int t = 0; t < 4; t++) sum[t] = 0.f + e[t];
+#define SV_ROWS4_SUM(CTRL, RM)                                                              \
+    _Pragma("unroll") for (int t = 0; t < 4; t++) sum[t] += dpp_f32<CTRL, RM>(0.f, sum[t]);
+    SV_ROWS4_SUM(DPP_SHR1, 0xf) SV_ROWS4_SUM(DPP_SHR2, 0xf) SV_ROWS4_SUM(DPP_SHR4, 0xf)
+    SV_ROWS4_SUM(DPP_SHR8, 0xf) SV_ROWS4_SUM(DPP_BCAST15, 0xa) SV_ROWS4_SUM(DPP_BCAST31, 0xc)
+#undef SV_ROWS4_SUM
+    uint32_t hi[4];
+#pragma unroll
+    for (int t = 0; t < 4; t++) {
+        const float inv = 1.f / lane63(sum[t]);
+        hi[t] = lane < E ? route_hi(e[t] * inv) : 0u;
+    }
+    float pr[4][8];
+#pragma unroll
+    for (int r = 0; r < 8; r++) {
+        if (r < k) {
+            uint32_t mx[4];
+#pragma unroll
+            for (int t = 0; t < 4; t++) mx[t] = hi[t];
+#define SV_ROWS4_UMAX(CTRL, RM)                                                             \
+            _Pragma("unroll") for (int t = 0; t < 4; t++) mx[t] = dpp_max_u32<CTRL, RM>(mx[t]);
+            SV_ROWS4_UMAX(DPP_SHR1, 0xf) SV_ROWS4_UMAX(DPP_SHR2, 0xf) SV_ROWS4_UMAX(DPP_SHR4, 0xf)
+            SV_ROWS4_UMAX(DPP_SHR8, 0xf) SV_ROWS4_UMAX(DPP_BCAST15, 0xa) SV_ROWS4_UMAX(DPP_BCAST31, 0xc)
+#undef SV_ROWS4_UMAX
+#pragma unroll
+            for (int t = 0; t < 4; t++) {
+                const uint32_t b = (uint32_t)__builtin_amdgcn_readlane((int)mx[t], 63);
+                const int ew = __builtin_ctzll(__ballot(hi[t] == b));   // the lowest expert holding it
+                pr[t][r] = route_hi_value(b);
+                hi[t] = lane == ew ? 0u : hi[t];
+                if (lane == 0 && t < T) sel[t * k + r] = ew;
+            }
+        } else {
+#pragma unroll
+            for (int t = 0; t < 4; t++) pr[t][r] = 0.f;
+        }
+    }
+    if (lane < k) {
+#pragma unroll
+        for (int t = 0; t < 4; t++) {
+            if (t >= T) break;
+            float gsum = 0.f;
+#pragma unroll
+            for (int rr = 0; rr < 8; rr++) gsum += rr < k ? pr[t][rr] : 0.f;   // in rank order
+            float pe = pr[t][0];
+#pragma unroll
+            for (int rr = 1; rr < 8; rr++) pe = lane == rr ? pr[t][rr] : pe;
+            gate_out[t * k + lane] = renorm ? pe / gsum : pe;
+        }
+    }
+}
+
 // ---------------------------------------------------------------- paged KV
 // With a page table the cache of (sequence b, layer l, KV head h) is split in
 // pages of `page` positions: table [B][max_pages] holds physical page indices

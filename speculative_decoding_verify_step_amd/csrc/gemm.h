@@ -55,6 +55,15 @@ struct GemmArgs {
     const int* sel;         // grouped, few rows: tiles implied by the selections [T][topk]
                             // (then tiles/n_tiles/gather are unused; see implied_tile)
     int sel_T, sel_k, sel_E, sel_S;
+    // selections made here (SwiGLU): with sel_logits set (router logits
+    // [T][E], T <= 4, E <= 64) every workgroup selects the experts itself
+    // (router_select_to) instead of reading `sel`, and workgroup 0 publishes
+    // them for the kernels that follow (sel_out, gate_out, dbg_sel_out: [T][topk])
+    const float* sel_logits;
+    int sel_renorm;
+    int* sel_out;
+    float* gate_out;
+    int* dbg_sel_out;
     int MT;                 // row tiles in the grid (dense: ceil(M / BM); grouped: max tiles)
     int NT;                 // column tiles (16*NF*WAVES columns each)
     void* out;              // STORE: fp32 [ksplit][rows][ldo]; SWIGLU: act [rows][ldo]
@@ -331,7 +340,31 @@ __global__ __launch_bounds__(64 * WAVES) void gemm_kernel(GemmArgs a)
     int xtok = -1;   // implied tiles: activation row of this lane's row l16 (MF == 1)
     if (a.sel) {
         const int A = a.sel_T * a.sel_k;
-        const int sv = min(max(a.sel[min(lane, A - 1)], 0), a.sel_E - 1);
+        int sraw = 0;
+        bool selected = false;
+        if constexpr (MODE == GM_SWIGLU) {
+            if (a.sel_logits) {
+                // the routing's selection of every row (T <= 4, E <= 64): all
+                // rows' logits in one round trip, then the selections in this wave
+                __shared__ int ssel[WAVES][64];
+                __shared__ float sgate[WAVES][64];
+                const int E = a.sel_E;
+                float lv[4];
+#pragma unroll
+                for (int t = 0; t < 4; t++) lv[t] = a.sel_logits[(size_t)min(t, a.sel_T - 1) * E + min(lane, E - 1)];
+                router_select_rows4(E, a.sel_k, a.sel_renorm != 0, a.sel_T, lv, ssel[wave], sgate[wave]);
+                __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+                sraw = ssel[wave][min(lane, A - 1)];
+                if (blockIdx.x == 0 && blockIdx.y == 0 && wave == 0 && lane < A) {
+                    a.sel_out[lane] = sraw;
+                    a.gate_out[lane] = sgate[0][lane];
+                    if (a.dbg_sel_out) a.dbg_sel_out[lane] = sraw;
+                }
+                selected = true;
+            }
+        }
+        if (!selected) sraw = a.sel[min(lane, A - 1)];
+        const int sv = min(max(sraw, 0), a.sel_E - 1);
         const ImpliedTile it = implied_tile(sv, A, a.sel_T, a.sel_E, a.sel_S, mt);
         group = it.group;
         row0 = it.row0;

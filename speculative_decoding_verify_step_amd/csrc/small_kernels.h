@@ -248,81 +248,12 @@ SV_DEV void router_logits(const RowArgs& a, const float* hs, uint4 (&wv)[4][UPW]
     }
 }
 
-// Selection key of expert e with probability v: argmax_key's order (larger
-// probability first, then the lower index), with a NaN probability keeping
-// its index too (all-ones high half), so that every key is distinct.
-SV_DEV unsigned long long route_key(float v, int e)
-{
-    if (v != v) return (0xffffffffull << 32) | (unsigned long long)(0xffffffffu - (uint32_t)e);
-    return argmax_key(v, (uint32_t)e);
-}
-
-// The probability a selection key was made from (exact; NaN for NaN).
-SV_DEV float route_key_value(unsigned long long key)
-{
-    const uint32_t hi = (uint32_t)(key >> 32);
-    if (hi == 0xffffffffu) return __uint_as_float(0x7fc00000u);
-    return __uint_as_float((hi & 0x80000000u) ? (hi & 0x7fffffffu) : ~hi);
-}
-
-// Softmax over the E logits of row t (lane l holds experts l + 64 q) in fp32,
-// top-k by probability with the lower expert index first on ties, gates = the
-// selected probabilities (optionally renormalised, summed in rank order).  One
-// wave, k <= 8.  The r-th choice is the largest of the remaining distinct keys
-// (a DPP maximum over the wave, k rounds; the winner's owner lane drops its
-// key), which is the rank-r expert of the ordering above.  `kbuf` is unused
-// (kept for the callers' shared-memory layout).
+// Selection of row t for the routing kernels (router_select_to).
 SV_DEV void router_select(const RowArgs& a, int t, float (&p)[4], unsigned long long* kbuf,
                           unsigned short* sel_lds = nullptr)
 {
-    (void)kbuf;
-    const int lane = threadIdx.x & 63, E = a.E, k = a.topk;
-    float m = -INFINITY;
-#pragma unroll
-    for (int q = 0; q < 4; q++) m = fmaxf(m, p[q]);
-    m = wave_max(m);
-    float sum = 0.f;
-#pragma unroll
-    for (int q = 0; q < 4; q++) {
-        p[q] = (lane + 64 * q < E) ? __expf(p[q] - m) : 0.f;
-        sum += p[q];
-    }
-    sum = wave_sum(sum);
-    const float inv = 1.f / sum;
-    unsigned long long key[4];
-#pragma unroll
-    for (int q = 0; q < 4; q++) {
-        p[q] *= inv;
-        const int e = lane + 64 * q;
-        key[q] = e < E ? route_key(p[q], e) : 0ull;
-    }
-    float pr[8];
-#pragma unroll
-    for (int r = 0; r < 8; r++) {
-        pr[r] = 0.f;
-        if (r < k) {
-            unsigned long long best = umax64(umax64(key[0], key[1]), umax64(key[2], key[3]));
-            best = wave_max_u64(best);
-            const int e = (int)(0xffffffffu - (uint32_t)best);
-            pr[r] = route_key_value(best);
-#pragma unroll
-            for (int q = 0; q < 4; q++) key[q] = key[q] == best ? 0ull : key[q];
-            if (lane == 0) {
-                a.sel[t * k + r] = e;
-                if (sel_lds) sel_lds[t * k + r] = (unsigned short)e;
-                if (a.dbg_sel) a.dbg_sel[t * k + r] = e;
-            }
-        }
-    }
-    if (lane < k) {
-        float gsum = 0.f;
-#pragma unroll
-        for (int rr = 0; rr < 8; rr++) gsum += rr < k ? pr[rr] : 0.f;   // in rank order
-        float pe = pr[0];
-#pragma unroll
-        for (int rr = 1; rr < 8; rr++) pe = lane == rr ? pr[rr] : pe;
-        a.gate_out[t * k + lane] = a.renorm ? pe / gsum : pe;
-    }
+    (void)kbuf;   // unused (kept for the callers' shared-memory layout)
+    router_select_to(a.E, a.topk, a.renorm != 0, t, p, a.sel, a.gate_out, a.dbg_sel, sel_lds);
 }
 
 // Router permutation over all T rows (the selections already in shared
