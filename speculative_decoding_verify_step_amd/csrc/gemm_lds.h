@@ -17,8 +17,8 @@
 // carries elements KL*(2u + l/32) + 8h .. +7 of the step, for the weight
 // fragment (row l%32) and for the activation fragment (row l%32) alike.
 //
-// Used for the bf16 LM head at 129 .. 256 rows (batch 64: 136 -> 115 us per
-// launch, same box).  What bounds it is the copy into LDS, not the products:
+// Used for the bf16 LM head at 65 .. 256 rows (batch 64: 136 -> 115 us per
+// launch, same box; 128-row tiles up to 128 rows).  What bounds it is the copy into LDS, not the products:
 // with the products skipped the same launch took 105 us (about 6.2 TB/s of
 // operands moved into LDS, the 256 activation rows re-read for every
 // 256-column tile); the fp8 LM head and the SwiGLU and K-split projections
