@@ -1,15 +1,15 @@
 // gemm_lds.h -- dense GEMMs with up to 256 activation rows on bf16 matrix
 // cores, both operands staged in LDS by direct global -> LDS loads.
 //
-// A workgroup of RG x 4 waves owns a tile of RG*MR*32 activation rows x 256
-// weight rows (output columns; SwiGLU: 128 gate + the 128 matching up rows,
-// 128 outputs).  Every reduction step of the tiled16 layout (SK elements) is
+// A workgroup of RG x 4 waves owns a tile of RG*MR*32 activation rows x
+// 128*NF weight rows (output columns; SwiGLU: 128 gate + the 128 matching up
+// rows, 128 outputs).  Every reduction step of the tiled16 layout (SK elements) is
 // one pipeline stage: the workgroup copies the step's 16 weight pieces (one
 // 1 KiB piece per 16-row block, already in MFMA operand order) and its
 // activation operands (64 lanes x 16 bytes each, gathered from the row-major
 // activations in the order the matrix instruction reads them) straight into
 // LDS, S stages deep; no register staging.  Wave (rg, cg) multiplies its MR
-// activation fragments by its 2 weight fragments (32x32x16 products, fp32
+// activation fragments by its NF weight fragments (32x32x16 products, fp32
 // accumulation) for every stage, so each weight byte is read from HBM once
 // and each activation byte once per workgroup.
 //
@@ -27,15 +27,16 @@
 #include "gemm.h"
 #include "lds_dma.h"
 
-template <int WT, int MODE, int RG, int MR, int S>
+template <int WT, int MODE, int RG, int MR, int S, int NF = 2>
 __global__ __launch_bounds__(256 * RG) void gemm_lds_kernel(GemmArgs a)
 {
     static_assert(WT == SV_BF16 || WT == SV_FP8, "bf16 or fp8 weights");
-    constexpr int CG = 4, NF = 2, WAVES = RG * CG;
+    static_assert(MODE != GM_SWIGLU || NF == 2, "SwiGLU tiles: 128 gate + 128 up columns");
+    constexpr int CG = 4, WAVES = RG * CG;
     constexpr int WESZ = (WT == SV_FP8) ? 1 : 2;
     constexpr int KL = 16 / WESZ, SK = 4 * KL, XU = (WT == SV_FP8) ? 2 : 1;
     constexpr int BM = 32 * MR * RG;                 // activation rows per tile
-    constexpr int WPC = 16;                          // weight pieces per stage (256 weight rows)
+    constexpr int WPC = 8 * NF;                      // weight pieces per stage (128 NF weight rows)
     constexpr int XPC = (BM / 32) * 2 * XU;          // activation operand pieces per stage
     constexpr int PPS = WPC + XPC;
     static_assert(PPS % WAVES == 0, "pieces per wave");
@@ -53,7 +54,7 @@ __global__ __launch_bounds__(256 * RG) void gemm_lds_kernel(GemmArgs a)
     const int K = a.K, kspan = K / a.ksplit, kb = blockIdx.y * kspan, nst = kspan / SK;
     const int nrb = a.N / 16;                        // 16-row weight blocks (SwiGLU: gate part)
     // output columns of the tile: 256 (store, argmax) or 128 gate columns (SwiGLU)
-    constexpr int TN = (MODE == GM_SWIGLU) ? 128 : 256;
+    constexpr int TN = (MODE == GM_SWIGLU) ? 128 : 128 * NF;
     const int n_tile0 = nt * TN;
 
     // this wave's global -> LDS loads: piece p = wave * LPW + i

@@ -421,14 +421,17 @@ void launch_gemm_wide(int wt, int mode, GemmArgs& a, hipStream_t s)
     else launch_wide_t<SV_FP8>(mode, cs, a, grid, s);
 }
 
-// bf16 LM head at 65 .. 256 rows: both operands staged in LDS, 128- or 256-row
-// tiles of 8 waves, 4 stages (gemm_lds.h)
-// 65 .. 128 rows on 128-row tiles (batch 32: 2,301.7 -> 2,294.6 us per step
-// against the 128-row register-staged tiles, same box), 129 .. 256 on 256
+// bf16 LM head at 65 .. 256 rows: both operands staged in LDS, tiles of 8
+// waves (gemm_lds.h).  129 .. 256 rows: 256 x 256 tiles, 4 stages.  65 .. 128
+// rows: 128 x 512 tiles, 3 stages (120 KB), so each activation row is copied
+// once per 512 columns (batch 32: LM head 86.6 -> 72.5 us per launch, step
+// 2,301.7 -> 2,283.5 us against the register-staged 128 x 128 tiles, same box)
+int lm_head_lds_cols(int T) { return T <= 128 ? 512 : 256; }
+
 void launch_lm_head_lds(const GemmArgs& a, hipStream_t s)
 {
     dim3 grid((unsigned)(cdiv(a.NT * a.MT, 8) * 8), 1, 1), blk(512);
-    if (a.M <= 128) launch(gemm_lds_kernel<SV_BF16, GM_ARGMAX, 2, 2, 4>, grid, blk, 0, s, a);
+    if (a.M <= 128) launch(gemm_lds_kernel<SV_BF16, GM_ARGMAX, 2, 2, 3, 4>, grid, blk, 0, s, a);
     else launch(gemm_lds_kernel<SV_BF16, GM_ARGMAX, 2, 4, 4>, grid, blk, 0, s, a);
 }
 
@@ -1070,7 +1073,7 @@ static int step_impl(spec_verify_ctx* c, const spec_verify_weights* w, void* k_c
         if (big && packed && mode == GM_ARGMAX && wtd == SV_BF16 && T > 64 && T <= 256 &&
             Kd % wsteps(SV_BF16) == 0) {
             a.MT = 1;
-            a.NT = cdiv(N, 256);
+            a.NT = cdiv(N, lm_head_lds_cols(T));
             a.ksplit = 1;
             launch_lm_head_lds(a, s);
             last_nt = a.NT;
