@@ -156,6 +156,20 @@ def test_gqa_many_rows_attention_shapes(H, k_draft, head_dim, waves):
     assert stats["argmax_agree"] >= 0.8 * stats["positions"]
 
 
+@pytest.mark.parametrize("batch", [24, 40])
+def test_lds_lm_head_ragged_vocabulary(H, batch):
+    """The LDS-staged bf16 LM head on both of its tile shapes -- 96 rows on
+    128 x 512 tiles, 160 rows on 256 x 256 tiles -- with a vocabulary that
+    ends inside the last tile (5,008 = 9 x 512 + 400 = 19 x 256 + 144; the
+    library takes vocabularies in multiples of 16): the
+    argmax over the partial tile and the tile keys the acceptance reads."""
+    cfg = workloads.scaled(workloads.get_config("moe_b32"), n_layers=1, vocab=5008, batch=batch,
+                           ctx=("uniform", 30, 400))
+    stats, g = _verify_case(H, cfg, sampled=[0, batch // 2, batch - 1], label=f"lm_head_lds_b{batch}")
+    assert np.all(g["target"] >= 0) and np.all(g["target"] < cfg.vocab)
+    assert stats["argmax_agree"] >= 0.8 * stats["positions"]
+
+
 def test_dense_fp8_gqa_full_width_sampled(H):
     """The full fp8 dense layer width (hidden 2560, 32/8 heads, I 9728, vocab
     151,936) with 2 layers; two sequences of the batch checked."""
