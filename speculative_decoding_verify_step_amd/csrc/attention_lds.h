@@ -24,12 +24,14 @@
 SV_DEV float max_over_lane_groups(float v)
 {
     auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-    const float a = __uint_as_float(r[0]), b = __uint_as_float(r[1]);
-    v = a > b ? a : b;
+    v = fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
     auto r2 = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-    const float c = __uint_as_float(r2[0]), d = __uint_as_float(r2[1]);
-    return c > d ? c : d;
+    return fmaxf(__uint_as_float(r2[0]), __uint_as_float(r2[1]));
 }
+
+// bf16 1.0 in every element: the A operand whose product with the weights
+// gives each query row's weight sum
+constexpr uint32_t BF16_ONE_X2 = 0x3f803f80u;
 
 // One 32-key bf16 tile for one 16-row query fragment, as attn_tile, with
 // less vector-ALU work per score (the scores per tile are as many as the
@@ -40,12 +42,17 @@ SV_DEV float max_over_lane_groups(float v)
 //    exceeds it by more than 2^8 (lazy rescaling: weights 2^(s - base) stay
 //    below 2^8, exact in bf16's range and fp32 sums); the output and sum are
 //    rescaled only then, for the rows whose base moved;
-//  * the 1/sqrt(D) scale folds into the exponent's fused multiply-add.
+//  * the 1/sqrt(D) scale folds into the exponent's fused multiply-add;
+//  * the weight sum is one more matrix product, of the bf16 weights with a
+//    fragment of ones (`lsum`: every lane of query row l16 holds the row's
+//    sum), so the sum adds up exactly the rounded weights the output
+//    product uses;
+//  * maxima are plain float max instructions.
 // The partial (base, sum, output) means the same as attn_tile's.
 template <int DH>
 SV_DEV void attn_tile_lazy(const uint4 (&kf)[2][DH / 32], const uint4 (&vf)[DH / 16],
                            const uint4 (&qf)[DH / 32], int kt, int lg, int limit, bool nomask,
-                           float scale_log2, float& m_run, float& l_run, f32x4_t (&o)[DH / 16])
+                           float scale_log2, float& m_run, f32x4_t& lsum, f32x4_t (&o)[DH / 16])
 {
     constexpr int KL = 8, DS = DH / 32, DF = DH / 16, NB = 2;
     constexpr float TAU = 8.f;
@@ -59,29 +66,28 @@ SV_DEV void attn_tile_lazy(const uint4 (&kf)[2][DH / 32], const uint4 (&vf)[DH /
         for (int r = 0; r < 4; r++) s[4 * blk + r] = acc[r];
     }
     if (!nomask) {
+        const int rel = limit - (kt + KL * lg);   // score e is visible when e <= rel
 #pragma unroll
-        for (int e = 0; e < KL; e++) s[e] = (kt + KL * lg + e <= limit) ? s[e] : -INFINITY;
+        for (int e = 0; e < KL; e++) s[e] = (e <= rel) ? s[e] : -INFINITY;
     }
-    float mt = s[0];
-#pragma unroll
-    for (int e = 1; e < KL; e++) mt = mt > s[e] ? mt : s[e];
+    float mt = fmaxf(fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3])), fmaxf(fmaxf(s[4], s[5]), fmaxf(s[6], s[7])));
     mt = max_over_lane_groups(mt) * scale_log2;      // the scale is positive
     const bool grow = mt > m_run + TAU;              // also from an empty (-inf) base
     if (__any(grow)) {
         const float mnew = grow ? mt : m_run;
         const float alpha = grow ? exp2_fast(m_run - mnew) : 1.f;
         m_run = mnew;
-        l_run *= alpha;
+        lsum = lsum * alpha;
 #pragma unroll
         for (int d = 0; d < DF; d++) o[d] = o[d] * alpha;
     }
     const float nbase = (m_run == -INFINITY) ? 0.f : -m_run;
-    float p[KL], ps = 0.f;
+    float p[KL];
 #pragma unroll
-    for (int e = 0; e < KL; e++) { p[e] = exp2_fast(fmaf(s[e], scale_log2, nbase)); ps += p[e]; }
-    l_run += ps;
+    for (int e = 0; e < KL; e++) p[e] = exp2_fast(fmaf(s[e], scale_log2, nbase));
     const uint4 pb = make_uint4(pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]),
                                 pack_bf16x2(p[4], p[5]), pack_bf16x2(p[6], p[7]));
+    lsum = mma_bf16(make_uint4(BF16_ONE_X2, BF16_ONE_X2, BF16_ONE_X2, BF16_ONE_X2), pb, lsum);
 #pragma unroll
     for (int d = 0; d < DF; d++) o[d] = mma_bf16(vf[d], pb, o[d]);
 }
@@ -150,12 +156,12 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2))) vo
         }
     };
 
-    float m_run[FPW], l_run[FPW];
-    f32x4_t o[FPW][DF];
+    float m_run[FPW];
+    f32x4_t lsum[FPW], o[FPW][DF];
 #pragma unroll
     for (int i = 0; i < FPW; i++) {
         m_run[i] = -INFINITY;
-        l_run[i] = 0.f;
+        lsum[i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int d = 0; d < DF; d++) o[i][d] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     }
@@ -211,10 +217,12 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2))) vo
 #pragma unroll
         for (int i = 0; i < FPW; i++)
             attn_tile_lazy<DH>(kf, vf, qf[i], kt, lg, limit[i], before_ctx && (wave * FPW + i + 1) * 16 <= R,
-                               a.scale_log2, m_run[i], l_run[i], o[i]);
+                               a.scale_log2, m_run[i], lsum[i], o[i]);
     }
 
 #pragma unroll
     for (int i = 0; i < FPW; i++)
-        attn_write_partial<DH>(a, b, hkv, chunk, wave * FPW + i, l16, lg, m_run[i], l_run[i], o[i]);
+        // every lane group holds the whole row sum: a quarter each, which the
+        // writer's sum over the four lane groups restores exactly
+        attn_write_partial<DH>(a, b, hkv, chunk, wave * FPW + i, l16, lg, m_run[i], 0.25f * lsum[i][0], o[i]);
 }
