@@ -128,6 +128,80 @@ SV_DEV void attn_tile(const uint4 (&kf)[(BF ? 8 : 4) / 4][DH / (4 * (BF ? 8 : 4)
     }
 }
 
+// Maximum over the four 16-lane rows' lanes l, l ^ 16, l ^ 32, l ^ 48 (lane
+// groups lg of one query row) with the gfx950 row swaps: VALU only, no LDS
+// round trip.
+SV_DEV float max_over_lane_groups(float v)
+{
+    auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    v = fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+    auto r2 = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return fmaxf(__uint_as_float(r2[0]), __uint_as_float(r2[1]));
+}
+
+// bf16 1.0 in every element: the A operand whose product with the weights
+// gives each query row's weight sum
+constexpr uint32_t BF16_ONE_X2 = 0x3f803f80u;
+
+// One 32-key bf16 tile for one 16-row query fragment, as attn_tile, with
+// less vector-ALU work per score (the scores per tile are as many as the
+// products' multiply-adds per 256, so the ALU is what bounds many-row tiles):
+//  * the causal mask is applied only to tiles that reach past the context
+//    (`nomask`: every key of the tile is visible to every row);
+//  * the running maximum is a base that moves only when a row's tile maximum
+//    exceeds it by more than 2^8 (lazy rescaling: weights 2^(s - base) stay
+//    below 2^8, exact in bf16's range and fp32 sums); the output and sum are
+//    rescaled only then, for the rows whose base moved;
+//  * the 1/sqrt(D) scale folds into the exponent's fused multiply-add;
+//  * the weight sum is one more matrix product, of the bf16 weights with a
+//    fragment of ones (`lsum`: every lane of query row l16 holds the row's
+//    sum), so the sum adds up exactly the rounded weights the output
+//    product uses;
+//  * maxima are plain float max instructions.
+// The partial (base, sum, output) means the same as attn_tile's.
+template <int DH>
+SV_DEV void attn_tile_lazy(const uint4 (&kf)[2][DH / 32], const uint4 (&vf)[DH / 16],
+                           const uint4 (&qf)[DH / 32], int kt, int lg, int limit, bool nomask,
+                           float scale_log2, float& m_run, f32x4_t& lsum, f32x4_t (&o)[DH / 16])
+{
+    constexpr int KL = 8, DS = DH / 32, DF = DH / 16, NB = 2;
+    constexpr float TAU = 8.f;
+    float s[KL];
+#pragma unroll
+    for (int blk = 0; blk < NB; blk++) {
+        f32x4_t acc = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int st = 0; st < DS; st++) acc = mma_bf16(kf[blk][st], qf[st], acc);
+#pragma unroll
+        for (int r = 0; r < 4; r++) s[4 * blk + r] = acc[r];
+    }
+    if (!nomask) {
+        const int rel = limit - (kt + KL * lg);   // score e is visible when e <= rel
+#pragma unroll
+        for (int e = 0; e < KL; e++) s[e] = (e <= rel) ? s[e] : -INFINITY;
+    }
+    float mt = fmaxf(fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3])), fmaxf(fmaxf(s[4], s[5]), fmaxf(s[6], s[7])));
+    mt = max_over_lane_groups(mt) * scale_log2;      // the scale is positive
+    const bool grow = mt > m_run + TAU;              // also from an empty (-inf) base
+    if (__any(grow)) {
+        const float mnew = grow ? mt : m_run;
+        const float alpha = grow ? exp2_fast(m_run - mnew) : 1.f;
+        m_run = mnew;
+        lsum = lsum * alpha;
+#pragma unroll
+        for (int d = 0; d < DF; d++) o[d] = o[d] * alpha;
+    }
+    const float nbase = (m_run == -INFINITY) ? 0.f : -m_run;
+    float p[KL];
+#pragma unroll
+    for (int e = 0; e < KL; e++) p[e] = exp2_fast(fmaf(s[e], scale_log2, nbase));
+    const uint4 pb = make_uint4(pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]),
+                                pack_bf16x2(p[4], p[5]), pack_bf16x2(p[6], p[7]));
+    lsum = mma_bf16(make_uint4(BF16_ONE_X2, BF16_ONE_X2, BF16_ONE_X2, BF16_ONE_X2), pb, lsum);
+#pragma unroll
+    for (int d = 0; d < DF; d++) o[d] = mma_bf16(vf[d], pb, o[d]);
+}
+
 // Partial of one chunk for one 16-row query fragment (row r = 16 f + l16 of
 // the KV head's R rows): O^T[d = 16 df + 4 lg + i][row l16] and (max, sum).
 template <int DH>
@@ -229,11 +303,12 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(1, STREAM ? 
     }
 
     float m_run[QPW], l_run[QPW];
-    f32x4_t o[QPW][DF];
+    f32x4_t lsum[QPW], o[QPW][DF];   // bf16: row sums as products (lsum), fp32: l_run
 #pragma unroll
     for (int f = 0; f < QPW; f++) {
         m_run[f] = -INFINITY;
         l_run[f] = 0.f;
+        lsum[f] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int d = 0; d < DF; d++) o[f][d] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     }
@@ -267,14 +342,22 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(1, STREAM ? 
 #pragma unroll
         for (int d = 0; d < DF; d++) vf[d] = kvload(kt_v + (size_t)d * 1024);
         if (kt + KT > total) attn_clear_dead<BF, DF>(vf, kt, lg, total);
+        // every key of the tile at or before the context end: visible to every
+        // row of the block (rows past R are never written)
+        const bool before_ctx = kt + KT - 1 <= ctx;
 #pragma unroll
-        for (int f = 0; f < QPW; f++)
-            attn_tile<BF, DH>(kf, vf, qf[f], kt, lg, limit[f], a.scale_log2, m_run[f], l_run[f], o[f]);
+        for (int f = 0; f < QPW; f++) {
+            if constexpr (BF)
+                attn_tile_lazy<DH>(kf, vf, qf[f], kt, lg, limit[f], before_ctx, a.scale_log2, m_run[f], lsum[f], o[f]);
+            else
+                attn_tile<BF, DH>(kf, vf, qf[f], kt, lg, limit[f], a.scale_log2, m_run[f], l_run[f], o[f]);
+        }
     }
 
 #pragma unroll
     for (int f = 0; f < QPW; f++)
-        attn_write_partial<DH>(a, b, hkv, chunk, qgi * QPW + f, l16, lg, m_run[f], l_run[f], o[f]);
+        attn_write_partial<DH>(a, b, hkv, chunk, qgi * QPW + f, l16, lg, m_run[f],
+                               BF ? 0.25f * lsum[f][0] : l_run[f], o[f]);
 }
 
 // Merge the chunk partials of one (sequence, query head, position) row in
