@@ -399,12 +399,25 @@ int wide_col_tile(int mode) { return 32 * WIDE_WAVES * (mode == GM_SWIGLU ? WIDE
 
 // Steps per staged chunk: 2, except the fp8 LM head with 1 (three waves per
 // SIMD instead of two: 273 -> 262 us per launch at 256 rows, same box).
+// fp8 projections whose K split holds 16 or more reduction steps (the down
+// projection, K = 9,728 in 4 splits of 38) run the same 64 x 256 tiles on the
+// LDS-staged kernel with 3 stages (two steps in flight per workgroup without
+// registers): dense fp8 K = 31, down 41.3 -> 32.1 us per layer (step 1,904 ->
+// 1,833 us, same box).  Shorter splits (QKV, O: 8 steps), the fp8 SwiGLU
+// (41 -> 52 us) and LM head (33 -> 34 us per step), and bf16 at 256 rows (QKV
+// and O of batch 64: +12 us per step) measured no faster there.
+constexpr int WIDE_LDS_MIN_STEPS = 16;
+
 template <int WT>
 void launch_wide_t(int mode, int cs, const GemmArgs& a, dim3 grid, hipStream_t s)
 {
     const dim3 blk(64 * WIDE_WAVES);
     if (mode == GM_STORE) {
-        launch(gemm_wide_kernel<WT, WIDE_MW, WIDE_NW, GM_STORE, WIDE_WAVES, 2>, grid, blk, 0, s, a);
+        if (WT == SV_FP8 && a.K / a.ksplit >= WIDE_LDS_MIN_STEPS * WTraits<WT>::SK &&
+            (a.K / a.ksplit) % WTraits<WT>::SK == 0)
+            launch(gemm_lds_kernel<WT, GM_STORE, 1, WIDE_MW, 3, WIDE_NW>, grid, blk, 0, s, a);
+        else
+            launch(gemm_wide_kernel<WT, WIDE_MW, WIDE_NW, GM_STORE, WIDE_WAVES, 2>, grid, blk, 0, s, a);
     } else if (mode == GM_SWIGLU) {
         launch(gemm_wide_kernel<WT, WIDE_MW, WIDE_NW, GM_SWIGLU, WIDE_WAVES, 2>, grid, blk, 0, s, a);
     } else {
