@@ -404,8 +404,8 @@ int wide_col_tile(int mode) { return 32 * WIDE_WAVES * (mode == GM_SWIGLU ? WIDE
 // LDS-staged kernel with 3 stages (two steps in flight per workgroup without
 // registers): dense fp8 K = 31, down 41.3 -> 32.1 us per layer (step 1,904 ->
 // 1,833 us, same box).  Shorter splits (QKV, O: 8 steps), the fp8 SwiGLU
-// (41 -> 52 us) and LM head (33 -> 34 us per step), and bf16 at 256 rows (QKV
-// and O of batch 64: +12 us per step) measured no faster there.
+// (47.5 -> 52.1 us per layer), the fp8 LM head (265 -> 272 us) and bf16 at 256
+// rows (QKV and O of batch 64: 208 -> 220 us per step) measured no faster there.
 constexpr int WIDE_LDS_MIN_STEPS = 16;
 
 template <int WT>
