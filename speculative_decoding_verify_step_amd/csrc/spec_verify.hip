@@ -1105,6 +1105,19 @@ static int step_impl(spec_verify_ctx* c, const spec_verify_weights* w, void* k_c
                     a.ksplit = sp;
                 }
             }
+            // fp8 projections: the most K splits of 16 or more 64-long steps
+            // within 512 workgroups, which run on the LDS-staged kernel (see
+            // launch_wide_t; QKV of the dense fp8 model: 2 splits of 20 steps
+            // instead of 5 of 8 on the register-staged kernel, 23.2 -> 22.5 us
+            // per layer; down: 8 splits of 19 steps)
+            if (wide && wtd == SV_FP8 && mode == GM_STORE && allow_split > 1) {
+                const int steps64 = Kd / 64;
+                for (int sp = 2; sp <= allow_split; sp++) {
+                    if (steps64 % sp || steps64 / sp < WIDE_LDS_MIN_STEPS) continue;
+                    if (wgs * sp > 512) break;
+                    a.ksplit = sp;
+                }
+            }
             if (wide) launch_gemm_wide(wt, mode, a, s);
             else launch_gemm_big(wtd, mode, packed, a, s);
             last_nt = a.NT;
