@@ -177,6 +177,20 @@ def test_dense_fp8_gqa_full_width_sampled(H):
     _verify_case(H, cfg, sampled=[5], label="dense_fp8_wide")
 
 
+def test_fp8_lds_projections_ragged(H):
+    """fp8 projections on the LDS-staged kernel (K splits of 16 or more
+    64-long steps) with ragged tiles: 160 rows (row tiles of 64, 64, 32) and
+    hidden 1,216 = 4 x 256 + 192 output columns.  The O projection (K =
+    16 x 128 = 2,048) and the down projection (K = 2,048) each run 2 splits of
+    16 steps there; QKV and gate/up (K = 1,216, not a multiple of the 128-long
+    chunk) take the small-row kernel."""
+    cfg = workloads.scaled(workloads.get_config("dense_fp8_b8"), n_layers=2, hidden=1216, n_q=16,
+                           n_kv=4, dense_inter=2048, vocab=4096, batch=5,
+                           ctx=("uniform", 100, 900))
+    stats, _ = _verify_case(H, cfg, label="fp8_lds_ragged")
+    assert stats["argmax_agree"] >= 0.8 * stats["positions"]
+
+
 @pytest.mark.parametrize("name,overrides", [
     ("tiny_fp32", {"batch": 3, "ctx": ("uniform", 20, 400)}),
     ("moe_b32", {"n_layers": 2, "vocab": 4096, "batch": 5, "ctx": ("uniform", 30, 500)}),
