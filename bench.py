@@ -484,6 +484,7 @@ def block(cfg, r, steps, graph, sampled=False, kv_page=0):
                           "frac": step_gbs / HBM_PEAK_GBS,
                           "distinct_experts_per_layer": r["distinct_experts"]},
         "kernels": r["kernels"],
+        **({"sampling_us_per_step": r["sampling_us_per_step"]} if sampled else {}),
     }
 
 
@@ -686,6 +687,7 @@ def _line(cfg, r, steps, warmup, graph, args, blk):
         "p50_us": blk["p50_us"],
         "p90_us": blk["p90_us"],
         "kernels": blk["kernels"],
+        **({"sampling_us_per_step": blk["sampling_us_per_step"]} if "sampling_us_per_step" in blk else {}),
     }
     if cfg.name == HEADLINE and not args.sampled and not args.kv_page:
         # the batch-1 target applies to the whole step, not to one kernel
