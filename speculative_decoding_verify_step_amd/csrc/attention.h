@@ -72,28 +72,22 @@ SV_DEV void attn_clear_dead(uint4 (&vf)[DF], int kt, int lg, int total)
     }
 }
 
-// One key tile (4 KL keys) for one 16-row query fragment: the scores, the
-// running (max, sum) of each row and the output product.  Row l16's keys past
-// `limit` (causal end; -1 for a padding row) are masked.
-template <bool BF, int DH>
-SV_DEV void attn_tile(const uint4 (&kf)[(BF ? 8 : 4) / 4][DH / (4 * (BF ? 8 : 4))],
-                      const uint4 (&vf)[DH / 16], const uint4 (&qf)[DH / (4 * (BF ? 8 : 4))], int kt,
-                      int lg, int limit, float scale_log2, float& m_run, float& l_run,
-                      f32x4_t (&o)[DH / 16])
+// One key tile (16 keys) of an fp32 cache for one 16-row query fragment: the
+// scores, the running (max, sum) of each row and the output product.  Row
+// l16's keys past `limit` (causal end; -1 for a padding row) are masked.
+// (bf16 caches use attn_tile_lazy below.)
+template <int DH>
+SV_DEV void attn_tile_f32(const uint4 (&kf)[1][DH / 16], const uint4 (&vf)[DH / 16],
+                          const uint4 (&qf)[DH / 16], int kt, int lg, int limit, float scale_log2,
+                          float& m_run, float& l_run, f32x4_t (&o)[DH / 16])
 {
-    constexpr int KL = BF ? 8 : 4, DS = DH / (4 * KL), DF = DH / 16, NB = KL / 4;
+    constexpr int KL = 4, DS = DH / 16, DF = DH / 16;
     float s[KL];
+    f32x4_t acc = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int blk = 0; blk < NB; blk++) {
-        f32x4_t acc = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    for (int st = 0; st < DS; st++) acc = mma_f32x4(kf[0][st], qf[st], acc);
 #pragma unroll
-        for (int st = 0; st < DS; st++) {
-            if constexpr (BF) acc = mma_bf16(kf[blk][st], qf[st], acc);
-            else acc = mma_f32x4(kf[blk][st], qf[st], acc);
-        }
-#pragma unroll
-        for (int r = 0; r < 4; r++) s[4 * blk + r] = acc[r];
-    }
+    for (int r = 0; r < 4; r++) s[r] = acc[r];
     // lane (lg, l16) holds keys kt + KL*lg + e for row l16 of the fragment
     float mt = -INFINITY;
 #pragma unroll
@@ -112,19 +106,12 @@ SV_DEV void attn_tile(const uint4 (&kf)[(BF ? 8 : 4) / 4][DH / (4 * (BF ? 8 : 4)
 #pragma unroll
     for (int e = 0; e < KL; e++) { p[e] = exp2_fast(s[e] - muse); ps += p[e]; }
     l_run = l_run * alpha + ps;
-    uint4 pb;
-    if constexpr (BF) {
-        pb = make_uint4(pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]),
-                        pack_bf16x2(p[4], p[5]), pack_bf16x2(p[6], p[7]));
-    } else {
-        pb = make_uint4(__float_as_uint(p[0]), __float_as_uint(p[1]), __float_as_uint(p[2]),
-                        __float_as_uint(p[3]));
-    }
+    const uint4 pb = make_uint4(__float_as_uint(p[0]), __float_as_uint(p[1]), __float_as_uint(p[2]),
+                                __float_as_uint(p[3]));
 #pragma unroll
     for (int d = 0; d < DF; d++) {
         o[d] = o[d] * alpha;
-        if constexpr (BF) o[d] = mma_bf16(vf[d], pb, o[d]);
-        else o[d] = mma_f32x4(vf[d], pb, o[d]);
+        o[d] = mma_f32x4(vf[d], pb, o[d]);
     }
 }
 
@@ -143,7 +130,7 @@ SV_DEV float max_over_lane_groups(float v)
 // gives each query row's weight sum
 constexpr uint32_t BF16_ONE_X2 = 0x3f803f80u;
 
-// One 32-key bf16 tile for one 16-row query fragment, as attn_tile, with
+// One 32-key bf16 tile for one 16-row query fragment, as attn_tile_f32, with
 // less vector-ALU work per score (the scores per tile are as many as the
 // products' multiply-adds per 256, so the ALU is what bounds many-row tiles):
 //  * the causal mask is applied only to tiles that reach past the context
@@ -158,7 +145,7 @@ constexpr uint32_t BF16_ONE_X2 = 0x3f803f80u;
 //    sum), so the sum adds up exactly the rounded weights the output
 //    product uses;
 //  * maxima are plain float max instructions.
-// The partial (base, sum, output) means the same as attn_tile's.
+// The partial (base, sum, output) means the same as attn_tile_f32's.
 template <int DH>
 SV_DEV void attn_tile_lazy(const uint4 (&kf)[2][DH / 32], const uint4 (&vf)[DH / 16],
                            const uint4 (&qf)[DH / 32], int kt, int lg, int limit, bool nomask,
@@ -350,7 +337,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(1, STREAM ? 
             if constexpr (BF)
                 attn_tile_lazy<DH>(kf, vf, qf[f], kt, lg, limit[f], before_ctx, a.scale_log2, m_run[f], lsum[f], o[f]);
             else
-                attn_tile<BF, DH>(kf, vf, qf[f], kt, lg, limit[f], a.scale_log2, m_run[f], l_run[f], o[f]);
+                attn_tile_f32<DH>(kf, vf, qf[f], kt, lg, limit[f], a.scale_log2, m_run[f], l_run[f], o[f]);
         }
     }
 
