@@ -138,12 +138,15 @@ def test_dense_fp8_gqa_scaled(H):
     assert stats["argmax_agree"] >= 0.8 * stats["positions"]
 
 
-@pytest.mark.parametrize("k_draft,head_dim,waves", [(15, 128, 2), (63, 128, 8), (31, 64, 4), (7, 64, 1)])
+@pytest.mark.parametrize("k_draft,head_dim,waves", [(15, 128, 2), (63, 128, 8), (31, 64, 4), (7, 64, 1),
+                                                    (4, 128, 1)])
 def test_gqa_many_rows_attention_shapes(H, k_draft, head_dim, waves):
     """The LDS-ring attention kernel (17 .. 256 query rows per KV head) at
     each of its workgroup shapes: (K+1) x 4 grouped query heads = 64, 256,
     128 and 32 rows (2, 8, 4 and 1 waves of two 16-row fragments), head
-    dimension 128 and 64, contexts that end mid-tile and mid-chunk."""
+    dimension 128 and 64, contexts that end mid-tile and mid-chunk; and 20
+    rows, whose second fragment holds 12 padding rows (never written, and
+    the tiles before the context end skip the mask for every row)."""
     cfg = workloads.scaled(workloads.get_config("dense_fp8_b8"), n_layers=1, hidden=512, n_q=8,
                            n_kv=2, head_dim=head_dim, dense_inter=1024, vocab=4096, batch=2,
                            k_draft=k_draft, ctx=("uniform", 60, 700))
