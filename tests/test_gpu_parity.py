@@ -159,6 +159,19 @@ def test_gqa_many_rows_attention_shapes(H, k_draft, head_dim, waves):
     assert stats["argmax_agree"] >= 0.8 * stats["positions"]
 
 
+def test_gqa_split_kernel_one_fragment(H):
+    """Grouped-query attention on the split-KV kernel: K = 3 with 4 query
+    heads per KV head gives 16 rows per KV head (one fragment, below the
+    LDS-ring kernel's 17), so each fragment mixes the rows of 4 query heads
+    at 4 positions and the causal limit differs from row to row."""
+    cfg = workloads.scaled(workloads.get_config("dense_fp8_b8"), n_layers=2, hidden=512, n_q=8,
+                           n_kv=2, dense_inter=1024, vocab=4096, batch=6, k_draft=3,
+                           ctx=("uniform", 30, 700))
+    assert (cfg.k_draft + 1) * (cfg.n_q // cfg.n_kv) == 16
+    stats, _ = _verify_case(H, cfg, label="gqa_split_16rows")
+    assert stats["argmax_agree"] >= 0.8 * stats["positions"]
+
+
 @pytest.mark.parametrize("batch", [24, 40])
 def test_lds_lm_head_ragged_vocabulary(H, batch):
     """The LDS-staged bf16 LM head on both of its tile shapes -- 96 rows on
