@@ -172,6 +172,36 @@ def test_gqa_split_kernel_one_fragment(H):
     assert stats["argmax_agree"] >= 0.8 * stats["positions"]
 
 
+@pytest.mark.parametrize("batch", [3, 5, 9])
+def test_dense_bf16_ffn_row_counts(H, batch):
+    """A dense SwiGLU decoder with bf16 weights (the dense workload's shape in
+    bf16, scaled) at 96, 160 and 288 rows (K = 31): the bf16 dense path's
+    large-row kernels -- 128-row SwiGLU tiles up to 128 rows, the 32x32
+    SwiGLU and projection kernel above 128, the LDS-staged LM head up to 256
+    rows and the 32x32 argmax LM head above 256."""
+    cfg = workloads.scaled(workloads.get_config("dense_fp8_b8"), n_layers=2, hidden=512, n_q=8,
+                           n_kv=2, dense_inter=1024, vocab=4096, batch=batch, wdtype="bf16",
+                           ctx=("uniform", 60, 500))
+    stats, _ = _verify_case(H, cfg, label=f"dense_bf16_b{batch}")
+    assert stats["argmax_agree"] >= 0.8 * stats["positions"]
+
+
+def test_long_context_batch1_chunk_merge(H):
+    """Batch 1 with a 9,000-position context: 64-key attention chunks, so the
+    merge combines about 140 chunk partials per row (eight chunk weights per
+    lane)."""
+    cfg = workloads.scaled(workloads.get_config("moe_b1"), vocab=8192, ctx=("fixed", 9000))
+    _verify_case(H, cfg, label="b1_ctx9000")
+
+
+def test_mha_head_dim_64(H):
+    """Multi-head attention with head dimension 64 (20 heads of 64 over
+    hidden 1,280) on the split-KV kernel."""
+    cfg = workloads.scaled(workloads.get_config("moe_b32"), n_layers=2, n_q=20, n_kv=20, head_dim=64,
+                           vocab=4096, batch=3, ctx=("uniform", 50, 600))
+    _verify_case(H, cfg, label="mha_d64")
+
+
 @pytest.mark.parametrize("batch", [24, 40])
 def test_lds_lm_head_ragged_vocabulary(H, batch):
     """The LDS-staged bf16 LM head on both of its tile shapes -- 96 rows on
