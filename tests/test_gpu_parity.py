@@ -90,6 +90,19 @@ def test_tiny_fp32_full_size(H):
     assert stats["accept_checked"] == 1
 
 
+@pytest.mark.parametrize("batch,k_draft,n_q,n_kv", [(3, 7, 8, 2), (17, 3, 4, 4)])
+def test_fp32_more_rows(H, batch, k_draft, n_q, n_kv):
+    """The fp32 path beyond the tiny workload's four rows: grouped-query heads
+    (4 per KV head, K = 7: 32 rows per KV head, two fragments per wave of the
+    split-KV kernel) with contexts up to 1,500 (the merge over up to 24
+    chunks), and 68 rows (the large-row GEMMs and the separate embedding and
+    rotary kernels at fp32)."""
+    cfg = workloads.scaled(workloads.get_config("tiny_fp32"), batch=batch, k_draft=k_draft, n_q=n_q,
+                           n_kv=n_kv, ctx=("uniform", 60, 1500))
+    stats, _ = _verify_case(H, cfg, label=f"fp32_b{batch}_k{k_draft}")
+    assert stats["max_rel_logit_err"] < 1e-4
+
+
 def test_moe_batch1_full_size(H):
     cfg = workloads.get_config("moe_b1")
     stats, _ = _verify_case(H, cfg, label="moe_b1")
@@ -139,7 +152,7 @@ def test_dense_fp8_gqa_scaled(H):
 
 
 @pytest.mark.parametrize("k_draft,head_dim,waves", [(15, 128, 2), (63, 128, 8), (31, 64, 4), (7, 64, 1),
-                                                    (4, 128, 1)])
+                                                    (4, 128, 1), (15, 64, 2), (63, 64, 8)])
 def test_gqa_many_rows_attention_shapes(H, k_draft, head_dim, waves):
     """The LDS-ring attention kernel (17 .. 256 query rows per KV head) at
     each of its workgroup shapes: (K+1) x 4 grouped query heads = 64, 256,
