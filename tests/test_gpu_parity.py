@@ -172,6 +172,29 @@ def test_gqa_many_rows_attention_shapes(H, k_draft, head_dim, waves):
     assert stats["argmax_agree"] >= 0.8 * stats["positions"]
 
 
+@pytest.mark.parametrize("batch,k_draft", [(1, 31), (3, 15)])
+def test_dense_fp8_few_rows(H, batch, k_draft):
+    """fp8 weights at 32 and 48 rows: the fused embedding + QKV + rotary
+    kernel and the few-row GEMMs with two and four row fragments."""
+    cfg = workloads.scaled(workloads.get_config("dense_fp8_b8"), n_layers=2, hidden=512, n_q=8,
+                           n_kv=2, dense_inter=1024, vocab=4096, batch=batch, k_draft=k_draft,
+                           ctx=("uniform", 60, 500))
+    stats, _ = _verify_case(H, cfg, label=f"fp8_rows{batch * (k_draft + 1)}")
+    assert stats["argmax_agree"] >= 0.8 * stats["positions"]
+
+
+def test_gqa_more_than_256_rows_per_kv_head(H):
+    """512 query rows per KV head (K = 63, 8 query heads per KV head), past
+    the LDS-ring kernel's 256: the split-KV kernel with four fragments per
+    wave and eight query groups per KV head."""
+    cfg = workloads.scaled(workloads.get_config("dense_fp8_b8"), n_layers=1, hidden=512, n_q=16,
+                           n_kv=2, dense_inter=1024, vocab=4096, batch=1, k_draft=63,
+                           ctx=("uniform", 100, 700))
+    assert (cfg.k_draft + 1) * (cfg.n_q // cfg.n_kv) == 512
+    stats, _ = _verify_case(H, cfg, label="gqa_rows512")
+    assert stats["argmax_agree"] >= 0.8 * stats["positions"]
+
+
 def test_gqa_split_kernel_one_fragment(H):
     """Grouped-query attention on the split-KV kernel: K = 3 with 4 query
     heads per KV head gives 16 rows per KV head (one fragment, below the
@@ -428,14 +451,17 @@ def test_pack_tiled16_layout(H, dtype, rows, cols):
     assert torch.equal(got, want)
 
 
-def test_row_major_and_tiled16_layouts_agree_bitwise(H):
+@pytest.mark.parametrize("batch", [17, 5, 12])
+def test_row_major_and_tiled16_layouts_agree_bitwise(H, batch):
     """The two weight layouts feed the same values in the same order to the
-    same arithmetic: every output is bit-identical."""
-    cfg = workloads.scaled(workloads.get_config("moe_b32"), n_layers=2, vocab=4096, batch=17,
+    same arithmetic: every output is bit-identical -- at 68 rows (the
+    large-row kernels), 20 and 48 rows (two and four row fragments on the
+    few-row kernels)."""
+    cfg = workloads.scaled(workloads.get_config("moe_b32"), n_layers=2, vocab=4096, batch=batch,
                            ctx=("uniform", 40, 300))
     case = H.Case(cfg)
     outs = []
-    for layout in ("row_major", "tiled16"):   # 68 rows: both GEMM paths in both layouts
+    for layout in ("row_major", "tiled16"):
         H.say(f"[layouts] {layout}")
         run = H.GpuRun(case, layout=layout)
         outs.append(run.step(case.committed, case.rtok[0], case.ctx))
