@@ -38,10 +38,12 @@ def test_mxfp4_batched_scaled(H, batch, n_experts, top_k, n_shared):
     assert stats["argmax_agree"] >= 0.9 * stats["positions"]
 
 
-@pytest.mark.parametrize("batch", [16, 40])
+@pytest.mark.parametrize("batch", [16, 40, 64, 5])
 def test_mxfp4_many_rows(H, batch):
-    """64 and 160 verified rows: the large-row kernel (activation chunks in
-    LDS) for the grouped experts and the LM head, with MXFP4 weights."""
+    """64, 160 and 256 verified rows: the large-row kernel (activation chunks
+    in LDS) for the grouped experts (16- and, at 256 rows, 32-row expert
+    tiles) and the LM head, with MXFP4 weights; and 20 rows (the few-row
+    LM head with two row fragments)."""
     cfg = workloads.scaled(workloads.get_config("moe_b1_mxfp4"), n_layers=2, batch=batch,
                            vocab=4112, ctx=("uniform", 5, 300), norm_gain_std=0.2)
     stats, _ = _run(H, cfg, f"mxfp4_many_rows_b{batch}")

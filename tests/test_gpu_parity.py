@@ -118,11 +118,14 @@ def test_moe_batched_scaled(H):
     assert stats["argmax_agree"] >= 0.9 * stats["positions"]
 
 
-@pytest.mark.parametrize("batch,n_experts,top_k", [(5, 16, 4), (20, 16, 4), (16, 8, 6)])
+@pytest.mark.parametrize("batch,n_experts,top_k", [(5, 16, 4), (20, 16, 4), (16, 8, 6), (10, 4, 2),
+                                                  (14, 4, 3)])
 def test_moe_small_shapes(H, batch, n_experts, top_k):
     """Small MoE shapes: head_dim 128 with 2 heads, one shared expert, contexts
     from 1 token, norm gains away from 1.  Rows per expert ~1 (one-wave expert
-    tiles), ~20 (32-row tiles of the large-row kernel) and ~48 (64-row tiles)."""
+    tiles), ~20 (32-row tiles of the large-row kernel) and ~48 (64-row tiles),
+    and on the few-row kernel (under 64 rows) ~20 and ~42 (32- and 64-row
+    expert tiles)."""
     cfg = workloads.scaled(workloads.get_config("moe_b1"), n_layers=2, hidden=256, n_q=2, n_kv=2,
                            n_experts=n_experts, expert_inter=128, top_k=top_k, n_shared=1,
                            vocab=2048, batch=batch, ctx=("uniform", 1, 200), norm_gain_std=0.2)
@@ -222,12 +225,13 @@ def test_dense_bf16_ffn_row_counts(H, batch):
     assert stats["argmax_agree"] >= 0.8 * stats["positions"]
 
 
-def test_long_context_batch1_chunk_merge(H):
-    """Batch 1 with a 9,000-position context: 64-key attention chunks, so the
-    merge combines about 140 chunk partials per row (eight chunk weights per
-    lane)."""
-    cfg = workloads.scaled(workloads.get_config("moe_b1"), vocab=8192, ctx=("fixed", 9000))
-    _verify_case(H, cfg, label="b1_ctx9000")
+@pytest.mark.parametrize("ctx", [3000, 9000])
+def test_long_context_batch1_chunk_merge(H, ctx):
+    """Batch 1 with a 3,000- or 9,000-position context: 64-key attention
+    chunks, so the merge combines about 47 or 140 chunk partials per row (two
+    or eight chunk weights per lane)."""
+    cfg = workloads.scaled(workloads.get_config("moe_b1"), vocab=8192, ctx=("fixed", ctx))
+    _verify_case(H, cfg, label=f"b1_ctx{ctx}")
 
 
 def test_mha_head_dim_64(H):
