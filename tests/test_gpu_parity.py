@@ -455,12 +455,12 @@ def test_pack_tiled16_layout(H, dtype, rows, cols):
     assert torch.equal(got, want)
 
 
-@pytest.mark.parametrize("batch", [17, 5, 12])
+@pytest.mark.parametrize("batch", [17, 5, 12, 64])
 def test_row_major_and_tiled16_layouts_agree_bitwise(H, batch):
     """The two weight layouts feed the same values in the same order to the
     same arithmetic: every output is bit-identical -- at 68 rows (the
     large-row kernels), 20 and 48 rows (two and four row fragments on the
-    few-row kernels)."""
+    few-row kernels) and 256 rows (32-row expert tiles)."""
     cfg = workloads.scaled(workloads.get_config("moe_b32"), n_layers=2, vocab=4096, batch=batch,
                            ctx=("uniform", 40, 300))
     case = H.Case(cfg)
