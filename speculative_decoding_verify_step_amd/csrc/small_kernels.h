@@ -356,11 +356,14 @@ SV_DEV void permute_rows(const RowArgs& a, char* lds)
 // round trip.  ROUTE (MoE, after attention): S workgroups per row each
 // recompute the update and the norm (workgroup 0 writes them) and take E/S of
 // the router's experts; with S > 1 they write the logits for the selection in
-// route_finish_kernel, with S = 1 the row selects its experts here.
-template <bool BF, bool MOE, bool ROUTE = false, int UPW = 4>
+// route_finish_kernel, with S = 1 the row selects its experts here.  NSP
+// bounds the K-splits (or, MoE, the shared experts, at most 8) that a column
+// loads: the launch picks the smallest power of two that covers them, so
+// that no load repeats a partial.
+template <bool BF, bool MOE, bool ROUTE = false, int UPW = 4, int NSP = 16>
 __global__ __launch_bounds__(1024) void residual_norm_kernel(RowArgs a)
 {
-    constexpr int RT = 1024, EPT = 2, NS = ROUTE ? 4 : 16;
+    constexpr int RT = 1024, EPT = 2, NS = ROUTE ? 4 : NSP, NSH = NSP < 8 ? NSP : 8;
     __shared__ __align__(16) float smem[2 * 8192];   // row update, gains
     __shared__ float shw[RT / 64];
     __shared__ float logit[256];
@@ -395,7 +398,7 @@ __global__ __launch_bounds__(1024) void residual_norm_kernel(RowArgs a)
     const float* __restrict__ shrow =
         (MOE && a.n_shared > 0) ? y + ((size_t)T * a.topk + t) * H : y;
     const int nlast = MOE ? max(a.n_shared, 1) - 1 : max(a.nsplit, 1) - 1;
-    float xv[EPT], gv[EPT], pv[EPT][16];
+    float xv[EPT], gv[EPT], pv[EPT][MOE ? 8 + NSH : NS];
     auto loads = [&](int i0) {
 #pragma unroll
         for (int u = 0; u < EPT; u++) {
@@ -406,7 +409,7 @@ __global__ __launch_bounds__(1024) void residual_norm_kernel(RowArgs a)
 #pragma unroll
                 for (int r = 0; r < 8; r++) pv[u][r] = ld_at(y + (size_t)slot[r] * H, off);
 #pragma unroll
-                for (int sx = 0; sx < 8; sx++)
+                for (int sx = 0; sx < NSH; sx++)
                     pv[u][8 + sx] = ld_at(shrow + (size_t)min(sx, nlast) * pstride, off);
             } else {
 #pragma unroll
@@ -425,7 +428,7 @@ __global__ __launch_bounds__(1024) void residual_norm_kernel(RowArgs a)
                 for (int r = 0; r < 8; r++) d += gate[r] * (r < a.topk ? pv[u][r] : 0.f);
                 float sh = 0.f;
 #pragma unroll
-                for (int sx = 0; sx < 8; sx++) sh += sx < a.n_shared ? pv[u][8 + sx] : 0.f;
+                for (int sx = 0; sx < NSH; sx++) sh += sx < a.n_shared ? pv[u][8 + sx] : 0.f;
                 d += sh;
             } else {
 #pragma unroll
@@ -625,8 +628,10 @@ SV_DEV size_t v_cache_index(int pos, int d, int D)
 // to the attention input and k, v to the caches at position ctx + j.  One
 // wave per (row, head); grid (T, n_q + 2 n_kv).  A lane owns one rotary pair
 // (q, k heads) or two channels (v heads) and issues the loads of every K-split
-// partial of them at once; the rotary table read waits only for ctx.
-template <bool BF>
+// partial of them at once (NS >= nsplit loads per channel: the launch picks
+// the smallest power of two, so that no load repeats a partial); the rotary
+// table read waits only for ctx.
+template <bool BF, int NS>
 __global__ __launch_bounds__(64) void rope_append_kernel(RopeArgs a)
 {
     const int t = blockIdx.x, hh = blockIdx.y, lane = threadIdx.x;
@@ -636,13 +641,13 @@ __global__ __launch_bounds__(64) void rope_append_kernel(RopeArgs a)
     typedef typename Act<BF>::T AT;
     const float* __restrict__ src = a.qkv + (size_t)t * QKV + (size_t)hh * D;
     const size_t sstride = (size_t)a.T * QKV;
-    float p0[16], p1[16];
+    float p0[NS], p1[NS];
     const bool rot = hh < a.n_q + a.n_kv;
     // rotary heads: channels lane and lane + half; value heads: lane and lane + 64
     const int i0 = lane, i1 = rot ? lane + half : lane + 64;
     const bool ok0 = rot ? lane < half : lane < D, ok1 = rot ? lane < half : lane + 64 < D;
-    load_strided<16>(src + (ok0 ? i0 : 0), ok0 ? a.nsplit : 0, sstride, p0);
-    load_strided<16>(src + (ok1 ? i1 : 0), ok1 ? a.nsplit : 0, sstride, p1);
+    load_strided<NS>(src + (ok0 ? i0 : 0), ok0 ? a.nsplit : 0, sstride, p0);
+    load_strided<NS>(src + (ok1 ? i1 : 0), ok1 ? a.nsplit : 0, sstride, p1);
     const int ctx = a.ctx_in[b];
     const bool write_cache = a.seq_err[b] == 0;
     const int pos = min(max(ctx, 0), a.cap - K1) + j;

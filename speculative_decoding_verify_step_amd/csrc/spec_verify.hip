@@ -537,6 +537,32 @@ void launch_qkv_rope(int wt, int MF, bool packed, bool embed, const QkvArgs& a, 
 #undef QKV_CASE
 }
 
+// Rotary + cache append over the K-split partials of the QKV projection: the
+// kernel instance with the fewest loads per channel that covers the splits
+template <bool BF>
+void launch_rope_append(dim3 grid, hipStream_t s, const RopeArgs& rp)
+{
+    if (rp.nsplit <= 1) rope_append_kernel<BF, 1><<<grid, 64, 0, s>>>(rp);
+    else if (rp.nsplit <= 2) rope_append_kernel<BF, 2><<<grid, 64, 0, s>>>(rp);
+    else if (rp.nsplit <= 4) rope_append_kernel<BF, 4><<<grid, 64, 0, s>>>(rp);
+    else if (rp.nsplit <= 8) rope_append_kernel<BF, 8><<<grid, 64, 0, s>>>(rp);
+    else rope_append_kernel<BF, 16><<<grid, 64, 0, s>>>(rp);
+}
+
+// Residual update + RMSNorm of every row: the kernel instance with the fewest
+// loads per column that covers the K-split partials (dense) or the shared
+// experts' outputs (MoE combine)
+template <bool BF, bool MOE>
+void launch_residual_norm(int T, hipStream_t s, const RowArgs& ra)
+{
+    const int n = MOE ? ra.n_shared : ra.nsplit;
+    if (n <= 1) residual_norm_kernel<BF, MOE, false, 4, 1><<<T, 1024, 0, s>>>(ra);
+    else if (n <= 2) residual_norm_kernel<BF, MOE, false, 4, 2><<<T, 1024, 0, s>>>(ra);
+    else if (n <= 4) residual_norm_kernel<BF, MOE, false, 4, 4><<<T, 1024, 0, s>>>(ra);
+    else if (n <= 8) residual_norm_kernel<BF, MOE, false, 4, 8><<<T, 1024, 0, s>>>(ra);
+    else residual_norm_kernel<BF, MOE, false, 4, 16><<<T, 1024, 0, s>>>(ra);
+}
+
 // K split: enough waves to cover the GPU, each split at least 4 reduction steps
 int pick_ksplit(long waves, int K, int step, int smax = KS_MAX)
 {
@@ -1173,8 +1199,8 @@ static int step_impl(spec_verify_ctx* c, const spec_verify_weights* w, void* k_c
         ra.nsplit = ks;
         ra.gain = w->layers[0].attn_norm;
         ra.dbg_hidden = nullptr;
-        if (bf) residual_norm_kernel<true, false><<<T, 1024, 0, s>>>(ra);
-        else residual_norm_kernel<false, false><<<T, 1024, 0, s>>>(ra);
+        if (bf) launch_residual_norm<true, false>(T, s, ra);
+        else launch_residual_norm<false, false>(T, s, ra);
     }
     for (int l = 0; l < L; l++) {
         const spec_verify_layer& Lw = w->layers[l];
@@ -1211,8 +1237,8 @@ static int step_impl(spec_verify_ctx* c, const spec_verify_weights* w, void* k_c
             rp.kvp = kvp;
             rp.err_word = c->err_word;
             dim3 grid(T, k.n_q_heads + 2 * k.n_kv_heads);
-            if (bf) rope_append_kernel<true><<<grid, 64, 0, s>>>(rp);
-            else rope_append_kernel<false><<<grid, 64, 0, s>>>(rp);
+            if (bf) launch_rope_append<true>(grid, s, rp);
+            else launch_rope_append<false>(grid, s, rp);
         }
 
         at.layer = l;
@@ -1286,8 +1312,8 @@ static int step_impl(spec_verify_ctx* c, const spec_verify_weights* w, void* k_c
             if (!implied || (S > 1 && !sel_in_gemm)) route_finish_kernel<<<1, 1024, 0, s>>>(ra);
         } else {
             ra.x_out = c->x;
-            if (bf) residual_norm_kernel<true, false><<<T, 1024, 0, s>>>(ra);
-            else residual_norm_kernel<false, false><<<T, 1024, 0, s>>>(ra);
+            if (bf) launch_residual_norm<true, false>(T, s, ra);
+            else launch_residual_norm<false, false>(T, s, ra);
         }
 
         // ---- feed-forward half
@@ -1378,8 +1404,8 @@ static int step_impl(spec_verify_ctx* c, const spec_verify_weights* w, void* k_c
             ra.dbg_hidden = dbg_h;
             ra.x = c->x2;
             ra.x_out = c->x;
-            if (bf) residual_norm_kernel<true, true><<<T, 1024, 0, s>>>(ra);
-            else residual_norm_kernel<false, true><<<T, 1024, 0, s>>>(ra);
+            if (bf) launch_residual_norm<true, true>(T, s, ra);
+            else launch_residual_norm<false, true>(T, s, ra);
         } else {
             const int I = k.dense_inter;
             {
@@ -1396,8 +1422,8 @@ static int step_impl(spec_verify_ctx* c, const spec_verify_weights* w, void* k_c
             ra.dbg_hidden = dbg_h;
             ra.x = c->x;
             ra.x_out = c->x;
-            if (bf) residual_norm_kernel<true, false><<<T, 1024, 0, s>>>(ra);
-            else residual_norm_kernel<false, false><<<T, 1024, 0, s>>>(ra);
+            if (bf) launch_residual_norm<true, false>(T, s, ra);
+            else launch_residual_norm<false, false>(T, s, ra);
         }
     }
 
