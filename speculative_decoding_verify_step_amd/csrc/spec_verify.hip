@@ -399,39 +399,43 @@ int wide_col_tile(int mode) { return 32 * WIDE_WAVES * (mode == GM_SWIGLU ? WIDE
 
 // Steps per staged chunk: 2, except the fp8 LM head with 1 (three waves per
 // SIMD instead of two: 273 -> 262 us per launch at 256 rows, same box).
-// fp8 projections whose K split holds 16 or more reduction steps (the down
-// projection, K = 9,728 in 4 splits of 38) run the same 64 x 256 tiles on the
-// LDS-staged kernel with 3 stages (two steps in flight per workgroup without
-// registers): dense fp8 K = 31, down 41.3 -> 32.1 us per layer (step 1,904 ->
-// 1,833 us, same box).  Shorter splits (QKV, O: 8 steps), the fp8 SwiGLU
-// (47.5 -> 52.1 us per layer), the fp8 LM head (265 -> 272 us) and bf16 at 256
-// rows (QKV and O of batch 64: 208 -> 220 us per step) measured no faster there.
+// fp8 projections whose K split holds 16 or more 64-long reduction steps
+// (the planner then takes the most such splits within 512 workgroups: dense
+// fp8 QKV 2 x 20, O 4 x 16, down 8 x 19 steps) run the same 64 x 256 tiles on
+// the LDS-staged kernel with 3 stages (two steps in flight per workgroup
+// without registers): dense fp8 K = 31, down 41.3 -> 32.1 us per layer (step
+// 1,904 -> 1,833 us, same box).  Splits of 8 steps, the fp8 SwiGLU (47.5 ->
+// 52.1 us per layer), the fp8 LM head (265 -> 272 us) and bf16 at 256 rows
+// (QKV and O of batch 64: 208 -> 220 us per step) measured no faster there.
 constexpr int WIDE_LDS_MIN_STEPS = 16;
 
 template <int WT>
-void launch_wide_t(int mode, int cs, const GemmArgs& a, dim3 grid, hipStream_t s)
+void launch_wide_t(int mode, const GemmArgs& a, dim3 grid, hipStream_t s)
 {
     const dim3 blk(64 * WIDE_WAVES);
     if (mode == GM_STORE) {
-        if (WT == SV_FP8 && a.K / a.ksplit >= WIDE_LDS_MIN_STEPS * WTraits<WT>::SK &&
-            (a.K / a.ksplit) % WTraits<WT>::SK == 0)
-            launch(gemm_lds_kernel<WT, GM_STORE, 1, WIDE_MW, 3, WIDE_NW>, grid, blk, 0, s, a);
-        else
-            launch(gemm_wide_kernel<WT, WIDE_MW, WIDE_NW, GM_STORE, WIDE_WAVES, 2>, grid, blk, 0, s, a);
+        if constexpr (WT == SV_FP8) {
+            const int span = a.K / a.ksplit;
+            if (span >= WIDE_LDS_MIN_STEPS * WTraits<WT>::SK && span % WTraits<WT>::SK == 0) {
+                launch(gemm_lds_kernel<WT, GM_STORE, 1, WIDE_MW, 3, WIDE_NW>, grid, blk, 0, s, a);
+                return;
+            }
+        }
+        launch(gemm_wide_kernel<WT, WIDE_MW, WIDE_NW, GM_STORE, WIDE_WAVES, 2>, grid, blk, 0, s, a);
     } else if (mode == GM_SWIGLU) {
         launch(gemm_wide_kernel<WT, WIDE_MW, WIDE_NW, GM_SWIGLU, WIDE_WAVES, 2>, grid, blk, 0, s, a);
     } else {
-        if (cs == 1) launch(gemm_wide_kernel<WT, WIDE_MW, WIDE_NW, GM_ARGMAX, WIDE_WAVES, 1>, grid, blk, 0, s, a);
-        else launch(gemm_wide_kernel<WT, WIDE_MW, WIDE_NW, GM_ARGMAX, WIDE_WAVES, 2>, grid, blk, 0, s, a);
+        // LM head: fp8 one reduction step per chunk, bf16 two
+        constexpr int CS = WT == SV_FP8 ? 1 : 2;
+        launch(gemm_wide_kernel<WT, WIDE_MW, WIDE_NW, GM_ARGMAX, WIDE_WAVES, CS>, grid, blk, 0, s, a);
     }
 }
 
 void launch_gemm_wide(int wt, int mode, GemmArgs& a, hipStream_t s)
 {
     dim3 grid((unsigned)(cdiv(a.NT, 8) * 8 * a.MT), (unsigned)a.ksplit, 1);
-    const int cs = (mode == GM_ARGMAX && wt == SV_FP8) ? 1 : 2;
-    if (wt == SV_BF16) launch_wide_t<SV_BF16>(mode, cs, a, grid, s);
-    else launch_wide_t<SV_FP8>(mode, cs, a, grid, s);
+    if (wt == SV_BF16) launch_wide_t<SV_BF16>(mode, a, grid, s);
+    else launch_wide_t<SV_FP8>(mode, a, grid, s);
 }
 
 // bf16 LM head at 65 .. 256 rows: both operands staged in LDS, tiles of 8
