@@ -144,6 +144,29 @@ def test_moe_few_assignments(H, batch, n_experts, top_k, n_shared):
     _verify_case(H, cfg, label=f"moe_few_b{batch}_e{n_experts}_k{top_k}_s{n_shared}")
 
 
+@pytest.mark.parametrize("batch,n_experts,top_k", [(3, 16, 4), (20, 16, 4)])
+def test_moe_fp8_experts(H, batch, n_experts, top_k):
+    """e4m3 weights with per-row scales in the MoE decoder (router, experts,
+    projections, LM head): 12 rows (the few-row kernels, tiles and slots
+    implied by the selections) and 80 rows (the grouped large-row kernel
+    with device-built tiles)."""
+    cfg = workloads.scaled(workloads.get_config("moe_b1"), n_layers=2, hidden=256, n_q=2, n_kv=2,
+                           n_experts=n_experts, expert_inter=128, top_k=top_k, n_shared=1,
+                           vocab=2048, batch=batch, ctx=("uniform", 1, 200), norm_gain_std=0.2,
+                           wdtype="fp8")
+    _verify_case(H, cfg, label=f"moe_fp8_b{batch}_e{n_experts}_k{top_k}")
+
+
+def test_moe_fp8_batch1_shapes(H):
+    """The batch-1 MoE layer's shapes (hidden 1,280, 64 experts, top-6, two
+    shared experts, expert width 896) with e4m3 weights: the selections made
+    inside the expert gate/up kernel, the K-split expert down projection and
+    the small-row LM head, on fp8 operands (smaller vocabulary)."""
+    cfg = workloads.scaled(workloads.get_config("moe_b1"), vocab=8192, wdtype="fp8")
+    stats, _ = _verify_case(H, cfg, label="moe_fp8_b1")
+    assert stats["argmax_agree"] >= 0.75 * stats["positions"]
+
+
 def test_dense_fp8_gqa_scaled(H):
     """Block drafts (K = 31) on the dense GQA decoder with e4m3 weights:
     4 query heads per KV head, 128 query rows per KV head."""
