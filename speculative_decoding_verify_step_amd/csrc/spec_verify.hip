@@ -559,12 +559,12 @@ void launch_rope_append(dim3 grid, hipStream_t s, const RopeArgs& rp)
 template <bool BF, bool MOE>
 void launch_residual_norm(int T, hipStream_t s, const RowArgs& ra)
 {
-    const int n = MOE ? ra.n_shared : ra.nsplit;
+    const int n = MOE ? ra.n_shared : ra.nsplit;   // shared experts <= 8, splits <= 16
     if (n <= 1) residual_norm_kernel<BF, MOE, false, 4, 1><<<T, 1024, 0, s>>>(ra);
     else if (n <= 2) residual_norm_kernel<BF, MOE, false, 4, 2><<<T, 1024, 0, s>>>(ra);
     else if (n <= 4) residual_norm_kernel<BF, MOE, false, 4, 4><<<T, 1024, 0, s>>>(ra);
-    else if (n <= 8) residual_norm_kernel<BF, MOE, false, 4, 8><<<T, 1024, 0, s>>>(ra);
-    else residual_norm_kernel<BF, MOE, false, 4, 16><<<T, 1024, 0, s>>>(ra);
+    else if (MOE || n <= 8) residual_norm_kernel<BF, MOE, false, 4, 8><<<T, 1024, 0, s>>>(ra);
+    else if constexpr (!MOE) residual_norm_kernel<BF, MOE, false, 4, 16><<<T, 1024, 0, s>>>(ra);
 }
 
 // K split: enough waves to cover the GPU, each split at least 4 reduction steps

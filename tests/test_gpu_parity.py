@@ -40,7 +40,8 @@ def _bits(t):
     return t.view(torch.int16) if t.element_size() == 2 else t.view(torch.int32)
 
 
-def _verify_case(H, cfg, sampled=None, batch=None, check_kv=True, label="", poison=False):
+def _verify_case(H, cfg, sampled=None, batch=None, check_kv=True, label="", poison=False,
+                 layout="tiled16"):
     case = H.Case(cfg)
     B = cfg.batch if batch is None else batch
     if poison:
@@ -49,7 +50,7 @@ def _verify_case(H, cfg, sampled=None, batch=None, check_kv=True, label="", pois
     H.say(f"[{label}] {cfg.name}: B={B} L={cfg.n_layers} H={cfg.hidden} V={cfg.vocab} "
           f"K={cfg.k_draft} cap={case.cap} ctx={case.ctx[:B].tolist()[:8]} sampled={sampled}")
     drafts = case.drafts(sampled)
-    run = H.GpuRun(case, batch=B)
+    run = H.GpuRun(case, batch=B, layout=layout)
     g = run.step(case.committed[:B], drafts[:B], case.ctx[:B])
     H.say(f"[{label}] gpu step done: accepted={g['accepted'][:8].tolist()}")
     orc = case.oracle()
@@ -90,16 +91,18 @@ def test_tiny_fp32_full_size(H):
     assert stats["accept_checked"] == 1
 
 
-@pytest.mark.parametrize("batch,k_draft,n_q,n_kv", [(3, 7, 8, 2), (17, 3, 4, 4)])
-def test_fp32_more_rows(H, batch, k_draft, n_q, n_kv):
+@pytest.mark.parametrize("batch,k_draft,n_q,n_kv,head_dim", [(3, 7, 8, 2, 64), (17, 3, 4, 4, 64),
+                                                            (5, 3, 2, 2, 128), (9, 3, 4, 2, 128)])
+def test_fp32_more_rows(H, batch, k_draft, n_q, n_kv, head_dim):
     """The fp32 path beyond the tiny workload's four rows: grouped-query heads
     (4 per KV head, K = 7: 32 rows per KV head, two fragments per wave of the
     split-KV kernel) with contexts up to 1,500 (the merge over up to 24
-    chunks), and 68 rows (the large-row GEMMs and the separate embedding and
-    rotary kernels at fp32)."""
+    chunks), 68 rows (the large-row GEMMs and the separate embedding and
+    rotary kernels at fp32), and head dimension 128 at 20 and 36 rows (the
+    fused QKV kernel with two and four row fragments)."""
     cfg = workloads.scaled(workloads.get_config("tiny_fp32"), batch=batch, k_draft=k_draft, n_q=n_q,
-                           n_kv=n_kv, ctx=("uniform", 60, 1500))
-    stats, _ = _verify_case(H, cfg, label=f"fp32_b{batch}_k{k_draft}")
+                           n_kv=n_kv, head_dim=head_dim, ctx=("uniform", 60, 1500))
+    stats, _ = _verify_case(H, cfg, label=f"fp32_b{batch}_k{k_draft}_d{head_dim}")
     assert stats["max_rel_logit_err"] < 1e-4
 
 
@@ -132,12 +135,14 @@ def test_moe_small_shapes(H, batch, n_experts, top_k):
     _verify_case(H, cfg, label=f"moe_small_shapes_b{batch}_e{n_experts}_k{top_k}")
 
 
-@pytest.mark.parametrize("batch,n_experts,top_k,n_shared", [(4, 32, 4, 2), (1, 64, 8, 0)])
+@pytest.mark.parametrize("batch,n_experts,top_k,n_shared", [(4, 32, 4, 2), (1, 64, 8, 0), (4, 16, 2, 3),
+                                                            (2, 8, 2, 8)])
 def test_moe_few_assignments(H, batch, n_experts, top_k, n_shared):
     """Few assignments (T <= 16, T * top_k <= 64, at most 64 experts): the
     grouped GEMMs and the combine take expert tiles and slots from the
     selections.  Covers all 64 lanes holding an assignment (16 rows x top-4),
-    two shared experts, and none."""
+    none, two, three and eight shared experts (the combine's shared-expert
+    loads sized for 1, 2, 4 and 8)."""
     cfg = workloads.scaled(workloads.get_config("moe_b1"), n_layers=2, hidden=256, n_q=2, n_kv=2,
                            n_experts=n_experts, expert_inter=128, top_k=top_k, n_shared=n_shared,
                            vocab=2048, batch=batch, ctx=("uniform", 1, 200), norm_gain_std=0.2)
@@ -495,3 +500,50 @@ def test_row_major_and_tiled16_layouts_agree_bitwise(H, batch):
         run.close()
     for k in ("logits", "hidden", "target", "accepted", "next_tok", "ctx_out", "routing"):
         assert np.array_equal(outs[0][k], outs[1][k], equal_nan=True), k
+
+
+@pytest.mark.parametrize("name,overrides", [
+    ("tiny_fp32", dict(batch=1)),
+    ("tiny_fp32", dict(batch=17, n_q=4, n_kv=4, head_dim=128, ctx=("uniform", 60, 400))),
+    ("dense_fp8_b8", dict(n_layers=1, hidden=512, n_q=8, n_kv=2, dense_inter=1024, vocab=4096, batch=2,
+                          k_draft=7, ctx=("uniform", 60, 400))),
+    ("moe_b1", dict(n_layers=2, hidden=256, n_q=2, n_kv=2, n_experts=16, expert_inter=128, top_k=4,
+                    n_shared=1, vocab=2048, batch=3, ctx=("uniform", 1, 200), wdtype="fp8")),
+])
+def test_layouts_agree_bitwise_fp32_and_fp8(H, name, overrides):
+    """The row-major and tiled16 weight layouts bit for bit with fp32 weights
+    (4 rows, and 68 rows at head dimension 128) and e4m3 weights (dense at
+    16 rows, MoE at 12 rows): the row-major kernels of these dtypes against
+    the tiled ones, which the other tests compare with the oracle.  (Above
+    64 rows tiled e4m3 weights run the wide-tile kernels with other K
+    splits: see the next test.)"""
+    cfg = workloads.scaled(workloads.get_config(name), **overrides)
+    case = H.Case(cfg)
+    outs = []
+    for layout in ("row_major", "tiled16"):
+        H.say(f"[layouts {cfg.wdtype} T={cfg.batch * (cfg.k_draft + 1)}] {layout}")
+        run = H.GpuRun(case, layout=layout)
+        outs.append(run.step(case.committed, case.rtok[0], case.ctx))
+        run.close()
+    for k in ("logits", "hidden", "target", "accepted", "next_tok", "ctx_out", "routing"):
+        if outs[1][k] is None:   # routing of a dense model
+            assert outs[0][k] is None, k
+            continue
+        assert np.array_equal(outs[0][k], outs[1][k], equal_nan=True), k
+
+
+@pytest.mark.parametrize("name,overrides", [
+    ("dense_fp8_b8", dict(n_layers=1, hidden=512, n_q=8, n_kv=2, dense_inter=1024, vocab=4096, batch=3,
+                          k_draft=31, ctx=("uniform", 60, 400))),
+    ("moe_b1", dict(n_layers=2, hidden=256, n_q=2, n_kv=2, n_experts=16, expert_inter=128, top_k=4,
+                    n_shared=1, vocab=2048, batch=20, ctx=("uniform", 1, 200), wdtype="fp8")),
+])
+def test_row_major_fp8_many_rows(H, name, overrides):
+    """Row-major e4m3 weights above 64 rows (dense at 96, MoE at 80) run the
+    16x16 large-row kernels where the tiled layout runs the wide-tile and
+    LDS-staged ones with other K splits (another summation order, so not
+    bit-identical): compared with the oracle."""
+    cfg = workloads.scaled(workloads.get_config(name), **overrides)
+    stats, _ = _verify_case(H, cfg, label=f"fp8_row_major_{cfg.ffn}", layout="row_major")
+    assert stats["argmax_agree"] >= 0.8 * stats["positions"]
+
