@@ -214,18 +214,27 @@ SV_DEV unsigned long long wave_or_u64(unsigned long long v)
 // E <= 64), without a permutation pass.  The permuted order is the stable
 // counting sort of the assignments by expert: assignment j with expert e sits
 // at slot (number of assignments with a smaller expert) + (number of earlier
-// assignments with expert e); tile i is the i-th expert present in ascending
-// order, then one tile per shared expert over all T rows.  `sv` is lane l's
-// selection (any value for l >= A).
+// assignments with expert e).  Tiles 0 .. n_shared - 1 are the shared experts,
+// each over all T rows (they need no selection, so their workgroups start
+// loading weights at once); tile n_shared + i is the i-th expert present in
+// ascending order.  `sv` is lane l's selection (any value for l >= A; not
+// used for a shared tile).
 struct ImpliedTile { int group, row0, nrows; unsigned long long members; };
 
 SV_DEV ImpliedTile implied_tile(int sv, int A, int T, int E, int n_shared, int tile)
 {
     const int lane = threadIdx.x & 63;
     const bool act = lane < A;
+    ImpliedTile r{0, 0, 0, 0ull};
+    if (tile < n_shared) {
+        r.group = E + tile;
+        r.row0 = A + tile * T;
+        r.nrows = T;
+        return r;
+    }
+    tile -= n_shared;
     const unsigned long long present = wave_or_u64(act ? 1ull << sv : 0ull);
     const int distinct = __popcll(present);
-    ImpliedTile r{0, 0, 0, 0ull};
     if (tile < distinct) {
         const bool bit = (present >> lane) & 1ull;
         const int pre = __popcll(present & ((1ull << lane) - 1ull));
@@ -234,10 +243,6 @@ SV_DEV ImpliedTile implied_tile(int sv, int A, int T, int E, int n_shared, int t
         r.row0 = __popcll(__ballot(act && sv < e));
         r.members = __ballot(act && sv == e);
         r.nrows = __popcll(r.members);
-    } else if (tile < distinct + n_shared) {
-        r.group = E + (tile - distinct);
-        r.row0 = A + (tile - distinct) * T;
-        r.nrows = T;
     }
     return r;
 }

@@ -342,8 +342,11 @@ __global__ __launch_bounds__(64 * WAVES) void gemm_kernel(GemmArgs a)
         const int A = a.sel_T * a.sel_k;
         int sraw = 0;
         bool selected = false;
+        // shared-expert tiles need no selection (workgroup 0 still makes and
+        // publishes it)
+        const bool shared_tile = mt < a.sel_S;
         if constexpr (MODE == GM_SWIGLU) {
-            if (a.sel_logits) {
+            if (a.sel_logits && (!shared_tile || (blockIdx.x == 0 && blockIdx.y == 0))) {
                 // the routing's selection of every row (T <= 4, E <= 64): all
                 // rows' logits in one round trip, then the selections in this wave
                 __shared__ int ssel[WAVES][64];
@@ -363,7 +366,7 @@ __global__ __launch_bounds__(64 * WAVES) void gemm_kernel(GemmArgs a)
                 selected = true;
             }
         }
-        if (!selected) sraw = a.sel[min(lane, A - 1)];
+        if (!selected && !shared_tile) sraw = a.sel[min(lane, A - 1)];
         const int sv = min(max(sraw, 0), a.sel_E - 1);
         const ImpliedTile it = implied_tile(sv, A, a.sel_T, a.sel_E, a.sel_S, mt);
         group = it.group;
