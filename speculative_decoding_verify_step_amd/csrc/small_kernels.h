@@ -249,10 +249,8 @@ SV_DEV void router_logits(const RowArgs& a, const float* hs, uint4 (&wv)[4][UPW]
 }
 
 // Selection of row t for the routing kernels (router_select_to).
-SV_DEV void router_select(const RowArgs& a, int t, float (&p)[4], unsigned long long* kbuf,
-                          unsigned short* sel_lds = nullptr)
+SV_DEV void router_select(const RowArgs& a, int t, float (&p)[4], unsigned short* sel_lds = nullptr)
 {
-    (void)kbuf;   // unused (kept for the callers' shared-memory layout)
     router_select_to(a.E, a.topk, a.renorm != 0, t, p, a.sel, a.gate_out, a.dbg_sel, sel_lds);
 }
 
@@ -485,7 +483,7 @@ __global__ __launch_bounds__(1024) void residual_norm_kernel(RowArgs a)
                 for (int q = 0; q < 4; q++)
                     p[q] = lane + 64 * q < E ? logit[min(lane + 64 * q, E - 1)] : -INFINITY;
                 // the row buffer is free after the logits: wave 0's key scratch
-                router_select(a, t, p, reinterpret_cast<unsigned long long*>(smem));
+                router_select(a, t, p);
             }
         }
     }
@@ -562,7 +560,6 @@ SV_DEV void permute_rows_wave(const RowArgs& a, const unsigned short* sel, unsig
 __global__ __launch_bounds__(1024) void route_finish_kernel(RowArgs a)
 {
     __shared__ __align__(16) char lds[81920];
-    __shared__ __align__(16) unsigned long long kscr[16][256 + 8];   // per-wave selection scratch
     const int T = a.T, E = a.E, k = a.topk, tid = threadIdx.x, lane = tid & 63;
     unsigned short* sel = perm_sel_lds(a, lds);
     if (a.S > 1) {
@@ -572,7 +569,7 @@ __global__ __launch_bounds__(1024) void route_finish_kernel(RowArgs a)
             for (int q = 0; q < 4; q++) p[q] = a.logits_g[(size_t)row * E + min(lane + 64 * q, E - 1)];
 #pragma unroll
             for (int q = 0; q < 4; q++) p[q] = lane + 64 * q < E ? p[q] : -INFINITY;
-            router_select(a, row, p, kscr[tid >> 6], sel);
+            router_select(a, row, p, sel);
         }
     } else {
         for (int i = tid; i < T * k; i += 1024) sel[i] = (unsigned short)a.sel[i];
