@@ -334,11 +334,13 @@ constexpr int big_nf(int mode) { return mode == GM_STORE ? 1 : BIG_NF; }
 template <int MODE, bool PK>
 void launch_big_m(int wt, const GemmArgs& a, dim3 grid, hipStream_t s)
 {
+    // (fp32 weights never take the large-row path: it needs bf16 or fp8 weights)
     constexpr int NF = big_nf(MODE);
-    if (wt == SV_F32) launch(gemm_bigm_kernel<SV_F32, BIG_MF, NF, MODE, PK>, grid, dim3(256), 0, s, a);
-    else if (wt == SV_BF16) launch(gemm_bigm_kernel<SV_BF16, BIG_MF, NF, MODE, PK>, grid, dim3(256), 0, s, a);
+    if (wt == SV_BF16) launch(gemm_bigm_kernel<SV_BF16, BIG_MF, NF, MODE, PK>, grid, dim3(256), 0, s, a);
     else if (wt == SV_FP8) launch(gemm_bigm_kernel<SV_FP8, BIG_MF, NF, MODE, PK>, grid, dim3(256), 0, s, a);
-    else if constexpr (PK) launch(gemm_bigm_kernel<SV_MXFP4, BIG_MF, NF, MODE, PK>, grid, dim3(256), 0, s, a);
+    else if constexpr (PK) {
+        if (wt == SV_MXFP4) launch(gemm_bigm_kernel<SV_MXFP4, BIG_MF, NF, MODE, PK>, grid, dim3(256), 0, s, a);
+    }
 }
 
 // Grouped (expert) GEMMs on the large-row kernel: MF row fragments per tile,
@@ -1051,8 +1053,7 @@ static int step_impl(spec_verify_ctx* c, const spec_verify_weights* w, void* k_c
     // QKV, rotary, cache append) is one kernel
     const bool big = T >= 64 && wt != SV_F32;
     if (big && !dp) {
-        if (bf) embed_norm_kernel<true><<<T, 1024, 0, s>>>(ra);
-        else embed_norm_kernel<false><<<T, 1024, 0, s>>>(ra);
+        embed_norm_kernel<true><<<T, 1024, 0, s>>>(ra);   // large rows: bf16 activations
     }
     QkvArgs qa;
     memset(&qa, 0, sizeof(qa));
@@ -1241,8 +1242,7 @@ static int step_impl(spec_verify_ctx* c, const spec_verify_weights* w, void* k_c
             rp.kvp = kvp;
             rp.err_word = c->err_word;
             dim3 grid(T, k.n_q_heads + 2 * k.n_kv_heads);
-            if (bf) launch_rope_append<true>(grid, s, rp);
-            else launch_rope_append<false>(grid, s, rp);
+            launch_rope_append<true>(grid, s, rp);   // large rows: bf16 activations
         }
 
         at.layer = l;
