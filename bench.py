@@ -54,12 +54,12 @@ HBM_PEAK_GBS = 8000.0
 # sources it was measured on (SHA-256 prefix of every .h / .hip file of the
 # library's csrc/, in name order).
 MEASURED_TRAFFIC = {   # the dominant kernel of each workload (see DOMINANT)
-    "moe_b1": {"source_sha": "1dbcb845d99d311e", "read_bytes": 331_100_000, "write_bytes": 65_000},
-    "moe_b32": {"source_sha": "1dbcb845d99d311e", "read_bytes": 305_513_000, "write_bytes": 1_835_000},
+    "moe_b1": {"source_sha": "5718c341cd100a7d", "read_bytes": 331_100_000, "write_bytes": 65_000},
+    "moe_b32": {"source_sha": "5718c341cd100a7d", "read_bytes": 305_513_000, "write_bytes": 1_835_000},
     # the whole 100-step chain (contexts growing as in the benchmark)
-    "moe_b64_long": {"source_sha": "1dbcb845d99d311e", "read_bytes": 1_604_064_000,
+    "moe_b64_long": {"source_sha": "5718c341cd100a7d", "read_bytes": 1_604_064_000,
                      "write_bytes": 13_945_000},
-    "dense_fp8_b8": {"source_sha": "1dbcb845d99d311e", "read_bytes": 124_073_000, "write_bytes": 31_229_000},
+    "dense_fp8_b8": {"source_sha": "5718c341cd100a7d", "read_bytes": 124_073_000, "write_bytes": 31_229_000},
 }
 
 

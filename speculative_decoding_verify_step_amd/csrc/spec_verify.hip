@@ -492,9 +492,22 @@ void launch_attention_lds(int D, int NW, dim3 grid, const AttnArgs& at, hipStrea
 template <bool BF, int DH, bool ST>
 void launch_attention_t(int QPW, dim3 grid, const AttnArgs& at, hipStream_t s)
 {
-    if (QPW == 4) launch(attn_split_kernel<BF, 4, DH, ST>, grid, dim3(64), 0, s, at);
-    else if (QPW == 2) launch(attn_split_kernel<BF, 2, DH, ST>, grid, dim3(64), 0, s, at);
-    else launch(attn_split_kernel<BF, 1, DH, ST>, grid, dim3(64), 0, s, at);
+    if constexpr (BF) {
+        // bf16 caches with 17 .. 256 rows per KV head take the LDS-ring kernel,
+        // so the split kernel sees one fragment per wave, or four above 256
+        // rows (several query groups, never streamed); the plan checks this
+        if constexpr (!ST) {
+            if (QPW == 4) {
+                launch(attn_split_kernel<BF, 4, DH, false>, grid, dim3(64), 0, s, at);
+                return;
+            }
+        }
+        launch(attn_split_kernel<BF, 1, DH, ST>, grid, dim3(64), 0, s, at);
+    } else {
+        if (QPW == 4) launch(attn_split_kernel<BF, 4, DH, ST>, grid, dim3(64), 0, s, at);
+        else if (QPW == 2) launch(attn_split_kernel<BF, 2, DH, ST>, grid, dim3(64), 0, s, at);
+        else launch(attn_split_kernel<BF, 1, DH, ST>, grid, dim3(64), 0, s, at);
+    }
 }
 
 // split-KV attention; streaming K/V loads when each tile has one reader
@@ -750,6 +763,10 @@ int plan_context(spec_verify_ctx* c, const spec_verify_config& cfg, int dev)
         const double kv_bytes = 2.0 * k.max_batch * k.n_layers * k.n_kv_heads * (double)k.kv_capacity *
                                 k.head_dim * (k.kv_dtype == SV_F32 ? 4 : 2);
         c->att_stream = c->att_QG == 1 && kv_bytes > 1024.0 * 1024 * 1024;
+        // the bf16 split kernel exists with one fragment per wave, and with
+        // four for several query groups (launch_attention_t)
+        if (c->bf && !(c->att_QPW == 1 || (c->att_QPW == 4 && !c->att_stream)))
+            return fail(SV_ERR_UNSUPPORTED, "no split-KV attention instance for this shape");
         long work = (long)k.max_batch * k.n_kv_heads * c->att_QG * k.kv_capacity;
         int ch = 64;
         const long waves_target = c->att_QPW >= 4 ? 2048 : 2 * 2048;   // busier waves: fewer of them
