@@ -262,6 +262,16 @@ def test_long_context_batch1_chunk_merge(H, ctx):
     _verify_case(H, cfg, label=f"b1_ctx{ctx}")
 
 
+@pytest.mark.parametrize("ctx", [3000, 9000])
+def test_long_context_fp32_chunk_merge(H, ctx):
+    """The fp32 path at a 3,000- or 9,000-position context: the split-KV
+    kernel's 64-key chunks and the fp32 merge over about 47 or 141 chunk
+    partials per row (two or eight chunk weights per lane)."""
+    cfg = workloads.scaled(workloads.get_config("tiny_fp32"), ctx=("fixed", ctx))
+    stats, _ = _verify_case(H, cfg, label=f"fp32_ctx{ctx}")
+    assert stats["max_rel_logit_err"] < 1e-4
+
+
 def test_mha_head_dim_64(H):
     """Multi-head attention with head dimension 64 (20 heads of 64 over
     hidden 1,280) on the split-KV kernel."""
